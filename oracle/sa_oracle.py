@@ -1,0 +1,268 @@
+"""CPU oracle of the retrieval-sparse attention path -- TEST INFRASTRUCTURE ONLY.
+
+Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may import this module. It shares no code
+with the HIP path (long_context_sparse_sa_amd/), and the HIP path never calls it.
+
+Everything is computed in fp64 from the exactly decoded stored values (fp32, bfloat16 and FP8 E4M3 values are all
+exact in fp64). Library primitives (matmul, sort) serve as steps; nothing is blocked, fused or reordered beyond
+the definitions. Sources, cited by page title and section:
+
+  [LongCat] "LongCat Sparse Attention (LSA) deep-dive" (pinghaoyang.com.cn)
+      - section "DSA baseline: how the lightning indexer works": the indexer score equation, the arg-topK equation
+        and the sparse-attention equation over the latent rows c_s;
+      - section "Mechanism 1: streaming-aware indexing (SI)", sub-section on the budget: the selected set is the
+        disjoint union of sink, sliding window and the top-K of the indexer over the remaining positions;
+        sub-section on the HFA kernel: partial attentions merge exactly by log-sum-exp rescaling.
+  [LSA-8]   "LSA sparse attention: does it save memory? eight QKV entries" (alphalab.site)
+      - section 2: Latent Sparse Attention's four steps (index keys; buckets keeping a representative vector and
+        member positions; Flat search over representatives; read the chosen rows plus sink plus window);
+      - sections 3-4: the eight-entry worked example (stored/read bytes, attention outputs).
+
+Readings taken where the pages are silent (each also listed in the design doc):
+  * positions are 0-based; sink = [0, n_sink), window = [t-n_window+1, t], both clipped to [0, t];
+  * top-k counts only the sparse part and never includes sink or window positions;
+  * ties in the fp32 score go to the lower position; ties in bucket score go to the lower bucket id;
+  * the reported indexer score is the fp64 value rounded once to fp32, and selection orders by that fp32 value;
+  * the bucket score is q . rep (one head, no ReLU, no weight), computed in fp64 and rounded to fp32;
+  * a bucket representative is the fp64 mean of its member keys rounded once to fp32;
+  * an empty read set yields o = 0 and lse = -inf.
+
+Every function below is pinned by tests under tests/ (test_oracle_*.py); none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# ----------------------------------------------------------------------------------------------------------------
+# Storage decoding (format definitions: IEEE-754 binary32; bfloat16 = the upper 16 bits of binary32;
+# OCP 8-bit floating point E4M3 "fn": 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits, subnormals at
+# exponent field 0, no infinities, S.1111.111 is NaN).
+# ----------------------------------------------------------------------------------------------------------------
+
+
+def decode_f32(raw: np.ndarray) -> np.ndarray:
+    return np.asarray(raw, dtype=np.uint32).view(np.float32).astype(np.float64)
+
+
+def decode_bf16(raw: np.ndarray) -> np.ndarray:
+    u = np.asarray(raw, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def decode_e4m3(raw: np.ndarray) -> np.ndarray:
+    u = np.asarray(raw, dtype=np.uint8).astype(np.int64)
+    sign = np.where((u >> 7) & 1, -1.0, 1.0)
+    exp_field = (u >> 3) & 0xF
+    mant = (u & 0x7).astype(np.float64)
+    normal = (1.0 + mant / 8.0) * np.exp2(exp_field.astype(np.float64) - 7.0)
+    subnormal = (mant / 8.0) * np.exp2(-6.0)
+    val = sign * np.where(exp_field == 0, subnormal, normal)
+    return np.where((exp_field == 0xF) & ((u & 0x7) == 0x7), np.nan, val)
+
+
+def decode(raw: np.ndarray, dtype: str) -> np.ndarray:
+    return {"f32": decode_f32, "bf16": decode_bf16, "e4m3": decode_e4m3}[dtype](raw)
+
+
+# ----------------------------------------------------------------------------------------------------------------
+# Position sets ([LongCat] SI section, budget equations; 0-based)
+# ----------------------------------------------------------------------------------------------------------------
+
+
+def sink_positions(t: int, n_sink: int) -> np.ndarray:
+    return np.arange(0, min(n_sink, t + 1), dtype=np.int64)
+
+
+def window_positions(t: int, n_window: int) -> np.ndarray:
+    return np.arange(max(0, t - n_window + 1), t + 1, dtype=np.int64)
+
+
+def candidate_positions(t: int, n_sink: int, n_window: int) -> np.ndarray:
+    """Positions the indexer ranks: [0, t] minus sink minus window."""
+    s = np.arange(0, t + 1, dtype=np.int64)
+    fixed = np.union1d(sink_positions(t, n_sink), window_positions(t, n_window))
+    return np.setdiff1d(s, fixed, assume_unique=True)
+
+
+def read_set(t: int, n_sink: int, n_window: int, sparse) -> np.ndarray:
+    """R = sink U window U sparse, sorted ascending."""
+    fixed = np.union1d(sink_positions(t, n_sink), window_positions(t, n_window))
+    return np.union1d(fixed, np.asarray(sparse, dtype=np.int64))
+
+
+# ----------------------------------------------------------------------------------------------------------------
+# Step a1: the lightning indexer ([LongCat] DSA baseline section, indexer equation)
+#   I_{t,s} = sum_j w_{t,j} * ReLU(q_{t,j} . k_s), one key k_s shared by all heads j.
+# ----------------------------------------------------------------------------------------------------------------
+
+
+def index_score(q: np.ndarray, w: np.ndarray, k: np.ndarray, positions) -> np.ndarray:
+    """fp64 scores of one query over `positions`.
+
+    q: [H, d] fp64 (the query's indexer heads), w: [H] fp64, k: [L, d] fp64, positions: int array.
+    """
+    pos = np.asarray(positions, dtype=np.int64)
+    dots = k[pos] @ q.T                      # [n, H]: q_{t,j} . k_s
+    relu = np.maximum(dots, 0.0)             # ReLU per head
+    return relu @ w                          # sum_j w_{t,j} * ReLU(...)
+
+
+def index_score_f32(q, w, k, positions) -> np.ndarray:
+    """The reported score: the fp64 value rounded once to fp32."""
+    return index_score(q, w, k, positions).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------------------------------------------
+# Step a2: top-k with the sink/window budget ([LongCat] DSA baseline section, arg-topK equation; SI section,
+# sparse-part equation: the indexer ranks only positions outside sink and window)
+# ----------------------------------------------------------------------------------------------------------------
+
+
+def topk_positions(score32: np.ndarray, positions, k: int) -> np.ndarray:
+    """The min(k, n) positions with the largest fp32 score, ties to the lower position, listed ascending."""
+    pos = np.asarray(positions, dtype=np.int64)
+    s = np.asarray(score32, dtype=np.float32).astype(np.float64)
+    order = np.lexsort((pos, -s))            # primary key: score descending; secondary: position ascending
+    return np.sort(pos[order[:min(k, pos.size)]])
+
+
+def kth_score(score32: np.ndarray, positions, k: int) -> float:
+    """The fp32 score of the last selected element (the k-th in (score desc, position asc) order)."""
+    pos = np.asarray(positions, dtype=np.int64)
+    s = np.asarray(score32, dtype=np.float32).astype(np.float64)
+    if pos.size == 0:
+        return float("nan")
+    order = np.lexsort((pos, -s))
+    return float(s[order[min(k, pos.size) - 1]])
+
+
+def select_topk(q, w, k, t: int, k_sparse: int, n_sink: int, n_window: int):
+    """S_sparse for one query: returns (ascending positions, fp32 scores of all candidates, candidate positions)."""
+    cand = candidate_positions(t, n_sink, n_window)
+    sc = index_score_f32(q, w, k, cand)
+    return topk_positions(sc, cand, k_sparse), sc, cand
+
+
+# ----------------------------------------------------------------------------------------------------------------
+# Step a0: the bucket directory ([LSA-8] section 2, step 2: a representative vector and member positions)
+# ----------------------------------------------------------------------------------------------------------------
+
+
+def bucket_build(k: np.ndarray, assign: np.ndarray, n_buckets: int):
+    """Returns (reps [NB, d] fp32, offsets [NB+1] int64, members [L] int64).
+
+    members lists positions grouped by bucket, ascending inside each bucket (a stable sort by bucket id);
+    reps[c] is the fp64 mean of k over bucket c's members rounded once to fp32 (zeros for an empty bucket).
+    """
+    assign = np.asarray(assign, dtype=np.int64)
+    counts = np.bincount(assign, minlength=n_buckets)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    members = np.argsort(assign, kind="stable").astype(np.int64)
+    d = k.shape[1]
+    sums = np.zeros((n_buckets, d), dtype=np.float64)
+    nonempty = np.nonzero(counts)[0]
+    if nonempty.size:
+        sums[nonempty] = np.add.reduceat(k[members], offsets[nonempty], axis=0)
+    reps = np.zeros((n_buckets, d), dtype=np.float64)
+    reps[nonempty] = sums[nonempty] / counts[nonempty, None]
+    return reps.astype(np.float32), offsets, members
+
+
+# ----------------------------------------------------------------------------------------------------------------
+# Steps a3 + a4: Flat search over the representatives and expansion to member positions
+# ([LSA-8] section 2, steps 3-4)
+# ----------------------------------------------------------------------------------------------------------------
+
+
+def bucket_scores_f32(q: np.ndarray, reps32: np.ndarray) -> np.ndarray:
+    """q . rep_c for every bucket, fp64 rounded to fp32."""
+    return (np.asarray(reps32, dtype=np.float64) @ q).astype(np.float32)
+
+
+def top_buckets(score32: np.ndarray, offsets: np.ndarray, top_b: int) -> np.ndarray:
+    """The top_b non-empty buckets by (score desc, id asc), in that order."""
+    counts = np.diff(offsets)
+    ids = np.nonzero(counts > 0)[0]
+    s = np.asarray(score32, dtype=np.float32).astype(np.float64)[ids]
+    order = np.lexsort((ids, -s))
+    return ids[order[:min(top_b, ids.size)]]
+
+
+def bucket_select(q, reps32, offsets, members, t: int, top_b: int, n_sink: int, n_window: int):
+    """Returns (ascending sparse positions, chosen bucket ids, bucket scores)."""
+    sc = bucket_scores_f32(q, reps32)
+    chosen = top_buckets(sc, offsets, top_b)
+    if chosen.size:
+        pos = np.concatenate([members[offsets[c]:offsets[c + 1]] for c in chosen])
+    else:
+        pos = np.zeros(0, dtype=np.int64)
+    pos = pos[pos <= t]
+    fixed = np.union1d(sink_positions(t, n_sink), window_positions(t, n_window))
+    pos = np.setdiff1d(pos, fixed)
+    return np.sort(pos), chosen, sc
+
+
+# ----------------------------------------------------------------------------------------------------------------
+# Step a5: attention over the read set ([LongCat] DSA baseline section, sparse-attention equation over the
+# latent rows c_s shared by all query heads; [LSA-8] section 4: score q.k * scale, softmax, weighted V)
+# ----------------------------------------------------------------------------------------------------------------
+
+
+def attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float):
+    """Softmax attention of H heads over n rows. q [H, d_qk], K [n, d_qk], V [n, d_v] -> (o [H, d_v], lse [H])."""
+    H = q.shape[0]
+    if K.shape[0] == 0:
+        return np.zeros((H, V.shape[1])), np.full(H, -np.inf)
+    z = scale * (q @ K.T)                      # [H, n]
+    m = z.max(axis=1, keepdims=True)
+    e = np.exp(z - m)
+    Z = e.sum(axis=1, keepdims=True)
+    o = (e @ V) / Z
+    lse = (m + np.log(Z))[:, 0]
+    return o, lse
+
+
+def sparse_attn(q, kv, R, scale: float, d_qk: int, d_v: int, v=None):
+    """o over the rows R of the latent cache: K = kv[R, :d_qk], V = kv[R, :d_v] (or v[R, :d_v])."""
+    R = np.asarray(R, dtype=np.int64)
+    K = kv[R, :d_qk]
+    V = (v[R, :d_v] if v is not None else kv[R, :d_v])
+    return attention(q, K, V, scale)
+
+
+def merge_lse(parts):
+    """Exact merge of partial attentions over disjoint row sets by their log-sum-exp ([LongCat] SI section, HFA).
+
+    parts: list of (o [H, d_v], lse [H]). Returns (o, lse).
+    """
+    lses = np.stack([p[1] for p in parts])            # [P, H]
+    m = lses.max(axis=0)
+    finite = np.isfinite(m)
+    msafe = np.where(finite, m, 0.0)
+    wts = np.where(np.isfinite(lses), np.exp(lses - msafe), 0.0)
+    tot = wts.sum(axis=0)
+    o = sum(wts[i][:, None] * parts[i][0] for i in range(len(parts)))
+    o = np.where(tot[:, None] > 0, o / np.where(tot > 0, tot, 1.0)[:, None], 0.0)
+    lse = np.where(tot > 0, msafe + np.log(np.where(tot > 0, tot, 1.0)), -np.inf)
+    return o, lse
+
+
+# ----------------------------------------------------------------------------------------------------------------
+# One decode/prefill step of the whole path for one query
+# ----------------------------------------------------------------------------------------------------------------
+
+
+def dsa_step(q_idx, w, k_idx, q, kv, t: int, k_sparse: int, n_sink: int, n_window: int, scale: float,
+             d_qk: int, d_v: int):
+    sel, _, _ = select_topk(q_idx, w, k_idx, t, k_sparse, n_sink, n_window)
+    R = read_set(t, n_sink, n_window, sel)
+    o, lse = sparse_attn(q, kv, R, scale, d_qk, d_v)
+    return sel, o, lse
+
+
+def bucket_step(q_idx, reps32, offsets, members, q, kv, t: int, top_b: int, n_sink: int, n_window: int,
+                scale: float, d_qk: int, d_v: int):
+    sel, chosen, _ = bucket_select(q_idx, reps32, offsets, members, t, top_b, n_sink, n_window)
+    R = read_set(t, n_sink, n_window, sel)
+    o, lse = sparse_attn(q, kv, R, scale, d_qk, d_v)
+    return sel, chosen, o, lse
