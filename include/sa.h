@@ -94,10 +94,12 @@ SA_API int sa_index_score(const void* q, int q_dtype, const float* w, const void
  *   n_sel  [B] int32: |S_sparse,b|.
  *   The sink and window are not listed in idx; pass the same n_sink/n_window to sa_sparse_attn.
  *   k_sparse >= 1, n_sink >= 0, n_window >= 0. L < 2^31.
- *   ws / ws_bytes: workspace of at least sa_select_topk_workspace(L, B, H, k_sparse, algo) bytes.
- *   algo: an sa_topk_algo value.
+ *   ws / ws_bytes: workspace of at least sa_select_topk_workspace(L, B, H, d, q_dtype, k_dtype, k_sparse, algo)
+ *   bytes. 1 <= k_sparse <= 16384.
+ *   algo: an sa_topk_algo value; SA_TOPK_PER_QUERY needs d = 128, H in {32, 64} and bf16 or e4m3 inputs.
  * ------------------------------------------------------------------------------------------------------------- */
-SA_API size_t sa_select_topk_workspace(int64_t L, int32_t B, int32_t H, int32_t k_sparse, int algo);
+SA_API size_t sa_select_topk_workspace(int64_t L, int32_t B, int32_t H, int32_t d, int q_dtype, int k_dtype,
+                                       int32_t k_sparse, int algo);
 SA_API int sa_select_topk(const void* q, int q_dtype, const float* w, const void* k, int k_dtype, int64_t k_ld,
                           int64_t L, int32_t B, int32_t H, int32_t d, const int32_t* t, int32_t k_sparse,
                           int32_t n_sink, int32_t n_window, int32_t* idx, int32_t idx_ld, int32_t* n_sel,
@@ -127,7 +129,8 @@ SA_API int sa_bucket_build(const void* k, int k_dtype, int64_t k_ld, int64_t L, 
  *   idx      [B, cap] int32 out: ascending positions, -1 padding. n_sel [B] out: count, or -(needed count) when
  *            the expansion does not fit in cap (idx then holds no valid entries for that query).
  *   buckets_out [B, top_b] int32 out or NULL: chosen bucket ids in (score desc, id asc) order, -1 padding.
- *   1 <= top_b <= n_buckets; top_b <= 1024.
+ *   1 <= top_b <= n_buckets; top_b <= 1024; 1 <= cap <= 16384. assign/offsets/members must be as
+ *   sa_bucket_build wrote them (values outside [0, n_buckets) are undefined behaviour).
  *   ws / ws_bytes: at least sa_bucket_select_workspace(B, n_buckets, top_b) bytes.
  * ------------------------------------------------------------------------------------------------------------- */
 SA_API size_t sa_bucket_select_workspace(int32_t B, int32_t n_buckets, int32_t top_b);
@@ -145,6 +148,7 @@ SA_API int sa_bucket_select(const void* q, int q_dtype, int32_t B, int32_t d, co
  * are contiguous ranges; partial results over disjoint row subsets are merged exactly by their log-sum-exp
  * ([LongCat] SI section, HFA: online-softmax rescaling of the partial outputs).
  *   q    [B, H, d_qk] contiguous, dtype `dtype`     kv [L, kv_ld]     v [L, v_ld] or NULL
+ *   d_v <= 1024.
  *   dtype: F32 or BF16 for q, kv, v and out.
  *   idx  [B, idx_ld] int32: sparse positions; only the first clamp(n_sel[b], 0, idx_ld) entries are read. They
  *        must be distinct, inside [0, t_b] and outside sink_b and window_b (as sa_select_topk and

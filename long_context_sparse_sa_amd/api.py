@@ -1,0 +1,161 @@
+"""Thin torch-facing binding of the C ABI in include/sa.h: same names, argument marshalling only.
+
+Every function checks dtypes, shapes and devices, allocates outputs and workspace with torch (device memory is the
+caller's), and calls the HIP library on torch's current stream. No step of the method runs here.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+_DT = {torch.float32: _lib.SA_F32, torch.bfloat16: _lib.SA_BF16, torch.float8_e4m3fn: _lib.SA_E4M3}
+
+
+def _dtype(x: torch.Tensor) -> int:
+    if x.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {x.dtype}")
+    return _DT[x.dtype]
+
+
+def _ptr(x: Optional[torch.Tensor]) -> Optional[int]:
+    return None if x is None else x.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _need_cuda(*xs):
+    for x in xs:
+        if x is not None and not x.is_cuda:
+            raise ValueError("all tensors must live on the GPU")
+
+
+def _rows(x: torch.Tensor) -> int:
+    """Leading dimension (elements) of a 2-D row-major tensor whose rows may be padded."""
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("expected a 2-D tensor with unit column stride")
+    return x.stride(0)
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return ws
+    if ws is not None:
+        if ws.numel() * ws.element_size() < nbytes:
+            raise ValueError(f"workspace too small: need {nbytes} bytes")
+        return ws
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------------------------------------------------------
+
+
+def sa_index_score(q_idx, w, k_idx, t=None, s_begin: int = 0, s_end: Optional[int] = None, out=None, stream=None):
+    """scores[b, s - s_begin] of the lightning indexer over positions [s_begin, s_end) (-inf past t_b)."""
+    _need_cuda(q_idx, w, k_idx, t, out)
+    B, H, d = q_idx.shape
+    L = k_idx.shape[0]
+    s_end = L if s_end is None else s_end
+    if out is None:
+        out = torch.empty((B, max(1, s_end - s_begin)), dtype=torch.float32, device=q_idx.device)
+    st = _lib.load().sa_index_score(_ptr(q_idx), _dtype(q_idx), _ptr(w), _ptr(k_idx), _dtype(k_idx), _rows(k_idx), L,
+                                    B, H, d, _ptr(t), s_begin, s_end, _ptr(out), out.stride(0), _stream(stream))
+    _lib.check("sa_index_score", st)
+    return out[:, : s_end - s_begin]
+
+
+def sa_select_topk_workspace(L, B, H, d, q_dtype, k_dtype, k_sparse, algo=_lib.SA_TOPK_AUTO) -> int:
+    return int(_lib.load().sa_select_topk_workspace(L, B, H, d, q_dtype, k_dtype, k_sparse, algo))
+
+
+def sa_select_topk(q_idx, w, k_idx, k_sparse: int, n_sink: int = 0, n_window: int = 0, t=None,
+                   idx_ld: Optional[int] = None, algo: int = _lib.SA_TOPK_AUTO, ws=None, out=None, stream=None):
+    """(idx [B, idx_ld] ascending with -1 padding, n_sel [B]) of the top-k candidates outside sink and window."""
+    _need_cuda(q_idx, w, k_idx, t)
+    B, H, d = q_idx.shape
+    L = k_idx.shape[0]
+    idx_ld = k_sparse if idx_ld is None else idx_ld
+    lib = _lib.load()
+    nbytes = lib.sa_select_topk_workspace(L, B, H, d, _dtype(q_idx), _dtype(k_idx), k_sparse, algo)
+    ws = _workspace(nbytes, q_idx.device, ws)
+    if out is None:
+        idx = torch.empty((B, idx_ld), dtype=torch.int32, device=q_idx.device)
+        n_sel = torch.empty((B,), dtype=torch.int32, device=q_idx.device)
+    else:
+        idx, n_sel = out
+    st = lib.sa_select_topk(_ptr(q_idx), _dtype(q_idx), _ptr(w), _ptr(k_idx), _dtype(k_idx), _rows(k_idx), L, B, H, d,
+                            _ptr(t), k_sparse, n_sink, n_window, _ptr(idx), idx.stride(0), _ptr(n_sel), _ptr(ws),
+                            nbytes, algo, _stream(stream))
+    _lib.check("sa_select_topk", st)
+    return idx, n_sel
+
+
+def sa_bucket_build(k_idx, assign, n_buckets: int, ws=None, stream=None):
+    """(reps [NB, d] fp32, offsets [NB + 1] int32, members [L] int32) of the bucket directory."""
+    _need_cuda(k_idx, assign)
+    L, d = k_idx.shape
+    lib = _lib.load()
+    nbytes = lib.sa_bucket_build_workspace(L, n_buckets)
+    ws = _workspace(nbytes, k_idx.device, ws)
+    reps = torch.empty((n_buckets, d), dtype=torch.float32, device=k_idx.device)
+    offsets = torch.empty((n_buckets + 1,), dtype=torch.int32, device=k_idx.device)
+    members = torch.empty((L,), dtype=torch.int32, device=k_idx.device)
+    st = lib.sa_bucket_build(_ptr(k_idx), _dtype(k_idx), _rows(k_idx), L, d, _ptr(assign), n_buckets, _ptr(reps),
+                             _ptr(offsets), _ptr(members), _ptr(ws), nbytes, _stream(stream))
+    _lib.check("sa_bucket_build", st)
+    return reps, offsets, members
+
+
+def sa_bucket_select(q_idx, reps, offsets, members, L: int, top_b: int, n_sink: int = 0, n_window: int = 0,
+                     cap: int = 8192, t=None, return_buckets: bool = False, ws=None, stream=None):
+    """(idx [B, cap] ascending with -1 padding, n_sel [B] (negative: -needed on overflow)[, buckets [B, top_b]])."""
+    _need_cuda(q_idx, reps, offsets, members, t)
+    B, d = q_idx.shape
+    nb = reps.shape[0]
+    lib = _lib.load()
+    nbytes = lib.sa_bucket_select_workspace(B, nb, top_b)
+    ws = _workspace(nbytes, q_idx.device, ws)
+    idx = torch.empty((B, cap), dtype=torch.int32, device=q_idx.device)
+    n_sel = torch.empty((B,), dtype=torch.int32, device=q_idx.device)
+    buckets = torch.empty((B, top_b), dtype=torch.int32, device=q_idx.device) if return_buckets else None
+    st = lib.sa_bucket_select(_ptr(q_idx), _dtype(q_idx), B, d, _ptr(reps), _ptr(offsets), _ptr(members), nb, L,
+                              _ptr(t), top_b, n_sink, n_window, _ptr(idx), cap, _ptr(n_sel), _ptr(buckets), _ptr(ws),
+                              nbytes, _stream(stream))
+    _lib.check("sa_bucket_select", st)
+    return (idx, n_sel, buckets) if return_buckets else (idx, n_sel)
+
+
+def sa_sparse_attn_workspace(B, H, d_qk, d_v, max_rows, dtype) -> int:
+    return int(_lib.load().sa_sparse_attn_workspace(B, H, d_qk, d_v, max_rows, dtype))
+
+
+def sa_sparse_attn(q, kv, idx=None, n_sel=None, n_sink: int = 0, n_window: int = 0, scale: Optional[float] = None,
+                   t=None, v=None, d_v: Optional[int] = None, return_lse: bool = False, ws=None, out=None,
+                   stream=None):
+    """o [B, H, d_v] (and lse [B, H]) of softmax attention over sink U window U idx[b, :n_sel[b]]."""
+    _need_cuda(q, kv, idx, n_sel, t, v)
+    B, H, d_qk = q.shape
+    L = kv.shape[0]
+    if d_v is None:
+        d_v = v.shape[1] if v is not None else d_qk
+    scale = 1.0 / math.sqrt(d_qk) if scale is None else scale
+    idx_ld = idx.stride(0) if idx is not None else 0
+    lib = _lib.load()
+    max_rows = n_sink + n_window + idx_ld
+    nbytes = lib.sa_sparse_attn_workspace(B, H, d_qk, d_v, max_rows, _dtype(q))
+    ws = _workspace(nbytes, q.device, ws)
+    if out is None:
+        out = torch.empty((B, H, d_v), dtype=q.dtype, device=q.device)
+    lse = torch.empty((B, H), dtype=torch.float32, device=q.device) if return_lse else None
+    st = lib.sa_sparse_attn(_ptr(q), _ptr(kv), _ptr(v), _dtype(q), _rows(kv), _rows(v) if v is not None else 0, L, B,
+                            H, d_qk, d_v, _ptr(t), _ptr(idx), idx_ld, _ptr(n_sel), n_sink, n_window, float(scale),
+                            _ptr(out), _ptr(lse), _ptr(ws), nbytes, _stream(stream))
+    _lib.check("sa_sparse_attn", st)
+    return (out, lse) if return_lse else out

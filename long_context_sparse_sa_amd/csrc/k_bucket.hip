@@ -1,0 +1,297 @@
+// Bucket directory and Flat bucket search of Latent Sparse Attention (LSA eight-entry page, section 2: index keys
+// are grouped into buckets that keep a representative vector and their member positions; the Flat variant compares
+// the query with every representative; the chosen buckets expand to their positions, and sink and window positions
+// are read in addition).
+//
+// Build (once per cache):
+//   counts (atomics) -> offsets (exclusive scan) -> per-chunk bucket counts -> per-(chunk, bucket) start indices
+//   -> stable scatter (one wave per chunk, positions in ascending order) -> representatives (fp64 sums, one wave
+//   per bucket, rounded once to fp32).
+// Select (per step):
+//   one wave per bucket scores q . rep for every query and emits (key, bucket) candidates -> the exact top-b merge
+//   (ties to the lower bucket id) -> expansion of the chosen buckets' member ranges inside [sink end, window start)
+//   and an ascending sort in LDS.
+#include "sa_device.h"
+#include "sa_internal.h"
+
+namespace sa {
+namespace {
+
+constexpr int kChunkMin = 4096;
+constexpr int64_t kTableBudget = 1 << 24;  // entries of the (chunk x bucket) table
+constexpr int kMaxExpand = 16384;
+
+__global__ void k_fill_i32(int32_t* p, int64_t n, int32_t v) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
+}
+
+__global__ void k_count(const int32_t* __restrict__ assign, int64_t L, int32_t* __restrict__ counts) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < L; i += (int64_t)gridDim.x * blockDim.x)
+    atomicAdd(&counts[assign[i]], 1);
+}
+
+// Single-workgroup exclusive scan: offsets[c] = sum_{c' < c} counts[c'], offsets[nb] = total.
+__global__ __launch_bounds__(1024) void k_offsets(const int32_t* __restrict__ counts, int nb, int32_t* __restrict__ offsets) {
+  __shared__ int32_t part[1024];
+  const int tid = threadIdx.x;
+  const int per = (nb + 1023) / 1024;
+  const int lo = tid * per, hi = lo + per < nb ? lo + per : nb;
+  int32_t s = 0;
+  for (int i = lo; i < hi; ++i) s += counts[i];
+  part[tid] = s;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int32_t v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int32_t run = tid > 0 ? part[tid - 1] : 0;
+  for (int i = lo; i < hi; ++i) {
+    offsets[i] = run;
+    run += counts[i];
+  }
+  if (tid == 1023) offsets[nb] = part[1023];
+}
+
+__global__ void k_chunk_hist(const int32_t* __restrict__ assign, int64_t L, int64_t chunk, int nb,
+                             int32_t* __restrict__ table) {
+  const int64_t c = blockIdx.x;
+  const int64_t lo = c * chunk, hi = lo + chunk < L ? lo + chunk : L;
+  for (int64_t i = lo + threadIdx.x; i < hi; i += blockDim.x) atomicAdd(&table[c * nb + assign[i]], 1);
+}
+
+// table[chunk][c] <- offsets[c] + sum of the bucket's counts in earlier chunks
+__global__ void k_chunk_scan(const int32_t* __restrict__ offsets, int nb, int64_t n_chunks, int32_t* __restrict__ table) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= nb) return;
+  int32_t run = offsets[c];
+  for (int64_t ch = 0; ch < n_chunks; ++ch) {
+    const int32_t v = table[ch * nb + c];
+    table[ch * nb + c] = run;
+    run += v;
+  }
+}
+
+// Stable scatter: one wave walks its chunk in ascending position order, 64 positions at a time. A lane's slot in
+// its bucket is the bucket's running start plus the number of lower lanes with the same bucket.
+__global__ __launch_bounds__(64) void k_scatter(const int32_t* __restrict__ assign, int64_t L, int64_t chunk, int nb,
+                                                int32_t* __restrict__ table, int32_t* __restrict__ members) {
+  const int64_t c = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int64_t lo = c * chunk, hi = lo + chunk < L ? lo + chunk : L;
+  int32_t* row = table + c * nb;
+  for (int64_t base = lo; base < hi; base += kWave) {
+    const int64_t s = base + lane;
+    const bool valid = s < hi;
+    const int a = valid ? assign[s] : -1;
+    int rank = 0;
+    bool last = valid;
+    for (int j = 0; j < kWave; ++j) {
+      const int other = __shfl(a, j, kWave);
+      if (other == a) {
+        if (j < lane) ++rank;
+        if (j > lane) last = false;
+      }
+    }
+    int32_t start = 0;
+    if (valid) start = row[a];
+    if (valid) members[start + rank] = (int32_t)s;
+    wait_vmem();
+    __builtin_amdgcn_wave_barrier();
+    if (last) row[a] = start + rank + 1;
+    wait_vmem();
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// One wave per bucket: rep = (float)(sum of member keys in fp64 / count).
+template <int KT>
+__global__ __launch_bounds__(256) void k_reps(const void* __restrict__ k, int64_t k_ld, int d,
+                                              const int32_t* __restrict__ offsets, const int32_t* __restrict__ members,
+                                              int nb, float* __restrict__ reps) {
+  const int bucket = blockIdx.x * 4 + threadIdx.x / kWave;
+  const int lane = lane_id();
+  if (bucket >= nb) return;
+  const int lo = offsets[bucket], hi = offsets[bucket + 1];
+  for (int x0 = 0; x0 < d; x0 += kWave) {
+    const int x = x0 + lane;
+    double sum = 0.0;
+    if (x < d)
+      for (int i = lo; i < hi; ++i) sum += (double)load_elem<KT>(k, (int64_t)members[i] * k_ld + x);
+    if (x < d) reps[(int64_t)bucket * d + x] = hi > lo ? (float)(sum / (double)(hi - lo)) : 0.f;
+  }
+}
+
+// One wave per bucket scores every query (fp32 dot), emitting (key, bucket) for non-empty buckets into the
+// workgroup's segment of each query (segment capacity 4 = buckets per workgroup).
+template <int QT>
+__global__ __launch_bounds__(256) void k_bucket_scores(const void* __restrict__ q, int B, int d,
+                                                       const float* __restrict__ reps,
+                                                       const int32_t* __restrict__ offsets, int nb,
+                                                       uint32_t* __restrict__ seg_cnt, Cand* __restrict__ seg_data) {
+  extern __shared__ float qs[];  // [B * d]
+  __shared__ uint32_t cnt[4];
+  for (int i = threadIdx.x; i < B * d; i += blockDim.x) qs[i] = load_elem<QT>(q, i);
+  __syncthreads();
+  const int wave = threadIdx.x / kWave, lane = lane_id();
+  const int bucket = blockIdx.x * 4 + wave;
+  const bool valid = bucket < nb && offsets[bucket + 1] > offsets[bucket];
+  for (int b = 0; b < B; ++b) {
+    float acc = 0.f;
+    if (valid)
+      for (int x = lane; x < d; x += kWave) acc = fmaf(qs[b * d + x], reps[(int64_t)bucket * d + x], acc);
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, kWave);
+    // wave 0 collects the workgroup's candidates for query b in bucket order
+    if (lane == 0) cnt[wave] = valid ? 1u : 0u;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t n = 0;
+      for (int w = 0; w < 4; ++w) n += cnt[w];
+      seg_cnt[(int64_t)b * gridDim.x + blockIdx.x] = n;
+    }
+    if (lane == 0 && valid) {
+      uint32_t slot = 0;
+      for (int w = 0; w < wave; ++w) slot += cnt[w];
+      seg_data[((int64_t)b * gridDim.x + blockIdx.x) * 4 + slot] = Cand{score_key(acc), bucket};
+    }
+    __syncthreads();
+  }
+}
+
+// Expansion: the kept positions of a chosen bucket form the sub-range of its (ascending) member list inside
+// [lo, hi) with lo = end of the sink and hi = start of the window (which also excludes positions after t).
+__device__ __forceinline__ int lower_bound(const int32_t* a, int n, int32_t x) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (a[mid] < x) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(1024) void k_expand(const int32_t* __restrict__ chosen, const int32_t* __restrict__ n_chosen,
+                                                 int top_b, const int32_t* __restrict__ offsets,
+                                                 const int32_t* __restrict__ members, int64_t L,
+                                                 const int32_t* __restrict__ t, int n_sink, int n_window,
+                                                 int32_t* __restrict__ idx, int cap, int32_t* __restrict__ n_sel) {
+  __shared__ int32_t rng_lo[1024], rng_n[1024], rng_base[1024];
+  __shared__ int32_t buf[kMaxExpand];
+  __shared__ int32_t total_s;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int tb = t ? t[b] : (int)(L - 1);
+  const int ns = n_sink < tb + 1 ? n_sink : tb + 1;
+  int w0 = tb - n_window + 1;
+  w0 = w0 > ns ? w0 : ns;
+  const int nc = n_chosen[b];
+  if (tid < nc) {
+    const int c = chosen[(int64_t)b * top_b + tid];
+    const int o0 = offsets[c], o1 = offsets[c + 1];
+    const int a = lower_bound(members + o0, o1 - o0, ns);
+    const int z = lower_bound(members + o0, o1 - o0, w0);
+    rng_lo[tid] = o0 + a;
+    rng_n[tid] = z - a;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int i = 0; i < nc; ++i) {
+      rng_base[i] = run;
+      run += rng_n[i];
+    }
+    total_s = run;
+  }
+  __syncthreads();
+  const int total = total_s;
+  int32_t* out = idx + (int64_t)b * cap;
+  if (total > cap) {
+    for (int i = tid; i < cap; i += 1024) out[i] = -1;
+    if (tid == 0) n_sel[b] = -total;
+    return;
+  }
+  int n2 = 1;
+  while (n2 < total) n2 <<= 1;
+  for (int i = tid; i < n2; i += 1024) buf[i] = 0x7FFFFFFF;
+  __syncthreads();
+  for (int i = 0; i < nc; ++i)
+    for (int j = tid; j < rng_n[i]; j += 1024) buf[rng_base[i] + j] = members[rng_lo[i] + j];
+  __syncthreads();
+  for (int size = 2; size <= n2; size <<= 1)
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < (n2 >> 1); i += 1024) {
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool up = (lo & size) == 0;
+        const int32_t x = buf[lo], y = buf[hi];
+        if ((x > y) == up) {
+          buf[lo] = y;
+          buf[hi] = x;
+        }
+      }
+      __syncthreads();
+    }
+  for (int i = tid; i < cap; i += 1024) out[i] = i < total ? buf[i] : -1;
+  if (tid == 0) n_sel[b] = total;
+}
+
+}  // namespace
+
+BucketBuildPlan bucket_build_plan(int64_t L, int32_t nb) {
+  BucketBuildPlan p;
+  int64_t max_chunks = kTableBudget / (nb > 0 ? nb : 1);
+  if (max_chunks < 1) max_chunks = 1;
+  int64_t chunk = (L + max_chunks - 1) / max_chunks;
+  if (chunk < kChunkMin) chunk = kChunkMin;
+  chunk = (chunk + kWave - 1) / kWave * kWave;
+  p.chunk = chunk;
+  p.n_chunks = L > 0 ? (L + chunk - 1) / chunk : 0;
+  return p;
+}
+
+hipError_t launch_bucket_build(const void* k, int k_dtype, int64_t k_ld, int64_t L, int d, const int32_t* assign,
+                               int nb, float* reps, int32_t* offsets, int32_t* members, int32_t* counts,
+                               int32_t* table, const BucketBuildPlan& p, hipStream_t st) {
+  const int64_t tbl = p.n_chunks * (int64_t)nb;
+  hipLaunchKernelGGL(k_fill_i32, dim3(256), dim3(256), 0, st, counts, (int64_t)nb, 0);
+  if (tbl > 0) hipLaunchKernelGGL(k_fill_i32, dim3(1024), dim3(256), 0, st, table, tbl, 0);
+  if (L > 0) hipLaunchKernelGGL(k_count, dim3(1024), dim3(256), 0, st, assign, L, counts);
+  hipLaunchKernelGGL(k_offsets, dim3(1), dim3(1024), 0, st, counts, nb, offsets);
+  if (L > 0) {
+    hipLaunchKernelGGL(k_chunk_hist, dim3((unsigned)p.n_chunks), dim3(256), 0, st, assign, L, p.chunk, nb, table);
+    hipLaunchKernelGGL(k_chunk_scan, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, st, offsets, nb, p.n_chunks, table);
+    hipLaunchKernelGGL(k_scatter, dim3((unsigned)p.n_chunks), dim3(64), 0, st, assign, L, p.chunk, nb, table, members);
+  }
+  if (k_dtype == 0)
+    hipLaunchKernelGGL(k_reps<0>, dim3((unsigned)((nb + 3) / 4)), dim3(256), 0, st, k, k_ld, d, offsets, members, nb, reps);
+  else
+    hipLaunchKernelGGL(k_reps<1>, dim3((unsigned)((nb + 3) / 4)), dim3(256), 0, st, k, k_ld, d, offsets, members, nb, reps);
+  return hipGetLastError();
+}
+
+int bucket_expand_max() { return kMaxExpand; }
+int bucket_score_wgs(int nb) { return (nb + 3) / 4; }
+
+hipError_t launch_bucket_select(const void* q, int q_dtype, int B, int d, const float* reps, const int32_t* offsets,
+                                const int32_t* members, int nb, int64_t L, const int32_t* t, int top_b, int n_sink,
+                                int n_window, int32_t* idx, int cap, int32_t* n_sel, int32_t* buckets_out,
+                                uint32_t* seg_cnt, Cand* seg_data, int32_t* n_chosen, Cand* gather, int32_t* chosen,
+                                hipStream_t st) {
+  const int n_wg = bucket_score_wgs(nb);
+  const size_t lds = sizeof(float) * (size_t)B * d;
+  if (q_dtype == 0)
+    hipLaunchKernelGGL(k_bucket_scores<0>, dim3((unsigned)n_wg), dim3(256), lds, st, q, B, d, reps, offsets, nb, seg_cnt, seg_data);
+  else
+    hipLaunchKernelGGL(k_bucket_scores<1>, dim3((unsigned)n_wg), dim3(256), lds, st, q, B, d, reps, offsets, nb, seg_cnt, seg_data);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  int32_t* order = buckets_out ? buckets_out : chosen;
+  e = launch_merge(B, top_b, nullptr, 0, nullptr, seg_cnt, seg_data, n_wg, 4, gather, (int64_t)n_wg * 4, nullptr,
+                   nullptr, nullptr, 2, order, top_b, n_chosen, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_expand, dim3((unsigned)B), dim3(1024), 0, st, order, n_chosen, top_b, offsets, members, L, t,
+                     n_sink, n_window, idx, cap, n_sel);
+  return hipGetLastError();
+}
+
+}  // namespace sa

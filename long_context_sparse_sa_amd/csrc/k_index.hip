@@ -1,0 +1,394 @@
+// Lightning-indexer scoring for gfx950 (LongCat Sparse Attention deep-dive, DSA baseline section, indexer
+// equation): I(b, s) = sum_j w[b, j] * ReLU(q[b, j, :] . k[s, :]), one key row shared by all heads, no scale.
+//
+// Two kernels:
+//  * k_score_valu  -- any head count, width and dtype; one thread per position, fp32 accumulation.
+//  * k_score_mfma  -- d = 128 and H in {32, 64}: the (query-head x position) dot products are a dense contraction
+//    and run on the bf16 32x32x16 MFMA, one wave per query so that the ReLU-weighted head sum stays inside the
+//    wave. Key tiles of 64 positions are staged in LDS (bf16 rows by asynchronous DMA; e4m3 rows converted exactly
+//    to bf16 on the way in) and shared by the workgroup's four waves (four queries).
+// Both kernels either write the dense score row or emit only candidates whose score beats the caller's running
+// threshold, so a decode step never writes the [B, L] score matrix.
+#include <type_traits>
+
+#include "sa_device.h"
+#include "sa_internal.h"
+#include "sa_wave_select.h"
+
+namespace sa {
+namespace {
+
+constexpr int kValuKeysPerWg = 256;
+constexpr int kMfmaKeysPerWg = 512;
+constexpr int kTileKeys = 64;
+
+__device__ __forceinline__ bool is_candidate(int64_t s, int64_t t, int n_sink, int n_window) {
+  return s >= n_sink && s <= t - n_window;
+}
+
+template <int QT, int KT>
+__global__ __launch_bounds__(256) void k_score_valu(const void* __restrict__ q, const float* __restrict__ w,
+                                                    const void* __restrict__ k, int64_t k_ld, int64_t L, int H,
+                                                    int d, const int32_t* __restrict__ t, int64_t lo, int64_t hi,
+                                                    int mode, float* __restrict__ scores, int64_t scores_ld,
+                                                    int n_sink, int n_window, const uint32_t* __restrict__ thr_key,
+                                                    uint32_t* __restrict__ seg_cnt, Cand* __restrict__ seg_data) {
+  extern __shared__ float smem[];
+  float* qs = smem;            // [H * d]
+  float* ws = smem + H * d;    // [H]
+  __shared__ int n_emit;
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < H * d; i += blockDim.x) qs[i] = load_elem<QT>(q, (int64_t)b * H * d + i);
+  for (int i = tid; i < H; i += blockDim.x) ws[i] = w[(int64_t)b * H + i];
+  if (tid == 0) n_emit = 0;
+  __syncthreads();
+
+  const int64_t s = lo + (int64_t)blockIdx.x * kValuKeysPerWg + tid;
+  const int64_t tb = t ? (int64_t)t[b] : L - 1;
+  float score = 0.f;
+  if (s < hi) {
+    const int64_t row = s * k_ld;
+    for (int j = 0; j < H; ++j) {
+      float dot = 0.f;
+      for (int x = 0; x < d; ++x) dot = fmaf(qs[j * d + x], load_elem<KT>(k, row + x), dot);
+      score = fmaf(ws[j], fmaxf(dot, 0.f), score);
+    }
+  }
+  if (mode == kScoreDense) {
+    if (s < hi) scores[(int64_t)b * scores_ld + (s - lo)] = (s <= tb) ? score : -INFINITY;
+    return;
+  }
+  const uint32_t key = score_key(score);
+  const bool emit = s < hi && is_candidate(s, tb, n_sink, n_window) && key > thr_key[b];
+  const int64_t seg = (int64_t)b * gridDim.x + blockIdx.x;
+  if (emit) {
+    const int slot = atomicAdd(&n_emit, 1);
+    seg_data[seg * kValuKeysPerWg + slot] = Cand{key, (int32_t)s};
+  }
+  __syncthreads();
+  if (tid == 0) seg_cnt[seg] = (uint32_t)n_emit;
+}
+
+// ---- MFMA scoring building blocks ---------------------------------------------------------------------------------
+// NMT = H / 32 head tiles per query, d = 128. The dot products always run on the bf16 32x32x16 MFMA, whose sums
+// are exact for these operands. E4M3-stored keys and queries are converted exactly to bf16 on the way into LDS
+// and registers: the fp8 MFMA is not used because its internal accumulation loses about 2^-15 of the sum of
+// |products|, which would move scores by more than the selection tolerance.
+//
+// LDS key tile: 64 positions x 256 bytes of bf16; the 16-byte chunk c of position n is stored at chunk
+// c ^ (n % 16) so that the 32 lanes reading one chunk column spread over the banks.
+constexpr int kTileRowBytes = 256;
+constexpr int kTileChunks = 16;
+constexpr int kTileBytes = kTileKeys * kTileRowBytes;
+constexpr int kSteps = 8;  // MFMA k-steps of 16 dims
+
+__device__ __forceinline__ int tile_off(int n, int c) { return n * kTileRowBytes + 16 * (c ^ (n % kTileChunks)); }
+
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+
+// Exact E4M3 -> bf16 of the four bytes of `packed`.
+__device__ __forceinline__ bf16x4 e4m3x4_to_bf16(int packed) {
+  const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(packed, 1.0f, false);
+  const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(packed, 1.0f, true);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3);
+}
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(int a, int b) {
+  return __builtin_shufflevector(e4m3x4_to_bf16(a), e4m3x4_to_bf16(b), 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+template <bool E4M3>
+struct KeyLoader;
+
+// bf16 keys: the stored 256-byte rows go straight to LDS by asynchronous DMA (16 KB = 16 wave instructions).
+template <>
+struct KeyLoader<false> {
+  struct Regs {};
+  static __device__ __forceinline__ void fetch(const char* kbytes, int64_t ld_bytes, int64_t L, int64_t s0,
+                                               char* tile, int wave, int lane, Regs&) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int slot = (wave * 4 + j) * 64 + lane;
+      const int n = slot / kTileChunks;
+      const int c = (slot % kTileChunks) ^ (n % kTileChunks);
+      int64_t s = s0 + n;
+      s = s < L ? s : L - 1;  // rows past the end are never scored; keep the copy in bounds
+      dma16(kbytes + s * ld_bytes + c * 16, tile + (wave * 4 + j) * 1024);
+    }
+  }
+  static __device__ __forceinline__ void commit(const Regs&, char*, int) {}
+};
+
+// e4m3 keys: thread i loads 32 stored bytes (position i / 4, dims 32 (i % 4) ..) and writes 64 bytes of bf16.
+template <>
+struct KeyLoader<true> {
+  struct Regs {
+    i32x8 raw;
+  };
+  static __device__ __forceinline__ void fetch(const char* kbytes, int64_t ld_bytes, int64_t L, int64_t s0, char*,
+                                               int, int, Regs& r) {
+    const int tid = threadIdx.x;
+    int64_t s = s0 + tid / 4;
+    s = s < L ? s : L - 1;
+    r.raw = *reinterpret_cast<const i32x8*>(kbytes + s * ld_bytes + 32 * (tid % 4));
+  }
+  static __device__ __forceinline__ void commit(const Regs& r, char* tile, int tid) {
+    const int n = tid / 4, c0 = 4 * (tid % 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<bf16x8*>(tile + tile_off(n, c0 + j)) = e4m3x8_to_bf16(r.raw[2 * j], r.raw[2 * j + 1]);
+  }
+};
+
+// Query fragments (A operand, head = 32 * mt + lane % 32, dims 16 ks + 8 (lane / 32) ..) and the head weights in
+// the accumulator layout (this lane's 16 values of tile mt belong to heads 32 mt + 8 (r / 4) + 4 (lane / 32) + r % 4).
+template <int NMT, bool E4M3>
+__device__ __forceinline__ void load_query(const void* q, const float* w, int64_t b, int lane,
+                                           bf16x8 (&qa)[NMT][kSteps], float (&wv)[NMT][16]) {
+  constexpr int H = 32 * NMT;
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt) {
+    const int64_t e0 = (b * H + 32 * mt + (lane & 31)) * 128 + (lane >> 5) * 8;
+#pragma unroll
+    for (int ks = 0; ks < kSteps; ++ks) {
+      if constexpr (E4M3) {
+        const int2 raw = *reinterpret_cast<const int2*>(reinterpret_cast<const char*>(q) + e0 + ks * 16);
+        qa[mt][ks] = e4m3x8_to_bf16(raw.x, raw.y);
+      } else {
+        qa[mt][ks] = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint16_t*>(q) + e0 + ks * 16);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) wv[mt][r] = w[b * H + 32 * mt + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)];
+  }
+}
+
+// Score of position n = 32 * nt + lane % 32 of the tile, complete in lanes l and l ^ 32.
+template <int NMT>
+__device__ __forceinline__ float score_ntile(const char* tile, int nt, int lane, const bf16x8 (&qa)[NMT][kSteps],
+                                             const float (&wv)[NMT][16]) {
+  const int n = 32 * nt + (lane & 31);
+  f32x16 acc[NMT];
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt) acc[mt] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < kSteps; ++ks) {
+    const bf16x8 bk = *reinterpret_cast<const bf16x8*>(tile + tile_off(n, 2 * ks + (lane >> 5)));
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt][ks], bk, acc[mt], 0, 0, 0);
+  }
+  float part = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) part = fmaf(wv[mt][r], fmaxf(acc[mt][r], 0.f), part);
+  return part + wave_shfl_xor(part, 32);
+}
+
+// Split-L scoring: workgroup = 4 waves = 4 queries over kMfmaKeysPerWg positions.
+template <int NMT, bool E4M3>
+__global__ __launch_bounds__(256) void k_score_mfma(const void* __restrict__ q, const float* __restrict__ w,
+                                                    const void* __restrict__ k, int64_t k_ld, int64_t L, int B,
+                                                    const int32_t* __restrict__ t, int64_t lo, int64_t hi, int mode,
+                                                    float* __restrict__ scores, int64_t scores_ld, int n_sink,
+                                                    int n_window, const uint32_t* __restrict__ thr_key,
+                                                    uint32_t* __restrict__ seg_cnt, Cand* __restrict__ seg_data) {
+  typedef KeyLoader<E4M3> KL;
+  __shared__ __attribute__((aligned(1024))) char tiles[2][kTileBytes];
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const int b = blockIdx.y * 4 + wave;
+  const bool active = b < B;
+  const int64_t wg_lo = lo + (int64_t)blockIdx.x * kMfmaKeysPerWg;
+  const int64_t wg_hi = (wg_lo + kMfmaKeysPerWg < hi) ? wg_lo + kMfmaKeysPerWg : hi;
+  const int n_tiles = (int)((wg_hi - wg_lo + kTileKeys - 1) / kTileKeys);
+  const char* kbytes = reinterpret_cast<const char*>(k);
+  const int64_t ld_bytes = k_ld * (E4M3 ? 1 : 2);
+
+  bf16x8 qa[NMT][kSteps];
+  float wv[NMT][16];
+  uint32_t thr = 0;
+  int64_t tb = L - 1;
+  if (active) {
+    tb = t ? (int64_t)t[b] : L - 1;
+    if (mode == kScoreEmit) thr = thr_key[b];
+    load_query<NMT, E4M3>(q, w, b, lane, qa, wv);
+  }
+
+  int n_emit = 0;
+  const int64_t seg = (int64_t)b * gridDim.x + blockIdx.x;
+  typename KL::Regs regs;
+  KL::fetch(kbytes, ld_bytes, L, wg_lo, tiles[0], wave, lane, regs);
+  KL::commit(regs, tiles[0], threadIdx.x);
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    wait_vmem();
+    __syncthreads();
+    const bool more = tile + 1 < n_tiles;
+    if (more) KL::fetch(kbytes, ld_bytes, L, wg_lo + (int64_t)(tile + 1) * kTileKeys, tiles[(tile + 1) & 1], wave, lane, regs);
+    if (active) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const float score = score_ntile<NMT>(tiles[tile & 1], nt, lane, qa, wv);
+        const int64_t s = wg_lo + (int64_t)tile * kTileKeys + 32 * nt + (lane & 31);
+        const bool in_range = (lane < 32) && s < wg_hi;
+        if (mode == kScoreDense) {
+          if (in_range) scores[(int64_t)b * scores_ld + (s - lo)] = (s <= tb) ? score : -INFINITY;
+        } else {
+          const uint32_t key = score_key(score);
+          const bool emit = in_range && is_candidate(s, tb, n_sink, n_window) && key > thr;
+          const uint64_t m = ballot(emit);
+          if (emit) seg_data[seg * kMfmaKeysPerWg + n_emit + lanes_below(m)] = Cand{key, (int32_t)s};
+          n_emit += __popcll(m);
+        }
+      }
+    }
+    if (more) KL::commit(regs, tiles[(tile + 1) & 1], threadIdx.x);
+  }
+  if (active && mode == kScoreEmit && lane == 0) seg_cnt[seg] = (uint32_t)n_emit;
+}
+
+// Streaming selection for many queries (prefill chunk): workgroup = 4 waves = 4 queries, each wave streams its
+// query's candidate positions in ascending order, appends candidates that beat its running threshold to a
+// private buffer in global memory, and when the buffer is full keeps only the exact top-k (raising the threshold
+// to the k-th key). Positions arrive in ascending order, so a later candidate that only ties the k-th key can
+// never displace it: appending requires a strictly larger key.
+template <int NMT, bool E4M3>
+__global__ __launch_bounds__(256) void k_stream_select(const void* __restrict__ q, const float* __restrict__ w,
+                                                       const void* __restrict__ k, int64_t k_ld, int64_t L, int B,
+                                                       const int32_t* __restrict__ t, int kk, int n_sink,
+                                                       int n_window, Cand* __restrict__ buf,
+                                                       int32_t* __restrict__ buf_n, int cap) {
+  typedef KeyLoader<E4M3> KL;
+  __shared__ __attribute__((aligned(1024))) char tiles[2][kTileBytes];
+  __shared__ uint32_t hist[4][256];
+  __shared__ int64_t wave_end[4];
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const int b = blockIdx.x * 4 + wave;
+  const bool active = b < B;
+  const char* kbytes = reinterpret_cast<const char*>(k);
+  const int64_t ld_bytes = k_ld * (E4M3 ? 1 : 2);
+
+  const int64_t tb = active ? (t ? (int64_t)t[b] : L - 1) : -1;
+  const int64_t cand_end = active ? tb - n_window : -1;  // last candidate position (inclusive)
+  if (lane == 0) wave_end[wave] = cand_end;
+  bf16x8 qa[NMT][kSteps];
+  float wv[NMT][16];
+  if (active) load_query<NMT, E4M3>(q, w, b, lane, qa, wv);
+  __syncthreads();
+  int64_t end = wave_end[0];
+  for (int i = 1; i < 4; ++i) end = wave_end[i] > end ? wave_end[i] : end;
+  const int64_t s_begin = ((int64_t)n_sink / kTileKeys) * kTileKeys;
+  const int n_tiles = end >= s_begin ? (int)((end - s_begin) / kTileKeys + 1) : 0;
+
+  Cand* mybuf = buf + (int64_t)(active ? b : 0) * cap;
+  int n = 0;
+  uint32_t thr = 0;
+  typename KL::Regs regs;
+  if (n_tiles > 0) {
+    KL::fetch(kbytes, ld_bytes, L, s_begin, tiles[0], wave, lane, regs);
+    KL::commit(regs, tiles[0], threadIdx.x);
+  }
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    wait_vmem();
+    __syncthreads();
+    const bool more = tile + 1 < n_tiles;
+    if (more)
+      KL::fetch(kbytes, ld_bytes, L, s_begin + (int64_t)(tile + 1) * kTileKeys, tiles[(tile + 1) & 1], wave, lane, regs);
+    const int64_t s0 = s_begin + (int64_t)tile * kTileKeys;
+    if (active && s0 <= cand_end) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const float score = score_ntile<NMT>(tiles[tile & 1], nt, lane, qa, wv);
+        const int64_t s = s0 + 32 * nt + (lane & 31);
+        const uint32_t key = score_key(score);
+        const bool cand = (lane < 32) && s >= n_sink && s <= cand_end;
+        if (n + 32 > cap) {
+          wait_vmem();
+          thr = wave_select_compact(mybuf, n, kk, hist[wave], lane);
+          n = n < kk ? n : kk;
+        }
+        const bool emit = cand && key > thr;
+        const uint64_t m = ballot(emit);
+        if (emit) mybuf[n + lanes_below(m)] = Cand{key, (int32_t)s};
+        n += __popcll(m);
+      }
+    }
+    if (more) KL::commit(regs, tiles[(tile + 1) & 1], threadIdx.x);
+  }
+  if (active && lane == 0) buf_n[b] = n;
+}
+
+template <int QT, int KT>
+hipError_t launch_valu(const IndexerArgs& a, int64_t lo, int64_t hi, int mode, float* scores, int64_t scores_ld,
+                       int n_sink, int n_window, const uint32_t* thr, uint32_t* seg_cnt, Cand* seg_data,
+                       hipStream_t st) {
+  const int64_t n = hi - lo;
+  dim3 grid((unsigned)((n + kValuKeysPerWg - 1) / kValuKeysPerWg), (unsigned)a.B);
+  const size_t lds = sizeof(float) * ((size_t)a.H * a.d + a.H);
+  hipLaunchKernelGGL((k_score_valu<QT, KT>), grid, dim3(256), lds, st, a.q, a.w, a.k, a.k_ld, a.L, a.H, a.d, a.t,
+                     lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, seg_cnt, seg_data);
+  return hipGetLastError();
+}
+
+template <int NMT, bool FP8>
+hipError_t launch_mfma(const IndexerArgs& a, int64_t lo, int64_t hi, int mode, float* scores, int64_t scores_ld,
+                       int n_sink, int n_window, const uint32_t* thr, uint32_t* seg_cnt, Cand* seg_data,
+                       hipStream_t st) {
+  const int64_t n = hi - lo;
+  dim3 grid((unsigned)((n + kMfmaKeysPerWg - 1) / kMfmaKeysPerWg), (unsigned)((a.B + 3) / 4));
+  hipLaunchKernelGGL((k_score_mfma<NMT, FP8>), grid, dim3(256), 0, st, a.q, a.w, a.k, a.k_ld, a.L, a.B, a.t, lo, hi,
+                     mode, scores, scores_ld, n_sink, n_window, thr, seg_cnt, seg_data);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool score_uses_mfma(const IndexerArgs& a) {
+  const bool shape = a.d == 128 && (a.H == 32 || a.H == 64);
+  const bool types = (a.q_dtype == 1 && a.k_dtype == 1) || (a.q_dtype == 2 && a.k_dtype == 2);
+  return shape && types;
+}
+
+int score_keys_per_wg(const IndexerArgs& a) { return score_uses_mfma(a) ? kMfmaKeysPerWg : kValuKeysPerWg; }
+
+hipError_t launch_score(const IndexerArgs& a, int64_t lo, int64_t hi, int mode, float* scores, int64_t scores_ld,
+                        int n_sink, int n_window, const uint32_t* thr, uint32_t* seg_cnt, Cand* seg_data,
+                        hipStream_t st) {
+  if (hi <= lo) return hipSuccess;
+  if (score_uses_mfma(a)) {
+    const bool fp8 = a.q_dtype == 2;
+    if (a.H == 64)
+      return fp8 ? launch_mfma<2, true>(a, lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, seg_cnt, seg_data, st)
+                 : launch_mfma<2, false>(a, lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, seg_cnt, seg_data, st);
+    return fp8 ? launch_mfma<1, true>(a, lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, seg_cnt, seg_data, st)
+               : launch_mfma<1, false>(a, lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, seg_cnt, seg_data, st);
+  }
+  const int qt = a.q_dtype, kt = a.k_dtype;
+  if (qt == 0 && kt == 0) return launch_valu<0, 0>(a, lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, seg_cnt, seg_data, st);
+  if (qt == 1 && kt == 1) return launch_valu<1, 1>(a, lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, seg_cnt, seg_data, st);
+  if (qt == 2 && kt == 2) return launch_valu<2, 2>(a, lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, seg_cnt, seg_data, st);
+  return hipErrorInvalidValue;
+}
+
+bool stream_select_supported(const IndexerArgs& a) { return score_uses_mfma(a); }
+
+hipError_t launch_stream_select(const IndexerArgs& a, int k, int n_sink, int n_window, Cand* buf, int32_t* buf_n,
+                                int cap, hipStream_t st) {
+  if (!score_uses_mfma(a) || cap < k + 32) return hipErrorInvalidValue;
+  dim3 grid((unsigned)((a.B + 3) / 4));
+  const bool fp8 = a.q_dtype == 2;
+#define SA_STREAM(NMT, F8)                                                                                      \
+  hipLaunchKernelGGL((k_stream_select<NMT, F8>), grid, dim3(256), 0, st, a.q, a.w, a.k, a.k_ld, a.L, a.B, a.t, k, \
+                     n_sink, n_window, buf, buf_n, cap)
+  if (a.H == 64) {
+    if (fp8) SA_STREAM(2, true); else SA_STREAM(2, false);
+  } else {
+    if (fp8) SA_STREAM(1, true); else SA_STREAM(1, false);
+  }
+#undef SA_STREAM
+  return hipGetLastError();
+}
+
+}  // namespace sa

@@ -1,0 +1,113 @@
+// Internal launch interface between the C ABI host code and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sa {
+
+struct IndexerArgs {
+  const void* q;     // [B, H, d]
+  int q_dtype;
+  const float* w;    // [B, H]
+  const void* k;     // [L, k_ld]
+  int k_dtype;
+  int64_t k_ld;
+  int64_t L;
+  int B, H, d;
+  const int32_t* t;  // [B] or NULL
+};
+
+// One emitted candidate: (order-preserving key of the fp32 score, position).
+struct Cand {
+  uint32_t key;
+  int32_t pos;
+};
+
+enum ScoreMode { kScoreDense = 0, kScoreEmit = 1 };
+
+// Positions handled by one workgroup of the scoring kernel chosen for these arguments.
+int score_keys_per_wg(const IndexerArgs& a);
+// True when the MFMA scoring kernel serves these arguments.
+bool score_uses_mfma(const IndexerArgs& a);
+
+// Scores positions [lo, hi).
+//  kScoreDense: scores[b * scores_ld + (s - lo)] = I(b, s), or -inf for s > t_b.
+//  kScoreEmit:  for candidates s (n_sink <= s <= t_b - n_window) with score_key(I) > thr_key[b], append
+//               (key, s) to segment (b, wg): seg_data[(b * n_wg + wg) * keys_per_wg + i], count in
+//               seg_cnt[b * n_wg + wg], where n_wg = ceil((hi - lo) / keys_per_wg).
+hipError_t launch_score(const IndexerArgs& a, int64_t lo, int64_t hi, int mode, float* scores, int64_t scores_ld,
+                        int n_sink, int n_window, const uint32_t* thr_key, uint32_t* seg_cnt, Cand* seg_data,
+                        hipStream_t stream);
+
+// Exact top-k merge, one workgroup per query:
+//   candidates = kept_in[b * kept_ld + (0:kept_n_in[b])] (if kept_in) U all segment entries of query b; the
+//   gather buffer must hold kept_n_in[b] + n_seg * seg_cap entries per query.
+//   Keeps the k best by (key desc, pos asc) in kept_out[b, :] (count in kept_n_out[b]) and sets thr_out[b] to the
+//   k-th key (0 when fewer than k candidates exist). final_mode 1 writes instead idx[b, :] with the positions
+//   ascending and -1 padding, plus n_sel[b]; final_mode 2 writes them in (key desc, position asc) order.
+hipError_t launch_merge(int B, int k, const Cand* kept_in, int kept_ld, const int32_t* kept_n_in,
+                        const uint32_t* seg_cnt, const Cand* seg_data, int n_seg, int seg_cap, Cand* gather,
+                        int64_t gather_cap, Cand* kept_out, int32_t* kept_n_out, uint32_t* thr_out, int final_mode,
+                        int32_t* idx, int idx_ld, int32_t* n_sel, hipStream_t stream);
+int merge_max_k();
+// Fills p[0, n) with v (a kernel, so that it is safe inside captured graphs).
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t stream);
+
+// Streaming per-query selection for many queries (prefill chunk): one pass over each query's visible keys keeps
+// at most `cap` candidates per query in buf[b, :] (count in buf_n[b]) that contain the exact top-k.
+bool stream_select_supported(const IndexerArgs& a);
+hipError_t launch_stream_select(const IndexerArgs& a, int k, int n_sink, int n_window, Cand* buf, int32_t* buf_n,
+                                int cap, hipStream_t stream);
+
+// ---- buckets -----------------------------------------------------------------------------------------------------
+struct BucketBuildPlan {
+  int64_t chunk;      // positions per scatter chunk
+  int64_t n_chunks;
+};
+BucketBuildPlan bucket_build_plan(int64_t L, int32_t n_buckets);
+hipError_t launch_bucket_build(const void* k, int k_dtype, int64_t k_ld, int64_t L, int d, const int32_t* assign,
+                               int n_buckets, float* reps, int32_t* offsets, int32_t* members, int32_t* counts,
+                               int32_t* table, const BucketBuildPlan& plan, hipStream_t stream);
+
+int bucket_expand_max();
+// Workspace of the Flat search: seg_cnt [B * n_wg], seg_data [B * n_wg * 4], n_chosen [B], gather [B * n_wg * 4],
+// chosen [B * top_b], with n_wg = bucket_score_wgs(n_buckets).
+int bucket_score_wgs(int n_buckets);
+hipError_t launch_bucket_select(const void* q, int q_dtype, int B, int d, const float* reps, const int32_t* offsets,
+                                const int32_t* members, int n_buckets, int64_t L, const int32_t* t, int top_b,
+                                int n_sink, int n_window, int32_t* idx, int cap, int32_t* n_sel,
+                                int32_t* buckets_out, uint32_t* seg_cnt, Cand* seg_data, int32_t* n_chosen,
+                                Cand* gather, int32_t* chosen, hipStream_t stream);
+
+// ---- attention ---------------------------------------------------------------------------------------------------
+struct AttnArgs {
+  const void* q;
+  const void* kv;
+  const void* v;
+  int dtype;
+  int64_t kv_ld, v_ld, L;
+  int B, H, d_qk, d_v;
+  const int32_t* t;
+  const int32_t* idx;
+  int idx_ld;
+  const int32_t* n_sel;
+  int n_sink, n_window;
+  float scale;
+  void* out;
+  float* lse;
+};
+
+struct AttnPlan {
+  bool mfma;
+  int n_splits;
+  int rows_per_split;
+};
+AttnPlan attn_plan(int B, int H, int d_qk, int d_v, int64_t max_rows, int dtype, bool separate_v);
+// Bytes of split partials a plan needs, and an upper bound over every read-set bound <= max_rows.
+size_t attn_workspace_bytes(const AttnPlan& p, int B, int H, int d_v);
+size_t attn_workspace_bound(int B, int H, int d_qk, int d_v, int64_t max_rows, int dtype);
+hipError_t launch_attn(const AttnArgs& a, const AttnPlan& p, void* ws, hipStream_t stream);
+
+}  // namespace sa

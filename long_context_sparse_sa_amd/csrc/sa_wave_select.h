@@ -1,0 +1,122 @@
+// Exact radix selection helpers (wave level) for the top-k of (key desc, position asc).
+//
+// Candidates are (key, pos) pairs where key is the order-preserving image of an fp32 score. The k best are found
+// with four 8-bit radix passes over the key (most significant digit first); when several candidates share the
+// k-th key, four more passes over the position pick the lowest positions among them (ties go to the lower
+// position, as the selection rule requires). Positions are unique, so the result is exactly k candidates.
+#pragma once
+
+#include "sa_device.h"
+#include "sa_internal.h"
+
+namespace sa {
+
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v, int lane) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const uint32_t o = __shfl_up(v, off, kWave);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// One wave scans 256 histogram bins in the order of selection (descending digit for keys, ascending for
+// positions) and finds the bin in which the running count first reaches `need`. Returns the digit; `before` is
+// the number of candidates in bins ahead of it. All lanes return the same values.
+__device__ __forceinline__ uint32_t find_digit(const uint32_t* hist, uint32_t need, bool descending, int lane,
+                                               uint32_t* before, uint32_t* in_bin) {
+  uint32_t c[4];
+  uint32_t local = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int o = 4 * lane + i;
+    c[i] = hist[descending ? 255 - o : o];
+    local += c[i];
+  }
+  const uint32_t incl = wave_inclusive_scan(local, lane);
+  uint32_t run = incl - local;
+  int found = -1;
+  uint32_t fb = 0, fc = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (found < 0 && run < need && run + c[i] >= need) {
+      found = 4 * lane + i;
+      fb = run;
+      fc = c[i];
+    }
+    run += c[i];
+  }
+  const uint64_t m = ballot(found >= 0);
+  const int src = m ? (int)__builtin_ctzll(m) : 0;
+  const int o = __shfl(found, src, kWave);
+  *before = __shfl(fb, src, kWave);
+  *in_bin = __shfl(fc, src, kWave);
+  return (uint32_t)(descending ? 255 - o : o);
+}
+
+// Wave-level exact top-k of buf[0, n) (n > k is not required). Afterwards buf[0, min(n, k)) holds the selected
+// candidates (in their original relative order) and the return value is the k-th key (0 when n < k).
+// `hist` is 256 words of LDS private to this wave. Every lane must call it with the same n.
+__device__ __noinline__ uint32_t wave_select_compact(Cand* buf, int n, int k, uint32_t* hist, int lane) {
+  if (n < k) return 0u;
+  // ---- key passes
+  uint32_t prefix = 0, mask = 0, need = (uint32_t)k, ties = 0;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    for (int i = lane; i < 256; i += kWave) hist[i] = 0;
+    __builtin_amdgcn_wave_barrier();
+    for (int i = lane; i < n; i += kWave) {
+      const uint32_t key = buf[i].key;
+      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    }
+    __builtin_amdgcn_wave_barrier();
+    uint32_t before, in_bin;
+    const uint32_t dg = find_digit(hist, need, true, lane, &before, &in_bin);
+    need -= before;
+    ties = in_bin;
+    prefix |= dg << shift;
+    mask |= 255u << shift;
+    __builtin_amdgcn_wave_barrier();
+  }
+  const uint32_t kstar = prefix;
+  // ---- position passes among the candidates tied at the k-th key
+  int32_t pstar = 0x7FFFFFFF;
+  if (need < ties) {
+    uint32_t pprefix = 0, pmask = 0, pneed = need;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      for (int i = lane; i < 256; i += kWave) hist[i] = 0;
+      __builtin_amdgcn_wave_barrier();
+      for (int i = lane; i < n; i += kWave) {
+        const Cand e = buf[i];
+        const uint32_t p = (uint32_t)e.pos;
+        if (e.key == kstar && (p & pmask) == pprefix) atomicAdd(&hist[(p >> shift) & 255u], 1u);
+      }
+      __builtin_amdgcn_wave_barrier();
+      uint32_t before, in_bin;
+      const uint32_t dg = find_digit(hist, pneed, false, lane, &before, &in_bin);
+      pneed -= before;
+      pprefix |= dg << shift;
+      pmask |= 255u << shift;
+      __builtin_amdgcn_wave_barrier();
+    }
+    pstar = (int32_t)pprefix;
+  }
+  // ---- in-place stable compaction (writes never pass the read front)
+  int out = 0;
+  for (int base = 0; base < n; base += kWave) {
+    const int i = base + lane;
+    Cand e{0u, 0};
+    bool keep = false;
+    if (i < n) {
+      e = buf[i];
+      keep = e.key > kstar || (e.key == kstar && e.pos <= pstar);
+    }
+    const uint64_t m = ballot(keep);
+    if (keep) buf[out + lanes_below(m)] = e;
+    out += __popcll(m);
+  }
+  return kstar;
+}
+
+}  // namespace sa

@@ -1,0 +1,97 @@
+"""GPU parity of sa_bucket_build and sa_bucket_select against the oracle (LSA eight-entry page, section 2: buckets
+keep a representative and their member positions; Flat search over representatives; chosen buckets expand to
+positions, plus sink and window)."""
+import numpy as np
+import pytest
+import torch
+
+import long_context_sparse_sa_amd as sa
+from oracle import sa_oracle as O
+from sa_workloads import gen, get_workload
+from tests.gpu_helpers import band_compare, selected, to_f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _small_lsa(seed, L=60000, nb=1000, B=4):
+    wl = get_workload("lsa_flat_1m", L=L, n_buckets=nb, B=B)
+    inp = gen.make_inputs(wl, device=DEV, seed=seed, parts=("index",))
+    return wl, inp
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_build_matches_oracle(seed):
+    wl, inp = _small_lsa(seed)
+    reps, offsets, members = sa.sa_bucket_build(inp["k_idx"], inp["assign"], wl.n_buckets)
+    torch.cuda.synchronize()
+    r_o, off_o, mem_o = O.bucket_build(to_f64(inp["k_idx"]), inp["assign"].cpu().numpy(), wl.n_buckets)
+    np.testing.assert_array_equal(offsets.cpu().numpy(), off_o)
+    np.testing.assert_array_equal(members.cpu().numpy(), mem_o)
+    # fp64 sums rounded once: equal up to the summation order (at most one fp32 ulp)
+    np.testing.assert_allclose(reps.cpu().numpy(), r_o, rtol=2 ** -23, atol=1e-30)
+
+
+def test_build_toy_and_empty_buckets():
+    K = [[1, 0], [0.8, 0.2], [0.6, 0.4], [0.4, 0.6], [0, 1], [-0.2, 0.8], [-0.4, 0.6], [-0.6, 0.4]]
+    k = torch.zeros((8, 4), dtype=torch.float32, device=DEV)   # rows padded to 16 bytes
+    k[:, :2] = torch.tensor(K, device=DEV)
+    assign = torch.tensor([0, 0, 0, 0, 2, 2, 2, 2], dtype=torch.int32, device=DEV)
+    reps, offsets, members = sa.sa_bucket_build(k, assign, 3)
+    assert offsets.tolist() == [0, 4, 4, 8] and members.tolist() == list(range(8))
+    r = reps.cpu().numpy()
+    np.testing.assert_allclose(r[0, :2], [0.7, 0.3], rtol=1e-7)
+    np.testing.assert_allclose(r[2, :2], [-0.3, 0.7], rtol=1e-7)
+    assert np.all(r[1] == 0)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_select_matches_oracle(seed):
+    wl, inp = _small_lsa(seed)
+    L, B = wl.L, wl.B
+    reps, offsets, members = sa.sa_bucket_build(inp["k_idx"], inp["assign"], wl.n_buckets)
+    ts = [L - 1, L - 5000, 30000, 100]
+    t = torch.tensor(ts, dtype=torch.int32, device=DEV)
+    idx, nsel, buckets = sa.sa_bucket_select(inp["q_idx"], reps, offsets, members, L, 32, 4, 128, cap=8192, t=t,
+                                             return_buckets=True)
+    torch.cuda.synchronize()
+    qf = to_f64(inp["q_idx"])
+    r32, off, mem = reps.cpu().numpy(), offsets.cpu().numpy().astype(np.int64), members.cpu().numpy().astype(np.int64)
+    for b in range(B):
+        ref_pos, ref_chosen, sc = O.bucket_select(qf[b], r32, off, mem, ts[b], 32, 4, 128)
+        ids = np.nonzero(np.diff(off) > 0)[0]
+        got_chosen = buckets[b].cpu().numpy()
+        nband = band_compare(np.sort(got_chosen), np.sort(ref_chosen), ids, sc[ids], 32)
+        if nband == 0:
+            np.testing.assert_array_equal(got_chosen, ref_chosen)     # order: score desc, id asc
+            np.testing.assert_array_equal(selected(idx[b], nsel[b].item()), ref_pos)
+        # the expansion of whatever buckets the GPU chose must be exact
+        exp_pos = np.concatenate([mem[off[c]:off[c + 1]] for c in got_chosen])
+        lo, hi = O.sink_positions(ts[b], 4).size, max(O.sink_positions(ts[b], 4).size, ts[b] - 128 + 1)
+        exp_pos = np.sort(exp_pos[(exp_pos >= lo) & (exp_pos < hi)])
+        np.testing.assert_array_equal(selected(idx[b], nsel[b].item()), exp_pos)
+
+
+def test_select_overflow_reports_needed():
+    wl, inp = _small_lsa(3)
+    reps, offsets, members = sa.sa_bucket_build(inp["k_idx"], inp["assign"], wl.n_buckets)
+    idx, nsel = sa.sa_bucket_select(inp["q_idx"], reps, offsets, members, wl.L, 32, 4, 128, cap=16)
+    torch.cuda.synchronize()
+    assert torch.all(nsel < -16) and torch.all(idx == -1)
+
+
+def test_singleton_buckets_reduce_to_plain_topk():
+    """One position per bucket: rep = key and the search is a plain top-k of q.k."""
+    L, d, B, top = 3000, 16, 2, 40
+    g = torch.Generator(device="cpu").manual_seed(4)
+    k = torch.randint(-2, 3, (L, d), generator=g).float().to(DEV)
+    q = torch.randint(-2, 3, (B, d), generator=g).float().to(DEV)
+    assign = torch.arange(L, dtype=torch.int32, device=DEV)
+    reps, offsets, members = sa.sa_bucket_build(k, assign, L)
+    idx, nsel = sa.sa_bucket_select(q, reps, offsets, members, L, top, 0, 0, cap=64)
+    torch.cuda.synchronize()
+    kf, qf = k.double().cpu().numpy(), q.double().cpu().numpy()
+    for b in range(B):
+        sc = (kf @ qf[b]).astype(np.float32)
+        ref = O.topk_positions(sc, np.arange(L), top)
+        np.testing.assert_array_equal(selected(idx[b], nsel[b].item()), ref)

@@ -1,0 +1,128 @@
+"""GPU parity of sa_index_score and sa_select_topk against the oracle (LongCat deep-dive: DSA baseline section,
+indexer and arg-topK equations; SI section, top-K over positions outside sink and window).
+
+Integer-valued inputs make every score exact, so the selected sets must match bit for bit, ties included.
+Normal inputs compare outside the band of positions whose fp32 score lies within 1e-5 relative of the k-th score.
+"""
+import numpy as np
+import pytest
+import torch
+
+import long_context_sparse_sa_amd as sa
+from oracle import sa_oracle as O
+from tests.gpu_helpers import band_compare, selected, to_f64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+DT = {"f32": torch.float32, "bf16": torch.bfloat16, "e4m3": torch.float8_e4m3fn}
+
+
+def _inputs(seed, B, H, d, L, dtype, integer):
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    if integer:
+        q = torch.randint(-2, 3, (B, H, d), generator=g).float()
+        k = torch.randint(-2, 3, (L, d), generator=g).float()
+        w = torch.randint(0, 3, (B, H), generator=g).float()
+    else:
+        q = torch.randn((B, H, d), generator=g)
+        k = torch.randn((L, d), generator=g)
+        w = torch.randn((B, H), generator=g)
+    return q.to(DT[dtype]).to(DEV), w.to(DEV), k.to(DT[dtype]).to(DEV)
+
+
+@pytest.mark.parametrize("dtype,H,d", [("bf16", 64, 128), ("bf16", 32, 128), ("e4m3", 64, 128), ("f32", 4, 32),
+                                       ("bf16", 3, 16)])
+def test_index_score_dense(dtype, H, d):
+    B, L = 5, 3000
+    q, w, k = _inputs(11, B, H, d, L, dtype, integer=False)
+    t = torch.tensor([L - 1, 100, 2999, 0, 1500], dtype=torch.int32, device=DEV)
+    s0, s1 = 37, 2900
+    sc = sa.sa_index_score(q, w, k, t=t, s_begin=s0, s_end=s1)
+    torch.cuda.synchronize()
+    qf, wf, kf = to_f64(q), w.double().cpu().numpy(), to_f64(k)
+    got = sc.cpu().numpy()
+    for b in range(B):
+        pos = np.arange(s0, s1)
+        ref = O.index_score(qf[b], wf[b], kf, pos)
+        mag = np.abs(kf[pos] @ np.abs(qf[b]).T) @ np.abs(wf[b])      # bound on the magnitude of the summed terms
+        vis = pos <= t[b].item()
+        assert np.all(np.isneginf(got[b][~vis]))
+        err = np.abs(got[b][vis] - ref[vis])
+        assert np.all(err <= 1e-5 * mag[vis] + 1e-30), (b, err.max())
+
+
+ALGOS = [sa.SA_TOPK_SPLIT_L, sa.SA_TOPK_PER_QUERY]
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("dtype", ["bf16", "e4m3"])
+def test_topk_integer_exact_with_ties(algo, dtype):
+    """Integer-valued q, k in {-2..2} and w in {0,1,2}: scores are exact, selection must match bit for bit."""
+    B, H, d, L, kk = 6, 64, 128, 40000, 700
+    q, w, k = _inputs(5, B, H, d, L, dtype, integer=True)
+    ts = [L - 1, 39000, 20000, 17000, 5000, 900]
+    t = torch.tensor(ts, dtype=torch.int32, device=DEV)
+    idx, nsel = sa.sa_select_topk(q, w, k, kk, n_sink=3, n_window=50, t=t, algo=algo)
+    torch.cuda.synchronize()
+    qf, wf, kf = to_f64(q), w.double().cpu().numpy(), to_f64(k)
+    for b in range(B):
+        ref, sc, cand = O.select_topk(qf[b], wf[b], kf, ts[b], kk, 3, 50)
+        if b == 0:
+            assert np.unique(sc).size < sc.size / 4        # heavy ties are really exercised
+        got = selected(idx[b], nsel[b].item())
+        np.testing.assert_array_equal(got, ref)
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_topk_normal_band(algo):
+    B, H, d, L, kk = 8, 64, 128, 150000, 2048
+    q, w, k = _inputs(7, B, H, d, L, "bf16", integer=False)
+    idx, nsel = sa.sa_select_topk(q, w, k, kk, n_sink=4, n_window=128, algo=algo)
+    torch.cuda.synchronize()
+    qf, wf, kf = to_f64(q), w.double().cpu().numpy(), to_f64(k)
+    for b in (0, 3, 7):
+        ref, sc, cand = O.select_topk(qf[b], wf[b], kf, L - 1, kk, 4, 128)
+        band_compare(selected(idx[b], nsel[b].item()), ref, cand, sc, kk)
+
+
+def test_topk_valu_path_f32():
+    """The toy indexer shapes (4 heads x 32, fp32) take the VALU scorer."""
+    B, H, d, L, kk = 2, 4, 32, 1024, 64
+    q, w, k = _inputs(3, B, H, d, L, "f32", integer=False)
+    w = w.abs()
+    idx, nsel = sa.sa_select_topk(q, w, k, kk, n_sink=4, n_window=32)
+    torch.cuda.synchronize()
+    qf, wf, kf = to_f64(q), w.double().cpu().numpy(), to_f64(k)
+    for b in range(B):
+        ref, sc, cand = O.select_topk(qf[b], wf[b], kf, L - 1, kk, 4, 32)
+        band_compare(selected(idx[b], nsel[b].item()), ref, cand, sc, kk)
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_topk_degenerate(algo):
+    """k larger than the candidate set, k = 1, and queries whose sink and window cover every visible position."""
+    B, H, d, L = 4, 64, 128, 3000
+    q, w, k = _inputs(9, B, H, d, L, "bf16", integer=True)
+    ts = [2999, 10, 1, 600]
+    t = torch.tensor(ts, dtype=torch.int32, device=DEV)
+    qf, wf, kf = to_f64(q), w.double().cpu().numpy(), to_f64(k)
+    for kk in (1, 5000):
+        idx, nsel = sa.sa_select_topk(q, w, k, kk, n_sink=4, n_window=8, t=t, algo=algo, idx_ld=kk + 3)
+        torch.cuda.synchronize()
+        for b in range(B):
+            ref, sc, cand = O.select_topk(qf[b], wf[b], kf, ts[b], kk, 4, 8)
+            np.testing.assert_array_equal(selected(idx[b], nsel[b].item()), ref)
+
+
+def test_topk_all_equal_scores():
+    """Every score equal: the lowest candidate positions win."""
+    B, H, d, L, kk = 2, 64, 128, 20000, 300
+    q = torch.zeros((B, H, d), dtype=torch.bfloat16, device=DEV)
+    w = torch.ones((B, H), device=DEV)
+    k = torch.ones((L, d), dtype=torch.bfloat16, device=DEV)
+    for algo in ALGOS:
+        idx, nsel = sa.sa_select_topk(q, w, k, kk, n_sink=2, n_window=3, algo=algo)
+        torch.cuda.synchronize()
+        for b in range(B):
+            np.testing.assert_array_equal(selected(idx[b], nsel[b].item()), np.arange(2, 2 + kk))
