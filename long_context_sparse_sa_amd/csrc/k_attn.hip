@@ -165,13 +165,17 @@ constexpr int kRowChunks = 72;
 constexpr int kRowBytes = 1152;
 constexpr int kTileRows = 32;
 constexpr int kTileBytes = kTileRows * kRowBytes;        // 36864
-constexpr int kDmaPerWave = kTileBytes / 1024 / 4;       // 9
-constexpr int kMaxRowsPerSplit = 1024;
+constexpr int kDmaPerWave = kTileBytes / 1024 / 4;       // 9 wave instructions of 1 KB per tile
+constexpr int kNBuf = 4;                                 // LDS tiles: up to 3 in flight while one is consumed
+constexpr int kMaxRowsPerSplit = 512;
 constexpr int kQSteps = kRowElems / 32;                  // 18 k-steps of 32 dims
+constexpr float kRescaleSlack = 8.f;                     // log2 headroom before the running max is raised
 
 // chunk c of row n lives at chunk slot c ^ (n & 7) (the XOR stays inside the aligned group of 8 chunks)
 __device__ __forceinline__ int chunk_slot(int n, int c) { return c ^ (n & 7); }
 
+// Grid: 1-D, block id = group + n_groups * split with group = (query, 64-head group). When n_groups is a multiple
+// of 8, every split of a group (and the combine blocks of its heads) runs on the same XCD and shares its L2.
 template <int DV>
 __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                                                    int64_t kv_ld, int64_t L, int H, const int32_t* __restrict__ t,
@@ -181,13 +185,23 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
                                                    float* __restrict__ part_o, float* __restrict__ part_ml,
                                                    uint16_t* __restrict__ out, float* __restrict__ lse) {
   constexpr int NT = DV / 16;  // 16-wide output tiles per head group
-  __shared__ __attribute__((aligned(1024))) char tiles[2][kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char tiles[kNBuf][kTileBytes];
   __shared__ int32_t pos_s[kMaxRowsPerSplit];
-  const int split = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
+  const int n_groups = (int)gridDim.x / n_splits;
+  const int group = (int)blockIdx.x % n_groups, split = (int)blockIdx.x / n_groups;
+  const int HG = H / 64;
+  const int b = group / HG, hg = group % HG;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   const int g = lane >> 4;         // lane group 0..3
   const int li = lane & 15;        // lane in group
   const int h = 64 * hg + 16 * wave + li;  // the head this lane works for
+  const int64_t bh = (int64_t)b * H + h;
+
+  // Q^T fragments (B operand): head h, dims 32 ks + 8 g .. +8
+  bf16x8 qf[kQSteps];
+#pragma unroll
+  for (int ks = 0; ks < kQSteps; ++ks)
+    qf[ks] = *reinterpret_cast<const bf16x8*>(q + bh * kRowElems + 32 * ks + 8 * g);
 
   const RowList R = make_rows(b, L, t, idx, idx_ld, n_sel, n_sink, n_window);
   const int n_rows = R.count();
@@ -195,7 +209,6 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
   int r_end = r_begin + rows_per_split;
   r_end = r_end < n_rows ? r_end : n_rows;
   const int n_my = r_end - r_begin;
-  const int64_t bh = (int64_t)b * H + h;
 
   if (n_my <= 0) {
     if (n_splits == 1) {
@@ -209,12 +222,6 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
   }
   const int n_tiles = (n_my + kTileRows - 1) / kTileRows;
   for (int r = tid; r < n_tiles * kTileRows; r += 256) pos_s[r] = r < n_my ? R.pos(r_begin + r) : 0;
-
-  // Q^T fragments (B operand): head h, dims 32 ks + 8 g .. +8
-  bf16x8 qf[kQSteps];
-#pragma unroll
-  for (int ks = 0; ks < kQSteps; ++ks)
-    qf[ks] = *reinterpret_cast<const bf16x8*>(q + bh * kRowElems + 32 * ks + 8 * g);
   __syncthreads();
 
   const char* kvb = reinterpret_cast<const char*>(kv);
@@ -233,24 +240,43 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
   f32x4 o[NT];
 #pragma unroll
   for (int i = 0; i < NT; ++i) o[i] = f32x4{};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_use = -INFINITY, l_run = 0.f;  // exponents are taken relative to m_use (log2 domain)
 
-  issue(0, 0);
+  // Per-lane LDS offsets. K fragment of row n = 16 mt + li, chunk 4 ks + g sits at
+  //   n * 1152 + 16 * ((4 ks + g) ^ (n & 7)) = li * 1152 + kofs[ks & 1] + 128 (ks >> 1) + 18432 mt,
+  // and the transpose-read source of row r0 (+16), chunk 2 nt + h at r0 * 1152 + vofs[nt & 3] + 128 (nt >> 2) (+18432),
+  // so every unrolled access is a base register plus a compile-time offset.
+  const int mk = li & 7;
+  const int kofs0 = li * kRowBytes + 16 * (g ^ mk);
+  const int kofs1 = li * kRowBytes + 16 * ((g ^ mk) ^ 4);
+  const int row0 = 4 * g + (li >> 2);
+  const int mv = row0 & 7;
+  const int hsel = (li & 3) >> 1;
+  int vofs[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) vofs[j] = row0 * kRowBytes + 16 * ((2 * j + hsel) ^ mv) + 8 * (li & 1);
+
+  const int n_pre = n_tiles < kNBuf - 1 ? n_tiles : kNBuf - 1;
+  for (int p = 0; p < n_pre; ++p) issue(p, p);
   for (int tile = 0; tile < n_tiles; ++tile) {
-    wait_vmem();
-    __syncthreads();
-    if (tile + 1 < n_tiles) issue(tile + 1, (tile + 1) & 1);
-    const char* tb = tiles[tile & 1];
+    // wait for this tile's copies; the (at most two) later tiles may stay in flight
+    const int newer = n_tiles - 1 - tile;
+    if (newer >= 2) wait_vmem_below<2 * kDmaPerWave>();
+    else if (newer == 1) wait_vmem_below<kDmaPerWave>();
+    else wait_vmem_below<0>();
+    lds_barrier();
+    if (tile + kNBuf - 1 < n_tiles) issue(tile + kNBuf - 1, (tile + kNBuf - 1) % kNBuf);
+    const char* tb = tiles[tile % kNBuf];
 
     // S^T (rows x heads): two 16-row halves
     f32x4 s[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       s[mt] = f32x4{};
-      const int n = 16 * mt + li;
 #pragma unroll
       for (int ks = 0; ks < kQSteps; ++ks) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(tb + n * kRowBytes + 16 * chunk_slot(n, 4 * ks + g));
+        const char* kp = tb + ((ks & 1) ? kofs1 : kofs0) + 128 * (ks >> 1) + 18432 * mt;
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kp);
         s[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], s[mt], 0, 0, 0);
       }
     }
@@ -268,35 +294,38 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
       }
     mt_max = fmaxf(mt_max, __shfl_xor(mt_max, 16, kWave));
     mt_max = fmaxf(mt_max, __shfl_xor(mt_max, 32, kWave));
-    const float m_new = fmaxf(m_run, mt_max);
-    const float alpha = exp2f(m_run - m_new);
+    // raise the reference only when this tile would exceed it by more than 2^kRescaleSlack
+    const bool raise = mt_max > m_use + kRescaleSlack;
+    if (__any(raise)) {
+      const float m_new = raise ? mt_max : m_use;
+      const float alpha = exp2f(m_use - m_new);  // 1 where not raised, 0 on the first tile
+      l_run *= alpha;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) o[nt] = o[nt] * alpha;
+      m_use = m_new;
+    }
     bf16x8 pf;
     float psum = 0.f;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = exp2f(x[mt][r] - m_new);
+        const float p = exp2f(x[mt][r] - m_use);
         psum += p;
         pf[4 * mt + r] = (__bf16)p;
       }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+    l_run += psum;
 
     // O^T (dv x heads) += V^T P^T; V^T fragments through LDS transpose reads.
     // A operand slots e = 0..3 -> tile rows 4 g + e, e = 4..7 -> rows 16 + 4 g + (e - 4), matching pf.
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const int c = 2 * nt + ((li & 3) >> 1);
-      const int half = 8 * (li & 1);
-      const int row0 = 4 * g + (li >> 2);
-      const int row1 = 16 + 4 * g + (li >> 2);
-      const i16x4 v0 = lds_read_tr16(tb + row0 * kRowBytes + 16 * chunk_slot(row0, c) + half);
-      const i16x4 v1 = lds_read_tr16(tb + row1 * kRowBytes + 16 * chunk_slot(row1, c) + half);
+      const char* vp = tb + vofs[nt & 3] + 128 * (nt >> 2);
+      const i16x4 v0 = lds_read_tr16(vp);
+      const i16x4 v1 = lds_read_tr16(vp + 18432);
       // whole-vector shuffle + bit_cast (a bit_cast of a single ext-vector element is not used here: clang lowers
       // it to element 0 for every index)
       const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-      o[nt] = o[nt] * alpha;
       o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, o[nt], 0, 0, 0);
     }
   }
@@ -312,24 +341,27 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
 #pragma unroll
       for (int r = 0; r < 4; ++r) dst[r] = f32_to_bf16_bits(o[nt][r] * inv);
     }
-    if (lse && g == 0) lse[bh] = (m_run + log2f(l_run)) * kLn2;
+    if (lse && g == 0) lse[bh] = (m_use + log2f(l_run)) * kLn2;
   } else {
     float* dst = part_o + (bh * n_splits + split) * DV;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) *reinterpret_cast<f32x4*>(dst + 16 * nt + 4 * g) = o[nt];
     if (g == 0) {
-      part_ml[(bh * n_splits + split) * 2 + 0] = m_run;
+      part_ml[(bh * n_splits + split) * 2 + 0] = m_use;
       part_ml[(bh * n_splits + split) * 2 + 1] = l_run;
     }
   }
 }
 
 // Exact merge of the splits of one (query, head): o = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i.
+// Block id = group + n_groups * j, head = 64 hg + j, matching the XCD of the attention blocks of that group.
 template <int DT>
-__global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ part_o,
-                                                      const float* __restrict__ part_ml, int n_splits, int d_v,
-                                                      void* __restrict__ out, float* __restrict__ lse) {
-  const int64_t bh = blockIdx.x;
+__global__ __launch_bounds__(64) void k_attn_combine(const float* __restrict__ part_o,
+                                                     const float* __restrict__ part_ml, int n_splits, int n_groups,
+                                                     int H, int d_v, void* __restrict__ out, float* __restrict__ lse) {
+  const int group = (int)blockIdx.x % n_groups, j = (int)blockIdx.x / n_groups;
+  const int HG = H / 64;
+  const int64_t bh = (int64_t)(group / HG) * H + 64 * (group % HG) + j;
   const float* ml = part_ml + bh * n_splits * 2;
   float M = -INFINITY;
   for (int i = 0; i < n_splits; ++i) M = fmaxf(M, ml[2 * i]);
@@ -337,14 +369,15 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
   if (M != -INFINITY)
     for (int i = 0; i < n_splits; ++i) Ls += exp2f(ml[2 * i] - M) * ml[2 * i + 1];
   const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
-  for (int dv = threadIdx.x; dv < d_v; dv += blockDim.x) {
-    float acc = 0.f;
+  for (int dv = 4 * threadIdx.x; dv < d_v; dv += 4 * blockDim.x) {
+    f32x4 acc = f32x4{};
     if (M != -INFINITY)
       for (int i = 0; i < n_splits; ++i) {
         const float wgt = exp2f(ml[2 * i] - M);
-        if (wgt != 0.f) acc = fmaf(wgt, part_o[(bh * n_splits + i) * d_v + dv], acc);
+        if (wgt != 0.f) acc += wgt * *reinterpret_cast<const f32x4*>(part_o + (bh * n_splits + i) * d_v + dv);
       }
-    store_out<DT>(out, bh * d_v + dv, acc * inv);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) store_out<DT>(out, bh * d_v + dv + r, acc[r] * inv);
   }
   if (lse && threadIdx.x == 0) lse[bh] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
 }
@@ -361,7 +394,7 @@ AttnPlan attn_plan(int B, int H, int d_qk, int d_v, int64_t max_rows, int dtype,
   }
   const int64_t units = B > 0 ? (int64_t)B * (H / 64) : 1;
   const int64_t rows = max_rows > 0 ? max_rows : 1;
-  int64_t splits = (512 + units - 1) / units;
+  int64_t splits = (256 + units - 1) / units;
   const int64_t max_splits = (rows + kTileRows - 1) / kTileRows;
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
@@ -379,14 +412,14 @@ size_t attn_workspace_bytes(const AttnPlan& p, int B, int H, int d_v) {
   return (size_t)B * H * p.n_splits * ((size_t)d_v + 2) * sizeof(float);
 }
 
-// attn_plan never uses more than max(ceil(512 / units), ceil(rows / kMaxRowsPerSplit)) splits, which grows with
+// attn_plan never uses more than max(ceil(256 / units), ceil(rows / kMaxRowsPerSplit)) splits, which grows with
 // rows, so this bound covers every call whose read sets are bounded by max_rows.
 size_t attn_workspace_bound(int B, int H, int d_qk, int d_v, int64_t max_rows, int dtype) {
   const AttnPlan p = attn_plan(B, H, d_qk, d_v, max_rows, dtype, false);
   if (!p.mfma) return 0;
   const int64_t units = B > 0 ? (int64_t)B * (H / 64) : 1;
   const int64_t rows = max_rows > 0 ? max_rows : 1;
-  int64_t s1 = (512 + units - 1) / units;
+  const int64_t s1 = (256 + units - 1) / units;
   const int64_t s2 = (rows + kMaxRowsPerSplit - 1) / kMaxRowsPerSplit;
   const int64_t s = s1 > s2 ? s1 : s2;
   return (size_t)B * H * s * ((size_t)d_v + 2) * sizeof(float);
@@ -409,7 +442,8 @@ hipError_t launch_attn(const AttnArgs& a, const AttnPlan& p, void* ws, hipStream
   }
   float* part_o = reinterpret_cast<float*>(ws);
   float* part_ml = part_o ? part_o + (size_t)a.B * a.H * p.n_splits * a.d_v : nullptr;
-  dim3 grid((unsigned)p.n_splits, (unsigned)(a.H / 64), (unsigned)a.B);
+  const int n_groups = a.B * (a.H / 64);
+  dim3 grid((unsigned)(n_groups * p.n_splits));
   const float sl2 = a.scale * kLog2e;
   const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q);
   const uint16_t* kv = reinterpret_cast<const uint16_t*>(a.kv);
@@ -422,8 +456,8 @@ hipError_t launch_attn(const AttnArgs& a, const AttnPlan& p, void* ws, hipStream
                        a.n_sel, a.n_sink, a.n_window, sl2, p.rows_per_split, p.n_splits, part_o, part_ml, out, a.lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_splits == 1) return e;
-  hipLaunchKernelGGL(k_attn_combine<1>, dim3((unsigned)(a.B * a.H)), dim3(256), 0, st, part_o, part_ml, p.n_splits,
-                     a.d_v, a.out, a.lse);
+  hipLaunchKernelGGL(k_attn_combine<1>, dim3((unsigned)(a.B * a.H)), dim3(64), 0, st, part_o, part_ml, p.n_splits,
+                     n_groups, a.H, a.d_v, a.out, a.lse);
   return hipGetLastError();
 }
 

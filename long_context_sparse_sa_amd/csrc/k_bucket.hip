@@ -123,40 +123,27 @@ __global__ __launch_bounds__(256) void k_reps(const void* __restrict__ k, int64_
   }
 }
 
-// One wave per bucket scores every query (fp32 dot), emitting (key, bucket) for non-empty buckets into the
-// workgroup's segment of each query (segment capacity 4 = buckets per workgroup).
+// One wave per bucket scores every query (fp32 dot) and writes the candidate slot cand[b * nb + bucket]:
+// (key, bucket) for a non-empty bucket, an empty slot (key 0) otherwise.
 template <int QT>
 __global__ __launch_bounds__(256) void k_bucket_scores(const void* __restrict__ q, int B, int d,
                                                        const float* __restrict__ reps,
                                                        const int32_t* __restrict__ offsets, int nb,
-                                                       uint32_t* __restrict__ seg_cnt, Cand* __restrict__ seg_data) {
+                                                       Cand* __restrict__ cand) {
   extern __shared__ float qs[];  // [B * d]
-  __shared__ uint32_t cnt[4];
   for (int i = threadIdx.x; i < B * d; i += blockDim.x) qs[i] = load_elem<QT>(q, i);
   __syncthreads();
   const int wave = threadIdx.x / kWave, lane = lane_id();
   const int bucket = blockIdx.x * 4 + wave;
-  const bool valid = bucket < nb && offsets[bucket + 1] > offsets[bucket];
+  if (bucket >= nb) return;
+  const bool valid = offsets[bucket + 1] > offsets[bucket];
   for (int b = 0; b < B; ++b) {
     float acc = 0.f;
     if (valid)
       for (int x = lane; x < d; x += kWave) acc = fmaf(qs[b * d + x], reps[(int64_t)bucket * d + x], acc);
 #pragma unroll
     for (int off = kWave / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, kWave);
-    // wave 0 collects the workgroup's candidates for query b in bucket order
-    if (lane == 0) cnt[wave] = valid ? 1u : 0u;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      uint32_t n = 0;
-      for (int w = 0; w < 4; ++w) n += cnt[w];
-      seg_cnt[(int64_t)b * gridDim.x + blockIdx.x] = n;
-    }
-    if (lane == 0 && valid) {
-      uint32_t slot = 0;
-      for (int w = 0; w < wave; ++w) slot += cnt[w];
-      seg_data[((int64_t)b * gridDim.x + blockIdx.x) * 4 + slot] = Cand{score_key(acc), bucket};
-    }
-    __syncthreads();
+    if (lane == 0) cand[(int64_t)b * nb + bucket] = valid ? Cand{score_key(acc), bucket} : Cand{0u, -1};
   }
 }
 
@@ -270,24 +257,22 @@ hipError_t launch_bucket_build(const void* k, int k_dtype, int64_t k_ld, int64_t
 }
 
 int bucket_expand_max() { return kMaxExpand; }
-int bucket_score_wgs(int nb) { return (nb + 3) / 4; }
 
 hipError_t launch_bucket_select(const void* q, int q_dtype, int B, int d, const float* reps, const int32_t* offsets,
                                 const int32_t* members, int nb, int64_t L, const int32_t* t, int top_b, int n_sink,
                                 int n_window, int32_t* idx, int cap, int32_t* n_sel, int32_t* buckets_out,
-                                uint32_t* seg_cnt, Cand* seg_data, int32_t* n_chosen, Cand* gather, int32_t* chosen,
-                                hipStream_t st) {
-  const int n_wg = bucket_score_wgs(nb);
+                                Cand* cand, int32_t* n_chosen, Cand* gather, int32_t* chosen, hipStream_t st) {
+  const unsigned n_wg = (unsigned)((nb + 3) / 4);
   const size_t lds = sizeof(float) * (size_t)B * d;
   if (q_dtype == 0)
-    hipLaunchKernelGGL(k_bucket_scores<0>, dim3((unsigned)n_wg), dim3(256), lds, st, q, B, d, reps, offsets, nb, seg_cnt, seg_data);
+    hipLaunchKernelGGL(k_bucket_scores<0>, dim3(n_wg), dim3(256), lds, st, q, B, d, reps, offsets, nb, cand);
   else
-    hipLaunchKernelGGL(k_bucket_scores<1>, dim3((unsigned)n_wg), dim3(256), lds, st, q, B, d, reps, offsets, nb, seg_cnt, seg_data);
+    hipLaunchKernelGGL(k_bucket_scores<1>, dim3(n_wg), dim3(256), lds, st, q, B, d, reps, offsets, nb, cand);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   int32_t* order = buckets_out ? buckets_out : chosen;
-  e = launch_merge(B, top_b, nullptr, 0, nullptr, seg_cnt, seg_data, n_wg, 4, gather, (int64_t)n_wg * 4, nullptr,
-                   nullptr, nullptr, 2, order, top_b, n_chosen, st);
+  e = launch_merge(B, top_b, nullptr, 0, nullptr, cand, nb, nullptr, nb, nullptr, gather, nb, nullptr, nullptr, nullptr,
+                   2, order, top_b, n_chosen, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_expand, dim3((unsigned)B), dim3(1024), 0, st, order, n_chosen, top_b, offsets, members, L, t,
                      n_sink, n_window, idx, cap, n_sel);

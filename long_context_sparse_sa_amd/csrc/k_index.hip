@@ -32,11 +32,13 @@ __global__ __launch_bounds__(256) void k_score_valu(const void* __restrict__ q, 
                                                     int d, const int32_t* __restrict__ t, int64_t lo, int64_t hi,
                                                     int mode, float* __restrict__ scores, int64_t scores_ld,
                                                     int n_sink, int n_window, const uint32_t* __restrict__ thr_key,
-                                                    uint32_t* __restrict__ seg_cnt, Cand* __restrict__ seg_data) {
+                                                    Cand* __restrict__ cand, int64_t cand_ld,
+                                                    uint32_t* __restrict__ cand_cnt) {
   extern __shared__ float smem[];
   float* qs = smem;            // [H * d]
   float* ws = smem + H * d;    // [H]
-  __shared__ int n_emit;
+  __shared__ int n_emit, emit_base;
+  __shared__ Cand staged[kValuKeysPerWg];
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
   for (int i = tid; i < H * d; i += blockDim.x) qs[i] = load_elem<QT>(q, (int64_t)b * H * d + i);
@@ -60,14 +62,16 @@ __global__ __launch_bounds__(256) void k_score_valu(const void* __restrict__ q, 
     return;
   }
   const uint32_t key = score_key(score);
-  const bool emit = s < hi && is_candidate(s, tb, n_sink, n_window) && key > thr_key[b];
-  const int64_t seg = (int64_t)b * gridDim.x + blockIdx.x;
-  if (emit) {
-    const int slot = atomicAdd(&n_emit, 1);
-    seg_data[seg * kValuKeysPerWg + slot] = Cand{key, (int32_t)s};
+  const bool is_cand = s < hi && is_candidate(s, tb, n_sink, n_window);
+  if (mode == kScoreAll) {
+    if (s < hi) cand[(int64_t)b * cand_ld + (s - lo)] = is_cand ? Cand{key, (int32_t)s} : Cand{0u, -1};
+    return;
   }
+  if (is_cand && key > (thr_key ? thr_key[b] : 0u)) staged[atomicAdd(&n_emit, 1)] = Cand{key, (int32_t)s};
   __syncthreads();
-  if (tid == 0) seg_cnt[seg] = (uint32_t)n_emit;
+  if (tid == 0) emit_base = n_emit ? (int)atomicAdd(&cand_cnt[b], (uint32_t)n_emit) : 0;
+  __syncthreads();
+  if (tid < n_emit) cand[(int64_t)b * cand_ld + emit_base + tid] = staged[tid];
 }
 
 // ---- MFMA scoring building blocks ---------------------------------------------------------------------------------
@@ -98,46 +102,53 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(int a, int b) {
   return __builtin_shufflevector(e4m3x4_to_bf16(a), e4m3x4_to_bf16(b), 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-template <bool E4M3>
+template <bool E4M3, int NW>
 struct KeyLoader;
 
 // bf16 keys: the stored 256-byte rows go straight to LDS by asynchronous DMA (16 KB = 16 wave instructions).
-template <>
-struct KeyLoader<false> {
+template <int NW>
+struct KeyLoader<false, NW> {
+  static constexpr int kPerWave = 16 / NW;
   struct Regs {};
   static __device__ __forceinline__ void fetch(const char* kbytes, int64_t ld_bytes, int64_t L, int64_t s0,
                                                char* tile, int wave, int lane, Regs&) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int slot = (wave * 4 + j) * 64 + lane;
+    for (int j = 0; j < kPerWave; ++j) {
+      const int slot = (wave * kPerWave + j) * 64 + lane;
       const int n = slot / kTileChunks;
       const int c = (slot % kTileChunks) ^ (n % kTileChunks);
       int64_t s = s0 + n;
       s = s < L ? s : L - 1;  // rows past the end are never scored; keep the copy in bounds
-      dma16(kbytes + s * ld_bytes + c * 16, tile + (wave * 4 + j) * 1024);
+      dma16(kbytes + s * ld_bytes + c * 16, tile + (wave * kPerWave + j) * 1024);
     }
   }
   static __device__ __forceinline__ void commit(const Regs&, char*, int) {}
 };
 
-// e4m3 keys: thread i loads 32 stored bytes (position i / 4, dims 32 (i % 4) ..) and writes 64 bytes of bf16.
-template <>
-struct KeyLoader<true> {
+// e4m3 keys: each thread loads BPT stored bytes of one position and writes them as 2 BPT bytes of bf16.
+template <int NW>
+struct KeyLoader<true, NW> {
+  static constexpr int BPT = 8192 / (64 * NW);      // raw bytes per thread (32 or 16)
+  static constexpr int TPK = 128 / BPT;             // threads per position
   struct Regs {
-    i32x8 raw;
+    int4 part[BPT / 16];
   };
   static __device__ __forceinline__ void fetch(const char* kbytes, int64_t ld_bytes, int64_t L, int64_t s0, char*,
                                                int, int, Regs& r) {
     const int tid = threadIdx.x;
-    int64_t s = s0 + tid / 4;
+    int64_t s = s0 + tid / TPK;
     s = s < L ? s : L - 1;
-    r.raw = *reinterpret_cast<const i32x8*>(kbytes + s * ld_bytes + 32 * (tid % 4));
+    const int4* src = reinterpret_cast<const int4*>(kbytes + s * ld_bytes + BPT * (tid % TPK));
+#pragma unroll
+    for (int p = 0; p < BPT / 16; ++p) r.part[p] = src[p];
   }
   static __device__ __forceinline__ void commit(const Regs& r, char* tile, int tid) {
-    const int n = tid / 4, c0 = 4 * (tid % 4);
+    const int n = tid / TPK, c0 = (BPT / 8) * (tid % TPK);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<bf16x8*>(tile + tile_off(n, c0 + j)) = e4m3x8_to_bf16(r.raw[2 * j], r.raw[2 * j + 1]);
+    for (int p = 0; p < BPT / 16; ++p) {
+      *reinterpret_cast<bf16x8*>(tile + tile_off(n, c0 + 2 * p)) = e4m3x8_to_bf16(r.part[p].x, r.part[p].y);
+      *reinterpret_cast<bf16x8*>(tile + tile_off(n, c0 + 2 * p + 1)) = e4m3x8_to_bf16(r.part[p].z, r.part[p].w);
+    }
   }
 };
 
@@ -186,23 +197,33 @@ __device__ __forceinline__ float score_ntile(const char* tile, int nt, int lane,
   return part + wave_shfl_xor(part, 32);
 }
 
-// Split-L scoring: workgroup = 4 waves = 4 queries over kMfmaKeysPerWg positions.
-template <int NMT, bool E4M3>
-__global__ __launch_bounds__(256) void k_score_mfma(const void* __restrict__ q, const float* __restrict__ w,
-                                                    const void* __restrict__ k, int64_t k_ld, int64_t L, int B,
-                                                    const int32_t* __restrict__ t, int64_t lo, int64_t hi, int mode,
-                                                    float* __restrict__ scores, int64_t scores_ld, int n_sink,
-                                                    int n_window, const uint32_t* __restrict__ thr_key,
-                                                    uint32_t* __restrict__ seg_cnt, Cand* __restrict__ seg_data) {
-  typedef KeyLoader<E4M3> KL;
-  __shared__ __attribute__((aligned(1024))) char tiles[2][kTileBytes];
+// Split-L scoring: workgroup = NQ waves = NQ queries. The 64-position tiles of [lo, hi) are dealt round-robin
+// to the gridDim.x workgroups of each query group, whose queries stay in registers. bf16 keys arrive by
+// asynchronous DMA into four LDS buffers (three tiles in flight); e4m3 keys are loaded two tiles ahead into a
+// register ring, converted and committed to two LDS buffers. Emitted candidates are staged per wave in LDS and
+// flushed with one atomicAdd on the query's counter whenever the stage could overflow, and at the end.
+template <int NMT, bool E4M3, int NQ>
+__global__ __launch_bounds__(64 * NQ) void k_score_mfma(const void* __restrict__ q, const float* __restrict__ w,
+                                                        const void* __restrict__ k, int64_t k_ld, int64_t L, int B,
+                                                        const int32_t* __restrict__ t, int64_t lo, int64_t hi,
+                                                        int mode, float* __restrict__ scores, int64_t scores_ld,
+                                                        int n_sink, int n_window,
+                                                        const uint32_t* __restrict__ thr_key,
+                                                        Cand* __restrict__ cand, int64_t cand_ld,
+                                                        uint32_t* __restrict__ cand_cnt) {
+  typedef KeyLoader<E4M3, NQ> KL;
+  constexpr int kNBuf = E4M3 ? 2 : 4;
+  constexpr int kStage = 512;
+  constexpr int kDmaPerWave = KeyLoader<false, NQ>::kPerWave;
+  __shared__ __attribute__((aligned(1024))) char tiles[kNBuf][kTileBytes];
+  __shared__ Cand staged[NQ][kStage];
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
-  const int b = blockIdx.y * 4 + wave;
+  const int b = blockIdx.y * NQ + wave;
   const bool active = b < B;
-  const int64_t wg_lo = lo + (int64_t)blockIdx.x * kMfmaKeysPerWg;
-  const int64_t wg_hi = (wg_lo + kMfmaKeysPerWg < hi) ? wg_lo + kMfmaKeysPerWg : hi;
-  const int n_tiles = (int)((wg_hi - wg_lo + kTileKeys - 1) / kTileKeys);
+  const int64_t tiles_total = (hi - lo + kTileKeys - 1) / kTileKeys;
+  const int64_t n_tiles = tiles_total > (int64_t)blockIdx.x ? (tiles_total - 1 - blockIdx.x) / gridDim.x + 1 : 0;
+  auto tile_start = [&](int64_t i) { return lo + ((int64_t)blockIdx.x + i * gridDim.x) * kTileKeys; };
   const char* kbytes = reinterpret_cast<const char*>(k);
   const int64_t ld_bytes = k_ld * (E4M3 ? 1 : 2);
 
@@ -212,40 +233,84 @@ __global__ __launch_bounds__(256) void k_score_mfma(const void* __restrict__ q, 
   int64_t tb = L - 1;
   if (active) {
     tb = t ? (int64_t)t[b] : L - 1;
-    if (mode == kScoreEmit) thr = thr_key[b];
+    if (mode == kScoreEmit && thr_key) thr = thr_key[b];
     load_query<NMT, E4M3>(q, w, b, lane, qa, wv);
   }
 
   int n_emit = 0;
-  const int64_t seg = (int64_t)b * gridDim.x + blockIdx.x;
-  typename KL::Regs regs;
-  KL::fetch(kbytes, ld_bytes, L, wg_lo, tiles[0], wave, lane, regs);
-  KL::commit(regs, tiles[0], threadIdx.x);
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    wait_vmem();
-    __syncthreads();
-    const bool more = tile + 1 < n_tiles;
-    if (more) KL::fetch(kbytes, ld_bytes, L, wg_lo + (int64_t)(tile + 1) * kTileKeys, tiles[(tile + 1) & 1], wave, lane, regs);
-    if (active) {
+  auto flush = [&]() {
+    int base = 0;
+    if (lane == 0) base = (int)atomicAdd(&cand_cnt[b], (uint32_t)n_emit);
+    base = __shfl(base, 0, kWave);
+    Cand* dst = cand + (int64_t)b * cand_ld + base;
+    for (int j = lane; j < n_emit; j += kWave) dst[j] = staged[wave][j];
+    n_emit = 0;
+  };
+  auto score_tile = [&](const char* tile, int64_t s0) {
+    if (!active || s0 >= hi) return;
+    if (mode == kScoreEmit && n_emit > kStage - kTileKeys) flush();
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const float score = score_ntile<NMT>(tiles[tile & 1], nt, lane, qa, wv);
-        const int64_t s = wg_lo + (int64_t)tile * kTileKeys + 32 * nt + (lane & 31);
-        const bool in_range = (lane < 32) && s < wg_hi;
-        if (mode == kScoreDense) {
-          if (in_range) scores[(int64_t)b * scores_ld + (s - lo)] = (s <= tb) ? score : -INFINITY;
+    for (int nt = 0; nt < 2; ++nt) {
+      const float score = score_ntile<NMT>(tile, nt, lane, qa, wv);
+      const int64_t s = s0 + 32 * nt + (lane & 31);
+      const bool in_range = (lane < 32) && s < hi;
+      if (mode == kScoreDense) {
+        if (in_range) scores[(int64_t)b * scores_ld + (s - lo)] = (s <= tb) ? score : -INFINITY;
+      } else {
+        const uint32_t key = score_key(score);
+        const bool is_cand = in_range && is_candidate(s, tb, n_sink, n_window);
+        if (mode == kScoreAll) {
+          if (in_range) cand[(int64_t)b * cand_ld + (s - lo)] = is_cand ? Cand{key, (int32_t)s} : Cand{0u, -1};
         } else {
-          const uint32_t key = score_key(score);
-          const bool emit = in_range && is_candidate(s, tb, n_sink, n_window) && key > thr;
+          const bool emit = is_cand && key > thr;
           const uint64_t m = ballot(emit);
-          if (emit) seg_data[seg * kMfmaKeysPerWg + n_emit + lanes_below(m)] = Cand{key, (int32_t)s};
+          if (emit) staged[wave][n_emit + lanes_below(m)] = Cand{key, (int32_t)s};
           n_emit += __popcll(m);
         }
       }
     }
-    if (more) KL::commit(regs, tiles[(tile + 1) & 1], threadIdx.x);
+  };
+
+  if constexpr (!E4M3) {
+    typename KL::Regs none;
+    const int64_t n_pre = n_tiles < kNBuf - 1 ? n_tiles : kNBuf - 1;
+    for (int64_t p = 0; p < n_pre; ++p) KL::fetch(kbytes, ld_bytes, L, tile_start(p), tiles[p], wave, lane, none);
+    for (int64_t i = 0; i < n_tiles; ++i) {
+      const int64_t newer = n_tiles - 1 - i;
+      if (newer >= 2) wait_vmem_below<2 * kDmaPerWave>();
+      else if (newer == 1) wait_vmem_below<kDmaPerWave>();
+      else wait_vmem_below<0>();
+      lds_barrier();
+      if (i + kNBuf - 1 < n_tiles)
+        KL::fetch(kbytes, ld_bytes, L, tile_start(i + kNBuf - 1), tiles[(i + kNBuf - 1) % kNBuf], wave, lane, none);
+      score_tile(tiles[i % kNBuf], tile_start(i));
+    }
+  } else {
+    typename KL::Regs ring[2];
+    if (n_tiles > 0) {
+      KL::fetch(kbytes, ld_bytes, L, tile_start(0), nullptr, wave, lane, ring[0]);
+      if (n_tiles > 1) KL::fetch(kbytes, ld_bytes, L, tile_start(1), nullptr, wave, lane, ring[1]);
+      KL::commit(ring[0], tiles[0], threadIdx.x);
+      if (n_tiles > 2) KL::fetch(kbytes, ld_bytes, L, tile_start(2), nullptr, wave, lane, ring[0]);
+    }
+    // tile i + 1 (ring slot (i + 1) % 2) goes to LDS while tile i is scored; its slot then takes tile i + 3.
+    // Unrolled by two so that ring slots and LDS buffers are compile-time (a runtime-indexed ring would live in
+    // scratch memory).
+    auto step = [&](int64_t i, auto P) {
+      constexpr int p = decltype(P)::value;
+      lds_barrier();
+      if (i + 1 < n_tiles) {
+        KL::commit(ring[1 - p], tiles[1 - p], threadIdx.x);
+        if (i + 3 < n_tiles) KL::fetch(kbytes, ld_bytes, L, tile_start(i + 3), nullptr, wave, lane, ring[1 - p]);
+      }
+      score_tile(tiles[p], tile_start(i));
+    };
+    for (int64_t i = 0; i < n_tiles; i += 2) {
+      step(i, std::integral_constant<int, 0>{});
+      if (i + 1 < n_tiles) step(i + 1, std::integral_constant<int, 1>{});
+    }
   }
-  if (active && mode == kScoreEmit && lane == 0) seg_cnt[seg] = (uint32_t)n_emit;
+  if (active && mode == kScoreEmit && n_emit > 0) flush();
 }
 
 // Streaming selection for many queries (prefill chunk): workgroup = 4 waves = 4 queries, each wave streams its
@@ -259,7 +324,7 @@ __global__ __launch_bounds__(256) void k_stream_select(const void* __restrict__ 
                                                        const int32_t* __restrict__ t, int kk, int n_sink,
                                                        int n_window, Cand* __restrict__ buf,
                                                        int32_t* __restrict__ buf_n, int cap) {
-  typedef KeyLoader<E4M3> KL;
+  typedef KeyLoader<E4M3, 4> KL;
   __shared__ __attribute__((aligned(1024))) char tiles[2][kTileBytes];
   __shared__ uint32_t hist[4][256];
   __shared__ int64_t wave_end[4];
@@ -322,24 +387,33 @@ __global__ __launch_bounds__(256) void k_stream_select(const void* __restrict__ 
 
 template <int QT, int KT>
 hipError_t launch_valu(const IndexerArgs& a, int64_t lo, int64_t hi, int mode, float* scores, int64_t scores_ld,
-                       int n_sink, int n_window, const uint32_t* thr, uint32_t* seg_cnt, Cand* seg_data,
-                       hipStream_t st) {
+                       int n_sink, int n_window, const uint32_t* thr, Cand* cand, int64_t cand_ld,
+                       uint32_t* cand_cnt, hipStream_t st) {
   const int64_t n = hi - lo;
   dim3 grid((unsigned)((n + kValuKeysPerWg - 1) / kValuKeysPerWg), (unsigned)a.B);
   const size_t lds = sizeof(float) * ((size_t)a.H * a.d + a.H);
   hipLaunchKernelGGL((k_score_valu<QT, KT>), grid, dim3(256), lds, st, a.q, a.w, a.k, a.k_ld, a.L, a.H, a.d, a.t,
-                     lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, seg_cnt, seg_data);
+                     lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, cand, cand_ld, cand_cnt);
   return hipGetLastError();
 }
 
-template <int NMT, bool FP8>
+// Workgroups per launch: about one per CU for 8-query workgroups (two per CU for 4-query ones), each walking
+// many tiles when the range is long.
+constexpr int kScoreTargetThreads = 256 * 512;
+
+template <int NMT, bool FP8, int NQ>
 hipError_t launch_mfma(const IndexerArgs& a, int64_t lo, int64_t hi, int mode, float* scores, int64_t scores_ld,
-                       int n_sink, int n_window, const uint32_t* thr, uint32_t* seg_cnt, Cand* seg_data,
-                       hipStream_t st) {
-  const int64_t n = hi - lo;
-  dim3 grid((unsigned)((n + kMfmaKeysPerWg - 1) / kMfmaKeysPerWg), (unsigned)((a.B + 3) / 4));
-  hipLaunchKernelGGL((k_score_mfma<NMT, FP8>), grid, dim3(256), 0, st, a.q, a.w, a.k, a.k_ld, a.L, a.B, a.t, lo, hi,
-                     mode, scores, scores_ld, n_sink, n_window, thr, seg_cnt, seg_data);
+                       int n_sink, int n_window, const uint32_t* thr, Cand* cand, int64_t cand_ld,
+                       uint32_t* cand_cnt, hipStream_t st) {
+  const int64_t n_tiles = (hi - lo + kTileKeys - 1) / kTileKeys;
+  const int groups = (a.B + NQ - 1) / NQ;
+  const int64_t target = kScoreTargetThreads / (64 * NQ);
+  int64_t per_group = (target + groups - 1) / groups;
+  if (per_group > n_tiles) per_group = n_tiles;
+  if (per_group < 1) per_group = 1;
+  dim3 grid((unsigned)per_group, (unsigned)groups);
+  hipLaunchKernelGGL((k_score_mfma<NMT, FP8, NQ>), grid, dim3(64 * NQ), 0, st, a.q, a.w, a.k, a.k_ld, a.L, a.B, a.t,
+                     lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, cand, cand_ld, cand_cnt);
   return hipGetLastError();
 }
 
@@ -354,21 +428,27 @@ bool score_uses_mfma(const IndexerArgs& a) {
 int score_keys_per_wg(const IndexerArgs& a) { return score_uses_mfma(a) ? kMfmaKeysPerWg : kValuKeysPerWg; }
 
 hipError_t launch_score(const IndexerArgs& a, int64_t lo, int64_t hi, int mode, float* scores, int64_t scores_ld,
-                        int n_sink, int n_window, const uint32_t* thr, uint32_t* seg_cnt, Cand* seg_data,
-                        hipStream_t st) {
+                        int n_sink, int n_window, const uint32_t* thr, Cand* cand, int64_t cand_ld,
+                        uint32_t* cand_cnt, hipStream_t st) {
   if (hi <= lo) return hipSuccess;
   if (score_uses_mfma(a)) {
     const bool fp8 = a.q_dtype == 2;
-    if (a.H == 64)
-      return fp8 ? launch_mfma<2, true>(a, lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, seg_cnt, seg_data, st)
-                 : launch_mfma<2, false>(a, lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, seg_cnt, seg_data, st);
-    return fp8 ? launch_mfma<1, true>(a, lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, seg_cnt, seg_data, st)
-               : launch_mfma<1, false>(a, lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, seg_cnt, seg_data, st);
+    const bool wide = a.B >= 8;
+#define SA_SCORE(NMT, F8, NQ) \
+  return launch_mfma<NMT, F8, NQ>(a, lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, cand, cand_ld, cand_cnt, st)
+    if (a.H == 64) {
+      if (fp8) { if (wide) SA_SCORE(2, true, 8); else SA_SCORE(2, true, 4); }
+      else { if (wide) SA_SCORE(2, false, 8); else SA_SCORE(2, false, 4); }
+    } else {
+      if (fp8) { if (wide) SA_SCORE(1, true, 8); else SA_SCORE(1, true, 4); }
+      else { if (wide) SA_SCORE(1, false, 8); else SA_SCORE(1, false, 4); }
+    }
+#undef SA_SCORE
   }
   const int qt = a.q_dtype, kt = a.k_dtype;
-  if (qt == 0 && kt == 0) return launch_valu<0, 0>(a, lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, seg_cnt, seg_data, st);
-  if (qt == 1 && kt == 1) return launch_valu<1, 1>(a, lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, seg_cnt, seg_data, st);
-  if (qt == 2 && kt == 2) return launch_valu<2, 2>(a, lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, seg_cnt, seg_data, st);
+  if (qt == 0 && kt == 0) return launch_valu<0, 0>(a, lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, cand, cand_ld, cand_cnt, st);
+  if (qt == 1 && kt == 1) return launch_valu<1, 1>(a, lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, cand, cand_ld, cand_cnt, st);
+  if (qt == 2 && kt == 2) return launch_valu<2, 2>(a, lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, cand, cand_ld, cand_cnt, st);
   return hipErrorInvalidValue;
 }
 

@@ -112,10 +112,10 @@ struct SplitLWs {
   uint32_t* thr;
   sa::Cand* kept;
   int32_t* kept_n;
-  uint32_t* seg_cnt;
-  sa::Cand* seg_data;
-  sa::Cand* gather;
-  int64_t n_seg_max, gather_cap;
+  uint32_t* cnt[2];      // candidate counters of alternating key ranges
+  sa::Cand* cand;        // [B, cand_ld] candidates of the current key range
+  sa::Cand* gather;      // [B, gather_cap]
+  int64_t cand_ld, gather_cap;
   size_t bytes;
 };
 
@@ -125,14 +125,15 @@ SplitLWs carve_split_l(void* ws, const sa::IndexerArgs& a, int k) {
   int64_t max_level = 0;
   for (size_t i = 0; i + 1 < lv.size(); ++i) max_level = std::max(max_level, lv[i + 1] - lv[i]);
   SplitLWs w{};
-  w.n_seg_max = (max_level + kpw - 1) / kpw;
-  w.gather_cap = k + w.n_seg_max * kpw;
+  w.cand_ld = max_level;
+  w.gather_cap = k + max_level;
   Carver c(ws);
   w.thr = c.take<uint32_t>(a.B);
   w.kept_n = c.take<int32_t>(a.B);
+  w.cnt[0] = c.take<uint32_t>(a.B);
+  w.cnt[1] = c.take<uint32_t>(a.B);
   w.kept = c.take<sa::Cand>((size_t)a.B * k);
-  w.seg_cnt = c.take<uint32_t>((size_t)a.B * w.n_seg_max);
-  w.seg_data = c.take<sa::Cand>((size_t)a.B * w.n_seg_max * kpw);
+  w.cand = c.take<sa::Cand>((size_t)a.B * w.cand_ld);
   w.gather = c.take<sa::Cand>((size_t)a.B * w.gather_cap);
   w.bytes = align_up(c.off, 256);
   return w;
@@ -190,7 +191,7 @@ SA_API int sa_index_score(const void* q, int q_dtype, const float* w, const void
   if (scores_ld < s_end - s_begin) return fail(SA_ERR_SHAPE, "scores_ld < s_end - s_begin");
   if (B == 0 || s_end == s_begin) return SA_OK;
   const sa::IndexerArgs a = make_indexer(q, q_dtype, w, k, k_dtype, k_ld, L, B, H, d, t);
-  hipError_t e = sa::launch_score(a, s_begin, s_end, sa::kScoreDense, scores, scores_ld, 0, 0, nullptr, nullptr,
+  hipError_t e = sa::launch_score(a, s_begin, s_end, sa::kScoreDense, scores, scores_ld, 0, 0, nullptr, nullptr, 0,
                                   nullptr, (hipStream_t)stream);
   return e == hipSuccess ? SA_OK : hip_fail(e, "sa_index_score");
 }
@@ -231,24 +232,26 @@ SA_API int sa_select_topk(const void* q, int q_dtype, const float* w, const void
     const PerQueryWs w2 = carve_per_query(ws, a, k_sparse);
     e = sa::launch_stream_select(a, k_sparse, n_sink, n_window, w2.buf, w2.buf_n, w2.cap, s);
     if (e != hipSuccess) return hip_fail(e, "sa_select_topk (stream)");
-    e = sa::launch_merge(B, k_sparse, w2.buf, w2.cap, w2.buf_n, nullptr, nullptr, 0, 0, w2.gather, w2.cap, nullptr,
+    e = sa::launch_merge(B, k_sparse, w2.buf, w2.cap, w2.buf_n, nullptr, 0, nullptr, 0, nullptr, w2.gather, w2.cap, nullptr,
                          nullptr, nullptr, 1, idx, idx_ld, n_sel, s);
     return e == hipSuccess ? SA_OK : hip_fail(e, "sa_select_topk (final merge)");
   }
   const SplitLWs w2 = carve_split_l(ws, a, k_sparse);
   const int kpw = sa::score_keys_per_wg(a);
   const std::vector<int64_t> lv = levels(L, k_sparse, kpw);
-  if ((e = sa::launch_fill_u32(w2.thr, B, 0u, s)) != hipSuccess) return hip_fail(e, "sa_select_topk (init)");
-  if ((e = sa::launch_fill_u32(reinterpret_cast<uint32_t*>(w2.kept_n), B, 0u, s)) != hipSuccess)
-    return hip_fail(e, "sa_select_topk (init)");
+  // Key ranges in ascending position order. The first range writes every candidate to a fixed slot; later ranges
+  // append only candidates above the k-th key kept so far, counting them in alternating counters that the previous
+  // merge cleared.
   for (size_t i = 0; i + 1 < lv.size(); ++i) {
     const int64_t lo = lv[i], hi = lv[i + 1];
-    const int n_seg = (int)((hi - lo + kpw - 1) / kpw);
-    const bool last = i + 2 == lv.size();
-    e = sa::launch_score(a, lo, hi, sa::kScoreEmit, nullptr, 0, n_sink, n_window, w2.thr, w2.seg_cnt, w2.seg_data, s);
+    const bool first = i == 0, last = i + 2 == lv.size();
+    uint32_t* cnt = w2.cnt[i % 2];
+    e = sa::launch_score(a, lo, hi, first ? sa::kScoreAll : sa::kScoreEmit, nullptr, 0, n_sink, n_window,
+                         first ? nullptr : w2.thr, w2.cand, w2.cand_ld, first ? nullptr : cnt, s);
     if (e != hipSuccess) return hip_fail(e, "sa_select_topk (score)");
-    e = sa::launch_merge(B, k_sparse, w2.kept, k_sparse, w2.kept_n, w2.seg_cnt, w2.seg_data, n_seg, kpw, w2.gather,
-                         w2.gather_cap, w2.kept, w2.kept_n, w2.thr, last ? 1 : 0, idx, idx_ld, n_sel, s);
+    e = sa::launch_merge(B, k_sparse, first ? nullptr : w2.kept, k_sparse, w2.kept_n, w2.cand, w2.cand_ld,
+                         first ? nullptr : cnt, hi - lo, w2.cnt[(i + 1) % 2], w2.gather, w2.gather_cap, w2.kept,
+                         w2.kept_n, w2.thr, last ? 1 : 0, idx, idx_ld, n_sel, s);
     if (e != hipSuccess) return hip_fail(e, "sa_select_topk (merge)");
   }
   return SA_OK;
@@ -284,12 +287,10 @@ SA_API int sa_bucket_build(const void* k, int k_dtype, int64_t k_ld, int64_t L, 
 
 SA_API size_t sa_bucket_select_workspace(int32_t B, int32_t n_buckets, int32_t top_b) {
   if (B < 0 || n_buckets < 1 || top_b < 1) return 0;
-  const int n_wg = sa::bucket_score_wgs(n_buckets);
   Carver c(nullptr);
-  c.take<uint32_t>((size_t)B * n_wg);
-  c.take<sa::Cand>((size_t)B * n_wg * 4);
+  c.take<sa::Cand>((size_t)B * n_buckets);
   c.take<int32_t>(B);
-  c.take<sa::Cand>((size_t)B * n_wg * 4);
+  c.take<sa::Cand>((size_t)B * n_buckets);
   c.take<int32_t>((size_t)B * top_b);
   return align_up(c.off, 256);
 }
@@ -309,16 +310,14 @@ SA_API int sa_bucket_select(const void* q, int q_dtype, int32_t B, int32_t d, co
   const size_t need = sa_bucket_select_workspace(B, n_buckets, top_b);
   if (!ws || ws_bytes < need) return fail(SA_ERR_WORKSPACE, "workspace needs %zu bytes", need);
   if (B == 0) return SA_OK;
-  const int n_wg = sa::bucket_score_wgs(n_buckets);
   Carver c(ws);
-  uint32_t* seg_cnt = c.take<uint32_t>((size_t)B * n_wg);
-  sa::Cand* seg_data = c.take<sa::Cand>((size_t)B * n_wg * 4);
+  sa::Cand* cand = c.take<sa::Cand>((size_t)B * n_buckets);
   int32_t* n_chosen = c.take<int32_t>(B);
-  sa::Cand* gather = c.take<sa::Cand>((size_t)B * n_wg * 4);
+  sa::Cand* gather = c.take<sa::Cand>((size_t)B * n_buckets);
   int32_t* chosen = c.take<int32_t>((size_t)B * top_b);
   hipError_t e = sa::launch_bucket_select(q, q_dtype, B, d, reps, offsets, members, n_buckets, L, t, top_b, n_sink,
-                                          n_window, idx, cap, n_sel, buckets_out, seg_cnt, seg_data, n_chosen,
-                                          gather, chosen, (hipStream_t)stream);
+                                          n_window, idx, cap, n_sel, buckets_out, cand, n_chosen, gather, chosen,
+                                          (hipStream_t)stream);
   return e == hipSuccess ? SA_OK : hip_fail(e, "sa_bucket_select");
 }
 

@@ -81,6 +81,18 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Waits until at most N vector-memory operations of this wave are outstanding (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmem_below() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier for an LDS hand-off: this wave's LDS operations complete, then s_barrier. Unlike
+// __syncthreads() it does not wait for outstanding global-memory operations, so asynchronous copies issued for
+// later tiles stay in flight; the asm memory clobber keeps the compiler from moving memory accesses across it.
+// Data copied into LDS asynchronously must be waited for (wait_vmem*) by each wave before the barrier.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // 16-byte asynchronous copy global -> LDS: lane i of the wave writes lds_base + 16 * i.
 __device__ __forceinline__ void dma16(const void* gsrc, void* lds_base) {
   __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)(lds_base), 16, 0, 0);

@@ -25,7 +25,7 @@ struct Cand {
   int32_t pos;
 };
 
-enum ScoreMode { kScoreDense = 0, kScoreEmit = 1 };
+enum ScoreMode { kScoreDense = 0, kScoreEmit = 1, kScoreAll = 2 };
 
 // Positions handled by one workgroup of the scoring kernel chosen for these arguments.
 int score_keys_per_wg(const IndexerArgs& a);
@@ -34,21 +34,24 @@ bool score_uses_mfma(const IndexerArgs& a);
 
 // Scores positions [lo, hi).
 //  kScoreDense: scores[b * scores_ld + (s - lo)] = I(b, s), or -inf for s > t_b.
-//  kScoreEmit:  for candidates s (n_sink <= s <= t_b - n_window) with score_key(I) > thr_key[b], append
-//               (key, s) to segment (b, wg): seg_data[(b * n_wg + wg) * keys_per_wg + i], count in
-//               seg_cnt[b * n_wg + wg], where n_wg = ceil((hi - lo) / keys_per_wg).
+//  kScoreAll:   cand[b * cand_ld + (s - lo)] = {score_key(I), s} for candidates s (n_sink <= s <= t_b - n_window),
+//               {0, -1} otherwise.
+//  kScoreEmit:  candidates with score_key(I) > thr_key[b] (any candidate when thr_key is NULL) are appended to
+//               cand[b * cand_ld + ...]; each workgroup reserves its range with one atomicAdd on cand_cnt[b], which
+//               must be 0 before the launch and ends as the number of appended candidates.
 hipError_t launch_score(const IndexerArgs& a, int64_t lo, int64_t hi, int mode, float* scores, int64_t scores_ld,
-                        int n_sink, int n_window, const uint32_t* thr_key, uint32_t* seg_cnt, Cand* seg_data,
-                        hipStream_t stream);
+                        int n_sink, int n_window, const uint32_t* thr_key, Cand* cand, int64_t cand_ld,
+                        uint32_t* cand_cnt, hipStream_t stream);
 
 // Exact top-k merge, one workgroup per query:
-//   candidates = kept_in[b * kept_ld + (0:kept_n_in[b])] (if kept_in) U all segment entries of query b; the
-//   gather buffer must hold kept_n_in[b] + n_seg * seg_cap entries per query.
+//   candidates = kept_in[b * kept_ld + (0:kept_n_in[b])] (if kept_in) U cand[b * cand_ld + (0:n_b)] with
+//   n_b = cand_cnt ? cand_cnt[b] : cand_n; entries whose key is 0 are empty slots. The gather buffer must hold
+//   kept_n_in[b] + n_b entries per query. When zero_cnt is set, zero_cnt[b] is cleared for the next key range.
 //   Keeps the k best by (key desc, pos asc) in kept_out[b, :] (count in kept_n_out[b]) and sets thr_out[b] to the
 //   k-th key (0 when fewer than k candidates exist). final_mode 1 writes instead idx[b, :] with the positions
 //   ascending and -1 padding, plus n_sel[b]; final_mode 2 writes them in (key desc, position asc) order.
-hipError_t launch_merge(int B, int k, const Cand* kept_in, int kept_ld, const int32_t* kept_n_in,
-                        const uint32_t* seg_cnt, const Cand* seg_data, int n_seg, int seg_cap, Cand* gather,
+hipError_t launch_merge(int B, int k, const Cand* kept_in, int kept_ld, const int32_t* kept_n_in, const Cand* cand,
+                        int64_t cand_ld, const uint32_t* cand_cnt, int64_t cand_n, uint32_t* zero_cnt, Cand* gather,
                         int64_t gather_cap, Cand* kept_out, int32_t* kept_n_out, uint32_t* thr_out, int final_mode,
                         int32_t* idx, int idx_ld, int32_t* n_sel, hipStream_t stream);
 int merge_max_k();
@@ -72,14 +75,12 @@ hipError_t launch_bucket_build(const void* k, int k_dtype, int64_t k_ld, int64_t
                                int32_t* table, const BucketBuildPlan& plan, hipStream_t stream);
 
 int bucket_expand_max();
-// Workspace of the Flat search: seg_cnt [B * n_wg], seg_data [B * n_wg * 4], n_chosen [B], gather [B * n_wg * 4],
-// chosen [B * top_b], with n_wg = bucket_score_wgs(n_buckets).
-int bucket_score_wgs(int n_buckets);
+// Workspace of the Flat search: cand [B * n_buckets], n_chosen [B], gather [B * n_buckets], chosen [B * top_b].
 hipError_t launch_bucket_select(const void* q, int q_dtype, int B, int d, const float* reps, const int32_t* offsets,
                                 const int32_t* members, int n_buckets, int64_t L, const int32_t* t, int top_b,
                                 int n_sink, int n_window, int32_t* idx, int cap, int32_t* n_sel,
-                                int32_t* buckets_out, uint32_t* seg_cnt, Cand* seg_data, int32_t* n_chosen,
-                                Cand* gather, int32_t* chosen, hipStream_t stream);
+                                int32_t* buckets_out, Cand* cand, int32_t* n_chosen, Cand* gather, int32_t* chosen,
+                                hipStream_t stream);
 
 // ---- attention ---------------------------------------------------------------------------------------------------
 struct AttnArgs {

@@ -57,11 +57,13 @@ ALGOS = [sa.SA_TOPK_SPLIT_L, sa.SA_TOPK_PER_QUERY]
 
 @pytest.mark.parametrize("algo", ALGOS)
 @pytest.mark.parametrize("dtype", ["bf16", "e4m3"])
-def test_topk_integer_exact_with_ties(algo, dtype):
-    """Integer-valued q, k in {-2..2} and w in {0,1,2}: scores are exact, selection must match bit for bit."""
-    B, H, d, L, kk = 6, 64, 128, 40000, 700
+@pytest.mark.parametrize("B", [6, 9])
+def test_topk_integer_exact_with_ties(algo, dtype, B):
+    """Integer-valued q, k in {-2..2} and w in {0,1,2}: scores are exact, selection must match bit for bit.
+    B = 6 runs 4-query workgroups, B = 9 runs 8-query workgroups with a partly empty second group."""
+    H, d, L, kk = 64, 128, 40000, 700
     q, w, k = _inputs(5, B, H, d, L, dtype, integer=True)
-    ts = [L - 1, 39000, 20000, 17000, 5000, 900]
+    ts = ([L - 1, 39000, 20000, 17000, 5000, 900, 33333, 123, 39999])[:B]
     t = torch.tensor(ts, dtype=torch.int32, device=DEV)
     idx, nsel = sa.sa_select_topk(q, w, k, kk, n_sink=3, n_window=50, t=t, algo=algo)
     torch.cuda.synchronize()
