@@ -256,6 +256,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
 #pragma unroll
   for (int j = 0; j < 4; ++j) vofs[j] = row0 * kRowBytes + 16 * ((2 * j + hsel) ^ mv) + 8 * (li & 1);
 
+  wait_vmem();  // the Q fragments are in registers before the tile copies start counting
   const int n_pre = n_tiles < kNBuf - 1 ? n_tiles : kNBuf - 1;
   for (int p = 0; p < n_pre; ++p) issue(p, p);
   for (int tile = 0; tile < n_tiles; ++tile) {

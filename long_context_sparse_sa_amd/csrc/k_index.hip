@@ -236,6 +236,7 @@ __global__ __launch_bounds__(64 * NQ) void k_score_mfma(const void* __restrict__
     if (mode == kScoreEmit && thr_key) thr = thr_key[b];
     load_query<NMT, E4M3>(q, w, b, lane, qa, wv);
   }
+  wait_vmem();  // the query fragments are in registers before the tile copies start counting
 
   int n_emit = 0;
   auto flush = [&]() {

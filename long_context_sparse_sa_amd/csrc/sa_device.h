@@ -79,13 +79,18 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
 }
 
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// Waits until at most N vector-memory operations of this wave are outstanding (they complete in issue order).
+// Waits until at most N vector-memory operations of this wave are outstanding (loads complete in issue order).
+// Emitted as a real s_waitcnt (vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt left at their no-wait maxima) so
+// that the compiler's own wait bookkeeping sees it and does not add waits of its own for older loads; the empty
+// asm with a memory clobber keeps memory accesses from moving across it.
 template <int N>
 __device__ __forceinline__ void wait_vmem_below() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+  asm volatile("" ::: "memory");
 }
+
+__device__ __forceinline__ void wait_vmem() { wait_vmem_below<0>(); }
 
 // Workgroup barrier for an LDS hand-off: this wave's LDS operations complete, then s_barrier. Unlike
 // __syncthreads() it does not wait for outstanding global-memory operations, so asynchronous copies issued for
@@ -94,8 +99,28 @@ __device__ __forceinline__ void wait_vmem_below() {
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // 16-byte asynchronous copy global -> LDS: lane i of the wave writes lds_base + 16 * i.
+//
+// Issued from inline asm on purpose. When the compiler sees a global->LDS copy it cannot tell which LDS bytes
+// it writes, so it drains every outstanding vector-memory operation (s_waitcnt vmcnt(0)) before the next LDS
+// read, which serialises a multi-buffered pipeline on the copies just issued for later tiles. Hidden in asm, the
+// copy is ordered only by the waits the caller places (wait_vmem_below / wait_vmem, then lds_barrier) before
+// reading the tile. Loads return in issue order, so "at most N outstanding" means every copy older than the
+// newest N has landed, whatever other loads the compiler interleaves. M0 (the LDS base of the copy) is saved
+// and restored so that no compiler-held M0 value is disturbed; the s_nop covers the M0-write -> LDS-DMA hazard.
+// The copy has no register result: the address registers are consumed at issue.
 __device__ __forceinline__ void dma16(const void* gsrc, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)(lds_base), 16, 0, 0);
+  const uint32_t m0 =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_base);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(gsrc), "s"(m0)
+      : "memory");
 }
 
 // LDS transpose read of four 16-bit values (gfx950 ds_read_b64_tr_b16). Within each group of 16 lanes, output
