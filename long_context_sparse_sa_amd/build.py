@@ -27,6 +27,12 @@ FLAGS = [
 ]
 
 
+# Per-source extra flags. The attention kernel keeps its MFMA accumulators in VGPRs: its online-softmax rescale
+# works on them with VALU instructions, and the default AGPR form copies them between the two register files on
+# every tile.
+EXTRA = {"k_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def hipcc() -> str:
     p = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(p):
@@ -37,7 +43,8 @@ def hipcc() -> str:
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [hipcc(), *FLAGS, *lang, "-I", os.path.join(ROOT, "include"), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *FLAGS, *EXTRA.get(src, []), *lang, "-I", os.path.join(ROOT, "include"), "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

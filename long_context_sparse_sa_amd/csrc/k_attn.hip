@@ -166,42 +166,62 @@ constexpr int kRowBytes = 1152;
 constexpr int kTileRows = 32;
 constexpr int kTileBytes = kTileRows * kRowBytes;        // 36864
 constexpr int kDmaPerWave = kTileBytes / 1024 / 4;       // 9 wave instructions of 1 KB per tile
-constexpr int kNBuf = 4;                                 // LDS tiles: up to 3 in flight while one is consumed
+constexpr int kNBuf = 3;                                 // LDS tiles: up to 2 in flight while one is consumed
 constexpr int kMaxRowsPerSplit = 512;
-constexpr int kQSteps = kRowElems / 32;                  // 18 k-steps of 32 dims
+constexpr int kQSteps = kRowElems / 2 / 16;              // 18 k-steps of 16 dims: each wave takes half the dims
 constexpr float kRescaleSlack = 8.f;                     // log2 headroom before the running max is raised
+constexpr int kPrefK = 4;                                // K fragments in flight ahead of the S^T MFMAs
+constexpr int kPrefV = 3;                                // V^T fragments in flight ahead of the O^T MFMAs
 
 // chunk c of row n lives at chunk slot c ^ (n & 7) (the XOR stays inside the aligned group of 8 chunks)
 __device__ __forceinline__ int chunk_slot(int n, int c) { return c ^ (n & 7); }
 
-// Grid: 1-D, block id = group + n_groups * split with group = (query, 64-head group). When n_groups is a multiple
-// of 8, every split of a group (and the combine blocks of its heads) runs on the same XCD and shares its L2.
+// Grid: 1-D. A unit is (query b, row split); every unit has H / 64 head groups. Block id
+// (u / 8) * 8 * HG + hg * 8 + u % 8 puts all head groups of unit u on the same XCD (block id mod 8), so the
+// second gather of a tile's rows is served by that XCD's L2.
+__device__ __forceinline__ void attn_block(int HG, int* u, int* hg) {
+  const int blk = (int)blockIdx.x;
+  *u = (blk / (8 * HG)) * 8 + blk % 8;
+  *hg = (blk / 8) % HG;
+}
+
+// Workgroup = 4 waves = 2 head blocks of 32 heads x 2 halves. The two waves of a head block each compute S^T = K Q^T
+// for their 32 heads over one half of the 576 dims (32x32x16 MFMA, their half of the query heads in registers),
+// add each other's partial through LDS (both get the same sum), run the same online softmax, and each accumulates
+// O^T = V^T P^T for its half of the value columns. P stays in the registers S^T produced it in: the C layout of
+// S^T holds, per lane, 8 rows of one head for each 16-row k-step, and the V^T fragments are read (LDS transpose
+// reads) in that same row order.
 template <int DV>
 __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                                                    int64_t kv_ld, int64_t L, int H, const int32_t* __restrict__ t,
                                                    const int32_t* __restrict__ idx, int idx_ld,
                                                    const int32_t* __restrict__ n_sel, int n_sink, int n_window,
-                                                   float scale_log2, int rows_per_split, int n_splits,
+                                                   float scale_log2, int rows_per_split, int n_splits, int n_units,
                                                    float* __restrict__ part_o, float* __restrict__ part_ml,
                                                    uint16_t* __restrict__ out, float* __restrict__ lse) {
-  constexpr int NT = DV / 16;  // 16-wide output tiles per head group
+  constexpr int DVH = DV / 2;   // value columns per wave
+  constexpr int NT = DVH / 32;  // 32-wide output tiles per wave
   __shared__ __attribute__((aligned(1024))) char tiles[kNBuf][kTileBytes];
   __shared__ int32_t pos_s[kMaxRowsPerSplit];
-  const int n_groups = (int)gridDim.x / n_splits;
-  const int group = (int)blockIdx.x % n_groups, split = (int)blockIdx.x / n_groups;
+  __shared__ f32x4 exch[4][4][kWave];  // partial S^T of each wave, by register group and lane
   const int HG = H / 64;
-  const int b = group / HG, hg = group % HG;
+  int u, hg;
+  attn_block(HG, &u, &hg);
+  if (u >= n_units) return;
+  const int b = u / n_splits, split = u % n_splits;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-  const int g = lane >> 4;         // lane group 0..3
-  const int li = lane & 15;        // lane in group
-  const int h = 64 * hg + 16 * wave + li;  // the head this lane works for
-  const int64_t bh = (int64_t)b * H + h;
+  const int hsel = lane >> 5;       // which 8 of each 16 dims / rows this lane carries
+  const int j = lane & 31;
+  const int hb = wave >> 1, dh = wave & 1;
+  const int head = 64 * hg + 32 * hb + j;
+  const int64_t bh = (int64_t)b * H + head;
+  const int dv0 = dh * DVH;
 
-  // Q^T fragments (B operand): head h, dims 32 ks + 8 g .. +8
+  // Q^T fragments (B operand): head `head`, dims 288 dh + 16 ks + 8 hsel .. +8
   bf16x8 qf[kQSteps];
 #pragma unroll
   for (int ks = 0; ks < kQSteps; ++ks)
-    qf[ks] = *reinterpret_cast<const bf16x8*>(q + bh * kRowElems + 32 * ks + 8 * g);
+    qf[ks] = *reinterpret_cast<const bf16x8*>(q + bh * kRowElems + 288 * dh + 16 * ks + 8 * hsel);
 
   const RowList R = make_rows(b, L, t, idx, idx_ld, n_sel, n_sink, n_window);
   const int n_rows = R.count();
@@ -212,11 +232,12 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
 
   if (n_my <= 0) {
     if (n_splits == 1) {
-      for (int i = g; i < DV; i += 4) out[bh * DV + i] = 0;
-      if (lse && g == 0) lse[bh] = -INFINITY;
-    } else if (g == 0) {
-      part_ml[(bh * n_splits + split) * 2 + 0] = -INFINITY;
-      part_ml[(bh * n_splits + split) * 2 + 1] = 0.f;
+      for (int i = tid; i < 64 * DV; i += 256) out[((int64_t)b * H + 64 * hg) * DV + i] = 0;
+      if (lse && tid < 64) lse[(int64_t)b * H + 64 * hg + tid] = -INFINITY;
+    } else if (tid < 64) {
+      const int64_t bh0 = (int64_t)b * H + 64 * hg + tid;
+      part_ml[(bh0 * n_splits + split) * 2 + 0] = -INFINITY;
+      part_ml[(bh0 * n_splits + split) * 2 + 1] = 0.f;
     }
     return;
   }
@@ -228,72 +249,96 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
   const int64_t ld_bytes = kv_ld * 2;
   auto issue = [&](int tile, int buf) {
 #pragma unroll
-    for (int j = 0; j < kDmaPerWave; ++j) {
-      const int slot = (wave * kDmaPerWave + j) * 64 + lane;
+    for (int jj = 0; jj < kDmaPerWave; ++jj) {
+      const int slot = (wave * kDmaPerWave + jj) * 64 + lane;
       const int n = slot / kRowChunks;
       const int c = chunk_slot(n, slot % kRowChunks);
       const int s = pos_s[tile * kTileRows + n];
-      dma16(kvb + (int64_t)s * ld_bytes + c * 16, &tiles[buf][(wave * kDmaPerWave + j) * 1024]);
+      dma16(kvb + (int64_t)s * ld_bytes + c * 16, &tiles[buf][(wave * kDmaPerWave + jj) * 1024]);
     }
   };
 
-  f32x4 o[NT];
+  f32x16 o[NT];
 #pragma unroll
-  for (int i = 0; i < NT; ++i) o[i] = f32x4{};
+  for (int i = 0; i < NT; ++i) o[i] = f32x16{};
   float m_use = -INFINITY, l_run = 0.f;  // exponents are taken relative to m_use (log2 domain)
 
-  // Per-lane LDS offsets. K fragment of row n = 16 mt + li, chunk 4 ks + g sits at
-  //   n * 1152 + 16 * ((4 ks + g) ^ (n & 7)) = li * 1152 + kofs[ks & 1] + 128 (ks >> 1) + 18432 mt,
-  // and the transpose-read source of row r0 (+16), chunk 2 nt + h at r0 * 1152 + vofs[nt & 3] + 128 (nt >> 2) (+18432),
-  // so every unrolled access is a base register plus a compile-time offset.
-  const int mk = li & 7;
-  const int kofs0 = li * kRowBytes + 16 * (g ^ mk);
-  const int kofs1 = li * kRowBytes + 16 * ((g ^ mk) ^ 4);
-  const int row0 = 4 * g + (li >> 2);
-  const int mv = row0 & 7;
-  const int hsel = (li & 3) >> 1;
-  int vofs[4];
+  // Per-lane LDS offsets (every unrolled access is a base register plus a compile-time offset).
+  // K fragment (A operand of S^T): row j, chunk 36 dh + 2 ks + hsel at its chunk slot:
+  //   kofs[ks & 3] + 128 * (ks >> 2).
+  int kofs[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) vofs[j] = row0 * kRowBytes + 16 * ((2 * j + hsel) ^ mv) + 8 * (li & 1);
+  for (int qq = 0; qq < 4; ++qq) kofs[qq] = j * kRowBytes + 16 * chunk_slot(j, 36 * dh + 2 * qq + hsel);
+  // V^T fragment (A operand of O^T) through transpose reads: in each 16-lane group gq = lane / 16, lane
+  // a + 4 r4 addresses row 4 hv + r4 (hv = gq / 2) at columns dv0 + 32 nt + 16 (gq & 1) + 4 a; the second read
+  // takes rows + 8, the second k-step rows + 16. Columns 4 a .. 4 a + 3 sit in chunk C0 + 4 nt at byte 8 (a & 1).
+  const int gq = lane >> 4, qa = lane & 3, r4 = (lane >> 2) & 3;
+  const int hv = gq >> 1;
+  const int vrow = 4 * hv + r4;
+  const int C0 = dv0 / 8 + 2 * (gq & 1) + (qa >> 1);
+  int vofs[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par) vofs[par] = vrow * kRowBytes + 16 * chunk_slot(vrow, C0 + 4 * par) + 8 * (qa & 1);
 
   wait_vmem();  // the Q fragments are in registers before the tile copies start counting
   const int n_pre = n_tiles < kNBuf - 1 ? n_tiles : kNBuf - 1;
   for (int p = 0; p < n_pre; ++p) issue(p, p);
   for (int tile = 0; tile < n_tiles; ++tile) {
-    // wait for this tile's copies; the (at most two) later tiles may stay in flight
-    const int newer = n_tiles - 1 - tile;
-    if (newer >= 2) wait_vmem_below<2 * kDmaPerWave>();
-    else if (newer == 1) wait_vmem_below<kDmaPerWave>();
+    // wait for this tile's copies; the next tile may stay in flight
+    if (tile + 1 < n_tiles) wait_vmem_below<kDmaPerWave>();
     else wait_vmem_below<0>();
     lds_barrier();
     if (tile + kNBuf - 1 < n_tiles) issue(tile + kNBuf - 1, (tile + kNBuf - 1) % kNBuf);
     const char* tb = tiles[tile % kNBuf];
 
-    // S^T (rows x heads): two 16-row halves
-    f32x4 s[2];
+    // S^T (32 rows x 32 heads) over all 576 dims
+    // partial S^T (32 rows x 32 heads) over this wave's 288 dims, then the partner's half through LDS. The K
+    // fragments run kPrefK steps ahead of the MFMAs in a register ring; the scheduling fences keep the compiler
+    // from pulling each read next to its MFMA, which would expose the LDS latency on every step.
+    auto k_frag = [&](int ks) { return *reinterpret_cast<const bf16x8*>(tb + kofs[ks & 3] + 128 * (ks >> 2)); };
+    bf16x8 kr[kPrefK];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      s[mt] = f32x4{};
+    for (int i = 0; i < kPrefK; ++i) kr[i] = k_frag(i);
+    f32x16 s = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < kQSteps; ++ks) {
-        const char* kp = tb + ((ks & 1) ? kofs1 : kofs0) + 128 * (ks >> 1) + 18432 * mt;
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kp);
-        s[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], s[mt], 0, 0, 0);
-      }
+    for (int ks = 0; ks < kQSteps; ++ks) {
+      const bf16x8 cur = kr[ks % kPrefK];
+      if (ks + kPrefK < kQSteps) kr[ks % kPrefK] = k_frag(ks + kPrefK);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[ks], s, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // this lane holds head h at tile rows 16 mt + 4 g + r
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) exch[wave][g4][lane] = f32x4{s[4 * g4], s[4 * g4 + 1], s[4 * g4 + 2], s[4 * g4 + 3]};
+    lds_barrier();
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x4 other = exch[wave ^ 1][g4][lane];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[4 * g4 + e] += other[e];
+    }
+    auto v_frag = [&](int i) {  // V^T fragment of step i = 2 nt + kk
+      const int nt = i >> 1, kk = i & 1;
+      const char* vp = tb + vofs[nt & 1] + 128 * (nt >> 1) + 18432 * kk;
+      const i16x4 v0 = lds_read_tr16(vp);
+      const i16x4 v1 = lds_read_tr16(vp + 9216);
+      // whole-vector shuffle + bit_cast (a bit_cast of a single ext-vector element is not used here: clang lowers
+      // it to element 0 for every index)
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    bf16x8 vr[kPrefV];
+#pragma unroll
+    for (int i = 0; i < kPrefV; ++i) vr[i] = v_frag(i);
+
+    // register r of this lane holds row 8 (r / 4) + 4 hsel + r % 4 of head `head`
     const int valid = n_my - tile * kTileRows;
-    float x[2][4];
+    float x[16];
     float mt_max = -INFINITY;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 16 * mt + 4 * g + r;
-        x[mt][r] = row < valid ? s[mt][r] * scale_log2 : -INFINITY;
-        mt_max = fmaxf(mt_max, x[mt][r]);
-      }
-    mt_max = fmaxf(mt_max, __shfl_xor(mt_max, 16, kWave));
+    for (int r = 0; r < 16; ++r) {
+      const int row = 8 * (r >> 2) + 4 * hsel + (r & 3);
+      x[r] = row < valid ? s[r] * scale_log2 : -INFINITY;
+      mt_max = fmaxf(mt_max, x[r]);
+    }
     mt_max = fmaxf(mt_max, __shfl_xor(mt_max, 32, kWave));
     // raise the reference only when this tile would exceed it by more than 2^kRescaleSlack
     const bool raise = mt_max > m_use + kRescaleSlack;
@@ -305,82 +350,122 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
       for (int nt = 0; nt < NT; ++nt) o[nt] = o[nt] * alpha;
       m_use = m_new;
     }
-    bf16x8 pf;
+    bf16x8 pf[2];
     float psum = 0.f;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = exp2f(x[mt][r] - m_use);
+      for (int e = 0; e < 8; ++e) {
+        const float p = exp2f(x[8 * kk + e] - m_use);
         psum += p;
-        pf[4 * mt + r] = (__bf16)p;
+        pf[kk][e] = (__bf16)p;
       }
     l_run += psum;
 
-    // O^T (dv x heads) += V^T P^T; V^T fragments through LDS transpose reads.
-    // A operand slots e = 0..3 -> tile rows 4 g + e, e = 4..7 -> rows 16 + 4 g + (e - 4), matching pf.
+    // O^T (value columns x heads) += V^T P^T; k-step kk covers rows 16 kk + {4 hsel .. +3, 8 + 4 hsel .. +3}.
+    // Step i = 2 nt + kk; its V^T fragment (two transpose reads) is fetched kPrefV steps ahead.
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const char* vp = tb + vofs[nt & 3] + 128 * (nt >> 2);
-      const i16x4 v0 = lds_read_tr16(vp);
-      const i16x4 v1 = lds_read_tr16(vp + 18432);
-      // whole-vector shuffle + bit_cast (a bit_cast of a single ext-vector element is not used here: clang lowers
-      // it to element 0 for every index)
-      const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-      o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, o[nt], 0, 0, 0);
+    for (int i = 0; i < 2 * NT; ++i) {
+      const bf16x8 cur = vr[i % kPrefV];
+      if (i + kPrefV < 2 * NT) vr[i % kPrefV] = v_frag(i + kPrefV);
+      o[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, pf[i & 1], o[i >> 1], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
-  // lanes h, h^16, h^32, h^48 hold disjoint rows of head h: reduce the sum
-  l_run += __shfl_xor(l_run, 16, kWave);
+  // lanes j and j + 32 hold disjoint rows of the same head: add their sums
   l_run += __shfl_xor(l_run, 32, kWave);
+  // register r of tile nt holds column dv0 + 32 nt + 8 (r / 4) + 4 hsel + r % 4 of head `head`
   if (n_splits == 1) {
     const float inv = 1.f / l_run;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      uint16_t* dst = out + bh * DV + 16 * nt + 4 * g;
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dst[r] = f32_to_bf16_bits(o[nt][r] * inv);
-    }
-    if (lse && g == 0) lse[bh] = (m_use + log2f(l_run)) * kLn2;
+      for (int g4 = 0; g4 < 4; ++g4) {
+        uint16_t* dst = out + bh * DV + dv0 + 32 * nt + 8 * g4 + 4 * hsel;
+        const uint32_t lo = f32_to_bf16_bits(o[nt][4 * g4 + 0] * inv) | ((uint32_t)f32_to_bf16_bits(o[nt][4 * g4 + 1] * inv) << 16);
+        const uint32_t hi = f32_to_bf16_bits(o[nt][4 * g4 + 2] * inv) | ((uint32_t)f32_to_bf16_bits(o[nt][4 * g4 + 3] * inv) << 16);
+        *reinterpret_cast<uint2*>(dst) = uint2{lo, hi};
+      }
+    if (lse && dh == 0 && hsel == 0) lse[bh] = (m_use + log2f(l_run)) * kLn2;
   } else {
-    float* dst = part_o + (bh * n_splits + split) * DV;
+    float* dst = part_o + (bh * n_splits + split) * DV + dv0;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) *reinterpret_cast<f32x4*>(dst + 16 * nt + 4 * g) = o[nt];
-    if (g == 0) {
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *reinterpret_cast<f32x4*>(dst + 32 * nt + 8 * g4 + 4 * hsel) =
+            f32x4{o[nt][4 * g4], o[nt][4 * g4 + 1], o[nt][4 * g4 + 2], o[nt][4 * g4 + 3]};
+    if (dh == 0 && hsel == 0) {
       part_ml[(bh * n_splits + split) * 2 + 0] = m_use;
       part_ml[(bh * n_splits + split) * 2 + 1] = l_run;
     }
   }
 }
 
-// Exact merge of the splits of one (query, head): o = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i.
-// Block id = group + n_groups * j, head = 64 hg + j, matching the XCD of the attention blocks of that group.
+// Exact merge of the row splits of one (query, head): o = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i.
+// One block of 256 threads per (query, head): the split weights are computed once into LDS, then thread i owns
+// four value columns and issues its split loads eight at a time.
+constexpr int kCombineThreads = 256;
+constexpr int kCombineMaxLdsSplits = 1024;
+
+__device__ __forceinline__ float block_reduce(float v, bool is_max, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float x = __shfl_xor(v, o, kWave);
+    v = is_max ? fmaxf(v, x) : v + x;
+  }
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < kCombineThreads / kWave; ++w) r = is_max ? fmaxf(r, red[w]) : r + red[w];
+  __syncthreads();
+  return r;
+}
+
 template <int DT>
-__global__ __launch_bounds__(64) void k_attn_combine(const float* __restrict__ part_o,
-                                                     const float* __restrict__ part_ml, int n_splits, int n_groups,
-                                                     int H, int d_v, void* __restrict__ out, float* __restrict__ lse) {
-  const int group = (int)blockIdx.x % n_groups, j = (int)blockIdx.x / n_groups;
-  const int HG = H / 64;
-  const int64_t bh = (int64_t)(group / HG) * H + 64 * (group % HG) + j;
+__global__ __launch_bounds__(kCombineThreads) void k_attn_combine(const float* __restrict__ part_o,
+                                                                  const float* __restrict__ part_ml, int n_splits,
+                                                                  int d_v, void* __restrict__ out,
+                                                                  float* __restrict__ lse) {
+  __shared__ float wsh[kCombineMaxLdsSplits];
+  __shared__ float red[kCombineThreads / kWave];
+  const int64_t bh = blockIdx.x;
+  const int tid = threadIdx.x;
   const float* ml = part_ml + bh * n_splits * 2;
   float M = -INFINITY;
-  for (int i = 0; i < n_splits; ++i) M = fmaxf(M, ml[2 * i]);
+  for (int i = tid; i < n_splits; i += kCombineThreads) M = fmaxf(M, ml[2 * i]);
+  M = block_reduce(M, true, red);
   float Ls = 0.f;
-  if (M != -INFINITY)
-    for (int i = 0; i < n_splits; ++i) Ls += exp2f(ml[2 * i] - M) * ml[2 * i + 1];
+  for (int i = tid; i < n_splits; i += kCombineThreads) {
+    const float w = M == -INFINITY ? 0.f : exp2f(ml[2 * i] - M);
+    if (i < kCombineMaxLdsSplits) wsh[i] = w;
+    Ls += w * ml[2 * i + 1];
+  }
+  Ls = block_reduce(Ls, false, red);  // its barriers also publish wsh
   const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
-  for (int dv = 4 * threadIdx.x; dv < d_v; dv += 4 * blockDim.x) {
+  auto weight = [&](int i) { return i < kCombineMaxLdsSplits ? wsh[i] : exp2f(ml[2 * i] - M); };
+  const int dv = 4 * tid;
+  if (dv < d_v) {
     f32x4 acc = f32x4{};
-    if (M != -INFINITY)
-      for (int i = 0; i < n_splits; ++i) {
-        const float wgt = exp2f(ml[2 * i] - M);
-        if (wgt != 0.f) acc += wgt * *reinterpret_cast<const f32x4*>(part_o + (bh * n_splits + i) * d_v + dv);
+    if (M != -INFINITY) {
+      const float* po = part_o + bh * n_splits * d_v + dv;
+      for (int i0 = 0; i0 < n_splits; i0 += 8) {
+        f32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          v[u] = i0 + u < n_splits ? *reinterpret_cast<const f32x4*>(po + (int64_t)(i0 + u) * d_v) : f32x4{};
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (i0 + u < n_splits) acc += weight(i0 + u) * v[u];
       }
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) store_out<DT>(out, bh * d_v + dv + r, acc[r] * inv);
   }
-  if (lse && threadIdx.x == 0) lse[bh] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
+  if (lse && tid == 0) lse[bh] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
 }
 
 }  // namespace
@@ -443,22 +528,25 @@ hipError_t launch_attn(const AttnArgs& a, const AttnPlan& p, void* ws, hipStream
   }
   float* part_o = reinterpret_cast<float*>(ws);
   float* part_ml = part_o ? part_o + (size_t)a.B * a.H * p.n_splits * a.d_v : nullptr;
-  const int n_groups = a.B * (a.H / 64);
-  dim3 grid((unsigned)(n_groups * p.n_splits));
+  const int HG = a.H / 64;
+  const int n_units = a.B * p.n_splits;
+  dim3 grid((unsigned)((n_units + 7) / 8 * 8 * HG));
   const float sl2 = a.scale * kLog2e;
   const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q);
   const uint16_t* kv = reinterpret_cast<const uint16_t*>(a.kv);
   uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
   if (a.d_v == 576)
     hipLaunchKernelGGL(k_attn_mfma<576>, grid, dim3(256), 0, st, q, kv, a.kv_ld, a.L, a.H, a.t, a.idx, a.idx_ld,
-                       a.n_sel, a.n_sink, a.n_window, sl2, p.rows_per_split, p.n_splits, part_o, part_ml, out, a.lse);
+                       a.n_sel, a.n_sink, a.n_window, sl2, p.rows_per_split, p.n_splits, n_units, part_o, part_ml, out,
+                       a.lse);
   else
     hipLaunchKernelGGL(k_attn_mfma<512>, grid, dim3(256), 0, st, q, kv, a.kv_ld, a.L, a.H, a.t, a.idx, a.idx_ld,
-                       a.n_sel, a.n_sink, a.n_window, sl2, p.rows_per_split, p.n_splits, part_o, part_ml, out, a.lse);
+                       a.n_sel, a.n_sink, a.n_window, sl2, p.rows_per_split, p.n_splits, n_units, part_o, part_ml, out,
+                       a.lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_splits == 1) return e;
-  hipLaunchKernelGGL(k_attn_combine<1>, dim3((unsigned)(a.B * a.H)), dim3(64), 0, st, part_o, part_ml, p.n_splits,
-                     n_groups, a.H, a.d_v, a.out, a.lse);
+  hipLaunchKernelGGL(k_attn_combine<1>, dim3((unsigned)(a.B * a.H)), dim3(kCombineThreads), 0, st, part_o, part_ml,
+                     p.n_splits, a.d_v, a.out, a.lse);
   return hipGetLastError();
 }
 

@@ -271,8 +271,16 @@ hipError_t launch_bucket_select(const void* q, int q_dtype, int B, int d, const 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   int32_t* order = buckets_out ? buckets_out : chosen;
-  e = launch_merge(B, top_b, nullptr, 0, nullptr, cand, nb, nullptr, nb, nullptr, gather, nb, nullptr, nullptr, nullptr,
-                   2, order, top_b, n_chosen, st);
+  MergeIn in{};
+  in.cand = cand;
+  in.cand_ld = nb;
+  in.n_slots = nb;
+  MergeOut out{};
+  out.final_mode = 2;
+  out.idx = order;
+  out.idx_ld = top_b;
+  out.n_sel = n_chosen;
+  e = launch_merge(B, top_b, in, gather, nb, out, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_expand, dim3((unsigned)B), dim3(1024), 0, st, order, n_chosen, top_b, offsets, members, L, t,
                      n_sink, n_window, idx, cap, n_sel);

@@ -33,17 +33,15 @@ __global__ __launch_bounds__(256) void k_score_valu(const void* __restrict__ q, 
                                                     int mode, float* __restrict__ scores, int64_t scores_ld,
                                                     int n_sink, int n_window, const uint32_t* __restrict__ thr_key,
                                                     Cand* __restrict__ cand, int64_t cand_ld,
-                                                    uint32_t* __restrict__ cand_cnt) {
+                                                    uint32_t* __restrict__ seg_cnt) {
   extern __shared__ float smem[];
   float* qs = smem;            // [H * d]
   float* ws = smem + H * d;    // [H]
-  __shared__ int n_emit, emit_base;
-  __shared__ Cand staged[kValuKeysPerWg];
+  __shared__ int wave_n[kValuKeysPerWg / kWave];
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
   for (int i = tid; i < H * d; i += blockDim.x) qs[i] = load_elem<QT>(q, (int64_t)b * H * d + i);
   for (int i = tid; i < H; i += blockDim.x) ws[i] = w[(int64_t)b * H + i];
-  if (tid == 0) n_emit = 0;
   __syncthreads();
 
   const int64_t s = lo + (int64_t)blockIdx.x * kValuKeysPerWg + tid;
@@ -67,11 +65,21 @@ __global__ __launch_bounds__(256) void k_score_valu(const void* __restrict__ q, 
     if (s < hi) cand[(int64_t)b * cand_ld + (s - lo)] = is_cand ? Cand{key, (int32_t)s} : Cand{0u, -1};
     return;
   }
-  if (is_cand && key > (thr_key ? thr_key[b] : 0u)) staged[atomicAdd(&n_emit, 1)] = Cand{key, (int32_t)s};
+  // emission in position order: this workgroup's segment holds its candidates above the threshold
+  const bool emit = is_cand && key > (thr_key ? thr_key[b] : 0u);
+  const uint64_t m = ballot(emit);
+  const int wave = tid / kWave;
+  if (lane_id() == 0) wave_n[wave] = __popcll(m);
   __syncthreads();
-  if (tid == 0) emit_base = n_emit ? (int)atomicAdd(&cand_cnt[b], (uint32_t)n_emit) : 0;
-  __syncthreads();
-  if (tid < n_emit) cand[(int64_t)b * cand_ld + emit_base + tid] = staged[tid];
+  int before = 0, total = 0;
+#pragma unroll
+  for (int i = 0; i < kValuKeysPerWg / kWave; ++i) {
+    before += i < wave ? wave_n[i] : 0;
+    total += wave_n[i];
+  }
+  Cand* seg = cand + (int64_t)b * cand_ld + (int64_t)blockIdx.x * kValuKeysPerWg;
+  if (emit) seg[before + lanes_below(m)] = Cand{key, (int32_t)s};
+  if (tid == 0) seg_cnt[(int64_t)b * gridDim.x + blockIdx.x] = (uint32_t)total;
 }
 
 // ---- MFMA scoring building blocks ---------------------------------------------------------------------------------
@@ -197,11 +205,12 @@ __device__ __forceinline__ float score_ntile(const char* tile, int nt, int lane,
   return part + wave_shfl_xor(part, 32);
 }
 
-// Split-L scoring: workgroup = NQ waves = NQ queries. The 64-position tiles of [lo, hi) are dealt round-robin
-// to the gridDim.x workgroups of each query group, whose queries stay in registers. bf16 keys arrive by
+// Split-L scoring: workgroup = NQ waves = NQ queries. Each of the gridDim.x workgroups of a query group scores a
+// contiguous run of the 64-position tiles of [lo, hi), with its queries in registers. bf16 keys arrive by
 // asynchronous DMA into four LDS buffers (three tiles in flight); e4m3 keys are loaded two tiles ahead into a
 // register ring, converted and committed to two LDS buffers. Emitted candidates are staged per wave in LDS and
-// flushed with one atomicAdd on the query's counter whenever the stage could overflow, and at the end.
+// flushed, in position order, to the workgroup's own segment whenever the stage could overflow and at the end;
+// the segment's count is stored last.
 template <int NMT, bool E4M3, int NQ>
 __global__ __launch_bounds__(64 * NQ) void k_score_mfma(const void* __restrict__ q, const float* __restrict__ w,
                                                         const void* __restrict__ k, int64_t k_ld, int64_t L, int B,
@@ -210,7 +219,7 @@ __global__ __launch_bounds__(64 * NQ) void k_score_mfma(const void* __restrict__
                                                         int n_sink, int n_window,
                                                         const uint32_t* __restrict__ thr_key,
                                                         Cand* __restrict__ cand, int64_t cand_ld,
-                                                        uint32_t* __restrict__ cand_cnt) {
+                                                        uint32_t* __restrict__ seg_cnt) {
   typedef KeyLoader<E4M3, NQ> KL;
   constexpr int kNBuf = E4M3 ? 2 : 4;
   constexpr int kStage = 512;
@@ -221,9 +230,13 @@ __global__ __launch_bounds__(64 * NQ) void k_score_mfma(const void* __restrict__
   const int wave = threadIdx.x / kWave;
   const int b = blockIdx.y * NQ + wave;
   const bool active = b < B;
+  // this workgroup scores the contiguous run of tiles [first_tile, first_tile + n_tiles)
   const int64_t tiles_total = (hi - lo + kTileKeys - 1) / kTileKeys;
-  const int64_t n_tiles = tiles_total > (int64_t)blockIdx.x ? (tiles_total - 1 - blockIdx.x) / gridDim.x + 1 : 0;
-  auto tile_start = [&](int64_t i) { return lo + ((int64_t)blockIdx.x + i * gridDim.x) * kTileKeys; };
+  const int64_t run = (tiles_total + gridDim.x - 1) / gridDim.x;
+  const int64_t first_tile = (int64_t)blockIdx.x * run;
+  const int64_t left = tiles_total - first_tile;
+  const int64_t n_tiles = left < 0 ? 0 : (left < run ? left : run);
+  auto tile_start = [&](int64_t i) { return lo + (first_tile + i) * kTileKeys; };
   const char* kbytes = reinterpret_cast<const char*>(k);
   const int64_t ld_bytes = k_ld * (E4M3 ? 1 : 2);
 
@@ -238,13 +251,12 @@ __global__ __launch_bounds__(64 * NQ) void k_score_mfma(const void* __restrict__
   }
   wait_vmem();  // the query fragments are in registers before the tile copies start counting
 
-  int n_emit = 0;
+  int n_emit = 0;     // staged in LDS
+  int64_t n_out = 0;  // already in this workgroup's segment
+  Cand* seg = cand + (int64_t)b * cand_ld + first_tile * kTileKeys;
   auto flush = [&]() {
-    int base = 0;
-    if (lane == 0) base = (int)atomicAdd(&cand_cnt[b], (uint32_t)n_emit);
-    base = __shfl(base, 0, kWave);
-    Cand* dst = cand + (int64_t)b * cand_ld + base;
-    for (int j = lane; j < n_emit; j += kWave) dst[j] = staged[wave][j];
+    for (int j = lane; j < n_emit; j += kWave) seg[n_out + j] = staged[wave][j];
+    n_out += n_emit;
     n_emit = 0;
   };
   auto score_tile = [&](const char* tile, int64_t s0) {
@@ -311,7 +323,10 @@ __global__ __launch_bounds__(64 * NQ) void k_score_mfma(const void* __restrict__
       if (i + 1 < n_tiles) step(i + 1, std::integral_constant<int, 1>{});
     }
   }
-  if (active && mode == kScoreEmit && n_emit > 0) flush();
+  if (active && mode == kScoreEmit) {
+    if (n_emit > 0) flush();
+    if (lane == 0) seg_cnt[(int64_t)b * gridDim.x + blockIdx.x] = (uint32_t)n_out;
+  }
 }
 
 // Streaming selection for many queries (prefill chunk): workgroup = 4 waves = 4 queries, each wave streams its
@@ -389,12 +404,12 @@ __global__ __launch_bounds__(256) void k_stream_select(const void* __restrict__ 
 template <int QT, int KT>
 hipError_t launch_valu(const IndexerArgs& a, int64_t lo, int64_t hi, int mode, float* scores, int64_t scores_ld,
                        int n_sink, int n_window, const uint32_t* thr, Cand* cand, int64_t cand_ld,
-                       uint32_t* cand_cnt, hipStream_t st) {
+                       uint32_t* seg_cnt, hipStream_t st) {
   const int64_t n = hi - lo;
   dim3 grid((unsigned)((n + kValuKeysPerWg - 1) / kValuKeysPerWg), (unsigned)a.B);
   const size_t lds = sizeof(float) * ((size_t)a.H * a.d + a.H);
   hipLaunchKernelGGL((k_score_valu<QT, KT>), grid, dim3(256), lds, st, a.q, a.w, a.k, a.k_ld, a.L, a.H, a.d, a.t,
-                     lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, cand, cand_ld, cand_cnt);
+                     lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, cand, cand_ld, seg_cnt);
   return hipGetLastError();
 }
 
@@ -402,19 +417,31 @@ hipError_t launch_valu(const IndexerArgs& a, int64_t lo, int64_t hi, int mode, f
 // many tiles when the range is long.
 constexpr int kScoreTargetThreads = 256 * 512;
 
-template <int NMT, bool FP8, int NQ>
-hipError_t launch_mfma(const IndexerArgs& a, int64_t lo, int64_t hi, int mode, float* scores, int64_t scores_ld,
-                       int n_sink, int n_window, const uint32_t* thr, Cand* cand, int64_t cand_ld,
-                       uint32_t* cand_cnt, hipStream_t st) {
-  const int64_t n_tiles = (hi - lo + kTileKeys - 1) / kTileKeys;
-  const int groups = (a.B + NQ - 1) / NQ;
+// Workgroups per query group, and the tiles of each contiguous run, for n_tiles tiles: about kScoreTargetThreads
+// threads in flight, and no workgroup left without tiles.
+void mfma_grid(int B, int NQ, int64_t n_tiles, int64_t* n_wg, int64_t* run) {
+  const int groups = B > NQ ? (B + NQ - 1) / NQ : 1;
   const int64_t target = kScoreTargetThreads / (64 * NQ);
   int64_t per_group = (target + groups - 1) / groups;
   if (per_group > n_tiles) per_group = n_tiles;
   if (per_group < 1) per_group = 1;
-  dim3 grid((unsigned)per_group, (unsigned)groups);
+  if (n_tiles < 1) n_tiles = 1;
+  const int64_t r0 = (n_tiles + per_group - 1) / per_group;
+  *n_wg = (n_tiles + r0 - 1) / r0;
+  *run = (n_tiles + *n_wg - 1) / *n_wg;
+}
+
+template <int NMT, bool FP8, int NQ>
+hipError_t launch_mfma(const IndexerArgs& a, int64_t lo, int64_t hi, int mode, float* scores, int64_t scores_ld,
+                       int n_sink, int n_window, const uint32_t* thr, Cand* cand, int64_t cand_ld,
+                       uint32_t* seg_cnt, hipStream_t st) {
+  const int64_t n_tiles = (hi - lo + kTileKeys - 1) / kTileKeys;
+  int64_t n_wg, run;
+  mfma_grid(a.B, NQ, n_tiles, &n_wg, &run);
+  if (n_tiles < 1 || a.B < 1) return hipSuccess;
+  dim3 grid((unsigned)n_wg, (unsigned)((a.B + NQ - 1) / NQ));
   hipLaunchKernelGGL((k_score_mfma<NMT, FP8, NQ>), grid, dim3(64 * NQ), 0, st, a.q, a.w, a.k, a.k_ld, a.L, a.B, a.t,
-                     lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, cand, cand_ld, cand_cnt);
+                     lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, cand, cand_ld, seg_cnt);
   return hipGetLastError();
 }
 
@@ -428,15 +455,30 @@ bool score_uses_mfma(const IndexerArgs& a) {
 
 int score_keys_per_wg(const IndexerArgs& a) { return score_uses_mfma(a) ? kMfmaKeysPerWg : kValuKeysPerWg; }
 
+EmitPlan score_emit_plan(const IndexerArgs& a, int64_t lo, int64_t hi) {
+  EmitPlan p{0, 0};
+  if (hi <= lo) return p;
+  if (score_uses_mfma(a)) {
+    int64_t n_wg, run;
+    mfma_grid(a.B, a.B >= 8 ? 8 : 4, (hi - lo + kTileKeys - 1) / kTileKeys, &n_wg, &run);
+    p.n_seg = (int)n_wg;
+    p.seg_cap = run * kTileKeys;
+  } else {
+    p.n_seg = (int)((hi - lo + kValuKeysPerWg - 1) / kValuKeysPerWg);
+    p.seg_cap = kValuKeysPerWg;
+  }
+  return p;
+}
+
 hipError_t launch_score(const IndexerArgs& a, int64_t lo, int64_t hi, int mode, float* scores, int64_t scores_ld,
                         int n_sink, int n_window, const uint32_t* thr, Cand* cand, int64_t cand_ld,
-                        uint32_t* cand_cnt, hipStream_t st) {
+                        uint32_t* seg_cnt, hipStream_t st) {
   if (hi <= lo) return hipSuccess;
   if (score_uses_mfma(a)) {
     const bool fp8 = a.q_dtype == 2;
     const bool wide = a.B >= 8;
 #define SA_SCORE(NMT, F8, NQ) \
-  return launch_mfma<NMT, F8, NQ>(a, lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, cand, cand_ld, cand_cnt, st)
+  return launch_mfma<NMT, F8, NQ>(a, lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, cand, cand_ld, seg_cnt, st)
     if (a.H == 64) {
       if (fp8) { if (wide) SA_SCORE(2, true, 8); else SA_SCORE(2, true, 4); }
       else { if (wide) SA_SCORE(2, false, 8); else SA_SCORE(2, false, 4); }
@@ -447,9 +489,9 @@ hipError_t launch_score(const IndexerArgs& a, int64_t lo, int64_t hi, int mode, 
 #undef SA_SCORE
   }
   const int qt = a.q_dtype, kt = a.k_dtype;
-  if (qt == 0 && kt == 0) return launch_valu<0, 0>(a, lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, cand, cand_ld, cand_cnt, st);
-  if (qt == 1 && kt == 1) return launch_valu<1, 1>(a, lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, cand, cand_ld, cand_cnt, st);
-  if (qt == 2 && kt == 2) return launch_valu<2, 2>(a, lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, cand, cand_ld, cand_cnt, st);
+  if (qt == 0 && kt == 0) return launch_valu<0, 0>(a, lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, cand, cand_ld, seg_cnt, st);
+  if (qt == 1 && kt == 1) return launch_valu<1, 1>(a, lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, cand, cand_ld, seg_cnt, st);
+  if (qt == 2 && kt == 2) return launch_valu<2, 2>(a, lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, cand, cand_ld, seg_cnt, st);
   return hipErrorInvalidValue;
 }
 

@@ -2,13 +2,15 @@
 // equation; SI section, the sparse part is the top-K over positions outside sink and window).
 //
 // One workgroup (1024 threads) per query gathers its candidates -- the k kept from earlier key ranges plus the
-// ones the scoring kernels emitted -- and keeps exactly the k best by (score desc, position asc):
-//   * candidate keys are staged in LDS; a min/max pass finds the bits all of them share, and radix passes (8-bit
-//     digits, privatized histograms) run only over the bits below that common prefix;
-//   * when several candidates share the k-th key, radix passes over their positions keep the lowest ones.
-// Intermediate calls keep the k best and publish the k-th key as the next threshold; the final call sorts the k
-// positions ascending (final_mode 1) or in (key desc, position asc) order (final_mode 2, used for bucket ids) with
-// a bitonic sort in LDS whose stages of stride <= 64 run inside one wave, and writes idx / n_sel.
+// slots or segments a scoring launch wrote -- and keeps exactly the k best by (score desc, position asc):
+//   * the gather and the output are order-preserving (ballot masks of 16 rounds of 1024 entries, one scan per
+//     batch), so inputs in ascending position order give outputs in ascending position order without a sort;
+//   * keys and positions live in LDS, or in the gather buffer in global memory when they do not fit; the storage
+//     is a compile-time choice, so every access is a plain LDS or global load;
+//   * the bits all keys share are skipped; 8-bit radix passes with eight privatized histograms find the k-th key;
+//     when several candidates share it, radix passes over their positions keep the lowest ones.
+// Intermediate calls keep the k best and publish the k-th key as the next threshold. Bucket ranking (final_mode
+// 2) is the one caller that needs (key desc, position asc) order; it sorts its at most top_b ids in LDS.
 #include "sa_device.h"
 #include "sa_internal.h"
 #include "sa_wave_select.h"
@@ -18,185 +20,281 @@ namespace {
 
 constexpr int kMergeThreads = 1024;
 constexpr int kMergeWaves = kMergeThreads / kWave;
-constexpr int kHistCopies = 4;        // private histograms, one per 4 waves
+constexpr int kHistCopies = 8;
+constexpr int kRounds = 16;  // rounds of 1024 entries compacted per batch
+constexpr int kBatch = kRounds * kMergeThreads;
 constexpr int kMaxSortK = 16384;
-constexpr int kBatch = 8;             // candidates loaded per thread before they are processed
-constexpr int kLdsBytes = 163840;     // LDS per workgroup on gfx950
+constexpr int kLdsBytes = 163840;  // LDS per workgroup on gfx950
 
 struct MergeShared {
-  uint32_t hist[kHistCopies][256];
-  uint32_t tot[256];
+  union {
+    uint32_t hist[kHistCopies][256];  // selection passes
+    struct {
+      int32_t off[kMergeThreads];  // gather: output offset and count of each segment of a chunk
+      int32_t cnt[kMergeThreads];
+    } seg;
+  } u;
+  uint64_t masks[kRounds][kMergeWaves];
+  int32_t moff[kRounds * kMergeWaves];
+  int32_t wsum[kMergeWaves];
+  int32_t batch_total;
   uint32_t digit, before, in_bin;
   uint32_t kmin, kmax;
-  int n, out;
 };
 
-__device__ __forceinline__ void wave_lds_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
+// Order-preserving compaction of one batch: entry r * 1024 + tid (r < kRounds) is flagged by f[r]. Returns the
+// number of flagged entries; slot[r] receives the rank of entry r among them. All threads must call.
+__device__ __forceinline__ int batch_slots(MergeShared& sh, const bool (&f)[kRounds], int (&slot)[kRounds], int tid) {
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  uint64_t m[kRounds];
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    m[r] = ballot(f[r]);
+    if (lane == 0) sh.masks[r][wave] = m[r];
+  }
+  __syncthreads();
+  if (wave == 0) {  // the 256 (round, wave) counts in entry order, four per lane
+    int c[4], local = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = 4 * lane + j;
+      c[j] = __popcll(sh.masks[e / kMergeWaves][e % kMergeWaves]);
+      local += c[j];
+    }
+    const int incl = (int)wave_inclusive_scan((uint32_t)local, lane);
+    int run = incl - local;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sh.moff[4 * lane + j] = run;
+      run += c[j];
+    }
+    if (lane == kWave - 1) sh.batch_total = incl;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) slot[r] = sh.moff[r * kMergeWaves + wave] + lanes_below(m[r]);
+  return sh.batch_total;
+}
 
-// Ascending bitonic sort of a[0, n2) in LDS (n2 a power of two, >= 2), all threads of the block. Thread t handles
-// pair indices t, t + 1024, ...; for strides <= 64 the 64 pairs of a wave touch 128 consecutive elements that no
-// other wave touches, so those stages need no block barrier.
-template <typename T>
-__device__ __forceinline__ void bitonic_sort(T* a, int n2, int tid) {
+// Block-wide exclusive scan of one int per thread; *total receives the sum. All threads must call.
+__device__ __forceinline__ int block_scan(MergeShared& sh, int v, int tid, int* total) {
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  const int incl = (int)wave_inclusive_scan((uint32_t)v, lane);
+  if (lane == kWave - 1) sh.wsum[wave] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kMergeWaves; ++w) {
+    const int x = sh.wsum[w];
+    before += w < wave ? x : 0;
+    all += x;
+  }
+  __syncthreads();
+  *total = all;
+  return before + incl - v;
+}
+
+__device__ __forceinline__ void note_minmax(uint32_t& lmin, uint32_t& lmax, uint32_t key) {
+  lmin = key < lmin ? key : lmin;
+  lmax = key > lmax ? key : lmax;
+}
+
+// One 8-bit radix pass over the entries whose value matches (prefix, mask), then the digit search in the order of
+// selection (descending for keys, ascending for positions). `val(i, &v)` yields the radix value of entry i, or
+// false when the entry does not take part.
+template <typename Val>
+__device__ __forceinline__ void radix_pass(MergeShared& sh, int n, Val val, uint32_t prefix, uint32_t mask, int shift,
+                                           uint32_t need, bool descending, int tid) {
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  for (int i = tid; i < kHistCopies * 256; i += kMergeThreads) (&sh.u.hist[0][0])[i] = 0;
+  __syncthreads();
+  uint32_t* h = sh.u.hist[wave % kHistCopies];
+  for (int base = 0; base < n; base += 4 * kMergeThreads) {
+    uint32_t v[4];
+    bool ok[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = base + j * kMergeThreads + tid;
+      ok[j] = i < n && val(i, &v[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (ok[j] && (v[j] & mask) == prefix) atomicAdd(&h[(v[j] >> shift) & 255u], 1u);
+  }
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t c[4], local = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int o = 4 * lane + j;
+      const int bin = descending ? 255 - o : o;
+      uint32_t s = 0;
+#pragma unroll
+      for (int cp = 0; cp < kHistCopies; ++cp) s += sh.u.hist[cp][bin];
+      c[j] = s;
+      local += s;
+    }
+    const uint32_t incl = wave_inclusive_scan(local, lane);
+    uint32_t run = incl - local;
+    int found = -1;
+    uint32_t fb = 0, fc = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (found < 0 && run < need && run + c[j] >= need) {
+        found = 4 * lane + j;
+        fb = run;
+        fc = c[j];
+      }
+      run += c[j];
+    }
+    const uint64_t m = ballot(found >= 0);
+    if (m && lane == (int)__builtin_ctzll(m)) {
+      sh.digit = (uint32_t)(descending ? 255 - found : found);
+      sh.before = fb;
+      sh.in_bin = fc;
+    }
+  }
+  __syncthreads();
+}
+
+// Ascending bitonic sort of a[0, n2) in LDS (n2 a power of two, >= 2), all threads of the block.
+__device__ __forceinline__ void bitonic_sort(uint64_t* a, int n2, int tid) {
   for (int size = 2; size <= n2; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       for (int i = tid; i < (n2 >> 1); i += kMergeThreads) {
         const int lo = 2 * i - (i & (stride - 1));
         const int hi = lo + stride;
         const bool up = (lo & size) == 0;
-        const T x = a[lo], y = a[hi];
+        const uint64_t x = a[lo], y = a[hi];
         if ((x > y) == up) {
           a[lo] = y;
           a[hi] = x;
         }
       }
-      const int next = stride > 1 ? stride >> 1 : size;
-      if (stride > 64 || next > 64)
-        __syncthreads();
-      else
-        wave_lds_fence();
+      __syncthreads();
     }
   }
-  __syncthreads();
 }
 
-// Block-wide histogram pass over the candidates matching (prefix, mask) on digit (v >> shift) & 255, then the
-// digit search. `src(i, &v)` gives the radix value of candidate i, or false when the candidate does not take part.
-template <typename Src>
-__device__ __forceinline__ void radix_pass(MergeShared& sh, int n, Src src, uint32_t prefix, uint32_t mask,
-                                           int shift, uint32_t need, bool descending, int tid, int wave) {
-  for (int i = tid; i < kHistCopies * 256; i += kMergeThreads) (&sh.hist[0][0])[i] = 0;
-  __syncthreads();
-  uint32_t* h = sh.hist[wave % kHistCopies];
-  for (int i = tid; i < n; i += kMergeThreads) {
-    uint32_t v;
-    if (src(i, &v) && (v & mask) == prefix) atomicAdd(&h[(v >> shift) & 255u], 1u);
-  }
-  __syncthreads();
-  if (tid < 256) {
-    uint32_t s = 0;
-#pragma unroll
-    for (int c = 0; c < kHistCopies; ++c) s += sh.hist[c][tid];
-    sh.tot[tid] = s;
-  }
-  __syncthreads();
-  if (tid < kWave) {
-    uint32_t before, in_bin;
-    const uint32_t dg = find_digit(sh.tot, need, descending, tid, &before, &in_bin);
-    if (tid == 0) {
-      sh.digit = dg;
-      sh.before = before;
-      sh.in_bin = in_bin;
-    }
-  }
-  __syncthreads();
-}
-
-// Dynamic LDS: [sort area: sort_bytes][candidate keys: up to key_cap]. The gather buffer always holds every
-// candidate; when they do not all fit in LDS the keys are read from it instead.
-__global__ __launch_bounds__(kMergeThreads) void k_merge(int k, const Cand* __restrict__ kept_in, int kept_ld,
-                                                         const int32_t* __restrict__ kept_n_in,
-                                                         const Cand* __restrict__ cand, int64_t cand_ld,
-                                                         const uint32_t* __restrict__ cand_cnt, int64_t cand_n,
-                                                         uint32_t* __restrict__ zero_cnt,
-                                                         Cand* __restrict__ gather, int64_t gather_cap,
-                                                         Cand* __restrict__ kept_out, int32_t* __restrict__ kept_n_out,
-                                                         uint32_t* __restrict__ thr_out, int final_mode,
-                                                         int32_t* __restrict__ idx, int idx_ld,
-                                                         int32_t* __restrict__ n_sel, int sort_bytes, int key_cap) {
-  __shared__ MergeShared sh;
-  extern __shared__ __attribute__((aligned(16))) char dyn[];
-  int32_t* sorted = reinterpret_cast<int32_t*>(dyn);
-  uint32_t* keys_s = reinterpret_cast<uint32_t*>(dyn + sort_bytes);
-  const int b = blockIdx.x;
+// Gather, select and write one query's result, with keys K[] and positions P[] in LDS (kLds) or in the gather
+// buffer in global memory.
+template <bool kLds>
+__device__ __forceinline__ void merge_body(MergeShared& sh, int b, int k, const MergeIn& in, const MergeOut& out,
+                                           uint32_t* __restrict__ K, int32_t* __restrict__ P, int nk,
+                                           uint64_t* sort_area) {
   const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
-  Cand* g = gather + (int64_t)b * gather_cap;
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  uint32_t lmin = 0xFFFFFFFFu, lmax = 0u;
 
-  const int nk = kept_in ? kept_n_in[b] : 0;
-  const int64_t nc = cand ? (cand_cnt ? (int64_t)cand_cnt[b] : cand_n) : 0;
-  const bool fits = nk + nc <= key_cap;
-  if (tid == 0) {
-    sh.n = 0;
-    sh.out = 0;
-    sh.kmin = 0xFFFFFFFFu;
-    sh.kmax = 0u;
-  }
-  __syncthreads();
-
-  // ---- gather: kBatch independent loads per thread, then one LDS atomic per wave for the slots
-  auto gather_from = [&](const Cand* src, int64_t cnt) {
-    for (int64_t base = 0; base < cnt; base += (int64_t)kMergeThreads * kBatch) {
-      Cand c[kBatch];
+  // ---- gather: the kept entries, then the slots (compacted) or the segments, all in input order
+  if (nk) {
+    const Cand* src = in.kept + (int64_t)b * in.kept_ld;
+    for (int base = 0; base < nk; base += 4 * kMergeThreads) {
+      Cand c[4];
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int64_t i = base + j * kMergeThreads + tid;
-        c[j] = i < cnt ? src[i] : Cand{0u, -1};
+      for (int j = 0; j < 4; ++j) {
+        const int i = base + j * kMergeThreads + tid;
+        c[j] = i < nk ? src[i] : Cand{0u, 0};
       }
-      uint64_t m[kBatch];
-      int tot = 0;
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        m[j] = ballot(c[j].key != 0u);  // key 0 marks an empty slot
-        tot += __popcll(m[j]);
-      }
-      int wb = 0;
-      if (lane == 0 && tot) wb = atomicAdd(&sh.n, tot);
-      wb = __shfl(wb, 0, kWave);
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        if (c[j].key != 0u) {
-          const int slot = wb + lanes_below(m[j]);
-          g[slot] = c[j];
-          if (fits) keys_s[slot] = c[j].key;
+      for (int j = 0; j < 4; ++j) {
+        const int i = base + j * kMergeThreads + tid;
+        if (i < nk) {
+          K[i] = c[j].key;
+          P[i] = c[j].pos;
+          note_minmax(lmin, lmax, c[j].key);
         }
-        wb += __popcll(m[j]);
       }
     }
-  };
-  if (nk) gather_from(kept_in + (int64_t)b * kept_ld, nk);
-  if (nc) gather_from(cand + (int64_t)b * cand_ld, nc);
+  }
+  int n = nk;
+  const Cand* cb = in.cand ? in.cand + (int64_t)b * in.cand_ld : nullptr;
+  if (cb && !in.seg_cnt) {
+    for (int64_t base = 0; base < in.n_slots; base += kBatch) {
+      Cand c[kRounds];
+      bool f[kRounds];
+      int slot[kRounds];
+#pragma unroll
+      for (int r = 0; r < kRounds; ++r) {
+        const int64_t i = base + r * kMergeThreads + tid;
+        c[r] = i < in.n_slots ? cb[i] : Cand{0u, 0};
+      }
+#pragma unroll
+      for (int r = 0; r < kRounds; ++r) f[r] = c[r].key != 0u;
+      const int got = batch_slots(sh, f, slot, tid);
+#pragma unroll
+      for (int r = 0; r < kRounds; ++r)
+        if (f[r]) {
+          K[n + slot[r]] = c[r].key;
+          P[n + slot[r]] = c[r].pos;
+          note_minmax(lmin, lmax, c[r].key);
+        }
+      n += got;
+    }
+  } else if (cb) {
+    for (int w0 = 0; w0 < in.n_seg; w0 += kMergeThreads) {
+      const int w = w0 + tid;
+      const int c = w < in.n_seg ? (int)in.seg_cnt[(int64_t)b * in.n_seg + w] : 0;
+      int total;
+      const int ex = block_scan(sh, c, tid, &total);
+      sh.u.seg.off[tid] = n + ex;
+      sh.u.seg.cnt[tid] = c;
+      __syncthreads();
+      const int nw = in.n_seg - w0 < kMergeThreads ? in.n_seg - w0 : kMergeThreads;
+      for (int j = wave; j < nw; j += kMergeWaves) {
+        const Cand* src = cb + (int64_t)(w0 + j) * in.seg_cap;
+        const int cnt = sh.u.seg.cnt[j], off = sh.u.seg.off[j];
+        for (int e0 = 0; e0 < cnt; e0 += 4 * kWave) {
+          Cand c4[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int e = e0 + u * kWave + lane;
+            c4[u] = e < cnt ? src[e] : Cand{0u, 0};
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int e = e0 + u * kWave + lane;
+            if (e < cnt) {
+              K[off + e] = c4[u].key;
+              P[off + e] = c4[u].pos;
+              note_minmax(lmin, lmax, c4[u].key);
+            }
+          }
+        }
+      }
+      n += total;
+      __syncthreads();
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint32_t x = __shfl_xor(lmin, o, kWave), y = __shfl_xor(lmax, o, kWave);
+    lmin = x < lmin ? x : lmin;
+    lmax = y > lmax ? y : lmax;
+  }
+  if (lane == 0) {
+    atomicMin(&sh.kmin, lmin);
+    atomicMax(&sh.kmax, lmax);
+  }
   __syncthreads();
-  const int n = sh.n;
-  if (zero_cnt && tid == 0) zero_cnt[b] = 0u;  // the next key range counts its candidates from zero
-  auto key_at = [&](int i) -> uint32_t { return fits ? keys_s[i] : g[i].key; };
 
   // ---- exact selection of min(k, n)
   uint32_t kstar = 0;
   int32_t pstar = 0x7FFFFFFF;
   if (n >= k) {
-    // bits shared by every candidate key
-    uint32_t lmin = 0xFFFFFFFFu, lmax = 0u;
-    for (int i = tid; i < n; i += kMergeThreads) {
-      const uint32_t v = key_at(i);
-      lmin = v < lmin ? v : lmin;
-      lmax = v > lmax ? v : lmax;
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const uint32_t x = __shfl_xor(lmin, off, kWave), y = __shfl_xor(lmax, off, kWave);
-      lmin = x < lmin ? x : lmin;
-      lmax = y > lmax ? y : lmax;
-    }
-    if (lane == 0) {
-      atomicMin(&sh.kmin, lmin);
-      atomicMax(&sh.kmax, lmax);
-    }
-    __syncthreads();
     const uint32_t kmin = sh.kmin, kmax = sh.kmax;
     uint32_t need = (uint32_t)k, ties = (uint32_t)n;
     int bits = kmin == kmax ? 0 : 32 - __clz(kmin ^ kmax);  // low bits that still differ
     uint32_t mask = bits == 32 ? 0u : ~((1u << bits) - 1u);
     uint32_t prefix = kmin & mask;
-    auto key_src = [&](int i, uint32_t* v) {
-      *v = key_at(i);
+    auto key_val = [&](int i, uint32_t* v) {
+      *v = K[i];
       return true;
     };
     while (bits > 0) {
       const int d = bits < 8 ? bits : 8;
       const int shift = bits - d;
-      radix_pass(sh, n, key_src, prefix, mask, shift, need, true, tid, wave);
+      radix_pass(sh, n, key_val, prefix, mask, shift, need, true, tid);
       need -= sh.before;
       ties = sh.in_bin;
       prefix |= sh.digit << shift;
@@ -207,14 +305,14 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(int k, const Cand* __re
     if (need < ties) {
       // several candidates share the k-th key: keep the `need` lowest positions among them
       uint32_t pprefix = 0, pmask = 0, pneed = need;
-      auto pos_src = [&](int i, uint32_t* v) {
-        if (key_at(i) != kstar) return false;
-        *v = (uint32_t)g[i].pos;
+      auto pos_val = [&](int i, uint32_t* v) {
+        if (K[i] != kstar) return false;
+        *v = (uint32_t)P[i];
         return true;
       };
       for (int pass = 0; pass < 4; ++pass) {
         const int shift = 24 - 8 * pass;
-        radix_pass(sh, n, pos_src, pprefix, pmask, shift, pneed, false, tid, wave);
+        radix_pass(sh, n, pos_val, pprefix, pmask, shift, pneed, false, tid);
         pneed -= sh.before;
         pprefix |= sh.digit << shift;
         pmask |= 255u << shift;
@@ -224,85 +322,112 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(int k, const Cand* __re
   }
   const int take = n < k ? n : k;
 
-  // ---- output, phase A: indices of the selected candidates into the sort area (wave-aggregated slots)
-  for (int base = 0; base < n; base += kMergeThreads) {
-    const int i = base + tid;
-    bool sel = false;
-    if (i < n) {
-      const uint32_t key = key_at(i);
-      sel = n < k || key > kstar || (key == kstar && g[i].pos <= pstar);
+  // ---- the selected entries, in input order
+  int done = 0;
+  for (int base = 0; base < n; base += kBatch) {
+    bool f[kRounds];
+    int slot[kRounds];
+    uint32_t kv[kRounds];
+    int32_t pv[kRounds];
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) {
+      const int i = base + r * kMergeThreads + tid;
+      kv[r] = 0u;
+      pv[r] = 0;
+      if (i < n) {
+        kv[r] = K[i];
+        pv[r] = P[i];
+      }
+      f[r] = i < n && (n < k || kv[r] > kstar || (kv[r] == kstar && pv[r] <= pstar));
     }
-    const uint64_t m = ballot(sel);
-    int wb = 0;
-    if (lane == 0 && m) wb = atomicAdd(&sh.out, __popcll(m));
-    wb = __shfl(wb, 0, kWave);
-    if (sel) sorted[wb + lanes_below(m)] = i;
+    const int got = batch_slots(sh, f, slot, tid);
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) {
+      if (!f[r]) continue;
+      const int o = done + slot[r];
+      if (out.final_mode == 0) out.kept_out[(int64_t)b * k + o] = Cand{kv[r], pv[r]};
+      else if (out.final_mode == 1) out.idx[(int64_t)b * out.idx_ld + o] = pv[r];
+      else sort_area[o] = ((uint64_t)(~kv[r]) << 32) | (uint32_t)pv[r];
+    }
+    done += got;
   }
-  __syncthreads();
-  // phase B: independent loads of the selected candidates
-  if (!final_mode) {
-    for (int s2 = tid; s2 < take; s2 += kMergeThreads) kept_out[(int64_t)b * k + s2] = g[sorted[s2]];
+  if (out.final_mode == 0) {
     if (tid == 0) {
-      kept_n_out[b] = take;
-      thr_out[b] = n >= k ? kstar : 0u;
+      out.kept_n_out[b] = take;
+      out.thr_out[b] = n >= k ? kstar : 0u;
     }
     return;
   }
-  int n2 = 2;
-  while (n2 < take) n2 <<= 1;
-  if (final_mode == 1) {
-    for (int s2 = tid; s2 < n2; s2 += kMergeThreads) sorted[s2] = s2 < take ? g[sorted[s2]].pos : 0x7FFFFFFF;
+  if (out.final_mode == 2 && take > 1) {
+    int n2 = 2;
+    while (n2 < take) n2 <<= 1;
     __syncthreads();
-    bitonic_sort(sorted, n2, tid);
-    for (int i = tid; i < idx_ld; i += kMergeThreads) idx[(int64_t)b * idx_ld + i] = i < take ? sorted[i] : -1;
-  } else {
-    // (key desc, position asc): sort ascending on (~key << 32 | position); the index list is read first
-    uint64_t* sorted64 = reinterpret_cast<uint64_t*>(dyn);
-    uint64_t v[kMaxSortK / 2 / kMergeThreads];
-#pragma unroll
-    for (int j = 0; j < kMaxSortK / 2 / kMergeThreads; ++j) {
-      const int s2 = j * kMergeThreads + tid;
-      v[j] = ~0ull;
-      if (s2 < take) {
-        const Cand e = g[sorted[s2]];
-        v[j] = ((uint64_t)(~e.key) << 32) | (uint32_t)e.pos;
-      }
-    }
+    for (int i = take + tid; i < n2; i += kMergeThreads) sort_area[i] = ~0ull;
     __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kMaxSortK / 2 / kMergeThreads; ++j) {
-      const int s2 = j * kMergeThreads + tid;
-      if (s2 < n2) sorted64[s2] = v[j];
-    }
+    bitonic_sort(sort_area, n2, tid);
+    for (int i = tid; i < take; i += kMergeThreads) out.idx[(int64_t)b * out.idx_ld + i] = (int32_t)(uint32_t)sort_area[i];
+  } else if (out.final_mode == 2 && take == 1) {
     __syncthreads();
-    bitonic_sort(sorted64, n2, tid);
-    for (int i = tid; i < idx_ld; i += kMergeThreads)
-      idx[(int64_t)b * idx_ld + i] = i < take ? (int32_t)(uint32_t)sorted64[i] : -1;
+    if (tid == 0) out.idx[(int64_t)b * out.idx_ld] = (int32_t)(uint32_t)sort_area[0];
   }
-  if (tid == 0) n_sel[b] = take;
+  for (int i = take + tid; i < out.idx_ld; i += kMergeThreads) out.idx[(int64_t)b * out.idx_ld + i] = -1;
+  if (tid == 0) out.n_sel[b] = take;
+}
+
+// Dynamic LDS: [keys: cap x 4 B][positions: cap x 4 B][bucket-rank sort area: sort_bytes].
+__global__ __launch_bounds__(kMergeThreads) void k_merge(int k, MergeIn in, Cand* __restrict__ gather,
+                                                         int64_t gather_cap, MergeOut out, int cap) {
+  __shared__ MergeShared sh;
+  extern __shared__ __attribute__((aligned(16))) char dyn[];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    sh.kmin = 0xFFFFFFFFu;
+    sh.kmax = 0u;
+  }
+  const int nk = in.kept ? in.kept_n[b] : 0;
+  int64_t n_in = 0;
+  if (in.cand && !in.seg_cnt) {
+    n_in = in.n_slots;
+  } else if (in.cand) {
+    int s = 0;
+    for (int w = tid; w < in.n_seg; w += kMergeThreads) s += (int)in.seg_cnt[(int64_t)b * in.n_seg + w];
+    int total;
+    block_scan(sh, s, tid, &total);
+    n_in = total;
+  }
+  __syncthreads();
+  uint64_t* sort_area = reinterpret_cast<uint64_t*>(dyn + (size_t)8 * cap);
+  if (nk + n_in <= cap) {
+    merge_body<true>(sh, b, k, in, out, reinterpret_cast<uint32_t*>(dyn), reinterpret_cast<int32_t*>(dyn + 4 * cap),
+                     nk, sort_area);
+  } else {
+    Cand* g = gather + (int64_t)b * gather_cap;
+    merge_body<false>(sh, b, k, in, out, reinterpret_cast<uint32_t*>(g), reinterpret_cast<int32_t*>(g) + gather_cap,
+                      nk, sort_area);
+  }
 }
 
 }  // namespace
 
-hipError_t launch_merge(int B, int k, const Cand* kept_in, int kept_ld, const int32_t* kept_n_in, const Cand* cand,
-                        int64_t cand_ld, const uint32_t* cand_cnt, int64_t cand_n, uint32_t* zero_cnt, Cand* gather,
-                        int64_t gather_cap, Cand* kept_out, int32_t* kept_n_out, uint32_t* thr_out, int final_mode,
-                        int32_t* idx, int idx_ld, int32_t* n_sel, hipStream_t st) {
-  if (k < 1 || (final_mode == 1 && k > kMaxSortK) || (final_mode == 2 && k > kMaxSortK / 2)) return hipErrorInvalidValue;
+hipError_t launch_merge(int B, int k, const MergeIn& in, Cand* gather, int64_t gather_cap, const MergeOut& out,
+                        hipStream_t st) {
+  if (k < 1 || k > kMaxSortK || (out.final_mode == 2 && k > kMaxSortK / 2)) return hipErrorInvalidValue;
+  if (B == 0) return hipSuccess;
   int n2 = 2;
   while (n2 < k) n2 <<= 1;
-  const int sort_bytes = n2 * (final_mode == 2 ? 8 : 4);
+  const int sort_bytes = out.final_mode == 2 ? 8 * n2 : 0;
   const int dyn = kLdsBytes - (int)sizeof(MergeShared) - 256;
-  const int key_cap = (dyn - sort_bytes) / 4;
+  const int cap = (dyn - sort_bytes) / 8;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_merge), hipFuncAttributeMaxDynamicSharedMemorySize, dyn);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_merge),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, dyn);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(k_merge, dim3((unsigned)B), dim3(kMergeThreads), (size_t)dyn, st, k, kept_in, kept_ld, kept_n_in,
-                     cand, cand_ld, cand_cnt, cand_n, zero_cnt, gather, gather_cap, kept_out, kept_n_out, thr_out,
-                     final_mode, idx, idx_ld, n_sel, sort_bytes, key_cap);
+  hipLaunchKernelGGL(k_merge, dim3((unsigned)B), dim3(kMergeThreads), (size_t)dyn, st, k, in, gather, gather_cap,
+                     out, cap);
   return hipGetLastError();
 }
 

@@ -112,10 +112,11 @@ struct SplitLWs {
   uint32_t* thr;
   sa::Cand* kept;
   int32_t* kept_n;
-  uint32_t* cnt[2];      // candidate counters of alternating key ranges
+  uint32_t* seg_cnt;     // [B, max_seg] per-workgroup candidate counts of the current key range
   sa::Cand* cand;        // [B, cand_ld] candidates of the current key range
   sa::Cand* gather;      // [B, gather_cap]
   int64_t cand_ld, gather_cap;
+  int max_seg;
   size_t bytes;
 };
 
@@ -123,15 +124,19 @@ SplitLWs carve_split_l(void* ws, const sa::IndexerArgs& a, int k) {
   const int kpw = sa::score_keys_per_wg(a);
   const std::vector<int64_t> lv = levels(a.L, k, kpw);
   int64_t max_level = 0;
-  for (size_t i = 0; i + 1 < lv.size(); ++i) max_level = std::max(max_level, lv[i + 1] - lv[i]);
+  int max_seg = 1;
+  for (size_t i = 0; i + 1 < lv.size(); ++i) {
+    max_level = std::max(max_level, lv[i + 1] - lv[i]);
+    if (i > 0) max_seg = std::max(max_seg, sa::score_emit_plan(a, lv[i], lv[i + 1]).n_seg);
+  }
   SplitLWs w{};
-  w.cand_ld = max_level;
-  w.gather_cap = k + max_level;
+  w.cand_ld = (int64_t)align_up((size_t)max_level, 512);
+  w.gather_cap = k + w.cand_ld;
+  w.max_seg = max_seg;
   Carver c(ws);
   w.thr = c.take<uint32_t>(a.B);
   w.kept_n = c.take<int32_t>(a.B);
-  w.cnt[0] = c.take<uint32_t>(a.B);
-  w.cnt[1] = c.take<uint32_t>(a.B);
+  w.seg_cnt = c.take<uint32_t>((size_t)a.B * max_seg);
   w.kept = c.take<sa::Cand>((size_t)a.B * k);
   w.cand = c.take<sa::Cand>((size_t)a.B * w.cand_ld);
   w.gather = c.take<sa::Cand>((size_t)a.B * w.gather_cap);
@@ -232,26 +237,53 @@ SA_API int sa_select_topk(const void* q, int q_dtype, const float* w, const void
     const PerQueryWs w2 = carve_per_query(ws, a, k_sparse);
     e = sa::launch_stream_select(a, k_sparse, n_sink, n_window, w2.buf, w2.buf_n, w2.cap, s);
     if (e != hipSuccess) return hip_fail(e, "sa_select_topk (stream)");
-    e = sa::launch_merge(B, k_sparse, w2.buf, w2.cap, w2.buf_n, nullptr, 0, nullptr, 0, nullptr, w2.gather, w2.cap, nullptr,
-                         nullptr, nullptr, 1, idx, idx_ld, n_sel, s);
+    sa::MergeIn in{};
+    in.kept = w2.buf;
+    in.kept_ld = w2.cap;
+    in.kept_n = w2.buf_n;
+    sa::MergeOut out{};
+    out.final_mode = 1;
+    out.idx = idx;
+    out.idx_ld = idx_ld;
+    out.n_sel = n_sel;
+    e = sa::launch_merge(B, k_sparse, in, w2.gather, w2.cap, out, s);
     return e == hipSuccess ? SA_OK : hip_fail(e, "sa_select_topk (final merge)");
   }
   const SplitLWs w2 = carve_split_l(ws, a, k_sparse);
   const int kpw = sa::score_keys_per_wg(a);
   const std::vector<int64_t> lv = levels(L, k_sparse, kpw);
-  // Key ranges in ascending position order. The first range writes every candidate to a fixed slot; later ranges
-  // append only candidates above the k-th key kept so far, counting them in alternating counters that the previous
-  // merge cleared.
+  // Key ranges in ascending position order. The first range writes every candidate to its position's slot; later
+  // ranges write only candidates above the k-th key kept so far, each workgroup into its own segment. Every merge
+  // keeps its input order, so the kept lists and the final index lists stay in ascending position order.
   for (size_t i = 0; i + 1 < lv.size(); ++i) {
     const int64_t lo = lv[i], hi = lv[i + 1];
     const bool first = i == 0, last = i + 2 == lv.size();
-    uint32_t* cnt = w2.cnt[i % 2];
     e = sa::launch_score(a, lo, hi, first ? sa::kScoreAll : sa::kScoreEmit, nullptr, 0, n_sink, n_window,
-                         first ? nullptr : w2.thr, w2.cand, w2.cand_ld, first ? nullptr : cnt, s);
+                         first ? nullptr : w2.thr, w2.cand, w2.cand_ld, first ? nullptr : w2.seg_cnt, s);
     if (e != hipSuccess) return hip_fail(e, "sa_select_topk (score)");
-    e = sa::launch_merge(B, k_sparse, first ? nullptr : w2.kept, k_sparse, w2.kept_n, w2.cand, w2.cand_ld,
-                         first ? nullptr : cnt, hi - lo, w2.cnt[(i + 1) % 2], w2.gather, w2.gather_cap, w2.kept,
-                         w2.kept_n, w2.thr, last ? 1 : 0, idx, idx_ld, n_sel, s);
+    sa::MergeIn in{};
+    in.kept = first ? nullptr : w2.kept;
+    in.kept_ld = k_sparse;
+    in.kept_n = w2.kept_n;
+    in.cand = w2.cand;
+    in.cand_ld = w2.cand_ld;
+    if (first) {
+      in.n_slots = hi - lo;
+    } else {
+      const sa::EmitPlan ep = sa::score_emit_plan(a, lo, hi);
+      in.seg_cnt = w2.seg_cnt;
+      in.n_seg = ep.n_seg;
+      in.seg_cap = ep.seg_cap;
+    }
+    sa::MergeOut out{};
+    out.final_mode = last ? 1 : 0;
+    out.kept_out = w2.kept;
+    out.kept_n_out = w2.kept_n;
+    out.thr_out = w2.thr;
+    out.idx = idx;
+    out.idx_ld = idx_ld;
+    out.n_sel = n_sel;
+    e = sa::launch_merge(B, k_sparse, in, w2.gather, w2.gather_cap, out, s);
     if (e != hipSuccess) return hip_fail(e, "sa_select_topk (merge)");
   }
   return SA_OK;

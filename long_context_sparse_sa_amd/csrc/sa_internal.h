@@ -32,28 +32,59 @@ int score_keys_per_wg(const IndexerArgs& a);
 // True when the MFMA scoring kernel serves these arguments.
 bool score_uses_mfma(const IndexerArgs& a);
 
+// Segmented emission: workgroup w of a kScoreEmit launch scores a contiguous run of positions and appends its
+// candidates, in ascending position order, to its own segment cand[b * cand_ld + w * seg_cap + ...]; it then
+// stores the count in seg_cnt[b * n_seg + w]. No atomics, so the concatenated segments are in ascending order.
+struct EmitPlan {
+  int n_seg;        // workgroups per query = segments per query
+  int64_t seg_cap;  // positions per workgroup = segment capacity
+};
+EmitPlan score_emit_plan(const IndexerArgs& a, int64_t lo, int64_t hi);
+
 // Scores positions [lo, hi).
 //  kScoreDense: scores[b * scores_ld + (s - lo)] = I(b, s), or -inf for s > t_b.
 //  kScoreAll:   cand[b * cand_ld + (s - lo)] = {score_key(I), s} for candidates s (n_sink <= s <= t_b - n_window),
 //               {0, -1} otherwise.
-//  kScoreEmit:  candidates with score_key(I) > thr_key[b] (any candidate when thr_key is NULL) are appended to
-//               cand[b * cand_ld + ...]; each workgroup reserves its range with one atomicAdd on cand_cnt[b], which
-//               must be 0 before the launch and ends as the number of appended candidates.
+//  kScoreEmit:  candidates with score_key(I) > thr_key[b] (any candidate when thr_key is NULL) go to the segments
+//               described by score_emit_plan(a, lo, hi); seg_cnt receives the per-segment counts.
 hipError_t launch_score(const IndexerArgs& a, int64_t lo, int64_t hi, int mode, float* scores, int64_t scores_ld,
                         int n_sink, int n_window, const uint32_t* thr_key, Cand* cand, int64_t cand_ld,
-                        uint32_t* cand_cnt, hipStream_t stream);
+                        uint32_t* seg_cnt, hipStream_t stream);
 
-// Exact top-k merge, one workgroup per query:
-//   candidates = kept_in[b * kept_ld + (0:kept_n_in[b])] (if kept_in) U cand[b * cand_ld + (0:n_b)] with
-//   n_b = cand_cnt ? cand_cnt[b] : cand_n; entries whose key is 0 are empty slots. The gather buffer must hold
-//   kept_n_in[b] + n_b entries per query. When zero_cnt is set, zero_cnt[b] is cleared for the next key range.
-//   Keeps the k best by (key desc, pos asc) in kept_out[b, :] (count in kept_n_out[b]) and sets thr_out[b] to the
-//   k-th key (0 when fewer than k candidates exist). final_mode 1 writes instead idx[b, :] with the positions
-//   ascending and -1 padding, plus n_sel[b]; final_mode 2 writes them in (key desc, position asc) order.
-hipError_t launch_merge(int B, int k, const Cand* kept_in, int kept_ld, const int32_t* kept_n_in, const Cand* cand,
-                        int64_t cand_ld, const uint32_t* cand_cnt, int64_t cand_n, uint32_t* zero_cnt, Cand* gather,
-                        int64_t gather_cap, Cand* kept_out, int32_t* kept_n_out, uint32_t* thr_out, int final_mode,
-                        int32_t* idx, int idx_ld, int32_t* n_sel, hipStream_t stream);
+// Candidates of one exact top-k merge, per query b, in this order:
+//   kept:     kept[b * kept_ld + (0:kept_n[b])]                                   (when kept != NULL)
+//   slots:    cand[b * cand_ld + (0:n_slots)], key 0 marking an empty slot       (when seg_cnt == NULL)
+//   segments: seg_cnt[b * n_seg + w] entries at cand[b * cand_ld + w * seg_cap], w = 0, 1, ...
+// The merge preserves this order. When the entries come in ascending position order, as every producer in this
+// library writes them, the selected positions come out ascending without a sort.
+struct MergeIn {
+  const Cand* kept;
+  int kept_ld;
+  const int32_t* kept_n;
+  const Cand* cand;
+  int64_t cand_ld;
+  int64_t n_slots;
+  const uint32_t* seg_cnt;
+  int n_seg;
+  int64_t seg_cap;
+};
+// final_mode 0: kept_out[b * k + (0:take)] = the k best (key desc, pos asc) in input order, kept_n_out[b] = take,
+//               thr_out[b] = the k-th key (0 when there are fewer than k candidates);
+// final_mode 1: idx[b, 0:take) = their positions in input order, -1 up to idx_ld, n_sel[b] = take;
+// final_mode 2: idx[b, 0:take) = their positions in (key desc, position asc) order (bucket ranking).
+struct MergeOut {
+  int final_mode;
+  Cand* kept_out;
+  int32_t* kept_n_out;
+  uint32_t* thr_out;
+  int32_t* idx;
+  int idx_ld;
+  int32_t* n_sel;
+};
+// `gather` must hold, per query, every candidate of the merge (kept plus slots or segment entries): it stores
+// them when they do not fit in LDS.
+hipError_t launch_merge(int B, int k, const MergeIn& in, Cand* gather, int64_t gather_cap, const MergeOut& out,
+                        hipStream_t stream);
 int merge_max_k();
 // Fills p[0, n) with v (a kernel, so that it is safe inside captured graphs).
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t stream);

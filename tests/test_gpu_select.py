@@ -128,3 +128,38 @@ def test_topk_all_equal_scores():
         torch.cuda.synchronize()
         for b in range(B):
             np.testing.assert_array_equal(selected(idx[b], nsel[b].item()), np.arange(2, 2 + kk))
+
+
+def test_topk_valu_path_levels():
+    """VALU scorer (4 heads x 32, fp32) over two key ranges: the second range emits into per-workgroup segments."""
+    B, H, d, L, kk = 3, 4, 32, 40000, 300
+    q, w, k = _inputs(13, B, H, d, L, "f32", integer=False)
+    ts = [L - 1, 30000, 17000]
+    t = torch.tensor(ts, dtype=torch.int32, device=DEV)
+    idx, nsel = sa.sa_select_topk(q, w, k, kk, n_sink=2, n_window=16, t=t, algo=sa.SA_TOPK_SPLIT_L)
+    torch.cuda.synchronize()
+    qf, wf, kf = to_f64(q), w.double().cpu().numpy(), to_f64(k)
+    for b in range(B):
+        ref, sc, cand = O.select_topk(qf[b], wf[b], kf, ts[b], kk, 2, 16)
+        band_compare(selected(idx[b], nsel[b].item()), ref, cand, sc, kk)
+
+
+def test_topk_rising_scores_many_emits():
+    """Scores rise with position (with runs of equal bf16 keys): every later key range emits almost all of its
+    positions, so the merges overflow LDS and run from the gather buffer; ties resolve to lower positions."""
+    B, H, d, L, kk = 2, 64, 128, 150000, 2048
+    k = torch.zeros((L, d), dtype=torch.float32)
+    k[:, 0] = torch.arange(L, dtype=torch.float32) / 1000.0
+    k = k.to(torch.bfloat16).to(DEV)
+    q = torch.zeros((B, H, d), dtype=torch.float32)
+    q[:, :, 0] = 1.0
+    q[1, :, 1] = 0.5
+    q = q.to(torch.bfloat16).to(DEV)
+    w = torch.ones((B, H), device=DEV)
+    idx, nsel = sa.sa_select_topk(q, w, k, kk, n_sink=4, n_window=64, algo=sa.SA_TOPK_SPLIT_L)
+    torch.cuda.synchronize()
+    qf, wf, kf = to_f64(q), w.double().cpu().numpy(), to_f64(k)
+    for b in range(B):
+        ref, sc, cand = O.select_topk(qf[b], wf[b], kf, L - 1, kk, 4, 64)
+        assert np.unique(sc).size < sc.size  # ties are exercised
+        np.testing.assert_array_equal(selected(idx[b], nsel[b].item()), ref)
