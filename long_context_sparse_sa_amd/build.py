@@ -27,10 +27,10 @@ FLAGS = [
 ]
 
 
-# Per-source extra flags. The attention kernel keeps its MFMA accumulators in VGPRs: its online-softmax rescale
-# works on them with VALU instructions, and the default AGPR form copies them between the two register files on
-# every tile.
-EXTRA = {"k_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source extra flags. The attention and indexer kernels keep their MFMA accumulators in VGPRs: their
+# epilogues (online-softmax rescale; ReLU and head weights) work on them with VALU instructions, and the default
+# AGPR form copies them between the two register files on every tile.
+EXTRA = {"k_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "k_index.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:

@@ -209,7 +209,8 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
   attn_block(HG, &u, &hg);
   if (u >= n_units) return;
   const int b = u / n_splits, split = u % n_splits;
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  const int tid = threadIdx.x, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform: DMA destinations stay scalar
   const int hsel = lane >> 5;       // which 8 of each 16 dims / rows this lane carries
   const int j = lane & 31;
   const int hb = wave >> 1, dh = wave & 1;

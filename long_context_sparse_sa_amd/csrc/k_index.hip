@@ -114,20 +114,39 @@ template <bool E4M3, int NW>
 struct KeyLoader;
 
 // bf16 keys: the stored 256-byte rows go straight to LDS by asynchronous DMA (16 KB = 16 wave instructions).
+// Each lane's byte offset inside a tile is computed once (init); a tile then costs one address add per copy,
+// except a tile that runs past row L - 1, which clamps its rows (rows past the end are never scored, the clamp
+// keeps the copy in bounds).
 template <int NW>
 struct KeyLoader<false, NW> {
   static constexpr int kPerWave = 16 / NW;
-  struct Regs {};
-  static __device__ __forceinline__ void fetch(const char* kbytes, int64_t ld_bytes, int64_t L, int64_t s0,
-                                               char* tile, int wave, int lane, Regs&) {
+  struct Regs {
+    int64_t off[kPerWave];
+  };
+  static __device__ __forceinline__ void init(Regs& r, int64_t ld_bytes, int wave, int lane) {
 #pragma unroll
     for (int j = 0; j < kPerWave; ++j) {
       const int slot = (wave * kPerWave + j) * 64 + lane;
       const int n = slot / kTileChunks;
       const int c = (slot % kTileChunks) ^ (n % kTileChunks);
-      int64_t s = s0 + n;
-      s = s < L ? s : L - 1;  // rows past the end are never scored; keep the copy in bounds
-      dma16(kbytes + s * ld_bytes + c * 16, tile + (wave * kPerWave + j) * 1024);
+      r.off[j] = n * ld_bytes + c * 16;
+    }
+  }
+  static __device__ __forceinline__ void fetch(const char* kbytes, int64_t ld_bytes, int64_t L, int64_t s0,
+                                               char* tile, int wave, int lane, Regs& r) {
+    const char* base = kbytes + s0 * ld_bytes;
+    if (s0 + kTileKeys <= L) {
+#pragma unroll
+      for (int j = 0; j < kPerWave; ++j) dma16(base + r.off[j], tile + (wave * kPerWave + j) * 1024);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kPerWave; ++j) {
+        const int slot = (wave * kPerWave + j) * 64 + lane;
+        const int n = slot / kTileChunks;
+        const int c = (slot % kTileChunks) ^ (n % kTileChunks);
+        const int64_t row = (s0 + n < L ? s0 + n : L - 1) - s0;
+        dma16(base + row * ld_bytes + c * 16, tile + (wave * kPerWave + j) * 1024);
+      }
     }
   }
   static __device__ __forceinline__ void commit(const Regs&, char*, int) {}
@@ -141,6 +160,7 @@ struct KeyLoader<true, NW> {
   struct Regs {
     int4 part[BPT / 16];
   };
+  static __device__ __forceinline__ void init(Regs&, int64_t, int, int) {}
   static __device__ __forceinline__ void fetch(const char* kbytes, int64_t ld_bytes, int64_t L, int64_t s0, char*,
                                                int, int, Regs& r) {
     const int tid = threadIdx.x;
@@ -183,26 +203,66 @@ __device__ __forceinline__ void load_query(const void* q, const float* w, int64_
   }
 }
 
-// Score of position n = 32 * nt + lane % 32 of the tile, complete in lanes l and l ^ 32.
+// ReLU as one integer max: a negative float (or -0) has a negative int image and becomes +0; other values pass.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// Scores of the 64 positions of a tile: score[nt] is position 32 nt + lane % 32, complete in lanes l and l ^ 32.
+// The eight key fragments of a 32-position half sit in a register ring: the half-0 fragments are read up front
+// and each slot is refilled with the matching half-1 fragment as soon as its MFMAs are issued, so every LDS read
+// has eight MFMA pairs to land. The half-1 MFMAs are interleaved with the half-0 ReLU-weighted head sum (two MFMAs,
+// then eight VALU instructions, per k-step), so the matrix unit and the VALU work at the same time.
 template <int NMT>
-__device__ __forceinline__ float score_ntile(const char* tile, int nt, int lane, const bf16x8 (&qa)[NMT][kSteps],
-                                             const float (&wv)[NMT][16]) {
-  const int n = 32 * nt + (lane & 31);
-  f32x16 acc[NMT];
+__device__ __forceinline__ void score_tile(const char* tile, int lane, const bf16x8 (&qa)[NMT][kSteps],
+                                           const float (&wv)[NMT][16], float (&score)[2]) {
+  static_assert(NMT * 16 % kSteps == 0, "head-sum chunks must divide evenly over the k-steps");
+  constexpr int kChunk = NMT * 16 / kSteps;  // half-0 accumulator elements folded per half-1 k-step
+  const int hs = lane >> 5;
+  auto frag = [&](int nt, int ks) {
+    return *reinterpret_cast<const bf16x8*>(tile + tile_off(32 * nt + (lane & 31), 2 * ks + hs));
+  };
+  bf16x8 fr[kSteps];
 #pragma unroll
-  for (int mt = 0; mt < NMT; ++mt) acc[mt] = f32x16{};
+  for (int ks = 0; ks < kSteps; ++ks) fr[ks] = frag(0, ks);
+  f32x16 acc0[NMT], acc1[NMT];
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt) {
+    acc0[mt] = f32x16{};
+    acc1[mt] = f32x16{};
+  }
+  // half 0
 #pragma unroll
   for (int ks = 0; ks < kSteps; ++ks) {
-    const bf16x8 bk = *reinterpret_cast<const bf16x8*>(tile + tile_off(n, 2 * ks + (lane >> 5)));
+    const bf16x8 bk = fr[ks];
+    fr[ks] = frag(1, ks);
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt][ks], bk, acc[mt], 0, 0, 0);
+    for (int mt = 0; mt < NMT; ++mt) acc0[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt][ks], bk, acc0[mt], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  float part = 0.f;
+  // half 1, with the half-0 head sum in the MFMA shadow
+  float part0 = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < kSteps; ++ks) {
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) acc1[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt][ks], fr[ks], acc1[mt], 0, 0, 0);
+#pragma unroll
+    for (int e = 0; e < kChunk; ++e) {
+      const int idx = ks * kChunk + e;
+      part0 = fmaf(wv[idx / 16][idx % 16], relu(acc0[idx / 16][idx % 16]), part0);
+    }
+  }
+#pragma unroll
+  for (int ks = 0; ks < kSteps; ++ks) {
+    __builtin_amdgcn_sched_group_barrier(0x008, NMT, 0);       // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 2 * kChunk, 0);  // VALU
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  float part1 = 0.f;
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) part = fmaf(wv[mt][r], fmaxf(acc[mt][r], 0.f), part);
-  return part + wave_shfl_xor(part, 32);
+    for (int r = 0; r < 16; ++r) part1 = fmaf(wv[mt][r], relu(acc1[mt][r]), part1);
+  score[0] = part0 + wave_shfl_xor(part0, 32);
+  score[1] = part1 + wave_shfl_xor(part1, 32);
 }
 
 // Split-L scoring: workgroup = NQ waves = NQ queries. Each of the gridDim.x workgroups of a query group scores a
@@ -227,7 +287,7 @@ __global__ __launch_bounds__(64 * NQ) void k_score_mfma(const void* __restrict__
   __shared__ __attribute__((aligned(1024))) char tiles[kNBuf][kTileBytes];
   __shared__ Cand staged[NQ][kStage];
   const int lane = lane_id();
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: addresses stay scalar
   const int b = blockIdx.y * NQ + wave;
   const bool active = b < B;
   // this workgroup scores the contiguous run of tiles [first_tile, first_tile + n_tiles)
@@ -259,12 +319,14 @@ __global__ __launch_bounds__(64 * NQ) void k_score_mfma(const void* __restrict__
     n_out += n_emit;
     n_emit = 0;
   };
-  auto score_tile = [&](const char* tile, int64_t s0) {
+  auto process_tile = [&](const char* tile, int64_t s0) {
     if (!active || s0 >= hi) return;
     if (mode == kScoreEmit && n_emit > kStage - kTileKeys) flush();
+    float sc[2];
+    score_tile<NMT>(tile, lane, qa, wv, sc);
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      const float score = score_ntile<NMT>(tile, nt, lane, qa, wv);
+      const float score = sc[nt];
       const int64_t s = s0 + 32 * nt + (lane & 31);
       const bool in_range = (lane < 32) && s < hi;
       if (mode == kScoreDense) {
@@ -286,6 +348,7 @@ __global__ __launch_bounds__(64 * NQ) void k_score_mfma(const void* __restrict__
 
   if constexpr (!E4M3) {
     typename KL::Regs none;
+    KL::init(none, ld_bytes, wave, lane);
     const int64_t n_pre = n_tiles < kNBuf - 1 ? n_tiles : kNBuf - 1;
     for (int64_t p = 0; p < n_pre; ++p) KL::fetch(kbytes, ld_bytes, L, tile_start(p), tiles[p], wave, lane, none);
     for (int64_t i = 0; i < n_tiles; ++i) {
@@ -296,7 +359,7 @@ __global__ __launch_bounds__(64 * NQ) void k_score_mfma(const void* __restrict__
       lds_barrier();
       if (i + kNBuf - 1 < n_tiles)
         KL::fetch(kbytes, ld_bytes, L, tile_start(i + kNBuf - 1), tiles[(i + kNBuf - 1) % kNBuf], wave, lane, none);
-      score_tile(tiles[i % kNBuf], tile_start(i));
+      process_tile(tiles[i % kNBuf], tile_start(i));
     }
   } else {
     typename KL::Regs ring[2];
@@ -316,7 +379,7 @@ __global__ __launch_bounds__(64 * NQ) void k_score_mfma(const void* __restrict__
         KL::commit(ring[1 - p], tiles[1 - p], threadIdx.x);
         if (i + 3 < n_tiles) KL::fetch(kbytes, ld_bytes, L, tile_start(i + 3), nullptr, wave, lane, ring[1 - p]);
       }
-      score_tile(tiles[p], tile_start(i));
+      process_tile(tiles[p], tile_start(i));
     };
     for (int64_t i = 0; i < n_tiles; i += 2) {
       step(i, std::integral_constant<int, 0>{});
@@ -329,24 +392,25 @@ __global__ __launch_bounds__(64 * NQ) void k_score_mfma(const void* __restrict__
   }
 }
 
-// Streaming selection for many queries (prefill chunk): workgroup = 4 waves = 4 queries, each wave streams its
+// Streaming selection for many queries (prefill chunk): workgroup = NQ waves = NQ queries, each wave streams its
 // query's candidate positions in ascending order, appends candidates that beat its running threshold to a
 // private buffer in global memory, and when the buffer is full keeps only the exact top-k (raising the threshold
 // to the k-th key). Positions arrive in ascending order, so a later candidate that only ties the k-th key can
 // never displace it: appending requires a strictly larger key.
-template <int NMT, bool E4M3>
-__global__ __launch_bounds__(256) void k_stream_select(const void* __restrict__ q, const float* __restrict__ w,
+template <int NMT, bool E4M3, int NQ>
+__global__ __launch_bounds__(64 * NQ) void k_stream_select(const void* __restrict__ q, const float* __restrict__ w,
                                                        const void* __restrict__ k, int64_t k_ld, int64_t L, int B,
                                                        const int32_t* __restrict__ t, int kk, int n_sink,
                                                        int n_window, Cand* __restrict__ buf,
                                                        int32_t* __restrict__ buf_n, int cap) {
-  typedef KeyLoader<E4M3, 4> KL;
-  __shared__ __attribute__((aligned(1024))) char tiles[2][kTileBytes];
-  __shared__ uint32_t hist[4][256];
-  __shared__ int64_t wave_end[4];
+  typedef KeyLoader<E4M3, NQ> KL;
+  constexpr int kNBufS = E4M3 ? 2 : 4;
+  __shared__ __attribute__((aligned(1024))) char tiles[kNBufS][kTileBytes];
+  __shared__ uint32_t hist[NQ][256];
+  __shared__ int64_t wave_end[NQ];
   const int lane = lane_id();
-  const int wave = threadIdx.x / kWave;
-  const int b = blockIdx.x * 4 + wave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: addresses stay scalar
+  const int b = blockIdx.x * NQ + wave;
   const bool active = b < B;
   const char* kbytes = reinterpret_cast<const char*>(k);
   const int64_t ld_bytes = k_ld * (E4M3 ? 1 : 2);
@@ -359,44 +423,68 @@ __global__ __launch_bounds__(256) void k_stream_select(const void* __restrict__ 
   if (active) load_query<NMT, E4M3>(q, w, b, lane, qa, wv);
   __syncthreads();
   int64_t end = wave_end[0];
-  for (int i = 1; i < 4; ++i) end = wave_end[i] > end ? wave_end[i] : end;
+  for (int i = 1; i < NQ; ++i) end = wave_end[i] > end ? wave_end[i] : end;
   const int64_t s_begin = ((int64_t)n_sink / kTileKeys) * kTileKeys;
   const int n_tiles = end >= s_begin ? (int)((end - s_begin) / kTileKeys + 1) : 0;
 
   Cand* mybuf = buf + (int64_t)(active ? b : 0) * cap;
   int n = 0;
   uint32_t thr = 0;
-  typename KL::Regs regs;
-  if (n_tiles > 0) {
-    KL::fetch(kbytes, ld_bytes, L, s_begin, tiles[0], wave, lane, regs);
-    KL::commit(regs, tiles[0], threadIdx.x);
-  }
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    wait_vmem();
-    __syncthreads();
-    const bool more = tile + 1 < n_tiles;
-    if (more)
-      KL::fetch(kbytes, ld_bytes, L, s_begin + (int64_t)(tile + 1) * kTileKeys, tiles[(tile + 1) & 1], wave, lane, regs);
-    const int64_t s0 = s_begin + (int64_t)tile * kTileKeys;
-    if (active && s0 <= cand_end) {
+  const int cend = (int)cand_end;  // positions fit in 32 bits
+  auto score_and_emit = [&](const char* tile, int64_t s0) {
+    if (!active || s0 > cand_end) return;
+    float sc[2];
+    score_tile<NMT>(tile, lane, qa, wv, sc);
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const float score = score_ntile<NMT>(tiles[tile & 1], nt, lane, qa, wv);
-        const int64_t s = s0 + 32 * nt + (lane & 31);
-        const uint32_t key = score_key(score);
-        const bool cand = (lane < 32) && s >= n_sink && s <= cand_end;
-        if (n + 32 > cap) {
-          wait_vmem();
-          thr = wave_select_compact(mybuf, n, kk, hist[wave], lane);
-          n = n < kk ? n : kk;
-        }
-        const bool emit = cand && key > thr;
-        const uint64_t m = ballot(emit);
-        if (emit) mybuf[n + lanes_below(m)] = Cand{key, (int32_t)s};
-        n += __popcll(m);
+    for (int nt = 0; nt < 2; ++nt) {
+      const int s = (int)s0 + 32 * nt + (lane & 31);
+      const uint32_t key = score_key(sc[nt]);
+      const bool cand = (lane < 32) && s >= n_sink && s <= cend;
+      if (n + 32 > cap) {
+        wait_vmem();
+        thr = wave_select_compact(mybuf, n, kk, hist[wave], lane);
+        n = n < kk ? n : kk;
       }
+      const bool emit = cand && key > thr;
+      const uint64_t m = ballot(emit);
+      if (emit) mybuf[n + lanes_below(m)] = Cand{key, s};
+      n += __popcll(m);
     }
-    if (more) KL::commit(regs, tiles[(tile + 1) & 1], threadIdx.x);
+  };
+  if constexpr (!E4M3) {
+    // bf16 keys: asynchronous DMA into four LDS buffers, three tiles in flight
+    typename KL::Regs none;
+    KL::init(none, ld_bytes, wave, lane);
+    const int n_pre = n_tiles < kNBufS - 1 ? n_tiles : kNBufS - 1;
+    for (int p = 0; p < n_pre; ++p)
+      KL::fetch(kbytes, ld_bytes, L, s_begin + (int64_t)p * kTileKeys, tiles[p], wave, lane, none);
+    for (int tile = 0; tile < n_tiles; ++tile) {
+      const int newer = n_tiles - 1 - tile;
+      if (newer >= 2) wait_vmem_below<2 * KL::kPerWave>();
+      else if (newer == 1) wait_vmem_below<KL::kPerWave>();
+      else wait_vmem_below<0>();
+      lds_barrier();
+      if (tile + kNBufS - 1 < n_tiles)
+        KL::fetch(kbytes, ld_bytes, L, s_begin + (int64_t)(tile + kNBufS - 1) * kTileKeys,
+                  tiles[(tile + kNBufS - 1) % kNBufS], wave, lane, none);
+      score_and_emit(tiles[tile % kNBufS], s_begin + (int64_t)tile * kTileKeys);
+    }
+  } else {
+    typename KL::Regs regs;
+    if (n_tiles > 0) {
+      KL::fetch(kbytes, ld_bytes, L, s_begin, tiles[0], wave, lane, regs);
+      KL::commit(regs, tiles[0], threadIdx.x);
+    }
+    for (int tile = 0; tile < n_tiles; ++tile) {
+      wait_vmem();
+      __syncthreads();
+      const bool more = tile + 1 < n_tiles;
+      if (more)
+        KL::fetch(kbytes, ld_bytes, L, s_begin + (int64_t)(tile + 1) * kTileKeys, tiles[(tile + 1) & 1], wave, lane,
+                  regs);
+      score_and_emit(tiles[tile & 1], s_begin + (int64_t)tile * kTileKeys);
+      if (more) KL::commit(regs, tiles[(tile + 1) & 1], threadIdx.x);
+    }
   }
   if (active && lane == 0) buf_n[b] = n;
 }
@@ -500,15 +588,19 @@ bool stream_select_supported(const IndexerArgs& a) { return score_uses_mfma(a); 
 hipError_t launch_stream_select(const IndexerArgs& a, int k, int n_sink, int n_window, Cand* buf, int32_t* buf_n,
                                 int cap, hipStream_t st) {
   if (!score_uses_mfma(a) || cap < k + 32) return hipErrorInvalidValue;
-  dim3 grid((unsigned)((a.B + 3) / 4));
+  // four queries per workgroup: two workgroups share each CU, so one's MFMA work overlaps the other's epilogue
+  // (eight queries per workgroup halve the key traffic but measured slower: the waves of a workgroup move in
+  // lockstep between tile barriers)
   const bool fp8 = a.q_dtype == 2;
-#define SA_STREAM(NMT, F8)                                                                                      \
-  hipLaunchKernelGGL((k_stream_select<NMT, F8>), grid, dim3(256), 0, st, a.q, a.w, a.k, a.k_ld, a.L, a.B, a.t, k, \
-                     n_sink, n_window, buf, buf_n, cap)
+  const int nq = 4;
+  dim3 grid((unsigned)((a.B + nq - 1) / nq));
+#define SA_STREAM(NMT, F8, NQ)                                                                                  \
+  hipLaunchKernelGGL((k_stream_select<NMT, F8, NQ>), grid, dim3(64 * NQ), 0, st, a.q, a.w, a.k, a.k_ld, a.L, a.B, \
+                     a.t, k, n_sink, n_window, buf, buf_n, cap)
   if (a.H == 64) {
-    if (fp8) SA_STREAM(2, true); else SA_STREAM(2, false);
+    if (fp8) SA_STREAM(2, true, 4); else SA_STREAM(2, false, 4);
   } else {
-    if (fp8) SA_STREAM(1, true); else SA_STREAM(1, false);
+    if (fp8) SA_STREAM(1, true, 4); else SA_STREAM(1, false, 4);
   }
 #undef SA_STREAM
   return hipGetLastError();

@@ -154,7 +154,7 @@ struct PerQueryWs {
 
 PerQueryWs carve_per_query(void* ws, const sa::IndexerArgs& a, int k) {
   PerQueryWs w{};
-  w.cap = (int)align_up((size_t)2 * k + 64, 64);
+  w.cap = (int)align_up((size_t)4 * k + 64, 64);  // a larger buffer means fewer compactions per query
   Carver c(ws);
   w.buf_n = c.take<int32_t>(a.B);
   w.buf = c.take<sa::Cand>((size_t)a.B * w.cap);

@@ -57,25 +57,71 @@ __device__ __forceinline__ uint32_t find_digit(const uint32_t* hist, uint32_t ne
 // Wave-level exact top-k of buf[0, n) (n > k is not required). Afterwards buf[0, min(n, k)) holds the selected
 // candidates (in their original relative order) and the return value is the k-th key (0 when n < k).
 // `hist` is 256 words of LDS private to this wave. Every lane must call it with the same n.
+// Every pass reads the buffer kBatchW entries per lane at a time, so the loads of a batch are in flight together;
+// the key passes cover only the bits below the prefix that every key shares.
+constexpr int kBatchW = 8;
+
+template <typename F>
+__device__ __forceinline__ void wave_batched(const Cand* buf, int n, int lane, F f) {
+  for (int base = 0; base < n; base += kWave * kBatchW) {
+    Cand c[kBatchW];
+#pragma unroll
+    for (int j = 0; j < kBatchW; ++j) {
+      const int i = base + j * kWave + lane;
+      c[j] = i < n ? buf[i] : Cand{0u, -1};
+    }
+#pragma unroll
+    for (int j = 0; j < kBatchW; ++j)
+      if (base + j * kWave + lane < n) f(c[j]);
+  }
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint32_t x = __shfl_xor(v, o, kWave);
+    v = x < v ? x : v;
+  }
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint32_t x = __shfl_xor(v, o, kWave);
+    v = x > v ? x : v;
+  }
+  return v;
+}
+
 __device__ __noinline__ uint32_t wave_select_compact(Cand* buf, int n, int k, uint32_t* hist, int lane) {
   if (n < k) return 0u;
-  // ---- key passes
-  uint32_t prefix = 0, mask = 0, need = (uint32_t)k, ties = 0;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
+  // ---- bits shared by every key
+  uint32_t lmin = 0xFFFFFFFFu, lmax = 0u;
+  wave_batched(buf, n, lane, [&](const Cand& e) {
+    lmin = e.key < lmin ? e.key : lmin;
+    lmax = e.key > lmax ? e.key : lmax;
+  });
+  const uint32_t kmin = wave_min_u32(lmin), kmax = wave_max_u32(lmax);
+  int bits = kmin == kmax ? 0 : 32 - __clz(kmin ^ kmax);
+  uint32_t mask = bits == 32 ? 0u : ~((1u << bits) - 1u);
+  uint32_t prefix = kmin & mask, need = (uint32_t)k, ties = (uint32_t)n;
+  // ---- key passes over the differing bits
+  while (bits > 0) {
+    const int d = bits < 8 ? bits : 8;
+    const int shift = bits - d;
     for (int i = lane; i < 256; i += kWave) hist[i] = 0;
     __builtin_amdgcn_wave_barrier();
-    for (int i = lane; i < n; i += kWave) {
-      const uint32_t key = buf[i].key;
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-    }
+    wave_batched(buf, n, lane, [&](const Cand& e) {
+      if ((e.key & mask) == prefix) atomicAdd(&hist[(e.key >> shift) & 255u], 1u);
+    });
     __builtin_amdgcn_wave_barrier();
     uint32_t before, in_bin;
     const uint32_t dg = find_digit(hist, need, true, lane, &before, &in_bin);
     need -= before;
     ties = in_bin;
     prefix |= dg << shift;
-    mask |= 255u << shift;
+    mask |= ((1u << d) - 1u) << shift;
+    bits -= d;
     __builtin_amdgcn_wave_barrier();
   }
   const uint32_t kstar = prefix;
@@ -87,11 +133,10 @@ __device__ __noinline__ uint32_t wave_select_compact(Cand* buf, int n, int k, ui
       const int shift = 24 - 8 * pass;
       for (int i = lane; i < 256; i += kWave) hist[i] = 0;
       __builtin_amdgcn_wave_barrier();
-      for (int i = lane; i < n; i += kWave) {
-        const Cand e = buf[i];
+      wave_batched(buf, n, lane, [&](const Cand& e) {
         const uint32_t p = (uint32_t)e.pos;
         if (e.key == kstar && (p & pmask) == pprefix) atomicAdd(&hist[(p >> shift) & 255u], 1u);
-      }
+      });
       __builtin_amdgcn_wave_barrier();
       uint32_t before, in_bin;
       const uint32_t dg = find_digit(hist, pneed, false, lane, &before, &in_bin);
@@ -102,19 +147,24 @@ __device__ __noinline__ uint32_t wave_select_compact(Cand* buf, int n, int k, ui
     }
     pstar = (int32_t)pprefix;
   }
-  // ---- in-place stable compaction (writes never pass the read front)
+  // ---- in-place stable compaction; a batch is loaded whole before any of it is written back, and writes never
+  // pass the read front
   int out = 0;
-  for (int base = 0; base < n; base += kWave) {
-    const int i = base + lane;
-    Cand e{0u, 0};
-    bool keep = false;
-    if (i < n) {
-      e = buf[i];
-      keep = e.key > kstar || (e.key == kstar && e.pos <= pstar);
+  for (int base = 0; base < n; base += kWave * kBatchW) {
+    Cand c[kBatchW];
+#pragma unroll
+    for (int j = 0; j < kBatchW; ++j) {
+      const int i = base + j * kWave + lane;
+      c[j] = i < n ? buf[i] : Cand{0u, -1};
     }
-    const uint64_t m = ballot(keep);
-    if (keep) buf[out + lanes_below(m)] = e;
-    out += __popcll(m);
+#pragma unroll
+    for (int j = 0; j < kBatchW; ++j) {
+      const int i = base + j * kWave + lane;
+      const bool keep = i < n && (c[j].key > kstar || (c[j].key == kstar && c[j].pos <= pstar));
+      const uint64_t m = ballot(keep);
+      if (keep) buf[out + lanes_below(m)] = c[j];
+      out += __popcll(m);
+    }
   }
   return kstar;
 }
