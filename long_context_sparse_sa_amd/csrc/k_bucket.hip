@@ -129,7 +129,7 @@ template <int QT>
 __global__ __launch_bounds__(256) void k_bucket_scores(const void* __restrict__ q, int B, int d,
                                                        const float* __restrict__ reps,
                                                        const int32_t* __restrict__ offsets, int nb,
-                                                       Cand* __restrict__ cand) {
+                                                       uint32_t* __restrict__ keys) {
   extern __shared__ float qs[];  // [B * d]
   for (int i = threadIdx.x; i < B * d; i += blockDim.x) qs[i] = load_elem<QT>(q, i);
   __syncthreads();
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(256) void k_bucket_scores(const void* __restrict__ 
       for (int x = lane; x < d; x += kWave) acc = fmaf(qs[b * d + x], reps[(int64_t)bucket * d + x], acc);
 #pragma unroll
     for (int off = kWave / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, kWave);
-    if (lane == 0) cand[(int64_t)b * nb + bucket] = valid ? Cand{score_key(acc), bucket} : Cand{0u, -1};
+    if (lane == 0) keys[(int64_t)b * nb + bucket] = valid ? score_key(acc) : 0u;
   }
 }
 
@@ -262,19 +262,21 @@ hipError_t launch_bucket_select(const void* q, int q_dtype, int B, int d, const 
                                 const int32_t* members, int nb, int64_t L, const int32_t* t, int top_b, int n_sink,
                                 int n_window, int32_t* idx, int cap, int32_t* n_sel, int32_t* buckets_out,
                                 Cand* cand, int32_t* n_chosen, Cand* gather, int32_t* chosen, hipStream_t st) {
+  uint32_t* keys = reinterpret_cast<uint32_t*>(cand);
   const unsigned n_wg = (unsigned)((nb + 3) / 4);
   const size_t lds = sizeof(float) * (size_t)B * d;
   if (q_dtype == 0)
-    hipLaunchKernelGGL(k_bucket_scores<0>, dim3(n_wg), dim3(256), lds, st, q, B, d, reps, offsets, nb, cand);
+    hipLaunchKernelGGL(k_bucket_scores<0>, dim3(n_wg), dim3(256), lds, st, q, B, d, reps, offsets, nb, keys);
   else
-    hipLaunchKernelGGL(k_bucket_scores<1>, dim3(n_wg), dim3(256), lds, st, q, B, d, reps, offsets, nb, cand);
+    hipLaunchKernelGGL(k_bucket_scores<1>, dim3(n_wg), dim3(256), lds, st, q, B, d, reps, offsets, nb, keys);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   int32_t* order = buckets_out ? buckets_out : chosen;
   MergeIn in{};
-  in.cand = cand;
-  in.cand_ld = nb;
+  in.slot_key = keys;
+  in.slot_ld = nb;
   in.n_slots = nb;
+  in.slot_pos0 = 0;  // a slot's position is its bucket id
   MergeOut out{};
   out.final_mode = 2;
   out.idx = order;

@@ -62,7 +62,7 @@ __global__ __launch_bounds__(256) void k_score_valu(const void* __restrict__ q, 
   const uint32_t key = score_key(score);
   const bool is_cand = s < hi && is_candidate(s, tb, n_sink, n_window);
   if (mode == kScoreAll) {
-    if (s < hi) cand[(int64_t)b * cand_ld + (s - lo)] = is_cand ? Cand{key, (int32_t)s} : Cand{0u, -1};
+    if (s < hi) reinterpret_cast<uint32_t*>(cand)[(int64_t)b * cand_ld + (s - lo)] = is_cand ? key : 0u;
     return;
   }
   // emission in position order: this workgroup's segment holds its candidates above the threshold
@@ -335,7 +335,7 @@ __global__ __launch_bounds__(64 * NQ) void k_score_mfma(const void* __restrict__
         const uint32_t key = score_key(score);
         const bool is_cand = in_range && is_candidate(s, tb, n_sink, n_window);
         if (mode == kScoreAll) {
-          if (in_range) cand[(int64_t)b * cand_ld + (s - lo)] = is_cand ? Cand{key, (int32_t)s} : Cand{0u, -1};
+          if (in_range) reinterpret_cast<uint32_t*>(cand)[(int64_t)b * cand_ld + (s - lo)] = is_cand ? key : 0u;
         } else {
           const bool emit = is_cand && key > thr;
           const uint64_t m = ballot(emit);

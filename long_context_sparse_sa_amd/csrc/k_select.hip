@@ -20,7 +20,10 @@ namespace {
 
 constexpr int kMergeThreads = 1024;
 constexpr int kMergeWaves = kMergeThreads / kWave;
-constexpr int kHistCopies = 8;
+constexpr int kHistCopies = 2;         // privatized histograms (by wave parity)
+constexpr int kDigitBits = 11;        // radix digit width: 2048 bins spread clustered keys thinly
+constexpr int kBins = 1 << kDigitBits;
+static_assert(kBins == 2 * 1024, "the digit search gives each of the 1024 threads two bins");
 constexpr int kRounds = 16;  // rounds of 1024 entries compacted per batch
 constexpr int kBatch = kRounds * kMergeThreads;
 constexpr int kMaxSortK = 16384;
@@ -28,7 +31,7 @@ constexpr int kLdsBytes = 163840;  // LDS per workgroup on gfx950
 
 struct MergeShared {
   union {
-    uint32_t hist[kHistCopies][256];  // selection passes
+    uint32_t hist[kHistCopies][kBins];  // selection passes
     struct {
       int32_t off[kMergeThreads];  // gather: output offset and count of each segment of a chunk
       int32_t cnt[kMergeThreads];
@@ -99,60 +102,64 @@ __device__ __forceinline__ void note_minmax(uint32_t& lmin, uint32_t& lmax, uint
   lmax = key > lmax ? key : lmax;
 }
 
-// One 8-bit radix pass over the entries whose value matches (prefix, mask), then the digit search in the order of
-// selection (descending for keys, ascending for positions). `val(i, &v)` yields the radix value of entry i, or
-// false when the entry does not take part.
-template <typename Val>
-__device__ __forceinline__ void radix_pass(MergeShared& sh, int n, Val val, uint32_t prefix, uint32_t mask, int shift,
-                                           uint32_t need, bool descending, int tid) {
+// One radix pass over a digit of d <= kDigitBits bits at `shift`, then the digit search in the order of selection
+// (descending for keys, ascending for positions). Key passes (kPos false) count the keys matching (prefix, mask);
+// position passes count the positions matching (prefix, mask) among entries whose key equals kstar. Loads are
+// unconditional (clamped index) and batched four per thread, so they are in flight together; only the counting
+// is predicated. Wave 0 then scans the bins, 32 per lane.
+template <bool kPos>
+__device__ __forceinline__ void radix_pass(MergeShared& sh, int n, const uint32_t* K, const int32_t* P, uint32_t kstar,
+                                           uint32_t prefix, uint32_t mask, int shift, int d, uint32_t need, int tid) {
   const int lane = tid & (kWave - 1), wave = tid / kWave;
-  for (int i = tid; i < kHistCopies * 256; i += kMergeThreads) (&sh.u.hist[0][0])[i] = 0;
+  const uint32_t dmask = (1u << d) - 1u;
+  for (int i = tid; i < kHistCopies * kBins; i += kMergeThreads) (&sh.u.hist[0][0])[i] = 0;
   __syncthreads();
   uint32_t* h = sh.u.hist[wave % kHistCopies];
   for (int base = 0; base < n; base += 4 * kMergeThreads) {
-    uint32_t v[4];
-    bool ok[4];
+    uint32_t kv[4], pv[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int i = base + j * kMergeThreads + tid;
-      ok[j] = i < n && val(i, &v[j]);
+      const int ic = i < n ? i : n - 1;
+      kv[j] = K[ic];
+      if (kPos) pv[j] = (uint32_t)P[ic];
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (ok[j] && (v[j] & mask) == prefix) atomicAdd(&h[(v[j] >> shift) & 255u], 1u);
+    for (int j = 0; j < 4; ++j) {
+      const bool in = base + j * kMergeThreads + tid < n;
+      const uint32_t v = kPos ? pv[j] : kv[j];
+      const bool ok = in && (!kPos || kv[j] == kstar) && (v & mask) == prefix;
+      if (ok) atomicAdd(&h[(v >> shift) & dmask], 1u);
+    }
   }
   __syncthreads();
-  if (wave == 0) {
-    uint32_t c[4], local = 0;
+  // digit search with every thread: thread t owns selection-order bins 2t and 2t + 1
+  const bool descending = !kPos;
+  const int nb = 1 << d;
+  uint32_t c[2], local = 0;
+  int binof[2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int o = 4 * lane + j;
-      const int bin = descending ? 255 - o : o;
-      uint32_t s = 0;
+  for (int e = 0; e < 2; ++e) {
+    const int o = 2 * tid + e;
+    binof[e] = descending ? nb - 1 - o : o;
+    c[e] = 0;
+    if (o < nb)
 #pragma unroll
-      for (int cp = 0; cp < kHistCopies; ++cp) s += sh.u.hist[cp][bin];
-      c[j] = s;
-      local += s;
-    }
-    const uint32_t incl = wave_inclusive_scan(local, lane);
-    uint32_t run = incl - local;
-    int found = -1;
-    uint32_t fb = 0, fc = 0;
+      for (int cp = 0; cp < kHistCopies; ++cp) c[e] += sh.u.hist[cp][binof[e]];
+    local += c[e];
+  }
+  const uint32_t winc = wave_inclusive_scan(local, lane);
+  if (lane == kWave - 1) sh.wsum[wave] = (int32_t)winc;
+  __syncthreads();
+  uint32_t before_w = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (found < 0 && run < need && run + c[j] >= need) {
-        found = 4 * lane + j;
-        fb = run;
-        fc = c[j];
-      }
-      run += c[j];
-    }
-    const uint64_t m = ballot(found >= 0);
-    if (m && lane == (int)__builtin_ctzll(m)) {
-      sh.digit = (uint32_t)(descending ? 255 - found : found);
-      sh.before = fb;
-      sh.in_bin = fc;
-    }
+  for (int w = 0; w < kMergeWaves; ++w) before_w += w < wave ? (uint32_t)sh.wsum[w] : 0u;
+  const uint32_t incl = before_w + winc, excl = incl - local;
+  if (excl < need && incl >= need) {
+    const bool first = excl + c[0] >= need;
+    sh.digit = (uint32_t)binof[first ? 0 : 1];
+    sh.before = first ? excl : excl + c[0];
+    sh.in_bin = c[first ? 0 : 1];
   }
   __syncthreads();
 }
@@ -209,29 +216,31 @@ __device__ __forceinline__ void merge_body(MergeShared& sh, int b, int k, const 
   }
   int n = nk;
   const Cand* cb = in.cand ? in.cand + (int64_t)b * in.cand_ld : nullptr;
-  if (cb && !in.seg_cnt) {
+  if (in.slot_key) {
+    const uint32_t* kb = in.slot_key + (int64_t)b * in.slot_ld;
     for (int64_t base = 0; base < in.n_slots; base += kBatch) {
-      Cand c[kRounds];
+      uint32_t c[kRounds];
       bool f[kRounds];
       int slot[kRounds];
 #pragma unroll
       for (int r = 0; r < kRounds; ++r) {
         const int64_t i = base + r * kMergeThreads + tid;
-        c[r] = i < in.n_slots ? cb[i] : Cand{0u, 0};
+        c[r] = i < in.n_slots ? kb[i] : 0u;
       }
 #pragma unroll
-      for (int r = 0; r < kRounds; ++r) f[r] = c[r].key != 0u;
+      for (int r = 0; r < kRounds; ++r) f[r] = c[r] != 0u;
       const int got = batch_slots(sh, f, slot, tid);
 #pragma unroll
       for (int r = 0; r < kRounds; ++r)
         if (f[r]) {
-          K[n + slot[r]] = c[r].key;
-          P[n + slot[r]] = c[r].pos;
-          note_minmax(lmin, lmax, c[r].key);
+          K[n + slot[r]] = c[r];
+          P[n + slot[r]] = in.slot_pos0 + (int32_t)(base + r * kMergeThreads + tid);
+          note_minmax(lmin, lmax, c[r]);
         }
       n += got;
     }
-  } else if (cb) {
+  }
+  if (cb) {
     for (int w0 = 0; w0 < in.n_seg; w0 += kMergeThreads) {
       const int w = w0 + tid;
       const int c = w < in.n_seg ? (int)in.seg_cnt[(int64_t)b * in.n_seg + w] : 0;
@@ -287,14 +296,10 @@ __device__ __forceinline__ void merge_body(MergeShared& sh, int b, int k, const 
     int bits = kmin == kmax ? 0 : 32 - __clz(kmin ^ kmax);  // low bits that still differ
     uint32_t mask = bits == 32 ? 0u : ~((1u << bits) - 1u);
     uint32_t prefix = kmin & mask;
-    auto key_val = [&](int i, uint32_t* v) {
-      *v = K[i];
-      return true;
-    };
     while (bits > 0) {
-      const int d = bits < 8 ? bits : 8;
+      const int d = bits < kDigitBits ? bits : kDigitBits;
       const int shift = bits - d;
-      radix_pass(sh, n, key_val, prefix, mask, shift, need, true, tid);
+      radix_pass<false>(sh, n, K, P, 0u, prefix, mask, shift, d, need, tid);
       need -= sh.before;
       ties = sh.in_bin;
       prefix |= sh.digit << shift;
@@ -305,17 +310,15 @@ __device__ __forceinline__ void merge_body(MergeShared& sh, int b, int k, const 
     if (need < ties) {
       // several candidates share the k-th key: keep the `need` lowest positions among them
       uint32_t pprefix = 0, pmask = 0, pneed = need;
-      auto pos_val = [&](int i, uint32_t* v) {
-        if (K[i] != kstar) return false;
-        *v = (uint32_t)P[i];
-        return true;
-      };
-      for (int pass = 0; pass < 4; ++pass) {
-        const int shift = 24 - 8 * pass;
-        radix_pass(sh, n, pos_val, pprefix, pmask, shift, pneed, false, tid);
+      // positions are below 2^31: digits of bits 30..20, 19..9 and 8..0
+      for (int pbits = 31; pbits > 0;) {
+        const int d = pbits < kDigitBits ? pbits : kDigitBits;
+        const int shift = pbits - d;
+        radix_pass<true>(sh, n, K, P, kstar, pprefix, pmask, shift, d, pneed, tid);
         pneed -= sh.before;
         pprefix |= sh.digit << shift;
-        pmask |= 255u << shift;
+        pmask |= ((1u << d) - 1u) << shift;
+        pbits -= d;
       }
       pstar = (int32_t)pprefix;
     }
@@ -386,15 +389,13 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(int k, MergeIn in, Cand
     sh.kmax = 0u;
   }
   const int nk = in.kept ? in.kept_n[b] : 0;
-  int64_t n_in = 0;
-  if (in.cand && !in.seg_cnt) {
-    n_in = in.n_slots;
-  } else if (in.cand) {
+  int64_t n_in = in.slot_key ? in.n_slots : 0;
+  if (in.cand && in.seg_cnt) {
     int s = 0;
     for (int w = tid; w < in.n_seg; w += kMergeThreads) s += (int)in.seg_cnt[(int64_t)b * in.n_seg + w];
     int total;
     block_scan(sh, s, tid, &total);
-    n_in = total;
+    n_in += total;
   }
   __syncthreads();
   uint64_t* sort_area = reinterpret_cast<uint64_t*>(dyn + (size_t)8 * cap);

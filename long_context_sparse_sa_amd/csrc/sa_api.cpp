@@ -265,11 +265,14 @@ SA_API int sa_select_topk(const void* q, int q_dtype, const float* w, const void
     in.kept = first ? nullptr : w2.kept;
     in.kept_ld = k_sparse;
     in.kept_n = w2.kept_n;
-    in.cand = w2.cand;
-    in.cand_ld = w2.cand_ld;
     if (first) {
+      in.slot_key = reinterpret_cast<const uint32_t*>(w2.cand);
+      in.slot_ld = w2.cand_ld;
       in.n_slots = hi - lo;
+      in.slot_pos0 = (int32_t)lo;
     } else {
+      in.cand = w2.cand;
+      in.cand_ld = w2.cand_ld;
       const sa::EmitPlan ep = sa::score_emit_plan(a, lo, hi);
       in.seg_cnt = w2.seg_cnt;
       in.n_seg = ep.n_seg;

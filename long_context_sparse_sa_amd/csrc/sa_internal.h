@@ -43,8 +43,8 @@ EmitPlan score_emit_plan(const IndexerArgs& a, int64_t lo, int64_t hi);
 
 // Scores positions [lo, hi).
 //  kScoreDense: scores[b * scores_ld + (s - lo)] = I(b, s), or -inf for s > t_b.
-//  kScoreAll:   cand[b * cand_ld + (s - lo)] = {score_key(I), s} for candidates s (n_sink <= s <= t_b - n_window),
-//               {0, -1} otherwise.
+//  kScoreAll:   the cand buffer is read as uint32 keys: keys[b * cand_ld + (s - lo)] = score_key(I) for candidates s
+//               (n_sink <= s <= t_b - n_window), 0 otherwise (the position is the slot's index).
 //  kScoreEmit:  candidates with score_key(I) > thr_key[b] (any candidate when thr_key is NULL) go to the segments
 //               described by score_emit_plan(a, lo, hi); seg_cnt receives the per-segment counts.
 hipError_t launch_score(const IndexerArgs& a, int64_t lo, int64_t hi, int mode, float* scores, int64_t scores_ld,
@@ -53,17 +53,21 @@ hipError_t launch_score(const IndexerArgs& a, int64_t lo, int64_t hi, int mode, 
 
 // Candidates of one exact top-k merge, per query b, in this order:
 //   kept:     kept[b * kept_ld + (0:kept_n[b])]                                   (when kept != NULL)
-//   slots:    cand[b * cand_ld + (0:n_slots)], key 0 marking an empty slot       (when seg_cnt == NULL)
-//   segments: seg_cnt[b * n_seg + w] entries at cand[b * cand_ld + w * seg_cap], w = 0, 1, ...
+//   slots:    keys slot_key[b * slot_ld + i], i < n_slots, for position slot_pos0 + i; key 0 marks an empty
+//             slot                                                              (when slot_key != NULL)
+//   segments: seg_cnt[b * n_seg + w] entries at cand[b * cand_ld + w * seg_cap], w = 0, 1, ...  (when seg_cnt)
 // The merge preserves this order. When the entries come in ascending position order, as every producer in this
 // library writes them, the selected positions come out ascending without a sort.
 struct MergeIn {
   const Cand* kept;
   int kept_ld;
   const int32_t* kept_n;
+  const uint32_t* slot_key;
+  int64_t slot_ld;
+  int64_t n_slots;
+  int32_t slot_pos0;
   const Cand* cand;
   int64_t cand_ld;
-  int64_t n_slots;
   const uint32_t* seg_cnt;
   int n_seg;
   int64_t seg_cap;
@@ -106,7 +110,8 @@ hipError_t launch_bucket_build(const void* k, int k_dtype, int64_t k_ld, int64_t
                                int32_t* table, const BucketBuildPlan& plan, hipStream_t stream);
 
 int bucket_expand_max();
-// Workspace of the Flat search: cand [B * n_buckets], n_chosen [B], gather [B * n_buckets], chosen [B * top_b].
+// Workspace of the Flat search: keys [B * n_buckets] (uint32, in a Cand-sized area), n_chosen [B],
+// gather [B * n_buckets], chosen [B * top_b].
 hipError_t launch_bucket_select(const void* q, int q_dtype, int B, int d, const float* reps, const int32_t* offsets,
                                 const int32_t* members, int n_buckets, int64_t L, const int32_t* t, int top_b,
                                 int n_sink, int n_window, int32_t* idx, int cap, int32_t* n_sel,

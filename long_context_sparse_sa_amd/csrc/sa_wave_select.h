@@ -11,13 +11,19 @@
 
 namespace sa {
 
+// Inclusive prefix sum over the 64 lanes with DPP row operations (no LDS round trips): shifts by 1, 2, 4 and 8
+// inside each row of 16 lanes, then row 0's total is broadcast into row 1 (and row 2's into row 3), then the
+// total of rows 0-1 into rows 2-3. Lanes a shift moves past the row start read `old` = 0.
 __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v, int lane) {
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const uint32_t o = __shfl_up(v, off, kWave);
-    if (lane >= off) v += o;
-  }
-  return v;
+  (void)lane;
+  int x = (int)v;
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1 and 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2 and 3
+  return (uint32_t)x;
 }
 
 // One wave scans 256 histogram bins in the order of selection (descending digit for keys, ascending for
