@@ -36,6 +36,8 @@ def parse():
     ap.add_argument("--cpu-sample-queries", type=int, default=0, help="0 = pick by workload")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="the oracle baseline repeats its query sample until this much CPU time has passed")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB five times (the reference for the HBM counters)")
     return ap.parse_args()
 
 
@@ -53,6 +55,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 5}))
+        return
     sa.load()
     dev = "cuda"
     wl = get_workload(args.workload)
@@ -179,6 +190,10 @@ def main():
                     "traffic": None, "algorithmic_flops_per_launch": i_flops, "launch_ms": round(t_sel * 1e3, 4),
                     "hbm_gbps": round(i_bytes / t_sel / 1e9, 1)}
         keys_per_s = pairs / t_sel
+    traffic = measured_traffic(wl.name)
+    if traffic:
+        sel_roof["traffic"] = traffic.get("select")
+        attn_roof["traffic"] = traffic.get("attn")
     dominant, other = (sel_roof, attn_roof) if t_sel >= t_att else (attn_roof, sel_roof)
 
     res = {
@@ -203,6 +218,29 @@ def main():
     res["host"] = {"cpu": platform.processor() or platform.machine(), "nproc": os.cpu_count(),
                    "gpu": torch.cuda.get_device_name(0)}
     print(json.dumps(res))
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per call of each stage from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary of this
+    workload (scaled by the plain-copy calibration), or None when there is none or when the kernel sources no
+    longer hash to the ones the counters were taken on."""
+    import glob
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    try:
+        rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+    except (IndexError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "long_context_sparse_sa_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    if h.hexdigest() != rec.get("source_sha256"):
+        return None
+    return {k: v["read_bytes"] + v["write_bytes"] for k, v in rec.items() if isinstance(v, dict)}
 
 
 def cpu_baseline(wl, base, n_sample, min_seconds):

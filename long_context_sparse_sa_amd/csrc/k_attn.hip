@@ -167,7 +167,7 @@ constexpr int kTileRows = 32;
 constexpr int kTileBytes = kTileRows * kRowBytes;        // 36864
 constexpr int kDmaPerWave = kTileBytes / 1024 / 4;       // 9 wave instructions of 1 KB per tile
 constexpr int kNBuf = 3;                                 // LDS tiles: up to 2 in flight while one is consumed
-constexpr int kMaxRowsPerSplit = 512;
+constexpr int kMaxRowsPerSplit = 4096;                   // positions of one split staged in LDS
 constexpr int kQSteps = kRowElems / 2 / 16;              // 18 k-steps of 16 dims: each wave takes half the dims
 constexpr float kRescaleSlack = 8.f;                     // log2 headroom before the running max is raised
 constexpr int kPrefK = 4;                                // K fragments in flight ahead of the S^T MFMAs
