@@ -173,8 +173,34 @@ constexpr float kRescaleSlack = 8.f;                     // log2 headroom before
 constexpr int kPrefK = 4;                                // K fragments in flight ahead of the S^T MFMAs
 constexpr int kPrefV = 3;                                // V^T fragments in flight ahead of the O^T MFMAs
 
-// chunk c of row n lives at chunk slot c ^ (n & 7) (the XOR stays inside the aligned group of 8 chunks)
-__device__ __forceinline__ int chunk_slot(int n, int c) { return c ^ (n & 7); }
+// Chunk c of row n lives at chunk slot c ^ f(n), f(n) = ((n >> 2) & 3) | (((n >> 1) & 1) << 2) (the XOR stays
+// inside the aligned group of 8 chunks; f has period 16). With 1152-byte rows this keeps both LDS read patterns
+// free of bank conflicts: 16 consecutive rows reading one chunk (K fragments), and 4 consecutive rows reading 4
+// consecutive chunks in 8-byte halves (V transpose reads of two lane groups).
+__device__ __forceinline__ int chunk_slot(int n, int c) { return c ^ (((n >> 2) & 3) | (((n >> 1) & 1) << 2)); }
+
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
+
+__device__ __forceinline__ bf16x8 lds_load_b128(uint32_t lds_addr) {
+  return *reinterpret_cast<__attribute__((address_space(3))) const bf16x8*>(lds_addr);
+}
+__device__ __forceinline__ i16x4 lds_read_tr16_at(uint32_t lds_addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_i16x4*>(lds_addr));
+}
+
+// Lanes l and l ^ 32 exchanged in one VALU instruction: the pair returned holds this lane's value and the partner's
+// (which is which depends on the half), so only symmetric combinations of the two are used.
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // Grid: 1-D. A unit is (query b, row split); every unit has H / 64 head groups. Block id
 // (u / 8) * 8 * HG + hg * 8 + u % 8 puts all head groups of unit u on the same XCD (block id mod 8), so the
@@ -246,17 +272,28 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
   for (int r = tid; r < n_tiles * kTileRows; r += 256) pos_s[r] = r < n_my ? R.pos(r_begin + r) : 0;
   __syncthreads();
 
-  const char* kvb = reinterpret_cast<const char*>(kv);
-  const int64_t ld_bytes = kv_ld * 2;
-  auto issue = [&](int tile, int buf) {
+  // DMA plan of this lane, the same for every tile: its chunk jj of the wave's share lands in row drow[jj] of the
+  // tile at chunk slot dcol[jj]; the source row address is gbase[jj] + position * row bytes (one 32x32->64 multiply-add
+  // per copy: positions are non-negative and a row is far below 4 GB).
+  const uint32_t ld_bytes = (uint32_t)(kv_ld * 2);
+  uint32_t drow[kDmaPerWave];
+  uint64_t gbase[kDmaPerWave];
 #pragma unroll
-    for (int jj = 0; jj < kDmaPerWave; ++jj) {
-      const int slot = (wave * kDmaPerWave + jj) * 64 + lane;
-      const int n = slot / kRowChunks;
-      const int c = chunk_slot(n, slot % kRowChunks);
-      const int s = pos_s[tile * kTileRows + n];
-      dma16(kvb + (int64_t)s * ld_bytes + c * 16, &tiles[buf][(wave * kDmaPerWave + jj) * 1024]);
-    }
+  for (int jj = 0; jj < kDmaPerWave; ++jj) {
+    const int slot = (wave * kDmaPerWave + jj) * 64 + lane;
+    const int n = slot / kRowChunks;
+    drow[jj] = 4u * n;
+    gbase[jj] = (uint64_t)(uintptr_t)kv + 16u * chunk_slot(n, slot % kRowChunks);
+  }
+  auto issue = [&](int tile, int buf) {
+    uint32_t s[kDmaPerWave];  // all position reads first: one LDS wait covers them
+#pragma unroll
+    for (int jj = 0; jj < kDmaPerWave; ++jj)
+      s[jj] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(pos_s) + tile * 4 * kTileRows + drow[jj]);
+#pragma unroll
+    for (int jj = 0; jj < kDmaPerWave; ++jj)
+      dma16(reinterpret_cast<const void*>(gbase[jj] + (uint64_t)s[jj] * ld_bytes),
+            &tiles[buf][(wave * kDmaPerWave + jj) * 1024]);
   };
 
   f32x16 o[NT];
@@ -264,39 +301,52 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
   for (int i = 0; i < NT; ++i) o[i] = f32x16{};
   float m_use = -INFINITY, l_run = 0.f;  // exponents are taken relative to m_use (log2 domain)
 
-  // Per-lane LDS offsets (every unrolled access is a base register plus a compile-time offset).
-  // K fragment (A operand of S^T): row j, chunk 36 dh + 2 ks + hsel at its chunk slot:
-  //   kofs[ks & 3] + 128 * (ks >> 2).
-  int kofs[4];
+  // Per-lane LDS byte offsets inside a tile (each unrolled access below is one of these plus a compile-time offset).
+  // K fragment (A operand of S^T): row j, chunk 36 dh + 2 ks + hsel at its chunk slot: kofs[ks & 3] + 128 (ks >> 2).
+  uint32_t kofs[4];
 #pragma unroll
   for (int qq = 0; qq < 4; ++qq) kofs[qq] = j * kRowBytes + 16 * chunk_slot(j, 36 * dh + 2 * qq + hsel);
   // V^T fragment (A operand of O^T) through transpose reads: in each 16-lane group gq = lane / 16, lane
   // a + 4 r4 addresses row 4 hv + r4 (hv = gq / 2) at columns dv0 + 32 nt + 16 (gq & 1) + 4 a; the second read
-  // takes rows + 8, the second k-step rows + 16. Columns 4 a .. 4 a + 3 sit in chunk C0 + 4 nt at byte 8 (a & 1).
+  // takes rows + 8 (its own base: the swizzle differs), the second k-step rows + 16 (same swizzle). Columns
+  // 4 a .. 4 a + 3 sit in chunk C0 + 4 nt at byte 8 (a & 1).
   const int gq = lane >> 4, qa = lane & 3, r4 = (lane >> 2) & 3;
   const int hv = gq >> 1;
   const int vrow = 4 * hv + r4;
   const int C0 = dv0 / 8 + 2 * (gq & 1) + (qa >> 1);
-  int vofs[2];
+  uint32_t vofs[4];  // [2 * (rows + 8 for the second read) + parity of nt]
 #pragma unroll
-  for (int par = 0; par < 2; ++par) vofs[par] = vrow * kRowBytes + 16 * chunk_slot(vrow, C0 + 4 * par) + 8 * (qa & 1);
+  for (int rd = 0; rd < 2; ++rd)
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int row = vrow + 8 * rd;
+      vofs[2 * rd + par] = row * kRowBytes + 16 * chunk_slot(row, C0 + 4 * par) + 8 * (qa & 1);
+    }
+  const uint32_t tiles_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)&tiles[0][0];
 
-  wait_vmem();  // the Q fragments are in registers before the tile copies start counting
-  const int n_pre = n_tiles < kNBuf - 1 ? n_tiles : kNBuf - 1;
-  for (int p = 0; p < n_pre; ++p) issue(p, p);
-  for (int tile = 0; tile < n_tiles; ++tile) {
+  // One tile: S^T, the online softmax, O^T. kPartial: the split's last tile is not full (rows past its end are
+  // masked to -inf); only that tile pays for the mask.
+  auto process = [&](int tile, auto partial) __attribute__((always_inline)) {
     // wait for this tile's copies; the next tile may stay in flight
     if (tile + 1 < n_tiles) wait_vmem_below<kDmaPerWave>();
     else wait_vmem_below<0>();
     lds_barrier();
     if (tile + kNBuf - 1 < n_tiles) issue(tile + kNBuf - 1, (tile + kNBuf - 1) % kNBuf);
-    const char* tb = tiles[tile % kNBuf];
+    // this tile's fragment bases, made opaque so that the compiler keeps one register per base and folds every
+    // constant into the instruction offset (instead of hoisting base + constant sums out of the loop)
+    const uint32_t tbase = tiles_lds + (uint32_t)((tile % kNBuf) * kTileBytes);
+    uint32_t kb[4], vb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kb[i] = tbase + kofs[i];
+      vb[i] = tbase + vofs[i];
+      asm volatile("" : "+v"(kb[i]), "+v"(vb[i]));
+    }
 
-    // S^T (32 rows x 32 heads) over all 576 dims
     // partial S^T (32 rows x 32 heads) over this wave's 288 dims, then the partner's half through LDS. The K
     // fragments run kPrefK steps ahead of the MFMAs in a register ring; the scheduling fences keep the compiler
     // from pulling each read next to its MFMA, which would expose the LDS latency on every step.
-    auto k_frag = [&](int ks) { return *reinterpret_cast<const bf16x8*>(tb + kofs[ks & 3] + 128 * (ks >> 2)); };
+    auto k_frag = [&](int ks) { return lds_load_b128(kb[ks & 3] + 128 * (ks >> 2)); };
     bf16x8 kr[kPrefK];
 #pragma unroll
     for (int i = 0; i < kPrefK; ++i) kr[i] = k_frag(i);
@@ -317,11 +367,10 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
 #pragma unroll
       for (int e = 0; e < 4; ++e) s[4 * g4 + e] += other[e];
     }
-    auto v_frag = [&](int i) {  // V^T fragment of step i = 2 nt + kk
-      const int nt = i >> 1, kk = i & 1;
-      const char* vp = tb + vofs[nt & 1] + 128 * (nt >> 1) + 18432 * kk;
-      const i16x4 v0 = lds_read_tr16(vp);
-      const i16x4 v1 = lds_read_tr16(vp + 9216);
+    auto v_frag = [&](int i) {  // V^T fragment of step i = kk * NT + nt
+      const int nt = i % NT, kk = i / NT;
+      const i16x4 v0 = lds_read_tr16_at(vb[nt & 1] + 128 * (nt >> 1) + 18432 * kk);
+      const i16x4 v1 = lds_read_tr16_at(vb[2 + (nt & 1)] + 128 * (nt >> 1) + 18432 * kk);
       // whole-vector shuffle + bit_cast (a bit_cast of a single ext-vector element is not used here: clang lowers
       // it to element 0 for every index)
       return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -330,22 +379,24 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
 #pragma unroll
     for (int i = 0; i < kPrefV; ++i) vr[i] = v_frag(i);
 
-    // register r of this lane holds row 8 (r / 4) + 4 hsel + r % 4 of head `head`
-    const int valid = n_my - tile * kTileRows;
-    float x[16];
-    float mt_max = -INFINITY;
+    // register r of this lane holds row 8 (r / 4) + 4 hsel + r % 4 of head `head`. The softmax works on raw
+    // scores: log2-domain exponent = score * scale_log2 - m_use.
+    if constexpr (decltype(partial)::value) {
+      const int valid = n_my - tile * kTileRows;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = 8 * (r >> 2) + 4 * hsel + (r & 3);
-      x[r] = row < valid ? s[r] * scale_log2 : -INFINITY;
-      mt_max = fmaxf(mt_max, x[r]);
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + 4 * hsel + (r & 3) >= valid) s[r] = -INFINITY;
     }
-    mt_max = fmaxf(mt_max, __shfl_xor(mt_max, 32, kWave));
+    float mt = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
+    mt = halves_max(mt);
+    mt *= scale_log2;  // finite: row 0 of a tile is always valid
     // raise the reference only when this tile would exceed it by more than 2^kRescaleSlack
-    const bool raise = mt_max > m_use + kRescaleSlack;
+    const bool raise = mt > m_use + kRescaleSlack;
     if (__any(raise)) {
-      const float m_new = raise ? mt_max : m_use;
-      const float alpha = exp2f(m_use - m_new);  // 1 where not raised, 0 on the first tile
+      const float m_new = raise ? mt : m_use;
+      const float alpha = __builtin_amdgcn_exp2f(m_use - m_new);  // 1 where not raised, 0 on the first tile
       l_run *= alpha;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) o[nt] = o[nt] * alpha;
@@ -357,25 +408,34 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float p = exp2f(x[8 * kk + e] - m_use);
+        // exponents are <= kRescaleSlack; results below 2^-126 flush to zero, far below bf16 resolution of the sum
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[8 * kk + e], scale_log2, -m_use));
         psum += p;
         pf[kk][e] = (__bf16)p;
       }
     l_run += psum;
 
     // O^T (value columns x heads) += V^T P^T; k-step kk covers rows 16 kk + {4 hsel .. +3, 8 + 4 hsel .. +3}.
-    // Step i = 2 nt + kk; its V^T fragment (two transpose reads) is fetched kPrefV steps ahead.
+    // Step i = kk * NT + nt (both k-steps of a tile are NT MFMAs apart); its V^T fragment (two transpose reads)
+    // is fetched kPrefV steps ahead.
 #pragma unroll
     for (int i = 0; i < 2 * NT; ++i) {
       const bf16x8 cur = vr[i % kPrefV];
       if (i + kPrefV < 2 * NT) vr[i % kPrefV] = v_frag(i + kPrefV);
-      o[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, pf[i & 1], o[i >> 1], 0, 0, 0);
+      o[i % NT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, pf[i / NT], o[i % NT], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-  }
+  };
+
+  wait_vmem();  // the Q fragments are in registers before the tile copies start counting
+  const int n_pre = n_tiles < kNBuf - 1 ? n_tiles : kNBuf - 1;
+  for (int p = 0; p < n_pre; ++p) issue(p, p);
+  const int n_full = n_my / kTileRows;
+  for (int tile = 0; tile < n_full; ++tile) process(tile, BoolTag<false>{});
+  if (n_full < n_tiles) process(n_full, BoolTag<true>{});
 
   // lanes j and j + 32 hold disjoint rows of the same head: add their sums
-  l_run += __shfl_xor(l_run, 32, kWave);
+  l_run = halves_sum(l_run);
   // register r of tile nt holds column dv0 + 32 nt + 8 (r / 4) + 4 hsel + r % 4 of head `head`
   if (n_splits == 1) {
     const float inv = 1.f / l_run;
@@ -527,6 +587,7 @@ hipError_t launch_attn(const AttnArgs& a, const AttnPlan& p, void* ws, hipStream
                          a.lse);
     return hipGetLastError();
   }
+  if ((uint64_t)a.kv_ld * 2 > 0xffffffffull) return hipErrorInvalidValue;  // row byte stride is a 32-bit multiplier
   float* part_o = reinterpret_cast<float*>(ws);
   float* part_ml = part_o ? part_o + (size_t)a.B * a.H * p.n_splits * a.d_v : nullptr;
   const int HG = a.H / 64;
