@@ -63,7 +63,8 @@ typedef enum {
 typedef enum {
   SA_TOPK_AUTO = 0,      /* the library picks by batch size                                            */
   SA_TOPK_SPLIT_L = 1,   /* few queries: key range split over workgroups, thresholds refined by levels  */
-  SA_TOPK_PER_QUERY = 2  /* many queries (prefill chunk): one streaming pass per query group             */
+  SA_TOPK_PER_QUERY = 2, /* many queries (prefill chunk): one streaming pass per query group             */
+  SA_TOPK_RADIX = 3      /* few queries: one key per position, radix select spread over workgroups      */
 } sa_topk_algo;
 
 SA_API const char* sa_status_string(int status);
@@ -88,8 +89,9 @@ SA_API int sa_index_score(const void* q, int q_dtype, const float* w, const void
  * sa_select_topk -- indexer scores fused with exact top-k selection and the sink/window budget ([LongCat] DSA
  * baseline section, arg-topK equation; SI section, sparse-part equation):
  *     S_sparse,b = the min(k_sparse, |C_b|) positions of C_b with the largest fp32 score I_{b,s}
- * where ties are broken towards the LOWER position. The score is the one sa_index_score defines (fp32). The
- * full score matrix is never written: only candidates that can still enter the top-k leave the kernels.
+ * where ties are broken towards the LOWER position. The score is the one sa_index_score defines (fp32).
+ * SA_TOPK_SPLIT_L and SA_TOPK_PER_QUERY never write the full score matrix (only candidates that can still enter
+ * the top-k leave the kernels); SA_TOPK_RADIX writes one 4-byte key per position and query to the workspace.
  *   idx    [B, idx_ld] int32, idx_ld >= k_sparse: S_sparse,b in ascending position order, then -1 padding.
  *   n_sel  [B] int32: |S_sparse,b|.
  *   The sink and window are not listed in idx; pass the same n_sink/n_window to sa_sparse_attn.

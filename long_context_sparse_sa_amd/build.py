@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 OUT = os.path.join(HERE, "libsa.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["sa_api.cpp", "k_index.hip", "k_select.hip", "k_bucket.hip", "k_attn.hip"]
+SOURCES = ["sa_api.cpp", "k_index.hip", "k_select.hip", "k_radix.hip", "k_bucket.hip", "k_attn.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -1,0 +1,302 @@
+// Exact top-k for few queries by a radix select spread over many workgroups (LongCat Sparse Attention deep-dive:
+// DSA baseline section, arg-topK equation; SI section, the sparse part is the top-K over positions outside sink
+// and window).
+//
+// Input: one order-preserving key per position, keys[b * keys_ld + s] for s < L, 0 for positions that are not
+// candidates (the scoring kernel's all-slots mode writes them). Each query's positions are cut into G chunks and
+// every (chunk, query) pair is one workgroup of every launch, so a handful of queries still fills the chip:
+//   pass 0, 1, 2  histograms of digits 31..21, 20..10 and 9..0 of the keys that match the digits found so far,
+//                 added into a global histogram per query and pass (each workgroup first re-derives the earlier
+//                 digits from the earlier histograms: a 2048-bin scan);
+//   count         per chunk, the keys above the k-th key kstar and the keys equal to it;
+//   write         per chunk, an order-preserving compaction of the selected positions at the chunk's offset (the
+//                 counts of the chunks before it). Among keys equal to kstar the lowest positions are kept: chunk j
+//                 keeps the first min(eq_j, need_eq - ties in chunks before j) of its ties.
+// The selected positions come out in ascending order, padded with -1 to idx_ld; n_sel = min(k, candidates).
+#include "sa_device.h"
+#include "sa_internal.h"
+#include "sa_wave_select.h"
+
+namespace sa {
+namespace {
+
+constexpr int kRThreads = 256;
+constexpr int kRWaves = kRThreads / kWave;
+constexpr int kRBins = 2048;
+constexpr int kChunkAlign = 1024;  // chunk starts are multiples of this many positions (aligned vector loads)
+constexpr int kTargetWgs = 512;
+
+__device__ __forceinline__ int pass_shift(int p) { return p == 0 ? 21 : (p == 1 ? 10 : 0); }
+__device__ __forceinline__ int pass_bins(int p) { return p == 2 ? 1024 : 2048; }
+
+struct RadixShared {
+  uint32_t hist[kRBins];
+  uint32_t wsum[kRWaves];
+  uint32_t wsum2[kRWaves];
+  uint32_t digit, before, total;
+};
+
+// Exclusive scan over the block of one value per thread; *total receives the block sum. All threads must call.
+__device__ __forceinline__ uint32_t block_excl_scan(RadixShared& sh, uint32_t v, uint32_t* total) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const uint32_t incl = wave_inclusive_scan(v, lane);
+  if (lane == kWave - 1) sh.wsum[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kRWaves; ++w) {
+    const uint32_t x = sh.wsum[w];
+    before += w < wave ? x : 0u;
+    all += x;
+  }
+  __syncthreads();
+  *total = all;
+  return before + incl - v;
+}
+
+// Block-wide search of one query's global histogram h (nbins bins) in descending bin order: the bin in which the
+// running count from the top first reaches need (>= 1). Returns false (digit 0) when all bins together hold
+// fewer than need. *before = count in the bins above the digit; *total = sum of all bins. All threads must call.
+__device__ bool find_desc(RadixShared& sh, const uint32_t* __restrict__ h, int nbins, uint32_t need, uint32_t* digit,
+                          uint32_t* before, uint32_t* total) {
+  const int tid = threadIdx.x;
+  const int per = nbins / kRThreads;  // 8 or 4 bins per thread, thread t takes descending ranks per*t ..
+  uint32_t c[8], local = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    c[e] = e < per ? h[nbins - 1 - (per * tid + e)] : 0u;
+    local += c[e];
+  }
+  uint32_t all;
+  const uint32_t excl = block_excl_scan(sh, local, &all);
+  if (excl < need && excl + local >= need) {
+    uint32_t run = excl;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (e < per && run < need && run + c[e] >= need) {
+        sh.digit = (uint32_t)(nbins - 1 - (per * tid + e));
+        sh.before = run;
+      }
+      run += c[e];
+    }
+  }
+  __syncthreads();
+  const bool ok = all >= need;
+  *digit = ok ? sh.digit : 0u;
+  *before = ok ? sh.before : 0u;
+  *total = all;
+  __syncthreads();
+  return ok;
+}
+
+// The k-th key of query b from the three pass histograms: kstar, the number of keys to keep among those equal to
+// it (need_eq >= 1), and the number of candidates. ok = false when there are fewer than k candidates (then every
+// candidate is kept: kstar = 0, need_eq = 0).
+struct KStar {
+  bool ok;
+  uint32_t kstar, need_eq, n_cand;
+};
+
+__device__ KStar derive_kstar(RadixShared& sh, const uint32_t* __restrict__ hist, int B, int b, int k) {
+  KStar r{false, 0u, 0u, 0u};
+  uint32_t d0, b0, tot;
+  r.ok = find_desc(sh, hist + ((size_t)0 * B + b) * kRBins, 2048, (uint32_t)k, &d0, &b0, &tot);
+  r.n_cand = tot;
+  if (!r.ok) return r;
+  uint32_t need = (uint32_t)k - b0, d1, b1, d2, b2, t1, t2;
+  find_desc(sh, hist + ((size_t)1 * B + b) * kRBins, 2048, need, &d1, &b1, &t1);
+  need -= b1;
+  find_desc(sh, hist + ((size_t)2 * B + b) * kRBins, 1024, need, &d2, &b2, &t2);
+  need -= b2;
+  r.kstar = (d0 << 21) | (d1 << 10) | d2;
+  r.need_eq = need;
+  return r;
+}
+
+// Chunk j of query b: positions [s0, s1).
+struct Chunk {
+  int64_t s0, s1;
+};
+__device__ __forceinline__ Chunk chunk_of(int64_t L, int64_t chunk) {
+  Chunk c;
+  c.s0 = (int64_t)blockIdx.x * chunk;
+  c.s1 = c.s0 + chunk < L ? c.s0 + chunk : L;
+  return c;
+}
+
+// Four keys at s (a multiple of 4; the row is padded to a multiple of 4 so the vector load stays inside it);
+// entries at or past s1 read as 0.
+__device__ __forceinline__ void load4(const uint32_t* __restrict__ row, int64_t s, int64_t s1, uint32_t (&v)[4]) {
+  const uint4 x = *reinterpret_cast<const uint4*>(row + s);
+  v[0] = s + 0 < s1 ? x.x : 0u;
+  v[1] = s + 1 < s1 ? x.y : 0u;
+  v[2] = s + 2 < s1 ? x.z : 0u;
+  v[3] = s + 3 < s1 ? x.w : 0u;
+}
+
+template <int PASS>
+__global__ __launch_bounds__(kRThreads) void k_radix_hist(const uint32_t* __restrict__ keys, int64_t keys_ld,
+                                                          int64_t L, int64_t chunk, int k, int B,
+                                                          uint32_t* __restrict__ hist) {
+  __shared__ RadixShared sh;
+  const int b = blockIdx.y, tid = threadIdx.x;
+  constexpr int nb = PASS == 2 ? 1024 : 2048;
+  constexpr int shift = PASS == 0 ? 21 : (PASS == 1 ? 10 : 0);
+  for (int i = tid; i < kRBins; i += kRThreads) sh.hist[i] = 0u;
+  uint32_t prefix = 0u, pmask = 0u;
+  if (PASS >= 1) {
+    uint32_t d0, b0, tot;
+    if (!find_desc(sh, hist + (size_t)b * kRBins, 2048, (uint32_t)k, &d0, &b0, &tot)) return;  // block-uniform
+    prefix = d0 << 21;
+    pmask = 0x7FFu << 21;
+    if (PASS == 2) {
+      uint32_t d1, b1, t1;
+      find_desc(sh, hist + ((size_t)B + b) * kRBins, 2048, (uint32_t)k - b0, &d1, &b1, &t1);
+      prefix |= d1 << 10;
+      pmask |= 0x7FFu << 10;
+    }
+  }
+  __syncthreads();
+  const Chunk c = chunk_of(L, chunk);
+  const uint32_t* row = keys + (int64_t)b * keys_ld;
+  for (int64_t s = c.s0 + 4 * tid; s < c.s1; s += 4 * kRThreads) {
+    uint32_t v[4];
+    load4(row, s, c.s1, v);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (v[e] != 0u && (v[e] & pmask) == prefix) atomicAdd(&sh.hist[(v[e] >> shift) & (nb - 1)], 1u);
+  }
+  __syncthreads();
+  uint32_t* g = hist + ((size_t)PASS * B + b) * kRBins;
+  for (int i = tid; i < nb; i += kRThreads) {
+    const uint32_t x = sh.hist[i];
+    if (x) atomicAdd(&g[i], x);
+  }
+}
+
+__global__ __launch_bounds__(kRThreads) void k_radix_count(const uint32_t* __restrict__ keys, int64_t keys_ld,
+                                                           int64_t L, int64_t chunk, int k, int B,
+                                                           const uint32_t* __restrict__ hist,
+                                                           uint32_t* __restrict__ cnt) {
+  __shared__ RadixShared sh;
+  const int b = blockIdx.y, tid = threadIdx.x;
+  const KStar ks = derive_kstar(sh, hist, B, b, k);
+  const Chunk c = chunk_of(L, chunk);
+  const uint32_t* row = keys + (int64_t)b * keys_ld;
+  uint32_t gt = 0, eq = 0;
+  for (int64_t s = c.s0 + 4 * tid; s < c.s1; s += 4 * kRThreads) {
+    uint32_t v[4];
+    load4(row, s, c.s1, v);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      gt += v[e] > ks.kstar ? 1u : 0u;
+      eq += (ks.ok && v[e] == ks.kstar) ? 1u : 0u;
+    }
+  }
+  uint32_t tg, te;
+  block_excl_scan(sh, gt, &tg);
+  block_excl_scan(sh, eq, &te);
+  if (tid == 0) {
+    cnt[((int64_t)b * gridDim.x + blockIdx.x) * 2 + 0] = tg;
+    cnt[((int64_t)b * gridDim.x + blockIdx.x) * 2 + 1] = te;
+  }
+}
+
+__global__ __launch_bounds__(kRThreads) void k_radix_write(const uint32_t* __restrict__ keys, int64_t keys_ld,
+                                                           int64_t L, int64_t chunk, int k, int B,
+                                                           const uint32_t* __restrict__ hist,
+                                                           const uint32_t* __restrict__ cnt,
+                                                           int32_t* __restrict__ idx, int idx_ld,
+                                                           int32_t* __restrict__ n_sel) {
+  __shared__ RadixShared sh;
+  const int b = blockIdx.y, j = blockIdx.x, tid = threadIdx.x;
+  const int G = gridDim.x;
+  const KStar ks = derive_kstar(sh, hist, B, b, k);
+  // counts of the chunks before this one
+  const uint32_t* cb = cnt + (int64_t)b * G * 2;
+  uint32_t pg = 0, pe = 0;
+  for (int i = tid; i < j; i += kRThreads) {
+    pg += cb[2 * i];
+    pe += cb[2 * i + 1];
+  }
+  uint32_t pre_gt, pre_eq;
+  block_excl_scan(sh, pg, &pre_gt);
+  block_excl_scan(sh, pe, &pre_eq);
+  const uint32_t my_eq = cb[2 * j + 1];
+  const uint32_t ties_before = pre_eq < ks.need_eq ? pre_eq : ks.need_eq;
+  const uint32_t quota = ks.need_eq > pre_eq ? (my_eq < ks.need_eq - pre_eq ? my_eq : ks.need_eq - pre_eq) : 0u;
+  const int64_t off = (int64_t)pre_gt + ties_before;
+  int32_t* out = idx + (int64_t)b * idx_ld;
+
+  const Chunk c = chunk_of(L, chunk);
+  const uint32_t* row = keys + (int64_t)b * keys_ld;
+  uint32_t run_gt = 0, run_eq = 0;  // entries of this chunk before the current batch
+  for (int64_t base = c.s0; base < c.s1; base += 4 * kRThreads) {
+    const int64_t s = base + 4 * tid;
+    uint32_t v[4];
+    if (s < c.s1) load4(row, s, c.s1, v);
+    else v[0] = v[1] = v[2] = v[3] = 0u;
+    bool g[4], t[4];
+    uint32_t lg = 0, lt = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      g[e] = v[e] > ks.kstar;
+      t[e] = ks.ok && v[e] == ks.kstar;
+      lg += g[e] ? 1u : 0u;
+      lt += t[e] ? 1u : 0u;
+    }
+    uint32_t tot;
+    const uint32_t ex = block_excl_scan(sh, (lg << 16) | lt, &tot);  // at most 1024 of each per batch
+    uint32_t gb = run_gt + (ex >> 16), eb = run_eq + (ex & 0xFFFFu);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (g[e]) {
+        out[off + gb + (eb < quota ? eb : quota)] = (int32_t)(s + e);
+        ++gb;
+      } else if (t[e]) {
+        if (eb < quota) out[off + gb + eb] = (int32_t)(s + e);
+        ++eb;
+      }
+    }
+    run_gt += tot >> 16;
+    run_eq += tot & 0xFFFFu;
+  }
+  if (j == 0) {
+    const int take = ks.ok ? k : (int)ks.n_cand;
+    for (int i = take + tid; i < idx_ld; i += kRThreads) out[i] = -1;
+    if (tid == 0) n_sel[b] = take;
+  }
+}
+
+}  // namespace
+
+RadixPlan radix_plan(int B, int64_t L) {
+  RadixPlan p{};
+  p.keys_ld = (L + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
+  int64_t g = B > 0 ? (kTargetWgs + B - 1) / B : 1;
+  int64_t chunk = (L + g - 1) / g;
+  if (chunk < 2 * kChunkAlign) chunk = 2 * kChunkAlign;
+  chunk = (chunk + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
+  p.chunk = chunk;
+  p.n_chunks = (int)((L + chunk - 1) / chunk);
+  if (p.n_chunks < 1) p.n_chunks = 1;
+  return p;
+}
+
+size_t radix_hist_words(int B) { return (size_t)3 * B * kRBins; }
+
+hipError_t launch_radix_select(int B, int64_t L, int k, const RadixPlan& p, const uint32_t* keys,
+                               uint32_t* hist, uint32_t* cnt, int32_t* idx, int idx_ld, int32_t* n_sel,
+                               hipStream_t st) {
+  if (B == 0) return hipSuccess;
+  const dim3 grid((unsigned)p.n_chunks, (unsigned)B);
+  hipLaunchKernelGGL(k_radix_hist<0>, grid, dim3(kRThreads), 0, st, keys, p.keys_ld, L, p.chunk, k, B, hist);
+  hipLaunchKernelGGL(k_radix_hist<1>, grid, dim3(kRThreads), 0, st, keys, p.keys_ld, L, p.chunk, k, B, hist);
+  hipLaunchKernelGGL(k_radix_hist<2>, grid, dim3(kRThreads), 0, st, keys, p.keys_ld, L, p.chunk, k, B, hist);
+  hipLaunchKernelGGL(k_radix_count, grid, dim3(kRThreads), 0, st, keys, p.keys_ld, L, p.chunk, k, B, hist, cnt);
+  hipLaunchKernelGGL(k_radix_write, grid, dim3(kRThreads), 0, st, keys, p.keys_ld, L, p.chunk, k, B, hist, cnt, idx,
+                     idx_ld, n_sel);
+  return hipGetLastError();
+}
+
+}  // namespace sa

@@ -87,9 +87,33 @@ constexpr int64_t kFirstLevel = 16384;
 constexpr int64_t kLevelGrowth = 8;
 constexpr int kAutoPerQueryMinB = 64;
 
+constexpr int64_t kAutoRadixMaxKeys = (int64_t)1 << 24;  // B * L up to which few queries take the radix select
+
 int resolve_algo(int algo, const sa::IndexerArgs& a) {
-  if (algo == SA_TOPK_AUTO) return (a.B >= kAutoPerQueryMinB && sa::stream_select_supported(a)) ? SA_TOPK_PER_QUERY : SA_TOPK_SPLIT_L;
-  return algo;
+  if (algo != SA_TOPK_AUTO) return algo;
+  if (a.B >= kAutoPerQueryMinB && sa::stream_select_supported(a)) return SA_TOPK_PER_QUERY;
+  // few queries: writing one key per position and selecting over all of them with every workgroup beats the
+  // level-by-level thresholds until the key buffer gets large (then the levels prune most of the writes)
+  return (int64_t)a.B * a.L <= kAutoRadixMaxKeys ? SA_TOPK_RADIX : SA_TOPK_SPLIT_L;
+}
+
+struct RadixWs {
+  sa::RadixPlan p;
+  uint32_t* hist;  // [3, B, 2048] pass histograms
+  uint32_t* cnt;   // [B, n_chunks, 2] per-chunk counts
+  uint32_t* keys;  // [B, keys_ld] one key per position
+  size_t bytes;
+};
+
+RadixWs carve_radix(void* ws, const sa::IndexerArgs& a) {
+  RadixWs w{};
+  w.p = sa::radix_plan(a.B, a.L);
+  Carver c(ws);
+  w.hist = c.take<uint32_t>(sa::radix_hist_words(a.B));
+  w.cnt = c.take<uint32_t>((size_t)2 * a.B * w.p.n_chunks);
+  w.keys = c.take<uint32_t>((size_t)a.B * w.p.keys_ld);
+  w.bytes = align_up(c.off, 256);
+  return w;
 }
 
 // Level boundaries of the split-L algorithm: [0, first), [first, 8 first), ... up to L. The first level holds at least
@@ -208,6 +232,7 @@ SA_API size_t sa_select_topk_workspace(int64_t L, int32_t B, int32_t H, int32_t 
   const sa::IndexerArgs a = make_indexer(nullptr, q_dtype, nullptr, nullptr, k_dtype, d, L, B, H, d, nullptr);
   const int alg = resolve_algo(algo, a);
   if (alg == SA_TOPK_PER_QUERY) return carve_per_query(nullptr, a, k_sparse).bytes;
+  if (alg == SA_TOPK_RADIX) return carve_radix(nullptr, a).bytes;
   return carve_split_l(nullptr, a, k_sparse).bytes;
 }
 
@@ -222,7 +247,7 @@ SA_API int sa_select_topk(const void* q, int q_dtype, const float* w, const void
     return fail(SA_ERR_SHAPE, "k_sparse must be in [1, %d]", sa::merge_max_k());
   if (idx_ld < k_sparse) return fail(SA_ERR_SHAPE, "idx_ld (%d) < k_sparse (%d)", idx_ld, k_sparse);
   if (n_sink < 0 || n_window < 0) return fail(SA_ERR_SHAPE, "n_sink and n_window must be >= 0");
-  if (algo < SA_TOPK_AUTO || algo > SA_TOPK_PER_QUERY) return fail(SA_ERR_SHAPE, "unknown algo %d", algo);
+  if (algo < SA_TOPK_AUTO || algo > SA_TOPK_RADIX) return fail(SA_ERR_SHAPE, "unknown algo %d", algo);
   const sa::IndexerArgs a = make_indexer(q, q_dtype, w, k, k_dtype, k_ld, L, B, H, d, t);
   const int alg = resolve_algo(algo, a);
   if (alg == SA_TOPK_PER_QUERY && !sa::stream_select_supported(a))
@@ -248,6 +273,18 @@ SA_API int sa_select_topk(const void* q, int q_dtype, const float* w, const void
     out.n_sel = n_sel;
     e = sa::launch_merge(B, k_sparse, in, w2.gather, w2.cap, out, s);
     return e == hipSuccess ? SA_OK : hip_fail(e, "sa_select_topk (final merge)");
+  }
+  if (alg == SA_TOPK_RADIX) {
+    // every position's key into the workspace (0 for positions outside the candidate range), then the radix
+    // select over all of them
+    const RadixWs w2 = carve_radix(ws, a);
+    e = sa::launch_fill_u32(w2.hist, (int64_t)sa::radix_hist_words(B), 0u, s);
+    if (e != hipSuccess) return hip_fail(e, "sa_select_topk (radix clear)");
+    e = sa::launch_score(a, 0, L, sa::kScoreAll, nullptr, 0, n_sink, n_window, nullptr,
+                         reinterpret_cast<sa::Cand*>(w2.keys), w2.p.keys_ld, nullptr, s);
+    if (e != hipSuccess) return hip_fail(e, "sa_select_topk (radix score)");
+    e = sa::launch_radix_select(B, L, k_sparse, w2.p, w2.keys, w2.hist, w2.cnt, idx, idx_ld, n_sel, s);
+    return e == hipSuccess ? SA_OK : hip_fail(e, "sa_select_topk (radix select)");
   }
   const SplitLWs w2 = carve_split_l(ws, a, k_sparse);
   const int kpw = sa::score_keys_per_wg(a);

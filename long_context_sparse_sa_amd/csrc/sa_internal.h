@@ -93,6 +93,19 @@ int merge_max_k();
 // Fills p[0, n) with v (a kernel, so that it is safe inside captured graphs).
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t stream);
 
+// Radix select over all positions for few queries (k_radix.hip). keys[b * keys_ld + s] (s < L) hold the
+// all-slots keys of the scoring kernel; the rest of each row is never read past the next multiple of 4.
+// hist holds radix_hist_words(B) words and must be zero on entry; cnt holds 2 * B * n_chunks words.
+struct RadixPlan {
+  int64_t keys_ld;  // row stride of keys (a multiple of 1024)
+  int64_t chunk;    // positions per workgroup
+  int n_chunks;     // workgroups per query
+};
+RadixPlan radix_plan(int B, int64_t L);
+size_t radix_hist_words(int B);
+hipError_t launch_radix_select(int B, int64_t L, int k, const RadixPlan& p, const uint32_t* keys, uint32_t* hist,
+                               uint32_t* cnt, int32_t* idx, int idx_ld, int32_t* n_sel, hipStream_t stream);
+
 // Streaming per-query selection for many queries (prefill chunk): one pass over each query's visible keys keeps
 // at most `cap` candidates per query in buf[b, :] (count in buf_n[b]) that contain the exact top-k.
 bool stream_select_supported(const IndexerArgs& a);

@@ -52,7 +52,7 @@ def test_index_score_dense(dtype, H, d):
         assert np.all(err <= 1e-5 * mag[vis] + 1e-30), (b, err.max())
 
 
-ALGOS = [sa.SA_TOPK_SPLIT_L, sa.SA_TOPK_PER_QUERY]
+ALGOS = [sa.SA_TOPK_SPLIT_L, sa.SA_TOPK_PER_QUERY, sa.SA_TOPK_RADIX]
 
 
 @pytest.mark.parametrize("algo", ALGOS)
@@ -88,12 +88,13 @@ def test_topk_normal_band(algo):
         band_compare(selected(idx[b], nsel[b].item()), ref, cand, sc, kk)
 
 
-def test_topk_valu_path_f32():
+@pytest.mark.parametrize("algo", [sa.SA_TOPK_SPLIT_L, sa.SA_TOPK_RADIX])
+def test_topk_valu_path_f32(algo):
     """The toy indexer shapes (4 heads x 32, fp32) take the VALU scorer."""
     B, H, d, L, kk = 2, 4, 32, 1024, 64
     q, w, k = _inputs(3, B, H, d, L, "f32", integer=False)
     w = w.abs()
-    idx, nsel = sa.sa_select_topk(q, w, k, kk, n_sink=4, n_window=32)
+    idx, nsel = sa.sa_select_topk(q, w, k, kk, n_sink=4, n_window=32, algo=algo)
     torch.cuda.synchronize()
     qf, wf, kf = to_f64(q), w.double().cpu().numpy(), to_f64(k)
     for b in range(B):
@@ -163,3 +164,22 @@ def test_topk_rising_scores_many_emits():
         ref, sc, cand = O.select_topk(qf[b], wf[b], kf, L - 1, kk, 4, 64)
         assert np.unique(sc).size < sc.size  # ties are exercised
         np.testing.assert_array_equal(selected(idx[b], nsel[b].item()), ref)
+
+
+def test_topk_radix_chunks_and_ties():
+    """Radix select over many chunks per query: integer scores tie heavily, so the k-th key is shared by entries of
+    several chunks and the lowest positions must win across chunk boundaries; one query has fewer candidates than
+    k (every candidate is kept, -1 padding after them)."""
+    B, H, d, L, kk = 3, 64, 128, 100000, 3000
+    q, w, k = _inputs(11, B, H, d, L, "bf16", integer=True)
+    ts = [L - 1, 60001, 2500]
+    t = torch.tensor(ts, dtype=torch.int32, device=DEV)
+    idx, nsel = sa.sa_select_topk(q, w, k, kk, n_sink=5, n_window=40, t=t, algo=sa.SA_TOPK_RADIX, idx_ld=kk + 17)
+    torch.cuda.synchronize()
+    qf, wf, kf = to_f64(q), w.double().cpu().numpy(), to_f64(k)
+    for b in range(B):
+        ref, sc, cand = O.select_topk(qf[b], wf[b], kf, ts[b], kk, 5, 40)
+        if b == 0:
+            assert np.unique(sc).size < sc.size / 4
+        np.testing.assert_array_equal(selected(idx[b], nsel[b].item()), ref)
+    assert nsel[2].item() == 2500 - 5 - 40 + 1
