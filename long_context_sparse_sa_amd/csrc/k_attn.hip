@@ -227,6 +227,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
                                                    uint16_t* __restrict__ out, float* __restrict__ lse) {
   constexpr int DVH = DV / 2;   // value columns per wave
   constexpr int NT = DVH / 32;  // 32-wide output tiles per wave
+  static_assert(2 * NT >= 16 && kQSteps >= 10 && kDmaPerWave == 9, "the copy schedule below places 5 + 4 copies");
   __shared__ __attribute__((aligned(1024))) char tiles[kNBuf][kTileBytes];
   __shared__ int32_t pos_s[kMaxRowsPerSplit];
   __shared__ f32x4 exch[4][4][kWave];  // partial S^T of each wave, by register group and lane
@@ -285,15 +286,20 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
     drow[jj] = 4u * n;
     gbase[jj] = (uint64_t)(uintptr_t)kv + 16u * chunk_slot(n, slot % kRowChunks);
   }
-  auto issue = [&](int tile, int buf) {
-    uint32_t s[kDmaPerWave];  // all position reads first: one LDS wait covers them
+  auto dma_rows = [&](int tile, uint32_t* s) {  // source positions of this lane's copies (LDS reads, one wait)
 #pragma unroll
     for (int jj = 0; jj < kDmaPerWave; ++jj)
       s[jj] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(pos_s) + tile * 4 * kTileRows + drow[jj]);
+  };
+  auto dma_one = [&](int jj, const uint32_t* s, int buf) {
+    dma16(reinterpret_cast<const void*>(gbase[jj] + (uint64_t)s[jj] * ld_bytes),
+          &tiles[buf][(wave * kDmaPerWave + jj) * 1024]);
+  };
+  auto issue = [&](int tile, int buf) {
+    uint32_t s[kDmaPerWave];
+    dma_rows(tile, s);
 #pragma unroll
-    for (int jj = 0; jj < kDmaPerWave; ++jj)
-      dma16(reinterpret_cast<const void*>(gbase[jj] + (uint64_t)s[jj] * ld_bytes),
-            &tiles[buf][(wave * kDmaPerWave + jj) * 1024]);
+    for (int jj = 0; jj < kDmaPerWave; ++jj) dma_one(jj, s, buf);
   };
 
   f32x16 o[NT];
@@ -331,7 +337,16 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
     if (tile + 1 < n_tiles) wait_vmem_below<kDmaPerWave>();
     else wait_vmem_below<0>();
     lds_barrier();
-    if (tile + kNBuf - 1 < n_tiles) issue(tile + kNBuf - 1, (tile + kNBuf - 1) % kNBuf);
+    // the copies of tile + kNBuf - 1 (into the buffer every wave finished with before the barrier) are spread over
+    // this tile's MFMAs: the CU's vector-memory path needs several hundred cycles for a tile, and a burst would
+    // hold this wave's instruction stream (and its MFMA issue) for all of it
+    const bool pre = tile + kNBuf - 1 < n_tiles;
+    const int pbuf = (tile + kNBuf - 1) % kNBuf;
+    uint32_t dpos[kDmaPerWave];
+    if (pre) dma_rows(tile + kNBuf - 1, dpos);
+    auto dma_at = [&](int jj) {
+      if (pre) dma_one(jj, dpos, pbuf);
+    };
     // this tile's fragment bases, made opaque so that the compiler keeps one register per base and folds every
     // constant into the instruction offset (instead of hoisting base + constant sums out of the loop)
     const uint32_t tbase = tiles_lds + (uint32_t)((tile % kNBuf) * kTileBytes);
@@ -350,14 +365,20 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
     bf16x8 kr[kPrefK];
 #pragma unroll
     for (int i = 0; i < kPrefK; ++i) kr[i] = k_frag(i);
-    f32x16 s = f32x16{};
+    // two accumulation chains (even and odd k-steps): a dependent MFMA waits for its predecessor's result
+    f32x16 s = f32x16{}, s_odd = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < kQSteps; ++ks) {
       const bf16x8 cur = kr[ks % kPrefK];
       if (ks + kPrefK < kQSteps) kr[ks % kPrefK] = k_frag(ks + kPrefK);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[ks], s, 0, 0, 0);
+      if (ks & 1)
+        s_odd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[ks], s_odd, 0, 0, 0);
+      else
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[ks], s, 0, 0, 0);
+      if ((ks & 1) && ks <= 9) dma_at(ks >> 1);  // copies 0..4
       __builtin_amdgcn_sched_barrier(0);
     }
+    s += s_odd;
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) exch[wave][g4][lane] = f32x4{s[4 * g4], s[4 * g4 + 1], s[4 * g4 + 2], s[4 * g4 + 3]};
     lds_barrier();
@@ -423,6 +444,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
       const bf16x8 cur = vr[i % kPrefV];
       if (i + kPrefV < 2 * NT) vr[i % kPrefV] = v_frag(i + kPrefV);
       o[i % NT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, pf[i / NT], o[i % NT], 0, 0, 0);
+      if ((i & 3) == 3 && i <= 15) dma_at(5 + (i >> 2));  // copies 5..8
       __builtin_amdgcn_sched_barrier(0);
     }
   };

@@ -206,14 +206,14 @@ __device__ __forceinline__ void load_query(const void* q, const float* w, int64_
 // ReLU as one integer max: a negative float (or -0) has a negative int image and becomes +0; other values pass.
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
-// Scores of the 64 positions of a tile: score[nt] is position 32 nt + lane % 32, complete in lanes l and l ^ 32.
+// Scores of the 64 positions of a tile: lane l returns the score of position l of the tile.
 // The eight key fragments of a 32-position half sit in a register ring: the half-0 fragments are read up front
 // and each slot is refilled with the matching half-1 fragment as soon as its MFMAs are issued, so every LDS read
 // has eight MFMA pairs to land. The half-1 MFMAs are interleaved with the half-0 ReLU-weighted head sum (two MFMAs,
 // then eight VALU instructions, per k-step), so the matrix unit and the VALU work at the same time.
 template <int NMT>
-__device__ __forceinline__ void score_tile(const char* tile, int lane, const bf16x8 (&qa)[NMT][kSteps],
-                                           const float (&wv)[NMT][16], float (&score)[2]) {
+__device__ __forceinline__ float score_tile(const char* tile, int lane, const bf16x8 (&qa)[NMT][kSteps],
+                                           const float (&wv)[NMT][16]) {
   static_assert(NMT * 16 % kSteps == 0, "head-sum chunks must divide evenly over the k-steps");
   constexpr int kChunk = NMT * 16 / kSteps;  // half-0 accumulator elements folded per half-1 k-step
   const int hs = lane >> 5;
@@ -261,8 +261,9 @@ __device__ __forceinline__ void score_tile(const char* tile, int lane, const bf1
   for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) part1 = fmaf(wv[mt][r], relu(acc1[mt][r]), part1);
-  score[0] = part0 + wave_shfl_xor(part0, 32);
-  score[1] = part1 + wave_shfl_xor(part1, 32);
+  // part0 / part1 hold the half-0 / half-1 sums over this lane's heads; lanes l and l ^ 32 cover the two head
+  // halves of the same position
+  return fold_halves(part0, part1);
 }
 
 // Split-L scoring: workgroup = NQ waves = NQ queries. Each of the gridDim.x workgroups of a query group scores a
@@ -322,26 +323,21 @@ __global__ __launch_bounds__(64 * NQ) void k_score_mfma(const void* __restrict__
   auto process_tile = [&](const char* tile, int64_t s0) {
     if (!active || s0 >= hi) return;
     if (mode == kScoreEmit && n_emit > kStage - kTileKeys) flush();
-    float sc[2];
-    score_tile<NMT>(tile, lane, qa, wv, sc);
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const float score = sc[nt];
-      const int64_t s = s0 + 32 * nt + (lane & 31);
-      const bool in_range = (lane < 32) && s < hi;
-      if (mode == kScoreDense) {
-        if (in_range) scores[(int64_t)b * scores_ld + (s - lo)] = (s <= tb) ? score : -INFINITY;
+    const float score = score_tile<NMT>(tile, lane, qa, wv);
+    const int64_t s = s0 + lane;  // lane order is position order
+    const bool in_range = s < hi;
+    if (mode == kScoreDense) {
+      if (in_range) scores[(int64_t)b * scores_ld + (s - lo)] = (s <= tb) ? score : -INFINITY;
+    } else {
+      const uint32_t key = score_key(score);
+      const bool is_cand = in_range && is_candidate(s, tb, n_sink, n_window);
+      if (mode == kScoreAll) {
+        if (in_range) reinterpret_cast<uint32_t*>(cand)[(int64_t)b * cand_ld + (s - lo)] = is_cand ? key : 0u;
       } else {
-        const uint32_t key = score_key(score);
-        const bool is_cand = in_range && is_candidate(s, tb, n_sink, n_window);
-        if (mode == kScoreAll) {
-          if (in_range) reinterpret_cast<uint32_t*>(cand)[(int64_t)b * cand_ld + (s - lo)] = is_cand ? key : 0u;
-        } else {
-          const bool emit = is_cand && key > thr;
-          const uint64_t m = ballot(emit);
-          if (emit) staged[wave][n_emit + lanes_below(m)] = Cand{key, (int32_t)s};
-          n_emit += __popcll(m);
-        }
+        const bool emit = is_cand && key > thr;
+        const uint64_t m = ballot(emit);
+        if (emit) staged[wave][n_emit + lanes_below(m)] = Cand{key, (int32_t)s};
+        n_emit += __popcll(m);
       }
     }
   };
@@ -433,23 +429,19 @@ __global__ __launch_bounds__(64 * NQ) void k_stream_select(const void* __restric
   const int cend = (int)cand_end;  // positions fit in 32 bits
   auto score_and_emit = [&](const char* tile, int64_t s0) {
     if (!active || s0 > cand_end) return;
-    float sc[2];
-    score_tile<NMT>(tile, lane, qa, wv, sc);
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int s = (int)s0 + 32 * nt + (lane & 31);
-      const uint32_t key = score_key(sc[nt]);
-      const bool cand = (lane < 32) && s >= n_sink && s <= cend;
-      if (n + 32 > cap) {
-        wait_vmem();
-        thr = wave_select_compact(mybuf, n, kk, hist[wave], lane);
-        n = n < kk ? n : kk;
-      }
-      const bool emit = cand && key > thr;
-      const uint64_t m = ballot(emit);
-      if (emit) mybuf[n + lanes_below(m)] = Cand{key, s};
-      n += __popcll(m);
+    const float score = score_tile<NMT>(tile, lane, qa, wv);
+    const int s = (int)s0 + lane;  // lane order is position order
+    const uint32_t key = score_key(score);
+    const bool cand = s >= n_sink && s <= cend;
+    if (n + kWave > cap) {
+      wait_vmem();
+      thr = wave_select_compact(mybuf, n, kk, hist[wave], lane);
+      n = n < kk ? n : kk;
     }
+    const bool emit = cand && key > thr;
+    const uint64_t m = ballot(emit);
+    if (emit) mybuf[n + lanes_below(m)] = Cand{key, s};
+    n += __popcll(m);
   };
   if constexpr (!E4M3) {
     // bf16 keys: asynchronous DMA into four LDS buffers, three tiles in flight

@@ -72,6 +72,14 @@ __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 __device__ __forceinline__ float wave_shfl_xor(float v, int m) { return __shfl_xor(v, m, kWave); }
 
+// One VALU lane exchange (v_permlane32_swap: lanes 32..63 of the first operand trade places with lanes 0..31 of
+// the second). The sum of the two results is, in lane l < 32, a_l + a_{l+32} and, in lane l >= 32, b_{l-32} + b_l:
+// two half-wave pair sums in one register.
+__device__ __forceinline__ float fold_halves(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
 // number of set bits of `mask` below this lane
