@@ -22,6 +22,14 @@ constexpr int kValuKeysPerWg = 256;
 constexpr int kMfmaKeysPerWg = 512;
 constexpr int kTileKeys = 64;
 
+// Zeroes clear[0, n) with every thread of the grid (a no-op for n = 0).
+__device__ __forceinline__ void clear_region(uint32_t* clear, int64_t n) {
+  if (n <= 0) return;
+  const int64_t nthr = (int64_t)gridDim.x * gridDim.y * blockDim.x;
+  for (int64_t i = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += nthr)
+    clear[i] = 0u;
+}
+
 __device__ __forceinline__ bool is_candidate(int64_t s, int64_t t, int n_sink, int n_window) {
   return s >= n_sink && s <= t - n_window;
 }
@@ -33,7 +41,9 @@ __global__ __launch_bounds__(256) void k_score_valu(const void* __restrict__ q, 
                                                     int mode, float* __restrict__ scores, int64_t scores_ld,
                                                     int n_sink, int n_window, const uint32_t* __restrict__ thr_key,
                                                     Cand* __restrict__ cand, int64_t cand_ld,
-                                                    uint32_t* __restrict__ seg_cnt) {
+                                                    uint32_t* __restrict__ seg_cnt, uint32_t* __restrict__ clear,
+                                                    int64_t clear_n) {
+  clear_region(clear, clear_n);
   extern __shared__ float smem[];
   float* qs = smem;            // [H * d]
   float* ws = smem + H * d;    // [H]
@@ -280,7 +290,9 @@ __global__ __launch_bounds__(64 * NQ) void k_score_mfma(const void* __restrict__
                                                         int n_sink, int n_window,
                                                         const uint32_t* __restrict__ thr_key,
                                                         Cand* __restrict__ cand, int64_t cand_ld,
-                                                        uint32_t* __restrict__ seg_cnt) {
+                                                        uint32_t* __restrict__ seg_cnt,
+                                                        uint32_t* __restrict__ clear, int64_t clear_n) {
+  clear_region(clear, clear_n);
   typedef KeyLoader<E4M3, NQ> KL;
   constexpr int kNBuf = E4M3 ? 2 : 4;
   constexpr int kStage = 512;
@@ -489,7 +501,8 @@ hipError_t launch_valu(const IndexerArgs& a, int64_t lo, int64_t hi, int mode, f
   dim3 grid((unsigned)((n + kValuKeysPerWg - 1) / kValuKeysPerWg), (unsigned)a.B);
   const size_t lds = sizeof(float) * ((size_t)a.H * a.d + a.H);
   hipLaunchKernelGGL((k_score_valu<QT, KT>), grid, dim3(256), lds, st, a.q, a.w, a.k, a.k_ld, a.L, a.H, a.d, a.t,
-                     lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, cand, cand_ld, seg_cnt);
+                     lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, cand, cand_ld, seg_cnt, a.clear,
+                     a.clear_n);
   return hipGetLastError();
 }
 
@@ -521,7 +534,7 @@ hipError_t launch_mfma(const IndexerArgs& a, int64_t lo, int64_t hi, int mode, f
   if (n_tiles < 1 || a.B < 1) return hipSuccess;
   dim3 grid((unsigned)n_wg, (unsigned)((a.B + NQ - 1) / NQ));
   hipLaunchKernelGGL((k_score_mfma<NMT, FP8, NQ>), grid, dim3(64 * NQ), 0, st, a.q, a.w, a.k, a.k_ld, a.L, a.B, a.t,
-                     lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, cand, cand_ld, seg_cnt);
+                     lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, cand, cand_ld, seg_cnt, a.clear, a.clear_n);
   return hipGetLastError();
 }
 

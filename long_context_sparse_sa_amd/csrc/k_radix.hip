@@ -283,13 +283,15 @@ RadixPlan radix_plan(int B, int64_t L) {
   return p;
 }
 
-size_t radix_hist_words(int B) { return (size_t)3 * B * kRBins; }
+// ctl layout: pass histograms [3, B, 2048] words, then per-chunk counts [B, n_chunks, 2] words.
+size_t radix_ctl_words(int B, const RadixPlan& p) { return (size_t)3 * B * kRBins + (size_t)2 * B * p.n_chunks; }
 
-hipError_t launch_radix_select(int B, int64_t L, int k, const RadixPlan& p, const uint32_t* keys,
-                               uint32_t* hist, uint32_t* cnt, int32_t* idx, int idx_ld, int32_t* n_sel,
-                               hipStream_t st) {
+hipError_t launch_radix_select(int B, int64_t L, int k, const RadixPlan& p, const uint32_t* keys, uint32_t* ctl,
+                               int32_t* idx, int idx_ld, int32_t* n_sel, hipStream_t st) {
   if (B == 0) return hipSuccess;
   const dim3 grid((unsigned)p.n_chunks, (unsigned)B);
+  uint32_t* hist = ctl;
+  uint32_t* cnt = ctl + (size_t)3 * B * kRBins;
   hipLaunchKernelGGL(k_radix_hist<0>, grid, dim3(kRThreads), 0, st, keys, p.keys_ld, L, p.chunk, k, B, hist);
   hipLaunchKernelGGL(k_radix_hist<1>, grid, dim3(kRThreads), 0, st, keys, p.keys_ld, L, p.chunk, k, B, hist);
   hipLaunchKernelGGL(k_radix_hist<2>, grid, dim3(kRThreads), 0, st, keys, p.keys_ld, L, p.chunk, k, B, hist);

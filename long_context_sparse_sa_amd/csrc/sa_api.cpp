@@ -99,8 +99,8 @@ int resolve_algo(int algo, const sa::IndexerArgs& a) {
 
 struct RadixWs {
   sa::RadixPlan p;
-  uint32_t* hist;  // [3, B, 2048] pass histograms
-  uint32_t* cnt;   // [B, n_chunks, 2] per-chunk counts
+  uint32_t* ctl;   // histograms, per-chunk counts and the chunk ticket (zeroed by the scoring launch)
+  size_t ctl_words;
   uint32_t* keys;  // [B, keys_ld] one key per position
   size_t bytes;
 };
@@ -109,8 +109,8 @@ RadixWs carve_radix(void* ws, const sa::IndexerArgs& a) {
   RadixWs w{};
   w.p = sa::radix_plan(a.B, a.L);
   Carver c(ws);
-  w.hist = c.take<uint32_t>(sa::radix_hist_words(a.B));
-  w.cnt = c.take<uint32_t>((size_t)2 * a.B * w.p.n_chunks);
+  w.ctl_words = sa::radix_ctl_words(a.B, w.p);
+  w.ctl = c.take<uint32_t>(w.ctl_words);
   w.keys = c.take<uint32_t>((size_t)a.B * w.p.keys_ld);
   w.bytes = align_up(c.off, 256);
   return w;
@@ -278,12 +278,13 @@ SA_API int sa_select_topk(const void* q, int q_dtype, const float* w, const void
     // every position's key into the workspace (0 for positions outside the candidate range), then the radix
     // select over all of them
     const RadixWs w2 = carve_radix(ws, a);
-    e = sa::launch_fill_u32(w2.hist, (int64_t)sa::radix_hist_words(B), 0u, s);
-    if (e != hipSuccess) return hip_fail(e, "sa_select_topk (radix clear)");
-    e = sa::launch_score(a, 0, L, sa::kScoreAll, nullptr, 0, n_sink, n_window, nullptr,
+    sa::IndexerArgs as = a;
+    as.clear = w2.ctl;  // the scoring launch zeroes the select's counters
+    as.clear_n = (int64_t)w2.ctl_words;
+    e = sa::launch_score(as, 0, L, sa::kScoreAll, nullptr, 0, n_sink, n_window, nullptr,
                          reinterpret_cast<sa::Cand*>(w2.keys), w2.p.keys_ld, nullptr, s);
     if (e != hipSuccess) return hip_fail(e, "sa_select_topk (radix score)");
-    e = sa::launch_radix_select(B, L, k_sparse, w2.p, w2.keys, w2.hist, w2.cnt, idx, idx_ld, n_sel, s);
+    e = sa::launch_radix_select(B, L, k_sparse, w2.p, w2.keys, w2.ctl, idx, idx_ld, n_sel, s);
     return e == hipSuccess ? SA_OK : hip_fail(e, "sa_select_topk (radix select)");
   }
   const SplitLWs w2 = carve_split_l(ws, a, k_sparse);

@@ -17,6 +17,10 @@ struct IndexerArgs {
   int64_t L;
   int B, H, d;
   const int32_t* t;  // [B] or NULL
+  // Optional: the scoring launch also zeroes clear[0, clear_n) (counters a following kernel accumulates into;
+  // saves a separate fill launch).
+  uint32_t* clear = nullptr;
+  int64_t clear_n = 0;
 };
 
 // One emitted candidate: (order-preserving key of the fp32 score, position).
@@ -95,16 +99,17 @@ hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t strea
 
 // Radix select over all positions for few queries (k_radix.hip). keys[b * keys_ld + s] (s < L) hold the
 // all-slots keys of the scoring kernel; the rest of each row is never read past the next multiple of 4.
-// hist holds radix_hist_words(B) words and must be zero on entry; cnt holds 2 * B * n_chunks words.
+// ctl holds radix_ctl_words(B, plan) words and must be zero on entry (the pass histograms, the per-chunk counts
+// and the chunk ticket).
 struct RadixPlan {
   int64_t keys_ld;  // row stride of keys (a multiple of 1024)
   int64_t chunk;    // positions per workgroup
   int n_chunks;     // workgroups per query
 };
 RadixPlan radix_plan(int B, int64_t L);
-size_t radix_hist_words(int B);
-hipError_t launch_radix_select(int B, int64_t L, int k, const RadixPlan& p, const uint32_t* keys, uint32_t* hist,
-                               uint32_t* cnt, int32_t* idx, int idx_ld, int32_t* n_sel, hipStream_t stream);
+size_t radix_ctl_words(int B, const RadixPlan& p);
+hipError_t launch_radix_select(int B, int64_t L, int k, const RadixPlan& p, const uint32_t* keys, uint32_t* ctl,
+                               int32_t* idx, int idx_ld, int32_t* n_sel, hipStream_t stream);
 
 // Streaming per-query selection for many queries (prefill chunk): one pass over each query's visible keys keeps
 // at most `cap` candidates per query in buf[b, :] (count in buf_n[b]) that contain the exact top-k.
