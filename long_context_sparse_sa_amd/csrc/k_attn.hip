@@ -227,7 +227,6 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
                                                    uint16_t* __restrict__ out, float* __restrict__ lse) {
   constexpr int DVH = DV / 2;   // value columns per wave
   constexpr int NT = DVH / 32;  // 32-wide output tiles per wave
-  static_assert(2 * NT >= 16 && kQSteps >= 10 && kDmaPerWave == 9, "the copy schedule below places 5 + 4 copies");
   __shared__ __attribute__((aligned(1024))) char tiles[kNBuf][kTileBytes];
   __shared__ int32_t pos_s[kMaxRowsPerSplit];
   __shared__ f32x4 exch[4][4][kWave];  // partial S^T of each wave, by register group and lane
@@ -244,12 +243,6 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
   const int head = 64 * hg + 32 * hb + j;
   const int64_t bh = (int64_t)b * H + head;
   const int dv0 = dh * DVH;
-
-  // Q^T fragments (B operand): head `head`, dims 288 dh + 16 ks + 8 hsel .. +8
-  bf16x8 qf[kQSteps];
-#pragma unroll
-  for (int ks = 0; ks < kQSteps; ++ks)
-    qf[ks] = *reinterpret_cast<const bf16x8*>(q + bh * kRowElems + 288 * dh + 16 * ks + 8 * hsel);
 
   const RowList R = make_rows(b, L, t, idx, idx_ld, n_sel, n_sink, n_window);
   const int n_rows = R.count();
@@ -302,6 +295,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
     for (int jj = 0; jj < kDmaPerWave; ++jj) dma_one(jj, s, buf);
   };
 
+  bf16x8 qf[kQSteps];
   f32x16 o[NT];
 #pragma unroll
   for (int i = 0; i < NT; ++i) o[i] = f32x16{};
@@ -337,16 +331,9 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
     if (tile + 1 < n_tiles) wait_vmem_below<kDmaPerWave>();
     else wait_vmem_below<0>();
     lds_barrier();
-    // the copies of tile + kNBuf - 1 (into the buffer every wave finished with before the barrier) are spread over
-    // this tile's MFMAs: the CU's vector-memory path needs several hundred cycles for a tile, and a burst would
-    // hold this wave's instruction stream (and its MFMA issue) for all of it
-    const bool pre = tile + kNBuf - 1 < n_tiles;
-    const int pbuf = (tile + kNBuf - 1) % kNBuf;
-    uint32_t dpos[kDmaPerWave];
-    if (pre) dma_rows(tile + kNBuf - 1, dpos);
-    auto dma_at = [&](int jj) {
-      if (pre) dma_one(jj, dpos, pbuf);
-    };
+    // the copies of tile + kNBuf - 1, into the buffer every wave finished with before the barrier (issued in one
+    // burst: spreading them over the MFMAs measured slower)
+    if (tile + kNBuf - 1 < n_tiles) issue(tile + kNBuf - 1, (tile + kNBuf - 1) % kNBuf);
     // this tile's fragment bases, made opaque so that the compiler keeps one register per base and folds every
     // constant into the instruction offset (instead of hoisting base + constant sums out of the loop)
     const uint32_t tbase = tiles_lds + (uint32_t)((tile % kNBuf) * kTileBytes);
@@ -365,20 +352,14 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
     bf16x8 kr[kPrefK];
 #pragma unroll
     for (int i = 0; i < kPrefK; ++i) kr[i] = k_frag(i);
-    // two accumulation chains (even and odd k-steps): a dependent MFMA waits for its predecessor's result
-    f32x16 s = f32x16{}, s_odd = f32x16{};
+    f32x16 s = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < kQSteps; ++ks) {
       const bf16x8 cur = kr[ks % kPrefK];
       if (ks + kPrefK < kQSteps) kr[ks % kPrefK] = k_frag(ks + kPrefK);
-      if (ks & 1)
-        s_odd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[ks], s_odd, 0, 0, 0);
-      else
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[ks], s, 0, 0, 0);
-      if ((ks & 1) && ks <= 9) dma_at(ks >> 1);  // copies 0..4
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[ks], s, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    s += s_odd;
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) exch[wave][g4][lane] = f32x4{s[4 * g4], s[4 * g4 + 1], s[4 * g4 + 2], s[4 * g4 + 3]};
     lds_barrier();
@@ -444,14 +425,18 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
       const bf16x8 cur = vr[i % kPrefV];
       if (i + kPrefV < 2 * NT) vr[i % kPrefV] = v_frag(i + kPrefV);
       o[i % NT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, pf[i / NT], o[i % NT], 0, 0, 0);
-      if ((i & 3) == 3 && i <= 15) dma_at(5 + (i >> 2));  // copies 5..8
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  wait_vmem();  // the Q fragments are in registers before the tile copies start counting
   const int n_pre = n_tiles < kNBuf - 1 ? n_tiles : kNBuf - 1;
   for (int p = 0; p < n_pre; ++p) issue(p, p);
+  // Q^T fragments (B operand): head `head`, dims 288 dh + 16 ks + 8 hsel .. +8. Loaded after the first tile copies
+  // so that the two latencies overlap; loads complete in issue order, so the loop's "at most N copies outstanding"
+  // waits stay conservative.
+#pragma unroll
+  for (int ks = 0; ks < kQSteps; ++ks)
+    qf[ks] = *reinterpret_cast<const bf16x8*>(q + bh * kRowElems + 288 * dh + 16 * ks + 8 * hsel);
   const int n_full = n_my / kTileRows;
   for (int tile = 0; tile < n_full; ++tile) process(tile, BoolTag<false>{});
   if (n_full < n_tiles) process(n_full, BoolTag<true>{});
