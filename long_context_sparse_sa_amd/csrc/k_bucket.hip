@@ -20,6 +20,7 @@ namespace {
 constexpr int kChunkMin = 4096;
 constexpr int64_t kTableBudget = 1 << 24;  // entries of the (chunk x bucket) table
 constexpr int kMaxExpand = 16384;
+constexpr int kBinMax = 16;  // entries per position bin sorted in registers by the expansion
 
 __global__ void k_fill_i32(int32_t* p, int64_t n, int32_t v) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
@@ -163,62 +164,138 @@ __global__ __launch_bounds__(1024) void k_expand(const int32_t* __restrict__ cho
                                                  const int32_t* __restrict__ members, int64_t L,
                                                  const int32_t* __restrict__ t, int n_sink, int n_window,
                                                  int32_t* __restrict__ idx, int cap, int32_t* __restrict__ n_sel) {
+  constexpr int kWaves = 1024 / kWave;
   __shared__ int32_t rng_lo[1024], rng_n[1024], rng_base[1024];
   __shared__ int32_t buf[kMaxExpand];
-  __shared__ int32_t total_s;
+  __shared__ int32_t tmp[kMaxExpand];
+  __shared__ int32_t bin_cnt[1024], bin_cur[1024];
+  __shared__ int32_t wsum[kWaves];
+  __shared__ int overflow;
   const int b = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
   const int tb = t ? t[b] : (int)(L - 1);
   const int ns = n_sink < tb + 1 ? n_sink : tb + 1;
   int w0 = tb - n_window + 1;
   w0 = w0 > ns ? w0 : ns;
   const int nc = n_chosen[b];
-  if (tid < nc) {
-    const int c = chosen[(int64_t)b * top_b + tid];
+  // each chosen bucket's members in [ns, w0): one wave per bucket counts, 64 members per load, how many lie below
+  // ns and below w0 (members are ascending, so the counts are the range's bounds)
+  for (int i = wave; i < nc; i += kWaves) {
+    const int c = chosen[(int64_t)b * top_b + i];
     const int o0 = offsets[c], o1 = offsets[c + 1];
-    const int a = lower_bound(members + o0, o1 - o0, ns);
-    const int z = lower_bound(members + o0, o1 - o0, w0);
-    rng_lo[tid] = o0 + a;
-    rng_n[tid] = z - a;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int i = 0; i < nc; ++i) {
-      rng_base[i] = run;
-      run += rng_n[i];
+    int below_ns = 0, below_w0 = 0;
+#pragma unroll 4
+    for (int e0 = o0; e0 < o1; e0 += kWave) {
+      const int e = e0 + lane;
+      const int32_t m = e < o1 ? members[e] : 0x7FFFFFFF;
+      below_ns += __popcll(ballot(m < ns));
+      below_w0 += __popcll(ballot(m < w0));
     }
-    total_s = run;
+    if (lane == 0) {
+      rng_lo[i] = o0 + below_ns;
+      rng_n[i] = below_w0 - below_ns;
+    }
   }
   __syncthreads();
-  const int total = total_s;
+  // output offsets of the ranges (exclusive scan over the chosen buckets, one per thread)
+  const int v = tid < nc ? rng_n[tid] : 0;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int x = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += x;
+  }
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    before += w < wave ? wsum[w] : 0;
+    total += wsum[w];
+  }
+  if (tid < nc) rng_base[tid] = before + incl - v;
   int32_t* out = idx + (int64_t)b * cap;
   if (total > cap) {
     for (int i = tid; i < cap; i += 1024) out[i] = -1;
     if (tid == 0) n_sel[b] = -total;
     return;
   }
-  int n2 = 1;
-  while (n2 < total) n2 <<= 1;
-  for (int i = tid; i < n2; i += 1024) buf[i] = 0x7FFFFFFF;
   __syncthreads();
-  for (int i = 0; i < nc; ++i)
-    for (int j = tid; j < rng_n[i]; j += 1024) buf[rng_base[i] + j] = members[rng_lo[i] + j];
+  // the ranges into LDS, one wave per bucket
+  for (int i = wave; i < nc; i += kWaves) {
+    const int lo = rng_lo[i], n = rng_n[i], base = rng_base[i];
+    for (int j = lane; j < n; j += kWave) buf[base + j] = members[lo + j];
+  }
   __syncthreads();
-  for (int size = 2; size <= n2; size <<= 1)
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < (n2 >> 1); i += 1024) {
-        const int lo = 2 * i - (i & (stride - 1));
-        const int hi = lo + stride;
-        const bool up = (lo & size) == 0;
-        const int32_t x = buf[lo], y = buf[hi];
-        if ((x > y) == up) {
-          buf[lo] = y;
-          buf[hi] = x;
-        }
-      }
-      __syncthreads();
+  // sort the positions (distinct: a position belongs to one bucket only) by binning them over [ns, w0) into 1024
+  // bins of equal width, one per thread, then sorting each bin's few entries in registers; a bin that gets more
+  // than kBinMax entries (clustered positions) sends the whole query to a bitonic sort instead
+  const int64_t span = (int64_t)w0 - ns > 0 ? (int64_t)w0 - ns : 1;
+  auto bin_of = [&](int32_t v) { return (int)(((int64_t)(v - ns) * 1024) / span); };
+  bin_cnt[tid] = 0;
+  if (tid == 0) overflow = 0;
+  __syncthreads();
+  for (int g = tid; g < total; g += 1024) atomicAdd(&bin_cnt[bin_of(buf[g])], 1);
+  __syncthreads();
+  const int my_cnt = bin_cnt[tid];
+  if (my_cnt > kBinMax) overflow = 1;
+  int incl2 = my_cnt;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int x = __shfl_up(incl2, o, kWave);
+    if (lane >= o) incl2 += x;
+  }
+  if (lane == kWave - 1) wsum[wave] = incl2;
+  __syncthreads();
+  int before2 = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) before2 += w < wave ? wsum[w] : 0;
+  const int my_start = before2 + incl2 - my_cnt;
+  bin_cur[tid] = my_start;
+  __syncthreads();
+  if (!overflow) {
+    for (int g = tid; g < total; g += 1024) {
+      const int32_t v = buf[g];
+      tmp[atomicAdd(&bin_cur[bin_of(v)], 1)] = v;
     }
-  for (int i = tid; i < cap; i += 1024) out[i] = i < total ? buf[i] : -1;
+    __syncthreads();
+    int32_t e[kBinMax];
+#pragma unroll
+    for (int i = 0; i < kBinMax; ++i) e[i] = i < my_cnt ? tmp[my_start + i] : 0x7FFFFFFF;
+    // odd-even transposition sort of the bin in registers
+#pragma unroll
+    for (int r = 0; r < kBinMax; ++r)
+#pragma unroll
+      for (int i = r & 1; i + 1 < kBinMax; i += 2) {
+        const int32_t x = e[i], y = e[i + 1];
+        e[i] = x < y ? x : y;
+        e[i + 1] = x < y ? y : x;
+      }
+#pragma unroll
+    for (int i = 0; i < kBinMax; ++i)
+      if (i < my_cnt) out[my_start + i] = e[i];
+  } else {
+    int n2 = 1;
+    while (n2 < total) n2 <<= 1;
+    for (int i = total + tid; i < n2; i += 1024) buf[i] = 0x7FFFFFFF;
+    __syncthreads();
+    for (int size = 2; size <= n2; size <<= 1)
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int i = tid; i < (n2 >> 1); i += 1024) {
+          const int lo = 2 * i - (i & (stride - 1));
+          const int hi = lo + stride;
+          const bool up = (lo & size) == 0;
+          const int32_t x = buf[lo], y = buf[hi];
+          if ((x > y) == up) {
+            buf[lo] = y;
+            buf[hi] = x;
+          }
+        }
+        __syncthreads();
+      }
+    for (int i = tid; i < total; i += 1024) out[i] = buf[i];
+  }
+  for (int i = total + tid; i < cap; i += 1024) out[i] = -1;
   if (tid == 0) n_sel[b] = total;
 }
 

@@ -95,3 +95,33 @@ def test_singleton_buckets_reduce_to_plain_topk():
         sc = (kf @ qf[b]).astype(np.float32)
         ref = O.topk_positions(sc, np.arange(L), top)
         np.testing.assert_array_equal(selected(idx[b], nsel[b].item()), ref)
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "large"])
+def test_expand_clustered_and_large(layout):
+    """Expansions whose positions crowd a few of the sort's position bins: buckets of contiguous positions, and a
+    few very large buckets (about 12K positions per query). The expansion must still be the exact ascending union."""
+    if layout == "contiguous":
+        L, d, B, nb, top, cap = 200000, 16, 3, 3125, 24, 4096     # bucket c = positions 64c .. 64c + 63
+        assign_np = (np.arange(L) // 64).astype(np.int32)
+    else:
+        L, d, B, nb, top, cap = 200000, 16, 3, 64, 4, 16384       # about 3125 positions per bucket
+        assign_np = np.random.default_rng(5).integers(0, nb, L).astype(np.int32)
+    g = torch.Generator(device="cpu").manual_seed(6)
+    k = torch.randn((L, d), generator=g).to(DEV)
+    q = torch.randn((B, d), generator=g).to(DEV)
+    assign = torch.as_tensor(assign_np, device=DEV)
+    reps, offsets, members = sa.sa_bucket_build(k, assign, nb)
+    ts = [L - 1, L // 2, 150000]
+    t = torch.tensor(ts, dtype=torch.int32, device=DEV)
+    idx, nsel, buckets = sa.sa_bucket_select(q, reps, offsets, members, L, top, 4, 64, cap=cap, t=t,
+                                             return_buckets=True)
+    torch.cuda.synchronize()
+    off, mem = offsets.cpu().numpy().astype(np.int64), members.cpu().numpy().astype(np.int64)
+    for b in range(B):
+        chosen = buckets[b].cpu().numpy()
+        exp_pos = np.concatenate([mem[off[c]:off[c + 1]] for c in chosen])
+        lo, hi = 4, ts[b] - 64 + 1
+        exp_pos = np.sort(exp_pos[(exp_pos >= lo) & (exp_pos < hi)])
+        assert exp_pos.size > (500 if layout == "contiguous" else 3000)
+        np.testing.assert_array_equal(selected(idx[b], nsel[b].item()), exp_pos)
