@@ -8,9 +8,9 @@
 //   -> stable scatter (one wave per chunk, positions in ascending order) -> representatives (fp64 sums, one wave
 //   per bucket, rounded once to fp32).
 // Select (per step):
-//   one wave per bucket scores q . rep for every query and emits (key, bucket) candidates -> the exact top-b merge
-//   (ties to the lower bucket id) -> expansion of the chosen buckets' member ranges inside [sink end, window start)
-//   and an ascending sort in LDS.
+//   four lanes per bucket score q . rep for every query and write one key per (query, bucket) -> the exact top-b
+//   merge (ties to the lower bucket id) -> expansion of the chosen buckets' member ranges inside [sink end, window
+//   start), sorted ascending by binning the positions (a bitonic sort when the bins crowd).
 #include "sa_device.h"
 #include "sa_internal.h"
 
@@ -124,27 +124,60 @@ __global__ __launch_bounds__(256) void k_reps(const void* __restrict__ k, int64_
   }
 }
 
-// One wave per bucket scores every query (fp32 dot) and writes the candidate slot cand[b * nb + bucket]:
-// (key, bucket) for a non-empty bucket, an empty slot (key 0) otherwise.
+// Scores every query against every representative (fp32 dot) and writes the slot keys[b * nb + bucket]: the
+// order-preserving key of the score for a non-empty bucket, 0 (empty slot) otherwise.
 template <int QT>
 __global__ __launch_bounds__(256) void k_bucket_scores(const void* __restrict__ q, int B, int d,
                                                        const float* __restrict__ reps,
                                                        const int32_t* __restrict__ offsets, int nb,
                                                        uint32_t* __restrict__ keys) {
-  extern __shared__ float qs[];  // [B * d]
+  extern __shared__ __attribute__((aligned(16))) float qs[];  // [B * d]
   for (int i = threadIdx.x; i < B * d; i += blockDim.x) qs[i] = load_elem<QT>(q, i);
   __syncthreads();
-  const int wave = threadIdx.x / kWave, lane = lane_id();
-  const int bucket = blockIdx.x * 4 + wave;
-  if (bucket >= nb) return;
-  const bool valid = offsets[bucket + 1] > offsets[bucket];
-  for (int b = 0; b < B; ++b) {
-    float acc = 0.f;
-    if (valid)
-      for (int x = lane; x < d; x += kWave) acc = fmaf(qs[b * d + x], reps[(int64_t)bucket * d + x], acc);
+  // four lanes per bucket, sixteen buckets per wave: each lane takes every fourth group of four dims of its
+  // bucket's representative, keeps it for all queries, and the four partial dot products meet in two lane swaps
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int qtr = lane & 3;
+  const int bucket = (blockIdx.x * 4 + wave) * 16 + (lane >> 2);
+  const bool in = bucket < nb;
+  const bool valid = in && offsets[bucket + 1] > offsets[bucket];
+  const float* r = reps + (int64_t)(in ? bucket : 0) * d;
+  for (int b0 = 0; b0 < B; b0 += 8) {
+    float acc[8];
 #pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, kWave);
-    if (lane == 0) keys[(int64_t)b * nb + bucket] = valid ? score_key(acc) : 0u;
+    for (int u = 0; u < 8; ++u) acc[u] = 0.f;
+    if ((d & 3) == 0) {
+      for (int x = 4 * qtr; x < d; x += 16) {
+        const float4 rv = *reinterpret_cast<const float4*>(r + x);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (b0 + u < B) {
+            const float4 qv = *reinterpret_cast<const float4*>(qs + (b0 + u) * d + x);
+            acc[u] = fmaf(qv.x, rv.x, acc[u]);
+            acc[u] = fmaf(qv.y, rv.y, acc[u]);
+            acc[u] = fmaf(qv.z, rv.z, acc[u]);
+            acc[u] = fmaf(qv.w, rv.w, acc[u]);
+          }
+        }
+      }
+    } else {
+      for (int x = qtr; x < d; x += 4) {
+        const float rv = r[x];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (b0 + u < B) acc[u] = fmaf(qs[(b0 + u) * d + x], rv, acc[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      acc[u] += __shfl_xor(acc[u], 1, kWave);
+      acc[u] += __shfl_xor(acc[u], 2, kWave);
+    }
+    if (qtr == 0 && in) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (b0 + u < B) keys[(int64_t)(b0 + u) * nb + bucket] = valid ? score_key(acc[u]) : 0u;
+    }
   }
 }
 
@@ -340,7 +373,7 @@ hipError_t launch_bucket_select(const void* q, int q_dtype, int B, int d, const 
                                 int n_window, int32_t* idx, int cap, int32_t* n_sel, int32_t* buckets_out,
                                 Cand* cand, int32_t* n_chosen, Cand* gather, int32_t* chosen, hipStream_t st) {
   uint32_t* keys = reinterpret_cast<uint32_t*>(cand);
-  const unsigned n_wg = (unsigned)((nb + 3) / 4);
+  const unsigned n_wg = (unsigned)((nb + 63) / 64);  // 64 buckets per workgroup
   const size_t lds = sizeof(float) * (size_t)B * d;
   if (q_dtype == 0)
     hipLaunchKernelGGL(k_bucket_scores<0>, dim3(n_wg), dim3(256), lds, st, q, B, d, reps, offsets, nb, keys);
