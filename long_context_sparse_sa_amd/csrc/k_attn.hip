@@ -457,13 +457,31 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
       }
     if (lse && dh == 0 && hsel == 0) lse[bh] = (m_use + log2f(l_run)) * kLn2;
   } else {
-    float* dst = part_o + (bh * n_splits + split) * DV + dv0;
+    // the partial rows leave through LDS (the tile buffers are free now), one head block at a time, so that every
+    // row of DV floats is written by consecutive threads as whole lines instead of 16 bytes per head per store
+    constexpr int kStageLd = DV + 4;  // padded row: the lanes of a column write land in different banks
+    static_assert(32 * kStageLd * 4 <= kNBuf * kTileBytes, "a head block's partial rows fit in the tile buffers");
+    float* stage = reinterpret_cast<float*>(&tiles[0][0]);
+    __syncthreads();  // every wave is done with the tile buffers
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+    for (int blk = 0; blk < 2; ++blk) {
+      if (hb == blk) {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4)
-        *reinterpret_cast<f32x4*>(dst + 32 * nt + 8 * g4 + 4 * hsel) =
-            f32x4{o[nt][4 * g4], o[nt][4 * g4 + 1], o[nt][4 * g4 + 2], o[nt][4 * g4 + 3]};
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4)
+            *reinterpret_cast<f32x4*>(stage + j * kStageLd + dv0 + 32 * nt + 8 * g4 + 4 * hsel) =
+                f32x4{o[nt][4 * g4], o[nt][4 * g4 + 1], o[nt][4 * g4 + 2], o[nt][4 * g4 + 3]};
+      }
+      __syncthreads();
+      for (int e = tid; e < 32 * (DV / 4); e += 256) {
+        const int h = e / (DV / 4), c = 4 * (e % (DV / 4));
+        const int64_t bh_h = (int64_t)b * H + 64 * hg + 32 * blk + h;
+        *reinterpret_cast<f32x4*>(part_o + (bh_h * n_splits + split) * DV + c) =
+            *reinterpret_cast<const f32x4*>(stage + h * kStageLd + c);
+      }
+      __syncthreads();
+    }
     if (dh == 0 && hsel == 0) {
       part_ml[(bh * n_splits + split) * 2 + 0] = m_use;
       part_ml[(bh * n_splits + split) * 2 + 1] = l_run;
