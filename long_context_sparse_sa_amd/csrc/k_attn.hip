@@ -445,16 +445,26 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
   l_run = halves_sum(l_run);
   // register r of tile nt holds column dv0 + 32 nt + 8 (r / 4) + 4 hsel + r % 4 of head `head`
   if (n_splits == 1) {
+    // the bf16 output rows leave through LDS (the tile buffers are free now) as whole rows
     const float inv = 1.f / l_run;
+    constexpr int kOutLd = DV + 8;  // padded row of bf16 (16 bytes) so that the lanes of a column spread over banks
+    uint16_t* ostage = reinterpret_cast<uint16_t*>(&tiles[0][0]);
+    static_assert(64 * kOutLd * 2 <= kNBuf * kTileBytes, "the workgroup's output rows fit in the tile buffers");
+    __syncthreads();  // every wave is done with the tile buffers
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        uint16_t* dst = out + bh * DV + dv0 + 32 * nt + 8 * g4 + 4 * hsel;
         const uint32_t lo = f32_to_bf16_bits(o[nt][4 * g4 + 0] * inv) | ((uint32_t)f32_to_bf16_bits(o[nt][4 * g4 + 1] * inv) << 16);
         const uint32_t hi = f32_to_bf16_bits(o[nt][4 * g4 + 2] * inv) | ((uint32_t)f32_to_bf16_bits(o[nt][4 * g4 + 3] * inv) << 16);
-        *reinterpret_cast<uint2*>(dst) = uint2{lo, hi};
+        *reinterpret_cast<uint2*>(ostage + (32 * hb + j) * kOutLd + dv0 + 32 * nt + 8 * g4 + 4 * hsel) = uint2{lo, hi};
       }
+    __syncthreads();
+    for (int e = tid; e < 64 * (DV / 8); e += 256) {
+      const int h = e / (DV / 8), c = 8 * (e % (DV / 8));
+      *reinterpret_cast<uint4*>(out + ((int64_t)b * H + 64 * hg + h) * DV + c) =
+          *reinterpret_cast<const uint4*>(ostage + h * kOutLd + c);
+    }
     if (lse && dh == 0 && hsel == 0) lse[bh] = (m_use + log2f(l_run)) * kLn2;
   } else {
     // the partial rows leave through LDS (the tile buffers are free now), one head block at a time, so that every
