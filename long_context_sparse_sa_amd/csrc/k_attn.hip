@@ -263,7 +263,29 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
     return;
   }
   const int n_tiles = (n_my + kTileRows - 1) / kTileRows;
-  for (int r = tid; r < n_tiles * kTileRows; r += 256) pos_s[r] = r < n_my ? R.pos(r_begin + r) : 0;
+  // positions of this split's rows into LDS: the selected-index loads of a thread are issued eight at a time
+  // (unconditional, clamped into the list) so that their latencies overlap
+  {
+    constexpr int kStageBatch = 8;
+    const int n_stage = n_tiles * kTileRows;
+    const int first_sel = R.ns + R.nw;  // read-set rows from here on come from the selected list
+    for (int r0 = 0; r0 < n_stage; r0 += 256 * kStageBatch) {
+      int32_t v[kStageBatch];
+#pragma unroll
+      for (int u = 0; u < kStageBatch; ++u) {
+        int js = r_begin + r0 + u * 256 + tid - first_sel;
+        js = js < 0 ? 0 : (js < R.nsel ? js : R.nsel - 1);
+        v[u] = R.nsel > 0 ? R.idx[js] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < kStageBatch; ++u) {
+        const int r = r0 + u * 256 + tid;
+        const int rr = r_begin + r;
+        if (r < n_stage)
+          pos_s[r] = r >= n_my ? 0 : (rr < R.ns ? rr : (rr < first_sel ? R.w0 + (rr - R.ns) : v[u]));
+      }
+    }
+  }
   __syncthreads();
 
   // DMA plan of this lane, the same for every tile: its chunk jj of the wave's share lands in row drow[jj] of the
