@@ -222,7 +222,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
                                                    int64_t kv_ld, int64_t L, int H, const int32_t* __restrict__ t,
                                                    const int32_t* __restrict__ idx, int idx_ld,
                                                    const int32_t* __restrict__ n_sel, int n_sink, int n_window,
-                                                   float scale_log2, int rows_per_split, int n_splits, int n_units,
+                                                   float scale_log2, int n_splits, int n_units,
                                                    float* __restrict__ part_o, float* __restrict__ part_ml,
                                                    uint16_t* __restrict__ out, float* __restrict__ lse) {
   constexpr int DVH = DV / 2;   // value columns per wave
@@ -246,8 +246,12 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
 
   const RowList R = make_rows(b, L, t, idx, idx_ld, n_sel, n_sink, n_window);
   const int n_rows = R.count();
-  const int r_begin = split * rows_per_split;
-  int r_end = r_begin + rows_per_split;
+  // the query's own read set is cut into n_splits tile-aligned parts of nearly equal size, so that read sets far
+  // below the bound the grid was planned for still spread over every split; since n_rows never exceeds that bound,
+  // no part exceeds the plan's rows per split (at most kMaxRowsPerSplit, the positions staged below)
+  const int n_row_tiles = (n_rows + kTileRows - 1) / kTileRows;
+  const int r_begin = (int)((int64_t)split * n_row_tiles / n_splits) * kTileRows;
+  int r_end = (int)((int64_t)(split + 1) * n_row_tiles / n_splits) * kTileRows;
   r_end = r_end < n_rows ? r_end : n_rows;
   const int n_my = r_end - r_begin;
 
@@ -596,16 +600,19 @@ AttnPlan attn_plan(int B, int H, int d_qk, int d_v, int64_t max_rows, int dtype,
     p.rows_per_split = 0;
     return p;
   }
+  // splits and tiles per split for the largest read set; a smaller one is cut into the same number of parts,
+  // each of at most ceil(tiles / splits) <= tps tiles
   const int64_t units = B > 0 ? (int64_t)B * (H / 64) : 1;
-  const int64_t rows = max_rows > 0 ? max_rows : 1;
+  const int64_t tiles = max_rows > 0 ? (max_rows + kTileRows - 1) / kTileRows : 1;
   int64_t splits = (256 + units - 1) / units;
-  const int64_t max_splits = (rows + kTileRows - 1) / kTileRows;
-  if (splits > max_splits) splits = max_splits;
+  if (splits > tiles) splits = tiles;
   if (splits < 1) splits = 1;
-  int64_t rps = (rows + splits - 1) / splits;
-  rps = (rps + kTileRows - 1) / kTileRows * kTileRows;
-  if (rps > kMaxRowsPerSplit) rps = kMaxRowsPerSplit;
-  splits = (rows + rps - 1) / rps;
+  int64_t tps = (tiles + splits - 1) / splits;
+  if (tps > kMaxRowsPerSplit / kTileRows) {
+    tps = kMaxRowsPerSplit / kTileRows;
+    splits = (tiles + tps - 1) / tps;
+  }
+  const int64_t rps = tps * kTileRows;
   p.n_splits = (int)splits;
   p.rows_per_split = (int)rps;
   return p;
@@ -616,15 +623,15 @@ size_t attn_workspace_bytes(const AttnPlan& p, int B, int H, int d_v) {
   return (size_t)B * H * p.n_splits * ((size_t)d_v + 2) * sizeof(float);
 }
 
-// attn_plan never uses more than max(ceil(256 / units), ceil(rows / kMaxRowsPerSplit)) splits, which grows with
-// rows, so this bound covers every call whose read sets are bounded by max_rows.
+// attn_plan never uses more than max(ceil(256 / units), ceil(tiles / (kMaxRowsPerSplit / kTileRows))) splits,
+// which grows with the tile count, so this bound covers every call whose read sets are bounded by max_rows.
 size_t attn_workspace_bound(int B, int H, int d_qk, int d_v, int64_t max_rows, int dtype) {
   const AttnPlan p = attn_plan(B, H, d_qk, d_v, max_rows, dtype, false);
   if (!p.mfma) return 0;
   const int64_t units = B > 0 ? (int64_t)B * (H / 64) : 1;
-  const int64_t rows = max_rows > 0 ? max_rows : 1;
+  const int64_t tiles = max_rows > 0 ? (max_rows + kTileRows - 1) / kTileRows : 1;
   const int64_t s1 = (256 + units - 1) / units;
-  const int64_t s2 = (rows + kMaxRowsPerSplit - 1) / kMaxRowsPerSplit;
+  const int64_t s2 = (tiles + kMaxRowsPerSplit / kTileRows - 1) / (kMaxRowsPerSplit / kTileRows);
   const int64_t s = s1 > s2 ? s1 : s2;
   return (size_t)B * H * s * ((size_t)d_v + 2) * sizeof(float);
 }
@@ -656,11 +663,11 @@ hipError_t launch_attn(const AttnArgs& a, const AttnPlan& p, void* ws, hipStream
   uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
   if (a.d_v == 576)
     hipLaunchKernelGGL(k_attn_mfma<576>, grid, dim3(256), 0, st, q, kv, a.kv_ld, a.L, a.H, a.t, a.idx, a.idx_ld,
-                       a.n_sel, a.n_sink, a.n_window, sl2, p.rows_per_split, p.n_splits, n_units, part_o, part_ml, out,
+                       a.n_sel, a.n_sink, a.n_window, sl2, p.n_splits, n_units, part_o, part_ml, out,
                        a.lse);
   else
     hipLaunchKernelGGL(k_attn_mfma<512>, grid, dim3(256), 0, st, q, kv, a.kv_ld, a.L, a.H, a.t, a.idx, a.idx_ld,
-                       a.n_sel, a.n_sink, a.n_window, sl2, p.rows_per_split, p.n_splits, n_units, part_o, part_ml, out,
+                       a.n_sel, a.n_sink, a.n_window, sl2, p.n_splits, n_units, part_o, part_ml, out,
                        a.lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_splits == 1) return e;

@@ -67,14 +67,14 @@ def test_toy_decode_config_fp32(seed):
     np.testing.assert_allclose(lse[0].double().cpu().numpy(), ol, atol=1e-5, rtol=0)
 
 
-def _mfma_case(seed, B, L, n_list, n_sink, n_window, d_v, q_scale=1.0, t=None, H=128):
+def _mfma_case(seed, B, L, n_list, n_sink, n_window, d_v, q_scale=1.0, t=None, H=128, idx_ld=None):
     g = torch.Generator(device="cpu").manual_seed(seed)
     q = (torch.randn((B, H, 576), generator=g) * q_scale).to(torch.bfloat16).to(DEV)
     kv = torch.randn((L, 576), generator=g).to(torch.bfloat16).to(DEV)
     rng = np.random.default_rng(seed)
     ts = [L - 1] * B if t is None else t
     sels = [_rand_sparse(rng, ts[b], n_sink, n_window, n_list[b]) for b in range(B)]
-    idx_ld = max(1, max(n_list))
+    idx_ld = max(1, max(n_list)) if idx_ld is None else idx_ld
     idx, nsel = _pack_idx(sels, idx_ld)
     tt = torch.tensor(ts, dtype=torch.int32, device=DEV)
     scale = 1 / math.sqrt(576)
@@ -97,6 +97,13 @@ def _mfma_case(seed, B, L, n_list, n_sink, n_window, d_v, q_scale=1.0, t=None, H
 def test_mfma_ragged_and_splits(d_v):
     # ragged read sets (not multiples of 32), one empty sparse part, one that needs several splits
     _mfma_case(0, B=4, L=8192, n_list=[2048, 77, 0, 1500], n_sink=4, n_window=128, d_v=d_v)
+
+
+def test_mfma_read_sets_far_below_bound():
+    # the grid is planned for idx_ld + sink + window rows; the actual read sets are far smaller, end on and off
+    # tile boundaries, and leave most splits of a query empty
+    _mfma_case(5, B=5, L=20000, n_list=[100, 1000, 0, 32 * 40 - 132, 6000], n_sink=4, n_window=128, d_v=576,
+               idx_ld=8192)
 
 
 def test_mfma_single_split_and_peaked():
