@@ -526,68 +526,61 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
 }
 
 // Exact merge of the row splits of one (query, head): o = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i.
-// One block of 256 threads per (query, head): the split weights are computed once into LDS, then thread i owns
-// four value columns and issues its split loads eight at a time.
-constexpr int kCombineThreads = 256;
-constexpr int kCombineMaxLdsSplits = 1024;
-
-__device__ __forceinline__ float block_reduce(float v, bool is_max, float* red) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float x = __shfl_xor(v, o, kWave);
-    v = is_max ? fmaxf(v, x) : v + x;
-  }
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  float r = red[0];
-#pragma unroll
-  for (int w = 1; w < kCombineThreads / kWave; ++w) r = is_max ? fmaxf(r, red[w]) : r + red[w];
-  __syncthreads();
-  return r;
-}
+// One block per (query, head); thread i owns four value columns. Its first eight split rows are requested before
+// anything else, and every thread derives the split weights itself from the (max, sum) pairs, which are the same
+// for the whole block (uniform loads), so the block needs no barrier. A split with no rows has max -inf and no
+// value row (its workspace row is never written): its weight is 0 and its row is skipped, not multiplied.
+constexpr int kCombineThreads = 192;  // four columns each: d_v <= 768
+constexpr int kCombineBatch = 8;
 
 template <int DT>
 __global__ __launch_bounds__(kCombineThreads) void k_attn_combine(const float* __restrict__ part_o,
                                                                   const float* __restrict__ part_ml, int n_splits,
                                                                   int d_v, void* __restrict__ out,
                                                                   float* __restrict__ lse) {
-  __shared__ float wsh[kCombineMaxLdsSplits];
-  __shared__ float red[kCombineThreads / kWave];
   const int64_t bh = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int dv = 4 * (int)threadIdx.x;
+  const bool act = dv < d_v;
   const float* ml = part_ml + bh * n_splits * 2;
+  const float* po = part_o + bh * n_splits * d_v + (act ? dv : 0);
+  f32x4 v[kCombineBatch];
+#pragma unroll
+  for (int u = 0; u < kCombineBatch; ++u)
+    v[u] = act && u < n_splits ? *reinterpret_cast<const f32x4*>(po + (int64_t)u * d_v) : f32x4{};
   float M = -INFINITY;
-  for (int i = tid; i < n_splits; i += kCombineThreads) M = fmaxf(M, ml[2 * i]);
-  M = block_reduce(M, true, red);
+  for (int i = 0; i < n_splits; ++i) M = fmaxf(M, ml[2 * i]);
   float Ls = 0.f;
-  for (int i = tid; i < n_splits; i += kCombineThreads) {
-    const float w = M == -INFINITY ? 0.f : exp2f(ml[2 * i] - M);
-    if (i < kCombineMaxLdsSplits) wsh[i] = w;
-    Ls += w * ml[2 * i + 1];
-  }
-  Ls = block_reduce(Ls, false, red);  // its barriers also publish wsh
-  const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
-  auto weight = [&](int i) { return i < kCombineMaxLdsSplits ? wsh[i] : exp2f(ml[2 * i] - M); };
-  const int dv = 4 * tid;
-  if (dv < d_v) {
-    f32x4 acc = f32x4{};
-    if (M != -INFINITY) {
-      const float* po = part_o + bh * n_splits * d_v + dv;
-      for (int i0 = 0; i0 < n_splits; i0 += 8) {
-        f32x4 v[8];
+  f32x4 acc = f32x4{};
+  if (M != -INFINITY) {
+    for (int i = 0; i < n_splits; ++i) Ls += exp2f(ml[2 * i] - M) * ml[2 * i + 1];
+    for (int i0 = 0; i0 < n_splits; i0 += kCombineBatch) {
+      if (i0 > 0) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-          v[u] = i0 + u < n_splits ? *reinterpret_cast<const f32x4*>(po + (int64_t)(i0 + u) * d_v) : f32x4{};
+        for (int u = 0; u < kCombineBatch; ++u)
+          v[u] = act && i0 + u < n_splits ? *reinterpret_cast<const f32x4*>(po + (int64_t)(i0 + u) * d_v) : f32x4{};
+      }
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (i0 + u < n_splits) acc += weight(i0 + u) * v[u];
+      for (int u = 0; u < kCombineBatch; ++u) {
+        if (i0 + u < n_splits) {
+          const float w = exp2f(ml[2 * (i0 + u)] - M);
+          if (w > 0.f) acc += w * v[u];
+        }
       }
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) store_out<DT>(out, bh * d_v + dv + r, acc[r] * inv);
   }
-  if (lse && tid == 0) lse[bh] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
+  const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+  if (act) {
+    if constexpr (DT == 1) {
+      uint2 pk;
+      pk.x = (uint32_t)f32_to_bf16_bits(acc[0] * inv) | ((uint32_t)f32_to_bf16_bits(acc[1] * inv) << 16);
+      pk.y = (uint32_t)f32_to_bf16_bits(acc[2] * inv) | ((uint32_t)f32_to_bf16_bits(acc[3] * inv) << 16);
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + bh * d_v + dv) = pk;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) store_out<DT>(out, bh * d_v + dv + r, acc[r] * inv);
+    }
+  }
+  if (lse && threadIdx.x == 0) lse[bh] = Ls > 0.f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
 }
 
 }  // namespace

@@ -67,7 +67,7 @@ def test_toy_decode_config_fp32(seed):
     np.testing.assert_allclose(lse[0].double().cpu().numpy(), ol, atol=1e-5, rtol=0)
 
 
-def _mfma_case(seed, B, L, n_list, n_sink, n_window, d_v, q_scale=1.0, t=None, H=128, idx_ld=None):
+def _mfma_case(seed, B, L, n_list, n_sink, n_window, d_v, q_scale=1.0, t=None, H=128, idx_ld=None, ws_fill=None):
     g = torch.Generator(device="cpu").manual_seed(seed)
     q = (torch.randn((B, H, 576), generator=g) * q_scale).to(torch.bfloat16).to(DEV)
     kv = torch.randn((L, 576), generator=g).to(torch.bfloat16).to(DEV)
@@ -78,7 +78,11 @@ def _mfma_case(seed, B, L, n_list, n_sink, n_window, d_v, q_scale=1.0, t=None, H
     idx, nsel = _pack_idx(sels, idx_ld)
     tt = torch.tensor(ts, dtype=torch.int32, device=DEV)
     scale = 1 / math.sqrt(576)
-    o, lse = sa.sa_sparse_attn(q, kv, idx, nsel, n_sink, n_window, scale, t=tt, d_v=d_v, return_lse=True)
+    ws = None
+    if ws_fill is not None:  # every workspace byte set, e.g. 0xFF: NaN in every float no kernel writes
+        nb = sa.sa_sparse_attn_workspace(B, H, 576, d_v, n_sink + n_window + idx_ld, sa.SA_BF16)
+        ws = torch.full((max(nb, 1),), ws_fill, dtype=torch.uint8, device=DEV)
+    o, lse = sa.sa_sparse_attn(q, kv, idx, nsel, n_sink, n_window, scale, t=tt, d_v=d_v, return_lse=True, ws=ws)
     torch.cuda.synchronize()
     qf, kvf = to_f64(q), to_f64(kv)
     worst = 0.0
@@ -102,8 +106,9 @@ def test_mfma_ragged_and_splits(d_v):
 def test_mfma_read_sets_far_below_bound():
     # the grid is planned for idx_ld + sink + window rows; the actual read sets are far smaller, end on and off
     # tile boundaries, and leave most splits of a query empty
+    # (splits with no rows leave their workspace rows unwritten: a NaN-filled workspace must not reach the output)
     _mfma_case(5, B=5, L=20000, n_list=[100, 1000, 0, 32 * 40 - 132, 6000], n_sink=4, n_window=128, d_v=576,
-               idx_ld=8192)
+               idx_ld=8192, ws_fill=0xFF)
 
 
 def test_mfma_single_split_and_peaked():
