@@ -6,10 +6,13 @@
 // candidates (the scoring kernel's all-slots mode writes them). Each query's positions are cut into G chunks and
 // every (chunk, query) pair is one workgroup of every launch, so a handful of queries still fills the chip:
 //   pass 0, 1, 2  histograms of digits 31..21, 20..10 and 9..0 of the keys that match the digits found so far,
-//                 added into a global histogram per query and pass (each workgroup first re-derives the earlier
-//                 digits from the earlier histograms: a 2048-bin scan);
-//   count         per chunk, the keys above the k-th key kstar and the keys equal to it;
-//   write         per chunk, an order-preserving compaction of the selected positions at the chunk's offset (the
+//                 added into a global histogram per query and pass. Pass p >= 1 finds digit p - 1 in the
+//                 histogram of pass p - 1 (a 2048-bin scan) and reads the digits before it from a per-query
+//                 record that the first chunk's workgroup of each earlier launch extended;
+//   count         the last digit, hence the k-th key kstar (recorded), then per chunk the keys above kstar and
+//                 the keys equal to it;
+//   write         per chunk (kstar from the record), an order-preserving compaction of the selected positions at
+//                 the chunk's offset (the
 //                 counts of the chunks before it). Among keys equal to kstar the lowest positions are kept: chunk j
 //                 keeps the first min(eq_j, need_eq - ties in chunks before j) of its ties.
 // The selected positions come out in ascending order, padded with -1 to idx_ld; n_sel = min(k, candidates).
@@ -97,20 +100,13 @@ struct KStar {
   uint32_t kstar, need_eq, n_cand;
 };
 
-__device__ KStar derive_kstar(RadixShared& sh, const uint32_t* __restrict__ hist, int B, int b, int k) {
-  KStar r{false, 0u, 0u, 0u};
-  uint32_t d0, b0, tot;
-  r.ok = find_desc(sh, hist + ((size_t)0 * B + b) * kRBins, 2048, (uint32_t)k, &d0, &b0, &tot);
-  r.n_cand = tot;
-  if (!r.ok) return r;
-  uint32_t need = (uint32_t)k - b0, d1, b1, d2, b2, t1, t2;
-  find_desc(sh, hist + ((size_t)1 * B + b) * kRBins, 2048, need, &d1, &b1, &t1);
-  need -= b1;
-  find_desc(sh, hist + ((size_t)2 * B + b) * kRBins, 1024, need, &d2, &b2, &t2);
-  need -= b2;
-  r.kstar = (d0 << 21) | (d1 << 10) | d2;
-  r.need_eq = need;
-  return r;
+// Per-query record of the digits found so far, kRecWords words: written by the workgroup of chunk 0 of the launch
+// that finds them, read by every workgroup of the later launches (a launch boundary orders the two).
+constexpr int kRecWords = 8;
+enum : int { kRecOk = 0, kRecNCand, kRecD0, kRecB0, kRecD1, kRecB1, kRecKStar, kRecNeedEq };
+
+__device__ __forceinline__ void store_rec(uint32_t* rec, int i, uint32_t v) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) rec[i] = v;
 }
 
 // Chunk j of query b: positions [s0, s1).
@@ -137,24 +133,33 @@ __device__ __forceinline__ void load4(const uint32_t* __restrict__ row, int64_t 
 template <int PASS>
 __global__ __launch_bounds__(kRThreads) void k_radix_hist(const uint32_t* __restrict__ keys, int64_t keys_ld,
                                                           int64_t L, int64_t chunk, int k, int B,
-                                                          uint32_t* __restrict__ hist) {
+                                                          uint32_t* __restrict__ hist, uint32_t* __restrict__ recs) {
   __shared__ RadixShared sh;
   const int b = blockIdx.y, tid = threadIdx.x;
   constexpr int nb = PASS == 2 ? 1024 : 2048;
   constexpr int shift = PASS == 0 ? 21 : (PASS == 1 ? 10 : 0);
+  uint32_t* rec = recs + (size_t)b * kRecWords;
   for (int i = tid; i < kRBins; i += kRThreads) sh.hist[i] = 0u;
   uint32_t prefix = 0u, pmask = 0u;
-  if (PASS >= 1) {
+  if (PASS == 1) {
     uint32_t d0, b0, tot;
-    if (!find_desc(sh, hist + (size_t)b * kRBins, 2048, (uint32_t)k, &d0, &b0, &tot)) return;  // block-uniform
+    const bool ok = find_desc(sh, hist + (size_t)b * kRBins, 2048, (uint32_t)k, &d0, &b0, &tot);
+    store_rec(rec, kRecOk, ok ? 1u : 0u);
+    store_rec(rec, kRecNCand, tot);
+    store_rec(rec, kRecD0, d0);
+    store_rec(rec, kRecB0, b0);
+    if (!ok) return;  // block-uniform: fewer than k candidates, every one is kept
     prefix = d0 << 21;
     pmask = 0x7FFu << 21;
-    if (PASS == 2) {
-      uint32_t d1, b1, t1;
-      find_desc(sh, hist + ((size_t)B + b) * kRBins, 2048, (uint32_t)k - b0, &d1, &b1, &t1);
-      prefix |= d1 << 10;
-      pmask |= 0x7FFu << 10;
-    }
+  } else if (PASS == 2) {
+    if (rec[kRecOk] == 0u) return;
+    const uint32_t d0 = rec[kRecD0], b0 = rec[kRecB0];
+    uint32_t d1, b1, t1;
+    find_desc(sh, hist + ((size_t)B + b) * kRBins, 2048, (uint32_t)k - b0, &d1, &b1, &t1);
+    store_rec(rec, kRecD1, d1);
+    store_rec(rec, kRecB1, b1);
+    prefix = (d0 << 21) | (d1 << 10);
+    pmask = (0x7FFu << 21) | (0x7FFu << 10);
   }
   __syncthreads();
   const Chunk c = chunk_of(L, chunk);
@@ -177,10 +182,20 @@ __global__ __launch_bounds__(kRThreads) void k_radix_hist(const uint32_t* __rest
 __global__ __launch_bounds__(kRThreads) void k_radix_count(const uint32_t* __restrict__ keys, int64_t keys_ld,
                                                            int64_t L, int64_t chunk, int k, int B,
                                                            const uint32_t* __restrict__ hist,
-                                                           uint32_t* __restrict__ cnt) {
+                                                           uint32_t* __restrict__ recs, uint32_t* __restrict__ cnt) {
   __shared__ RadixShared sh;
   const int b = blockIdx.y, tid = threadIdx.x;
-  const KStar ks = derive_kstar(sh, hist, B, b, k);
+  uint32_t* rec = recs + (size_t)b * kRecWords;
+  KStar ks{rec[kRecOk] != 0u, 0u, 0u, rec[kRecNCand]};
+  if (ks.ok) {
+    const uint32_t need = (uint32_t)k - rec[kRecB0] - rec[kRecB1];
+    uint32_t d2, b2, t2;
+    find_desc(sh, hist + ((size_t)2 * B + b) * kRBins, 1024, need, &d2, &b2, &t2);
+    ks.kstar = (rec[kRecD0] << 21) | (rec[kRecD1] << 10) | d2;
+    ks.need_eq = need - b2;
+  }
+  store_rec(rec, kRecKStar, ks.kstar);
+  store_rec(rec, kRecNeedEq, ks.need_eq);
   const Chunk c = chunk_of(L, chunk);
   const uint32_t* row = keys + (int64_t)b * keys_ld;
   uint32_t gt = 0, eq = 0;
@@ -204,14 +219,15 @@ __global__ __launch_bounds__(kRThreads) void k_radix_count(const uint32_t* __res
 
 __global__ __launch_bounds__(kRThreads) void k_radix_write(const uint32_t* __restrict__ keys, int64_t keys_ld,
                                                            int64_t L, int64_t chunk, int k, int B,
-                                                           const uint32_t* __restrict__ hist,
+                                                           const uint32_t* __restrict__ recs,
                                                            const uint32_t* __restrict__ cnt,
                                                            int32_t* __restrict__ idx, int idx_ld,
                                                            int32_t* __restrict__ n_sel) {
   __shared__ RadixShared sh;
   const int b = blockIdx.y, j = blockIdx.x, tid = threadIdx.x;
   const int G = gridDim.x;
-  const KStar ks = derive_kstar(sh, hist, B, b, k);
+  const uint32_t* rec = recs + (size_t)b * kRecWords;
+  const KStar ks{rec[kRecOk] != 0u, rec[kRecKStar], rec[kRecNeedEq], rec[kRecNCand]};
   // counts of the chunks before this one
   const uint32_t* cb = cnt + (int64_t)b * G * 2;
   uint32_t pg = 0, pe = 0;
@@ -283,8 +299,11 @@ RadixPlan radix_plan(int B, int64_t L) {
   return p;
 }
 
-// ctl layout: pass histograms [3, B, 2048] words, then per-chunk counts [B, n_chunks, 2] words.
-size_t radix_ctl_words(int B, const RadixPlan& p) { return (size_t)3 * B * kRBins + (size_t)2 * B * p.n_chunks; }
+// ctl layout: pass histograms [3, B, 2048] words, per-chunk counts [B, n_chunks, 2] words, then the per-query
+// digit records [B, kRecWords] words.
+size_t radix_ctl_words(int B, const RadixPlan& p) {
+  return (size_t)3 * B * kRBins + (size_t)2 * B * p.n_chunks + (size_t)kRecWords * B;
+}
 
 hipError_t launch_radix_select(int B, int64_t L, int k, const RadixPlan& p, const uint32_t* keys, uint32_t* ctl,
                                int32_t* idx, int idx_ld, int32_t* n_sel, hipStream_t st) {
@@ -292,11 +311,13 @@ hipError_t launch_radix_select(int B, int64_t L, int k, const RadixPlan& p, cons
   const dim3 grid((unsigned)p.n_chunks, (unsigned)B);
   uint32_t* hist = ctl;
   uint32_t* cnt = ctl + (size_t)3 * B * kRBins;
-  hipLaunchKernelGGL(k_radix_hist<0>, grid, dim3(kRThreads), 0, st, keys, p.keys_ld, L, p.chunk, k, B, hist);
-  hipLaunchKernelGGL(k_radix_hist<1>, grid, dim3(kRThreads), 0, st, keys, p.keys_ld, L, p.chunk, k, B, hist);
-  hipLaunchKernelGGL(k_radix_hist<2>, grid, dim3(kRThreads), 0, st, keys, p.keys_ld, L, p.chunk, k, B, hist);
-  hipLaunchKernelGGL(k_radix_count, grid, dim3(kRThreads), 0, st, keys, p.keys_ld, L, p.chunk, k, B, hist, cnt);
-  hipLaunchKernelGGL(k_radix_write, grid, dim3(kRThreads), 0, st, keys, p.keys_ld, L, p.chunk, k, B, hist, cnt, idx,
+  uint32_t* recs = cnt + (size_t)2 * B * p.n_chunks;
+  hipLaunchKernelGGL(k_radix_hist<0>, grid, dim3(kRThreads), 0, st, keys, p.keys_ld, L, p.chunk, k, B, hist, recs);
+  hipLaunchKernelGGL(k_radix_hist<1>, grid, dim3(kRThreads), 0, st, keys, p.keys_ld, L, p.chunk, k, B, hist, recs);
+  hipLaunchKernelGGL(k_radix_hist<2>, grid, dim3(kRThreads), 0, st, keys, p.keys_ld, L, p.chunk, k, B, hist, recs);
+  hipLaunchKernelGGL(k_radix_count, grid, dim3(kRThreads), 0, st, keys, p.keys_ld, L, p.chunk, k, B, hist, recs,
+                     cnt);
+  hipLaunchKernelGGL(k_radix_write, grid, dim3(kRThreads), 0, st, keys, p.keys_ld, L, p.chunk, k, B, recs, cnt, idx,
                      idx_ld, n_sel);
   return hipGetLastError();
 }
