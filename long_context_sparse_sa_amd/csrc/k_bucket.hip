@@ -8,9 +8,10 @@
 //   -> stable scatter (one wave per chunk, positions in ascending order) -> representatives (fp64 sums, one wave
 //   per bucket, rounded once to fp32).
 // Select (per step):
-//   four lanes per bucket score q . rep for every query and write one key per (query, bucket) -> the exact top-b
-//   merge (ties to the lower bucket id) -> expansion of the chosen buckets' member ranges inside [sink end, window
-//   start), sorted ascending by binning the positions (a bitonic sort when the bins crowd).
+//   four lanes per bucket score q . rep for every query and write one key per (query, bucket) -> one workgroup per
+//   query chooses the exact top-b (ties to the lower bucket id) and expands the chosen buckets' member ranges
+//   inside [sink end, window start), sorted ascending by binning the positions (a bitonic sort when the bins
+//   crowd).
 #include "sa_device.h"
 #include "sa_internal.h"
 
@@ -192,29 +193,159 @@ __device__ __forceinline__ int lower_bound(const int32_t* a, int n, int32_t x) {
   return lo;
 }
 
-__global__ __launch_bounds__(1024) void k_expand(const int32_t* __restrict__ chosen, const int32_t* __restrict__ n_chosen,
-                                                 int top_b, const int32_t* __restrict__ offsets,
-                                                 const int32_t* __restrict__ members, int64_t L,
-                                                 const int32_t* __restrict__ t, int n_sink, int n_window,
-                                                 int32_t* __restrict__ idx, int cap, int32_t* __restrict__ n_sel) {
+// One workgroup per query: the choice of its top_b buckets, then their expansion.
+//
+// Choice: the query's slot keys (16 per thread in registers; a longer row is re-read per pass) go through three
+// LDS histogram passes (digits 31..21, 20..10, 9..0 of the key) that find kstar, the top_b-th largest non-empty
+// slot. Chosen are the slots above kstar and, among the slots equal to it, the lowest bucket ids (an id limit is
+// searched only when there are more ties than places left). With fewer than top_b non-empty buckets every one is
+// chosen. The chosen (key, id) pairs are sorted into rank order (score desc, id asc) by a bitonic sort.
+__global__ __launch_bounds__(1024) void k_choose_expand(const uint32_t* __restrict__ keys, int nb, int top_b,
+                                                        int32_t* __restrict__ buckets_out,
+                                                        const int32_t* __restrict__ offsets,
+                                                        const int32_t* __restrict__ members, int64_t L,
+                                                        const int32_t* __restrict__ t, int n_sink, int n_window,
+                                                        int32_t* __restrict__ idx, int cap,
+                                                        int32_t* __restrict__ n_sel) {
   constexpr int kWaves = 1024 / kWave;
+  constexpr int kKeyRegs = 16;  // slots tid + 1024 m (m < kKeyRegs) stay in registers
   __shared__ int32_t rng_lo[1024], rng_n[1024], rng_base[1024];
+  __shared__ int32_t chosen[1024];
   __shared__ int32_t buf[kMaxExpand];
   __shared__ int32_t tmp[kMaxExpand];
   __shared__ int32_t bin_cnt[1024], bin_cur[1024];
   __shared__ int32_t wsum[kWaves];
   __shared__ int overflow;
+  __shared__ uint32_t sel_digit, sel_before, sel_n;
   const int b = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid / kWave;
+
+  // ---- choice of the buckets
+  const uint32_t* kr = keys + (int64_t)b * nb;
+  uint32_t kv[kKeyRegs];
+#pragma unroll
+  for (int m = 0; m < kKeyRegs; ++m) kv[m] = tid + 1024 * m < nb ? kr[tid + 1024 * m] : 0u;
+  auto for_keys = [&](auto&& f) {  // f(bucket id, slot key); slots past nb hold key 0 (empty)
+#pragma unroll
+    for (int m = 0; m < kKeyRegs; ++m) f(tid + 1024 * m, kv[m]);
+    for (int i = tid + 1024 * kKeyRegs; i < nb; i += 1024) f(i, kr[i]);
+  };
+  // block sum of one value per thread, with this thread's exclusive prefix
+  auto block_scan = [&](int v, int* total) {
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int x = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += x;
+    }
+    if (lane == kWave - 1) wsum[wave] = incl;
+    __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      before += w < wave ? wsum[w] : 0;
+      all += wsum[w];
+    }
+    __syncthreads();
+    *total = all;
+    return before + incl - v;
+  };
+  uint32_t* hist = reinterpret_cast<uint32_t*>(tmp);  // tmp is free until the expansion sorts
+  uint32_t need = (uint32_t)top_b, prefix = 0u, pmask = 0u;
+  int n_valid = 0;
+  bool full = true;  // at least top_b non-empty buckets
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const int nbins = pass == 2 ? 1024 : 2048;
+    for (int i = tid; i < 2048; i += 1024) hist[i] = 0u;
+    __syncthreads();
+    for_keys([&](int, uint32_t v) {
+      if (v != 0u && (v & pmask) == prefix) atomicAdd(&hist[(v >> shift) & (uint32_t)(nbins - 1)], 1u);
+    });
+    __syncthreads();
+    // descending search: thread t takes bins nbins - 1 - per t and (per = 2) the one below it
+    const int per = nbins / 1024;
+    const uint32_t c0 = hist[nbins - 1 - per * tid], c1 = per > 1 ? hist[nbins - 2 - per * tid] : 0u;
+    int tot;
+    const uint32_t ex = (uint32_t)block_scan((int)(c0 + c1), &tot);
+    if (ex < need && ex + c0 + c1 >= need) {
+      const bool first = ex + c0 >= need;
+      sel_digit = (uint32_t)(nbins - 1 - per * tid - (first ? 0 : 1));
+      sel_before = first ? ex : ex + c0;
+    }
+    __syncthreads();
+    if (pass == 0) {
+      n_valid = tot;
+      if ((uint32_t)tot < need) {  // block-uniform
+        full = false;
+        break;
+      }
+    }
+    prefix |= sel_digit << shift;
+    pmask |= (uint32_t)(nbins - 1) << shift;
+    need -= sel_before;
+    __syncthreads();
+  }
+  const uint32_t kstar = prefix;  // with full: chosen = slots above kstar + `need` of the slots equal to it
+  const int nc = full ? top_b : n_valid;
+  uint32_t id_lim = 0xFFFFFFFFu;  // slots equal to kstar are chosen when their id is below this
+  if (full) {
+    int my_ties = 0, n_ties;
+    for_keys([&](int, uint32_t v) { my_ties += v == kstar ? 1 : 0; });
+    block_scan(my_ties, &n_ties);
+    if ((uint32_t)n_ties > need) {  // block-uniform: the smallest limit that admits `need` ties
+      int lo = 0, hi = nb;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        int mine = 0, cnt;
+        for_keys([&](int i, uint32_t v) { mine += (v == kstar && i < mid) ? 1 : 0; });
+        block_scan(mine, &cnt);
+        if ((uint32_t)cnt >= need) hi = mid;
+        else lo = mid + 1;
+      }
+      id_lim = (uint32_t)lo;
+    }
+  }
+  // the chosen (key, id) pairs, unordered, then sorted: ascending (~key, id) = score desc, id asc
+  uint64_t* sorted = reinterpret_cast<uint64_t*>(buf);  // buf is free until the expansion
+  if (tid == 0) sel_n = 0u;
+  __syncthreads();
+  for_keys([&](int i, uint32_t v) {
+    const bool take = full ? (v > kstar || (v == kstar && (uint32_t)i < id_lim)) : v != 0u;
+    if (take) sorted[atomicAdd(&sel_n, 1u)] = ((uint64_t)~v << 32) | (uint32_t)i;
+  });
+  int n2 = 2;
+  while (n2 < nc) n2 <<= 1;
+  __syncthreads();
+  for (int i = nc + tid; i < n2; i += 1024) sorted[i] = ~0ull;
+  __syncthreads();
+  for (int size = 2; size <= n2; size <<= 1)
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < (n2 >> 1); i += 1024) {
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool up = (lo & size) == 0;
+        const uint64_t x = sorted[lo], y = sorted[hi];
+        if ((x > y) == up) {
+          sorted[lo] = y;
+          sorted[hi] = x;
+        }
+      }
+      __syncthreads();
+    }
+  if (tid < nc) chosen[tid] = (int32_t)(uint32_t)sorted[tid];
+  if (buckets_out && tid < top_b) buckets_out[(int64_t)b * top_b + tid] = tid < nc ? (int32_t)(uint32_t)sorted[tid] : -1;
+  __syncthreads();
+
+  // ---- expansion
   const int tb = t ? t[b] : (int)(L - 1);
   const int ns = n_sink < tb + 1 ? n_sink : tb + 1;
   int w0 = tb - n_window + 1;
   w0 = w0 > ns ? w0 : ns;
-  const int nc = n_chosen[b];
   // each chosen bucket's members in [ns, w0): one wave per bucket counts, 64 members per load, how many lie below
   // ns and below w0 (members are ascending, so the counts are the range's bounds)
   for (int i = wave; i < nc; i += kWaves) {
-    const int c = chosen[(int64_t)b * top_b + i];
+    const int c = chosen[i];
     const int o0 = offsets[c], o1 = offsets[c + 1];
     int below_ns = 0, below_w0 = 0;
 #pragma unroll 4
@@ -371,8 +502,7 @@ int bucket_expand_max() { return kMaxExpand; }
 hipError_t launch_bucket_select(const void* q, int q_dtype, int B, int d, const float* reps, const int32_t* offsets,
                                 const int32_t* members, int nb, int64_t L, const int32_t* t, int top_b, int n_sink,
                                 int n_window, int32_t* idx, int cap, int32_t* n_sel, int32_t* buckets_out,
-                                Cand* cand, int32_t* n_chosen, Cand* gather, int32_t* chosen, hipStream_t st) {
-  uint32_t* keys = reinterpret_cast<uint32_t*>(cand);
+                                uint32_t* keys, hipStream_t st) {
   const unsigned n_wg = (unsigned)((nb + 63) / 64);  // 64 buckets per workgroup
   const size_t lds = sizeof(float) * (size_t)B * d;
   if (q_dtype == 0)
@@ -381,21 +511,8 @@ hipError_t launch_bucket_select(const void* q, int q_dtype, int B, int d, const 
     hipLaunchKernelGGL(k_bucket_scores<1>, dim3(n_wg), dim3(256), lds, st, q, B, d, reps, offsets, nb, keys);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  int32_t* order = buckets_out ? buckets_out : chosen;
-  MergeIn in{};
-  in.slot_key = keys;
-  in.slot_ld = nb;
-  in.n_slots = nb;
-  in.slot_pos0 = 0;  // a slot's position is its bucket id
-  MergeOut out{};
-  out.final_mode = 2;
-  out.idx = order;
-  out.idx_ld = top_b;
-  out.n_sel = n_chosen;
-  e = launch_merge(B, top_b, in, gather, nb, out, st);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_expand, dim3((unsigned)B), dim3(1024), 0, st, order, n_chosen, top_b, offsets, members, L, t,
-                     n_sink, n_window, idx, cap, n_sel);
+  hipLaunchKernelGGL(k_choose_expand, dim3((unsigned)B), dim3(1024), 0, st, keys, nb, top_b, buckets_out, offsets,
+                     members, L, t, n_sink, n_window, idx, cap, n_sel);
   return hipGetLastError();
 }
 

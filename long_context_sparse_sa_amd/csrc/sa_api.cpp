@@ -361,10 +361,7 @@ SA_API int sa_bucket_build(const void* k, int k_dtype, int64_t k_ld, int64_t L, 
 SA_API size_t sa_bucket_select_workspace(int32_t B, int32_t n_buckets, int32_t top_b) {
   if (B < 0 || n_buckets < 1 || top_b < 1) return 0;
   Carver c(nullptr);
-  c.take<sa::Cand>((size_t)B * n_buckets);
-  c.take<int32_t>(B);
-  c.take<sa::Cand>((size_t)B * n_buckets);
-  c.take<int32_t>((size_t)B * top_b);
+  c.take<uint32_t>((size_t)B * n_buckets);  // one score key per (query, bucket)
   return align_up(c.off, 256);
 }
 
@@ -384,13 +381,9 @@ SA_API int sa_bucket_select(const void* q, int q_dtype, int32_t B, int32_t d, co
   if (!ws || ws_bytes < need) return fail(SA_ERR_WORKSPACE, "workspace needs %zu bytes", need);
   if (B == 0) return SA_OK;
   Carver c(ws);
-  sa::Cand* cand = c.take<sa::Cand>((size_t)B * n_buckets);
-  int32_t* n_chosen = c.take<int32_t>(B);
-  sa::Cand* gather = c.take<sa::Cand>((size_t)B * n_buckets);
-  int32_t* chosen = c.take<int32_t>((size_t)B * top_b);
+  uint32_t* keys = c.take<uint32_t>((size_t)B * n_buckets);
   hipError_t e = sa::launch_bucket_select(q, q_dtype, B, d, reps, offsets, members, n_buckets, L, t, top_b, n_sink,
-                                          n_window, idx, cap, n_sel, buckets_out, cand, n_chosen, gather, chosen,
-                                          (hipStream_t)stream);
+                                          n_window, idx, cap, n_sel, buckets_out, keys, (hipStream_t)stream);
   return e == hipSuccess ? SA_OK : hip_fail(e, "sa_bucket_select");
 }
 

@@ -133,8 +133,7 @@ int bucket_expand_max();
 hipError_t launch_bucket_select(const void* q, int q_dtype, int B, int d, const float* reps, const int32_t* offsets,
                                 const int32_t* members, int n_buckets, int64_t L, const int32_t* t, int top_b,
                                 int n_sink, int n_window, int32_t* idx, int cap, int32_t* n_sel,
-                                int32_t* buckets_out, Cand* cand, int32_t* n_chosen, Cand* gather, int32_t* chosen,
-                                hipStream_t stream);
+                                int32_t* buckets_out, uint32_t* keys, hipStream_t stream);
 
 // ---- attention ---------------------------------------------------------------------------------------------------
 struct AttnArgs {

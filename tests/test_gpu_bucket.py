@@ -125,3 +125,40 @@ def test_expand_clustered_and_large(layout):
         exp_pos = np.sort(exp_pos[(exp_pos >= lo) & (exp_pos < hi)])
         assert exp_pos.size > (500 if layout == "contiguous" else 3000)
         np.testing.assert_array_equal(selected(idx[b], nsel[b].item()), exp_pos)
+
+
+def test_choice_ties_long_rows_and_few_nonempty():
+    """Integer keys: every score is exact and ties are heavy. 20000 buckets of two members each (a row longer than
+    the part of the choice held in registers): the chosen ids, in rank order (score desc, id asc), and the
+    expanded positions match the oracle exactly. Then only 10 of 40 buckets hold members and top_b = 16: every
+    non-empty bucket is chosen and -1 pads the rank list."""
+    g = torch.Generator(device="cpu").manual_seed(6)
+    L, d, B, nb, top = 40000, 16, 3, 20000, 50
+    k = torch.randint(-2, 3, (L, d), generator=g).float().to(DEV)
+    q = torch.randint(-2, 3, (B, d), generator=g).float().to(DEV)
+    assign = (torch.arange(L) % nb).to(torch.int32).to(DEV)
+    reps, offsets, members = sa.sa_bucket_build(k, assign, nb)
+    idx, nsel, buckets = sa.sa_bucket_select(q, reps, offsets, members, L, top, 0, 0, cap=200, return_buckets=True)
+    torch.cuda.synchronize()
+    qf = q.double().cpu().numpy()
+    r32, off, mem = reps.cpu().numpy(), offsets.cpu().numpy().astype(np.int64), members.cpu().numpy().astype(np.int64)
+    for b in range(B):
+        ref_pos, ref_chosen, sc = O.bucket_select(qf[b], r32, off, mem, L - 1, top, 0, 0)
+        assert np.unique(sc).size < nb / 10                           # ties are really exercised
+        np.testing.assert_array_equal(buckets[b].cpu().numpy(), ref_chosen)
+        np.testing.assert_array_equal(selected(idx[b], nsel[b].item()), ref_pos)
+
+    L2, nb2, top2 = 500, 40, 16
+    k2 = torch.randint(-2, 3, (L2, d), generator=g).float().to(DEV)
+    assign2 = ((torch.arange(L2) % 10) * 4).to(torch.int32).to(DEV)     # buckets 0, 4, ..., 36
+    reps2, off2, mem2 = sa.sa_bucket_build(k2, assign2, nb2)
+    idx2, nsel2, buckets2 = sa.sa_bucket_select(q, reps2, off2, mem2, L2, top2, 0, 0, cap=512, return_buckets=True)
+    torch.cuda.synchronize()
+    o2, m2 = off2.cpu().numpy().astype(np.int64), mem2.cpu().numpy().astype(np.int64)
+    for b in range(B):
+        ref_pos, ref_chosen, sc = O.bucket_select(qf[b], reps2.cpu().numpy(), o2, m2, L2 - 1, top2, 0, 0)
+        assert ref_chosen.size == 10
+        got = buckets2[b].cpu().numpy()
+        np.testing.assert_array_equal(got[:10], ref_chosen)
+        assert np.all(got[10:] == -1)
+        np.testing.assert_array_equal(selected(idx2[b], nsel2[b].item()), np.arange(L2))
