@@ -64,7 +64,10 @@ typedef enum {
   SA_TOPK_AUTO = 0,      /* the library picks by batch size                                            */
   SA_TOPK_SPLIT_L = 1,   /* few queries: key range split over workgroups, thresholds refined by levels  */
   SA_TOPK_PER_QUERY = 2, /* many queries (prefill chunk): one streaming pass per query group             */
-  SA_TOPK_RADIX = 3      /* few queries: one key per position, radix select spread over workgroups      */
+  SA_TOPK_RADIX = 3,     /* few queries: one key per position, radix select spread over workgroups      */
+  SA_TOPK_RADIX_LEVELS = 4 /* few queries over long caches: the radix select over a prefix of the
+                            * positions (at most half of them and at most 2^24 keys over all queries), then
+                            * key ranges in which only keys above the prefix's k-th key are kept, merged  */
 } sa_topk_algo;
 
 SA_API const char* sa_status_string(int status);

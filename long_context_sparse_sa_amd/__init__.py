@@ -4,10 +4,11 @@ The hot path -- indexer scoring, exact top-k with sink/window budget (or Flat bu
 attention over the gathered latent rows -- runs in hand-written HIP kernels behind the C ABI of include/sa.h.
 This package is the thin Python binding of that library.
 """
-from ._lib import SA_BF16, SA_E4M3, SA_F32, SA_TOPK_AUTO, SA_TOPK_PER_QUERY, SA_TOPK_RADIX, SA_TOPK_SPLIT_L, SAError, load
+from ._lib import (SA_BF16, SA_E4M3, SA_F32, SA_TOPK_AUTO, SA_TOPK_PER_QUERY, SA_TOPK_RADIX, SA_TOPK_RADIX_LEVELS,
+                   SA_TOPK_SPLIT_L, SAError, load)
 from .api import (sa_bucket_build, sa_bucket_select, sa_index_score, sa_select_topk, sa_select_topk_workspace,
                   sa_sparse_attn, sa_sparse_attn_workspace)
 
-__all__ = ["SA_F32", "SA_BF16", "SA_E4M3", "SA_TOPK_AUTO", "SA_TOPK_SPLIT_L", "SA_TOPK_PER_QUERY", "SA_TOPK_RADIX", "SAError", "load",
+__all__ = ["SA_F32", "SA_BF16", "SA_E4M3", "SA_TOPK_AUTO", "SA_TOPK_SPLIT_L", "SA_TOPK_PER_QUERY", "SA_TOPK_RADIX", "SA_TOPK_RADIX_LEVELS", "SAError", "load",
            "sa_index_score", "sa_select_topk", "sa_select_topk_workspace", "sa_bucket_build", "sa_bucket_select",
            "sa_sparse_attn", "sa_sparse_attn_workspace"]

@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsa.so")
 
 SA_F32, SA_BF16, SA_E4M3 = 0, 1, 2
-SA_TOPK_AUTO, SA_TOPK_SPLIT_L, SA_TOPK_PER_QUERY, SA_TOPK_RADIX = 0, 1, 2, 3
+SA_TOPK_AUTO, SA_TOPK_SPLIT_L, SA_TOPK_PER_QUERY, SA_TOPK_RADIX, SA_TOPK_RADIX_LEVELS = 0, 1, 2, 3, 4
 STATUS = {0: "SA_OK", 1: "SA_ERR_NULL", 2: "SA_ERR_SHAPE", 3: "SA_ERR_DTYPE", 4: "SA_ERR_ALIGN",
           5: "SA_ERR_WORKSPACE", 6: "SA_ERR_UNSUPPORTED", 7: "SA_ERR_HIP"}
 

@@ -222,7 +222,8 @@ __global__ __launch_bounds__(kRThreads) void k_radix_write(const uint32_t* __res
                                                            const uint32_t* __restrict__ recs,
                                                            const uint32_t* __restrict__ cnt,
                                                            int32_t* __restrict__ idx, int idx_ld,
-                                                           int32_t* __restrict__ n_sel) {
+                                                           int32_t* __restrict__ n_sel, Cand* __restrict__ kept,
+                                                           uint32_t* __restrict__ thr_out) {
   __shared__ RadixShared sh;
   const int b = blockIdx.y, j = blockIdx.x, tid = threadIdx.x;
   const int G = gridDim.x;
@@ -242,7 +243,13 @@ __global__ __launch_bounds__(kRThreads) void k_radix_write(const uint32_t* __res
   const uint32_t ties_before = pre_eq < ks.need_eq ? pre_eq : ks.need_eq;
   const uint32_t quota = ks.need_eq > pre_eq ? (my_eq < ks.need_eq - pre_eq ? my_eq : ks.need_eq - pre_eq) : 0u;
   const int64_t off = (int64_t)pre_gt + ties_before;
-  int32_t* out = idx + (int64_t)b * idx_ld;
+  // rank r of the selection: position into idx, (key, position) into kept, whichever is given
+  int32_t* out = idx ? idx + (int64_t)b * idx_ld : nullptr;
+  Cand* kp = kept ? kept + (int64_t)b * k : nullptr;
+  auto put = [&](int64_t r, uint32_t key, int64_t pos) {
+    if (out) out[r] = (int32_t)pos;
+    if (kp) kp[r] = Cand{key, (int32_t)pos};
+  };
 
   const Chunk c = chunk_of(L, chunk);
   const uint32_t* row = keys + (int64_t)b * keys_ld;
@@ -267,10 +274,10 @@ __global__ __launch_bounds__(kRThreads) void k_radix_write(const uint32_t* __res
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if (g[e]) {
-        out[off + gb + (eb < quota ? eb : quota)] = (int32_t)(s + e);
+        put(off + gb + (eb < quota ? eb : quota), v[e], s + e);
         ++gb;
       } else if (t[e]) {
-        if (eb < quota) out[off + gb + eb] = (int32_t)(s + e);
+        if (eb < quota) put(off + gb + eb, v[e], s + e);
         ++eb;
       }
     }
@@ -279,8 +286,12 @@ __global__ __launch_bounds__(kRThreads) void k_radix_write(const uint32_t* __res
   }
   if (j == 0) {
     const int take = ks.ok ? k : (int)ks.n_cand;
-    for (int i = take + tid; i < idx_ld; i += kRThreads) out[i] = -1;
-    if (tid == 0) n_sel[b] = take;
+    if (out)
+      for (int i = take + tid; i < idx_ld; i += kRThreads) out[i] = -1;
+    if (tid == 0) {
+      n_sel[b] = take;
+      if (thr_out) thr_out[b] = ks.ok ? ks.kstar : 0u;  // later keys must beat the k-th key to enter
+    }
   }
 }
 
@@ -306,7 +317,8 @@ size_t radix_ctl_words(int B, const RadixPlan& p) {
 }
 
 hipError_t launch_radix_select(int B, int64_t L, int k, const RadixPlan& p, const uint32_t* keys, uint32_t* ctl,
-                               int32_t* idx, int idx_ld, int32_t* n_sel, hipStream_t st) {
+                               int32_t* idx, int idx_ld, int32_t* n_sel, Cand* kept, uint32_t* thr_out,
+                               hipStream_t st) {
   if (B == 0) return hipSuccess;
   const dim3 grid((unsigned)p.n_chunks, (unsigned)B);
   uint32_t* hist = ctl;
@@ -318,7 +330,7 @@ hipError_t launch_radix_select(int B, int64_t L, int k, const RadixPlan& p, cons
   hipLaunchKernelGGL(k_radix_count, grid, dim3(kRThreads), 0, st, keys, p.keys_ld, L, p.chunk, k, B, hist, recs,
                      cnt);
   hipLaunchKernelGGL(k_radix_write, grid, dim3(kRThreads), 0, st, keys, p.keys_ld, L, p.chunk, k, B, recs, cnt, idx,
-                     idx_ld, n_sel);
+                     idx_ld, n_sel, kept, thr_out);
   return hipGetLastError();
 }
 

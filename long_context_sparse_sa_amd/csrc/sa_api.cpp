@@ -93,8 +93,9 @@ int resolve_algo(int algo, const sa::IndexerArgs& a) {
   if (algo != SA_TOPK_AUTO) return algo;
   if (a.B >= kAutoPerQueryMinB && sa::stream_select_supported(a)) return SA_TOPK_PER_QUERY;
   // few queries: writing one key per position and selecting over all of them with every workgroup beats the
-  // level-by-level thresholds until the key buffer gets large (then the levels prune most of the writes)
-  return (int64_t)a.B * a.L <= kAutoRadixMaxKeys ? SA_TOPK_RADIX : SA_TOPK_SPLIT_L;
+  // level-by-level thresholds until the key buffer gets large; beyond that the radix select takes a prefix and
+  // its k-th key prunes the rest (measured faster than thresholds refined over geometric levels from 16K)
+  return (int64_t)a.B * a.L <= kAutoRadixMaxKeys ? SA_TOPK_RADIX : SA_TOPK_RADIX_LEVELS;
 }
 
 struct RadixWs {
@@ -118,6 +119,18 @@ RadixWs carve_radix(void* ws, const sa::IndexerArgs& a) {
 
 // Level boundaries of the split-L algorithm: [0, first), [first, 8 first), ... up to L. The first level holds at least
 // 4 k positions so that the first threshold already prunes.
+// Key ranges after a radix-selected prefix [0, f): [f, 8 f), [8 f, 64 f), ... up to L (none when f >= L).
+std::vector<int64_t> levels_after(int64_t f, int64_t L) {
+  std::vector<int64_t> b{f};
+  int64_t e = f * kLevelGrowth;
+  while (e < L) {
+    b.push_back(e);
+    e *= kLevelGrowth;
+  }
+  if (f < L) b.push_back(L);
+  return b;
+}
+
 std::vector<int64_t> levels(int64_t L, int k, int kpw) {
   int64_t first = kFirstLevel;
   if (first < 4 * (int64_t)k) first = 4 * (int64_t)k;
@@ -144,14 +157,14 @@ struct SplitLWs {
   size_t bytes;
 };
 
-SplitLWs carve_split_l(void* ws, const sa::IndexerArgs& a, int k) {
-  const int kpw = sa::score_keys_per_wg(a);
-  const std::vector<int64_t> lv = levels(a.L, k, kpw);
+// Workspace of a sequence of key ranges lv; first_slots: the first range writes one key per position (slots)
+// instead of emitting into per-workgroup segments.
+SplitLWs carve_levels(void* ws, const sa::IndexerArgs& a, int k, const std::vector<int64_t>& lv, bool first_slots) {
   int64_t max_level = 0;
   int max_seg = 1;
   for (size_t i = 0; i + 1 < lv.size(); ++i) {
     max_level = std::max(max_level, lv[i + 1] - lv[i]);
-    if (i > 0) max_seg = std::max(max_seg, sa::score_emit_plan(a, lv[i], lv[i + 1]).n_seg);
+    if (i > 0 || !first_slots) max_seg = std::max(max_seg, sa::score_emit_plan(a, lv[i], lv[i + 1]).n_seg);
   }
   SplitLWs w{};
   w.cand_ld = (int64_t)align_up((size_t)max_level, 512);
@@ -165,6 +178,39 @@ SplitLWs carve_split_l(void* ws, const sa::IndexerArgs& a, int k) {
   w.cand = c.take<sa::Cand>((size_t)a.B * w.cand_ld);
   w.gather = c.take<sa::Cand>((size_t)a.B * w.gather_cap);
   w.bytes = align_up(c.off, 256);
+  return w;
+}
+
+SplitLWs carve_split_l(void* ws, const sa::IndexerArgs& a, int k) {
+  return carve_levels(ws, a, k, levels(a.L, k, sa::score_keys_per_wg(a)), true);
+}
+
+// The radix-selected prefix [0, f): at most half the positions and at most kAutoRadixMaxKeys keys over all
+// queries, a multiple of the scoring workgroup's key count; a cache too short to split is selected whole.
+int64_t radix_prefix(const sa::IndexerArgs& a) {
+  const int64_t kpw = sa::score_keys_per_wg(a);
+  int64_t f = std::min<int64_t>(kAutoRadixMaxKeys / std::max(a.B, 1), a.L / 2);
+  f = f / kpw * kpw;
+  return f >= kpw ? f : a.L;
+}
+
+struct RadixLevelsWs {
+  int64_t prefix;
+  std::vector<int64_t> lv;  // key ranges after the prefix
+  RadixWs r;                // the prefix's radix select
+  SplitLWs l;               // the ranges after it (kept list, threshold, candidates)
+  size_t bytes;
+};
+
+RadixLevelsWs carve_radix_levels(void* ws, const sa::IndexerArgs& a, int k) {
+  RadixLevelsWs w{};
+  w.prefix = radix_prefix(a);
+  sa::IndexerArgs ap = a;
+  ap.L = w.prefix;
+  w.r = carve_radix(ws, ap);
+  w.lv = levels_after(w.prefix, a.L);
+  w.l = carve_levels(ws ? static_cast<char*>(ws) + w.r.bytes : nullptr, a, k, w.lv, false);
+  w.bytes = w.r.bytes + w.l.bytes;
   return w;
 }
 
@@ -233,6 +279,7 @@ SA_API size_t sa_select_topk_workspace(int64_t L, int32_t B, int32_t H, int32_t 
   const int alg = resolve_algo(algo, a);
   if (alg == SA_TOPK_PER_QUERY) return carve_per_query(nullptr, a, k_sparse).bytes;
   if (alg == SA_TOPK_RADIX) return carve_radix(nullptr, a).bytes;
+  if (alg == SA_TOPK_RADIX_LEVELS) return carve_radix_levels(nullptr, a, k_sparse).bytes;
   return carve_split_l(nullptr, a, k_sparse).bytes;
 }
 
@@ -247,7 +294,7 @@ SA_API int sa_select_topk(const void* q, int q_dtype, const float* w, const void
     return fail(SA_ERR_SHAPE, "k_sparse must be in [1, %d]", sa::merge_max_k());
   if (idx_ld < k_sparse) return fail(SA_ERR_SHAPE, "idx_ld (%d) < k_sparse (%d)", idx_ld, k_sparse);
   if (n_sink < 0 || n_window < 0) return fail(SA_ERR_SHAPE, "n_sink and n_window must be >= 0");
-  if (algo < SA_TOPK_AUTO || algo > SA_TOPK_RADIX) return fail(SA_ERR_SHAPE, "unknown algo %d", algo);
+  if (algo < SA_TOPK_AUTO || algo > SA_TOPK_RADIX_LEVELS) return fail(SA_ERR_SHAPE, "unknown algo %d", algo);
   const sa::IndexerArgs a = make_indexer(q, q_dtype, w, k, k_dtype, k_ld, L, B, H, d, t);
   const int alg = resolve_algo(algo, a);
   if (alg == SA_TOPK_PER_QUERY && !sa::stream_select_supported(a))
@@ -284,8 +331,51 @@ SA_API int sa_select_topk(const void* q, int q_dtype, const float* w, const void
     e = sa::launch_score(as, 0, L, sa::kScoreAll, nullptr, 0, n_sink, n_window, nullptr,
                          reinterpret_cast<sa::Cand*>(w2.keys), w2.p.keys_ld, nullptr, s);
     if (e != hipSuccess) return hip_fail(e, "sa_select_topk (radix score)");
-    e = sa::launch_radix_select(B, L, k_sparse, w2.p, w2.keys, w2.ctl, idx, idx_ld, n_sel, s);
+    e = sa::launch_radix_select(B, L, k_sparse, w2.p, w2.keys, w2.ctl, idx, idx_ld, n_sel, nullptr, nullptr, s);
     return e == hipSuccess ? SA_OK : hip_fail(e, "sa_select_topk (radix select)");
+  }
+  if (alg == SA_TOPK_RADIX_LEVELS) {
+    // the exact top-k of the prefix by the radix select, kept as (key, position) pairs with its k-th key as the
+    // threshold; then each later key range emits only keys above the threshold and a merge keeps the k best
+    const RadixLevelsWs w2 = carve_radix_levels(ws, a, k_sparse);
+    const bool whole = w2.prefix >= L;
+    sa::IndexerArgs as = a;
+    as.clear = w2.r.ctl;  // the scoring launch zeroes the select's counters
+    as.clear_n = (int64_t)w2.r.ctl_words;
+    e = sa::launch_score(as, 0, w2.prefix, sa::kScoreAll, nullptr, 0, n_sink, n_window, nullptr,
+                         reinterpret_cast<sa::Cand*>(w2.r.keys), w2.r.p.keys_ld, nullptr, s);
+    if (e != hipSuccess) return hip_fail(e, "sa_select_topk (prefix score)");
+    e = sa::launch_radix_select(B, w2.prefix, k_sparse, w2.r.p, w2.r.keys, w2.r.ctl, whole ? idx : nullptr, idx_ld,
+                                whole ? n_sel : w2.l.kept_n, whole ? nullptr : w2.l.kept,
+                                whole ? nullptr : w2.l.thr, s);
+    if (e != hipSuccess) return hip_fail(e, "sa_select_topk (prefix select)");
+    for (size_t i = 0; i + 1 < w2.lv.size(); ++i) {
+      const int64_t lo = w2.lv[i], hi = w2.lv[i + 1];
+      e = sa::launch_score(a, lo, hi, sa::kScoreEmit, nullptr, 0, n_sink, n_window, w2.l.thr, w2.l.cand,
+                           w2.l.cand_ld, w2.l.seg_cnt, s);
+      if (e != hipSuccess) return hip_fail(e, "sa_select_topk (score)");
+      sa::MergeIn in{};
+      in.kept = w2.l.kept;
+      in.kept_ld = k_sparse;
+      in.kept_n = w2.l.kept_n;
+      in.cand = w2.l.cand;
+      in.cand_ld = w2.l.cand_ld;
+      const sa::EmitPlan ep = sa::score_emit_plan(a, lo, hi);
+      in.seg_cnt = w2.l.seg_cnt;
+      in.n_seg = ep.n_seg;
+      in.seg_cap = ep.seg_cap;
+      sa::MergeOut out{};
+      out.final_mode = i + 2 == w2.lv.size() ? 1 : 0;
+      out.kept_out = w2.l.kept;
+      out.kept_n_out = w2.l.kept_n;
+      out.thr_out = w2.l.thr;
+      out.idx = idx;
+      out.idx_ld = idx_ld;
+      out.n_sel = n_sel;
+      e = sa::launch_merge(B, k_sparse, in, w2.l.gather, w2.l.gather_cap, out, s);
+      if (e != hipSuccess) return hip_fail(e, "sa_select_topk (merge)");
+    }
+    return SA_OK;
   }
   const SplitLWs w2 = carve_split_l(ws, a, k_sparse);
   const int kpw = sa::score_keys_per_wg(a);

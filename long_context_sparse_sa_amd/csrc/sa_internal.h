@@ -108,8 +108,11 @@ struct RadixPlan {
 };
 RadixPlan radix_plan(int B, int64_t L);
 size_t radix_ctl_words(int B, const RadixPlan& p);
+// The selection goes to idx (positions, -1 padded to idx_ld) and/or kept ([B, k] (key, position) pairs), either
+// may be NULL; n_sel[b] = min(k, candidates); thr_out (or NULL) receives the k-th key (0 with fewer candidates).
 hipError_t launch_radix_select(int B, int64_t L, int k, const RadixPlan& p, const uint32_t* keys, uint32_t* ctl,
-                               int32_t* idx, int idx_ld, int32_t* n_sel, hipStream_t stream);
+                               int32_t* idx, int idx_ld, int32_t* n_sel, Cand* kept, uint32_t* thr_out,
+                               hipStream_t stream);
 
 // Streaming per-query selection for many queries (prefill chunk): one pass over each query's visible keys keeps
 // at most `cap` candidates per query in buf[b, :] (count in buf_n[b]) that contain the exact top-k.

@@ -52,7 +52,7 @@ def test_index_score_dense(dtype, H, d):
         assert np.all(err <= 1e-5 * mag[vis] + 1e-30), (b, err.max())
 
 
-ALGOS = [sa.SA_TOPK_SPLIT_L, sa.SA_TOPK_PER_QUERY, sa.SA_TOPK_RADIX]
+ALGOS = [sa.SA_TOPK_SPLIT_L, sa.SA_TOPK_PER_QUERY, sa.SA_TOPK_RADIX, sa.SA_TOPK_RADIX_LEVELS]
 
 
 @pytest.mark.parametrize("algo", ALGOS)
@@ -88,7 +88,7 @@ def test_topk_normal_band(algo):
         band_compare(selected(idx[b], nsel[b].item()), ref, cand, sc, kk)
 
 
-@pytest.mark.parametrize("algo", [sa.SA_TOPK_SPLIT_L, sa.SA_TOPK_RADIX])
+@pytest.mark.parametrize("algo", [sa.SA_TOPK_SPLIT_L, sa.SA_TOPK_RADIX, sa.SA_TOPK_RADIX_LEVELS])
 def test_topk_valu_path_f32(algo):
     """The toy indexer shapes (4 heads x 32, fp32) take the VALU scorer."""
     B, H, d, L, kk = 2, 4, 32, 1024, 64
@@ -145,7 +145,8 @@ def test_topk_valu_path_levels():
         band_compare(selected(idx[b], nsel[b].item()), ref, cand, sc, kk)
 
 
-def test_topk_rising_scores_many_emits():
+@pytest.mark.parametrize("algo", [sa.SA_TOPK_SPLIT_L, sa.SA_TOPK_RADIX_LEVELS])
+def test_topk_rising_scores_many_emits(algo):
     """Scores rise with position (with runs of equal bf16 keys): every later key range emits almost all of its
     positions, so the merges overflow LDS and run from the gather buffer; ties resolve to lower positions."""
     B, H, d, L, kk = 2, 64, 128, 150000, 2048
@@ -157,7 +158,7 @@ def test_topk_rising_scores_many_emits():
     q[1, :, 1] = 0.5
     q = q.to(torch.bfloat16).to(DEV)
     w = torch.ones((B, H), device=DEV)
-    idx, nsel = sa.sa_select_topk(q, w, k, kk, n_sink=4, n_window=64, algo=sa.SA_TOPK_SPLIT_L)
+    idx, nsel = sa.sa_select_topk(q, w, k, kk, n_sink=4, n_window=64, algo=algo)
     torch.cuda.synchronize()
     qf, wf, kf = to_f64(q), w.double().cpu().numpy(), to_f64(k)
     for b in range(B):
