@@ -94,7 +94,9 @@ SA_API int sa_index_score(const void* q, int q_dtype, const float* w, const void
  *     S_sparse,b = the min(k_sparse, |C_b|) positions of C_b with the largest fp32 score I_{b,s}
  * where ties are broken towards the LOWER position. The score is the one sa_index_score defines (fp32).
  * SA_TOPK_SPLIT_L and SA_TOPK_PER_QUERY never write the full score matrix (only candidates that can still enter
- * the top-k leave the kernels); SA_TOPK_RADIX writes one 4-byte key per position and query to the workspace.
+ * the top-k leave the kernels); SA_TOPK_RADIX writes one 4-byte key per position and query to the workspace, and
+ * SA_TOPK_RADIX_LEVELS does so for the positions of its prefix only. SA_TOPK_AUTO takes PER_QUERY for B >= 64,
+ * RADIX while B * L <= 2^24, RADIX_LEVELS beyond.
  *   idx    [B, idx_ld] int32, idx_ld >= k_sparse: S_sparse,b in ascending position order, then -1 padding.
  *   n_sel  [B] int32: |S_sparse,b|.
  *   The sink and window are not listed in idx; pass the same n_sink/n_window to sa_sparse_attn.
