@@ -27,7 +27,7 @@ constexpr int kRThreads = 256;
 constexpr int kRWaves = kRThreads / kWave;
 constexpr int kRBins = 2048;
 constexpr int kChunkAlign = 1024;  // chunk starts are multiples of this many positions (aligned vector loads)
-constexpr int kTargetWgs = 512;
+constexpr int kTargetWgs = 1024;
 
 __device__ __forceinline__ int pass_shift(int p) { return p == 0 ? 21 : (p == 1 ? 10 : 0); }
 __device__ __forceinline__ int pass_bins(int p) { return p == 2 ? 1024 : 2048; }
