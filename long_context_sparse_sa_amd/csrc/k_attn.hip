@@ -244,6 +244,14 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
   const int64_t bh = (int64_t)b * H + head;
   const int dv0 = dh * DVH;
 
+  // Q^T fragments (B operand): head `head`, dims 288 dh + 16 ks + 8 hsel .. +8, requested first: they depend on
+  // nothing, so their latency overlaps the read-set bounds and position loads below (loads complete in issue
+  // order, so every later wait also covers them)
+  bf16x8 qf[kQSteps];
+#pragma unroll
+  for (int ks = 0; ks < kQSteps; ++ks)
+    qf[ks] = *reinterpret_cast<const bf16x8*>(q + bh * kRowElems + 288 * dh + 16 * ks + 8 * hsel);
+
   const RowList R = make_rows(b, L, t, idx, idx_ld, n_sel, n_sink, n_window);
   const int n_rows = R.count();
   // the query's own read set is cut into n_splits tile-aligned parts of nearly equal size, so that read sets far
@@ -321,7 +329,6 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
     for (int jj = 0; jj < kDmaPerWave; ++jj) dma_one(jj, s, buf);
   };
 
-  bf16x8 qf[kQSteps];
   f32x16 o[NT];
 #pragma unroll
   for (int i = 0; i < NT; ++i) o[i] = f32x16{};
@@ -457,12 +464,6 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
 
   const int n_pre = n_tiles < kNBuf - 1 ? n_tiles : kNBuf - 1;
   for (int p = 0; p < n_pre; ++p) issue(p, p);
-  // Q^T fragments (B operand): head `head`, dims 288 dh + 16 ks + 8 hsel .. +8. Loaded after the first tile copies
-  // so that the two latencies overlap; loads complete in issue order, so the loop's "at most N copies outstanding"
-  // waits stay conservative.
-#pragma unroll
-  for (int ks = 0; ks < kQSteps; ++ks)
-    qf[ks] = *reinterpret_cast<const bf16x8*>(q + bh * kRowElems + 288 * dh + 16 * ks + 8 * hsel);
   const int n_full = n_my / kTileRows;
   for (int tile = 0; tile < n_full; ++tile) process(tile, BoolTag<false>{});
   if (n_full < n_tiles) process(n_full, BoolTag<true>{});
