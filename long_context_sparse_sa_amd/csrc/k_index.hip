@@ -6,7 +6,7 @@
 //  * k_score_mfma  -- d = 128 and H in {32, 64}: the (query-head x position) dot products are a dense contraction
 //    and run on the bf16 32x32x16 MFMA, one wave per query so that the ReLU-weighted head sum stays inside the
 //    wave. Key tiles of 64 positions are staged in LDS (bf16 rows by asynchronous DMA; e4m3 rows converted exactly
-//    to bf16 on the way in) and shared by the workgroup's four waves (four queries).
+//    to bf16 on the way in) and shared by the workgroup's waves (four or eight queries: eight when B >= 8).
 // Both kernels either write the dense score row or emit only candidates whose score beats the caller's running
 // threshold, so a decode step never writes the [B, L] score matrix.
 #include <type_traits>
@@ -322,7 +322,8 @@ __global__ __launch_bounds__(64 * NQ) void k_score_mfma(const void* __restrict__
     if (mode == kScoreEmit && thr_key) thr = thr_key[b];
     load_query<NMT, E4M3>(q, w, b, lane, qa, wv);
   }
-  wait_vmem();  // the query fragments are in registers before the tile copies start counting
+  // no wait here: the query loads are older than every tile copy and loads complete in issue order, so the first
+  // tile's wait (at most two tiles of copies outstanding) also covers them
 
   int n_emit = 0;     // staged in LDS
   int64_t n_out = 0;  // already in this workgroup's segment
