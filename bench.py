@@ -164,7 +164,11 @@ def main():
     a_bytes = perf.attn_bytes(rows_total, wl.B, wl.H, wl.d_qk, wl.d_v, width, wl.attn_dtype)
     a_flops = perf.attn_flops(rows_total, wl.H, wl.d_qk, wl.d_v)
     attn_gbps = a_bytes / t_att / 1e9
-    attn_roof = {"kernel": "sa_sparse_attn (gather + MFMA + split combine)", "bound": "hbm",
+    # which kernels serve the workload (the same conditions the library applies)
+    attn_mfma = wl.attn_dtype == "bf16" and wl.d_qk == 576 and wl.d_v in (512, 576) and wl.H % 64 == 0
+    idx_mfma = wl.idx_dtype in ("bf16", "e4m3") and wl.d_I == 128 and wl.H_I in (32, 64)
+    attn_roof = {"kernel": "sa_sparse_attn (" + ("gather + MFMA + split combine" if attn_mfma
+                                                 else "fp32 VALU kernel, one block per head") + ")", "bound": "hbm",
                  "achieved": round(attn_gbps, 1), "peak": perf.PEAK_HBM_GBPS, "unit": "GB/s",
                  "frac": round(attn_gbps / perf.PEAK_HBM_GBPS, 4), "traffic": None,
                  "algorithmic_bytes_per_launch": a_bytes, "launch_ms": round(t_att * 1e3, 4),
@@ -184,8 +188,9 @@ def main():
         i_flops = perf.indexer_flops(pairs, wl.H_I, wl.d_I)
         i_bytes = perf.indexer_bytes(wl.L, wl.B, wl.H_I, wl.d_I, wl.idx_dtype)
         tf = i_flops / t_sel / 1e12
-        peak = perf.PEAK_TFLOPS["bf16"]
-        sel_roof = {"kernel": "sa_select_topk (MFMA scoring + exact top-k merges)", "bound": "mfma",
+        peak = perf.PEAK_TFLOPS["bf16" if idx_mfma else "f32_vector"]
+        sel_roof = {"kernel": "sa_select_topk (" + ("MFMA" if idx_mfma else "fp32 VALU") + " scoring + exact top-k)",
+                    "bound": "mfma" if idx_mfma else "alu",
                     "achieved": round(tf, 1), "peak": peak, "unit": "TFLOP/s", "frac": round(tf / peak, 4),
                     "traffic": None, "algorithmic_flops_per_launch": i_flops, "launch_ms": round(t_sel * 1e3, 4),
                     "hbm_gbps": round(i_bytes / t_sel / 1e9, 1)}
