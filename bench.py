@@ -44,8 +44,8 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (the sequence-sharded design is "
-              "documented, not built). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (sharding the cache along the "
+              "sequence is described in the design notes, not implemented). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -206,7 +206,7 @@ def main():
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": {"e4m3": "e4m3 index / bf16 attn", "bf16": "bf16", "f32": "f32"}[wl.idx_dtype],
-        "data": "synthetic (seeded N(0,1) queries, keys, latent rows; see DESIGN.md)",
+        "data": "synthetic (seeded N(0,1) queries, index keys and latent rows)",
         "config": {"workload": wl.name, "L": wl.L, "B": wl.B, "H_I": wl.H_I, "d_I": wl.d_I, "k_sparse": wl.k_sparse,
                    "n_buckets": wl.n_buckets, "top_b": wl.top_b, "n_sink": wl.n_sink, "n_window": wl.n_window,
                    "H": wl.H, "d_latent": width, "d_v": wl.d_v, "cache_copies_rotated": n_copies},

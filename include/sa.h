@@ -55,7 +55,7 @@ typedef enum {
   SA_ERR_DTYPE = 3,       /* unsupported dtype or dtype combination                         */
   SA_ERR_ALIGN = 4,       /* a pointer or leading dimension breaks the alignment rules      */
   SA_ERR_WORKSPACE = 5,   /* workspace pointer NULL or smaller than the query returned      */
-  SA_ERR_UNSUPPORTED = 6, /* valid arguments that this build has no kernel for              */
+  SA_ERR_UNSUPPORTED = 6, /* valid arguments that the library has no kernel for            */
   SA_ERR_HIP = 7          /* a HIP runtime call failed; sa_last_error() holds its message    */
 } sa_status;
 

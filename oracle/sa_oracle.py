@@ -18,7 +18,7 @@ the definitions. Sources, cited by page title and section:
         member positions; Flat search over representatives; read the chosen rows plus sink plus window);
       - sections 3-4: the eight-entry worked example (stored/read bytes, attention outputs).
 
-Readings taken where the pages are silent (each also listed in the design doc):
+Readings taken where the pages are silent:
   * positions are 0-based; sink = [0, n_sink), window = [t-n_window+1, t], both clipped to [0, t];
   * top-k counts only the sparse part and never includes sink or window positions;
   * ties in the fp32 score go to the lower position; ties in bucket score go to the lower bucket id;
