@@ -111,6 +111,13 @@ def test_mfma_read_sets_far_below_bound():
                idx_ld=8192, ws_fill=0xFF)
 
 
+@pytest.mark.parametrize("H", [64, 192])
+def test_mfma_head_groups(H):
+    # one and three 64-head groups per query (the block mapping interleaves a unit's head groups): ragged read sets,
+    # several splits per query
+    _mfma_case(6, B=3, L=9000, n_list=[1500, 33, 700], n_sink=4, n_window=128, d_v=576, H=H)
+
+
 def test_mfma_single_split_and_peaked():
     # many queries -> one split each; queries x8 give peaked softmax with |o| ~ |V|
     _mfma_case(1, B=64, L=4096, n_list=[40] * 64, n_sink=0, n_window=0, d_v=576, q_scale=8.0)

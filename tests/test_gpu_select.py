@@ -77,6 +77,33 @@ def test_topk_integer_exact_with_ties(algo, dtype, B):
 
 
 @pytest.mark.parametrize("algo", ALGOS)
+def test_topk_heads32_integer_exact(algo):
+    """32 indexer heads (one head tile per query wave): integer inputs, exact scores, bit-exact selection."""
+    B, H, d, L, kk = 5, 32, 128, 30000, 500
+    q, w, k = _inputs(15, B, H, d, L, "bf16", integer=True)
+    ts = [L - 1, 29000, 12000, 700, 20001]
+    t = torch.tensor(ts, dtype=torch.int32, device=DEV)
+    idx, nsel = sa.sa_select_topk(q, w, k, kk, n_sink=2, n_window=40, t=t, algo=algo)
+    torch.cuda.synchronize()
+    qf, wf, kf = to_f64(q), w.double().cpu().numpy(), to_f64(k)
+    for b in range(B):
+        ref, sc, cand = O.select_topk(qf[b], wf[b], kf, ts[b], kk, 2, 40)
+        np.testing.assert_array_equal(selected(idx[b], nsel[b].item()), ref)
+
+
+@pytest.mark.parametrize("algo", [sa.SA_TOPK_RADIX, sa.SA_TOPK_RADIX_LEVELS, sa.SA_TOPK_SPLIT_L])
+def test_topk_single_query(algo):
+    """B = 1: the radix select spreads one query over its largest number of chunks."""
+    B, H, d, L, kk = 1, 64, 128, 200000, 1000
+    q, w, k = _inputs(16, B, H, d, L, "bf16", integer=True)
+    idx, nsel = sa.sa_select_topk(q, w, k, kk, n_sink=1, n_window=16, algo=algo)
+    torch.cuda.synchronize()
+    qf, wf, kf = to_f64(q), w.double().cpu().numpy(), to_f64(k)
+    ref, sc, cand = O.select_topk(qf[0], wf[0], kf, L - 1, kk, 1, 16)
+    np.testing.assert_array_equal(selected(idx[0], nsel[0].item()), ref)
+
+
+@pytest.mark.parametrize("algo", ALGOS)
 def test_topk_normal_band(algo):
     B, H, d, L, kk = 8, 64, 128, 150000, 2048
     q, w, k = _inputs(7, B, H, d, L, "bf16", integer=False)
