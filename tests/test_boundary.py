@@ -101,6 +101,21 @@ def test_select_topk_workspace_sizes(lib):
     assert lib.sa_select_topk_workspace(0, 1, 1, 1, F32, F32, 1, 0) == 0
 
 
+def test_select_topk_auto_choices(lib):
+    # up to 2^24 keys over all queries AUTO takes the plain radix select (one key per position)
+    r = lib.sa_select_topk_workspace(131072, 16, 64, 128, BF16, BF16, 2048, 3)
+    assert r >= 16 * 131072 * 4
+    assert lib.sa_select_topk_workspace(131072, 16, 64, 128, BF16, BF16, 2048, 0) == r
+    # beyond that, the radix select over a prefix of at most 2^24 / B positions, then emission levels
+    L, B = 10_000_000, 4
+    w = lib.sa_select_topk_workspace(L, B, 64, 128, E4M3, E4M3, 2048, 4)
+    assert lib.sa_select_topk_workspace(L, B, 64, 128, E4M3, E4M3, 2048, 0) == w
+    prefix = (1 << 24) // B // 512 * 512
+    assert B * prefix * 4 <= w < B * L * 4 + B * (L - prefix) * 16 + (64 << 20)
+    # a cache too short to split is selected whole by the radix part
+    assert lib.sa_select_topk_workspace(600, 1, 64, 128, BF16, BF16, 100, 4) > 0
+
+
 def attn(lib, **kw):
     a = dict(q=A, kv=A, v=None, dt=BF16, kv_ld=576, v_ld=0, L=4096, B=2, H=128, dqk=576, dv=576, t=None, idx=A,
              idx_ld=64, nsel=A, ns=4, nw=8, scale=0.04, out=A, lse=None, ws=A, wsb=1 << 30)
