@@ -199,7 +199,8 @@ __device__ __forceinline__ int lower_bound(const int32_t* a, int n, int32_t x) {
 // LDS histogram passes (digits 31..21, 20..10, 9..0 of the key) that find kstar, the top_b-th largest non-empty
 // slot. Chosen are the slots above kstar and, among the slots equal to it, the lowest bucket ids (an id limit is
 // searched only when there are more ties than places left). With fewer than top_b non-empty buckets every one is
-// chosen. The chosen (key, id) pairs are sorted into rank order (score desc, id asc) by a bitonic sort.
+// chosen. The chosen (key, id) pairs are sorted into rank order (score desc, id asc) by a bitonic sort (in one
+// wave's registers when at most 64 are chosen).
 __global__ __launch_bounds__(1024) void k_choose_expand(const uint32_t* __restrict__ keys, int nb, int top_b,
                                                         int32_t* __restrict__ buckets_out,
                                                         const int32_t* __restrict__ offsets,
@@ -314,27 +315,50 @@ __global__ __launch_bounds__(1024) void k_choose_expand(const uint32_t* __restri
     const bool take = full ? (v > kstar || (v == kstar && (uint32_t)i < id_lim)) : v != 0u;
     if (take) sorted[atomicAdd(&sel_n, 1u)] = ((uint64_t)~v << 32) | (uint32_t)i;
   });
-  int n2 = 2;
-  while (n2 < nc) n2 <<= 1;
   __syncthreads();
-  for (int i = nc + tid; i < n2; i += 1024) sorted[i] = ~0ull;
-  __syncthreads();
-  for (int size = 2; size <= n2; size <<= 1)
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < (n2 >> 1); i += 1024) {
-        const int lo = 2 * i - (i & (stride - 1));
-        const int hi = lo + stride;
-        const bool up = (lo & size) == 0;
-        const uint64_t x = sorted[lo], y = sorted[hi];
-        if ((x > y) == up) {
-          sorted[lo] = y;
-          sorted[hi] = x;
+  if (nc <= kWave) {
+    // up to 64 chosen: wave 0 sorts them in registers (lane l holds entry l), a bitonic network over lane pairs
+    // exchanged by shuffles, with no workgroup barrier
+    if (wave == 0) {
+      uint64_t v = lane < nc ? sorted[lane] : ~0ull;
+#pragma unroll
+      for (int size = 2; size <= kWave; size <<= 1)
+#pragma unroll
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+          const uint32_t olo = (uint32_t)__shfl_xor((int)(uint32_t)v, stride, kWave);
+          const uint32_t ohi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), stride, kWave);
+          const uint64_t o = ((uint64_t)ohi << 32) | olo;
+          const bool keep_min = ((lane & stride) == 0) == ((lane & size) == 0);  // lower lane of an ascending pair
+          v = keep_min ? (o < v ? o : v) : (o > v ? o : v);
         }
-      }
-      __syncthreads();
+      if (lane < nc) chosen[lane] = (int32_t)(uint32_t)v;
+      if (buckets_out && lane < top_b) buckets_out[(int64_t)b * top_b + lane] = lane < nc ? (int32_t)(uint32_t)v : -1;
     }
-  if (tid < nc) chosen[tid] = (int32_t)(uint32_t)sorted[tid];
-  if (buckets_out && tid < top_b) buckets_out[(int64_t)b * top_b + tid] = tid < nc ? (int32_t)(uint32_t)sorted[tid] : -1;
+    if (buckets_out)
+      for (int i = kWave + tid; i < top_b; i += 1024) buckets_out[(int64_t)b * top_b + i] = -1;
+  } else {
+    int n2 = 2;
+    while (n2 < nc) n2 <<= 1;
+    for (int i = nc + tid; i < n2; i += 1024) sorted[i] = ~0ull;
+    __syncthreads();
+    for (int size = 2; size <= n2; size <<= 1)
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int i = tid; i < (n2 >> 1); i += 1024) {
+          const int lo = 2 * i - (i & (stride - 1));
+          const int hi = lo + stride;
+          const bool up = (lo & size) == 0;
+          const uint64_t x = sorted[lo], y = sorted[hi];
+          if ((x > y) == up) {
+            sorted[lo] = y;
+            sorted[hi] = x;
+          }
+        }
+        __syncthreads();
+      }
+    if (tid < nc) chosen[tid] = (int32_t)(uint32_t)sorted[tid];
+    if (buckets_out && tid < top_b)
+      buckets_out[(int64_t)b * top_b + tid] = tid < nc ? (int32_t)(uint32_t)sorted[tid] : -1;
+  }
   __syncthreads();
 
   // ---- expansion
