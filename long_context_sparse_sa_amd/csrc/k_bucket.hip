@@ -22,6 +22,26 @@ constexpr int kChunkMin = 4096;
 constexpr int64_t kTableBudget = 1 << 24;  // entries of the (chunk x bucket) table
 constexpr int kMaxExpand = 16384;
 constexpr int kBinMax = 16;  // entries per position bin sorted in registers by the expansion
+constexpr int kFastCand = 256;  // candidates ranked directly when the first digit pass leaves at most this many
+
+// Ascending sort of the n <= N entries at src into dst by an odd-even transposition network in registers.
+template <int N>
+__device__ __forceinline__ void sort_bin(const int32_t* src, int n, int32_t* dst) {
+  int32_t e[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) e[i] = i < n ? src[i] : 0x7FFFFFFF;
+#pragma unroll
+  for (int r = 0; r < N; ++r)
+#pragma unroll
+    for (int i = r & 1; i + 1 < N; i += 2) {
+      const int32_t x = e[i], y = e[i + 1];
+      e[i] = x < y ? x : y;
+      e[i + 1] = x < y ? y : x;
+    }
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    if (i < n) dst[i] = e[i];
+}
 
 __global__ void k_fill_i32(int32_t* p, int64_t n, int32_t v) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
@@ -195,12 +215,14 @@ __device__ __forceinline__ int lower_bound(const int32_t* a, int n, int32_t x) {
 
 // One workgroup per query: the choice of its top_b buckets, then their expansion.
 //
-// Choice: the query's slot keys (16 per thread in registers; a longer row is re-read per pass) go through three
-// LDS histogram passes (digits 31..21, 20..10, 9..0 of the key) that find kstar, the top_b-th largest non-empty
-// slot. Chosen are the slots above kstar and, among the slots equal to it, the lowest bucket ids (an id limit is
-// searched only when there are more ties than places left). With fewer than top_b non-empty buckets every one is
-// chosen. The chosen (key, id) pairs are sorted into rank order (score desc, id asc) by a bitonic sort (in one
-// wave's registers when at most 64 are chosen).
+// Choice: the query's slot keys (16 per thread in registers; a longer row is re-read per pass) go through an LDS
+// histogram of their top 11 bits, which gives the bin of the top_b-th largest non-empty slot. When that bin and
+// the bins above it hold at most kFastCand slots (the usual case: the top of the score distribution is thin),
+// those candidates are collected and each one's rank in (score desc, id asc) order is counted directly. Otherwise
+// two more passes (digits 20..10 and 9..0) find kstar, the top_b-th largest key; chosen are the slots above kstar
+// and, among the slots equal to it, the lowest bucket ids (an id limit is searched only when there are more ties
+// than places left), sorted into rank order by a bitonic sort (in one wave's registers when at most 64 are
+// chosen). With fewer than top_b non-empty buckets every one is chosen.
 __global__ __launch_bounds__(1024) void k_choose_expand(const uint32_t* __restrict__ keys, int nb, int top_b,
                                                         int32_t* __restrict__ buckets_out,
                                                         const int32_t* __restrict__ offsets,
@@ -254,7 +276,9 @@ __global__ __launch_bounds__(1024) void k_choose_expand(const uint32_t* __restri
   uint32_t* hist = reinterpret_cast<uint32_t*>(tmp);  // tmp is free until the expansion sorts
   uint32_t need = (uint32_t)top_b, prefix = 0u, pmask = 0u;
   int n_valid = 0;
-  bool full = true;  // at least top_b non-empty buckets
+  bool full = true;   // at least top_b non-empty buckets
+  bool fast = false;  // the candidates of the first pass are ranked directly
+  uint32_t fast_lo = 0u;
   for (int pass = 0; pass < 3; ++pass) {
     const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
     const int nbins = pass == 2 ? 1024 : 2048;
@@ -281,83 +305,110 @@ __global__ __launch_bounds__(1024) void k_choose_expand(const uint32_t* __restri
         full = false;
         break;
       }
+      if (sel_before + hist[sel_digit] <= (uint32_t)kFastCand) {  // block-uniform
+        fast = true;
+        fast_lo = sel_digit << 21;  // the candidates: keys whose top 11 bits are at least the digit
+        break;
+      }
     }
     prefix |= sel_digit << shift;
     pmask |= (uint32_t)(nbins - 1) << shift;
     need -= sel_before;
     __syncthreads();
   }
-  const uint32_t kstar = prefix;  // with full: chosen = slots above kstar + `need` of the slots equal to it
   const int nc = full ? top_b : n_valid;
-  uint32_t id_lim = 0xFFFFFFFFu;  // slots equal to kstar are chosen when their id is below this
-  if (full) {
-    int my_ties = 0, n_ties;
-    for_keys([&](int, uint32_t v) { my_ties += v == kstar ? 1 : 0; });
-    block_scan(my_ties, &n_ties);
-    if ((uint32_t)n_ties > need) {  // block-uniform: the smallest limit that admits `need` ties
-      int lo = 0, hi = nb;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        int mine = 0, cnt;
-        for_keys([&](int i, uint32_t v) { mine += (v == kstar && i < mid) ? 1 : 0; });
-        block_scan(mine, &cnt);
-        if ((uint32_t)cnt >= need) hi = mid;
-        else lo = mid + 1;
-      }
-      id_lim = (uint32_t)lo;
-    }
-  }
-  // the chosen (key, id) pairs, unordered, then sorted: ascending (~key, id) = score desc, id asc
   uint64_t* sorted = reinterpret_cast<uint64_t*>(buf);  // buf is free until the expansion
-  if (tid == 0) sel_n = 0u;
-  __syncthreads();
-  for_keys([&](int i, uint32_t v) {
-    const bool take = full ? (v > kstar || (v == kstar && (uint32_t)i < id_lim)) : v != 0u;
-    if (take) sorted[atomicAdd(&sel_n, 1u)] = ((uint64_t)~v << 32) | (uint32_t)i;
-  });
-  __syncthreads();
-  if (nc <= kWave) {
-    // up to 64 chosen: wave 0 sorts them in registers (lane l holds entry l), a bitonic network over lane pairs
-    // exchanged by shuffles, with no workgroup barrier
-    if (wave == 0) {
-      uint64_t v = lane < nc ? sorted[lane] : ~0ull;
-#pragma unroll
-      for (int size = 2; size <= kWave; size <<= 1)
-#pragma unroll
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-          const uint32_t olo = (uint32_t)__shfl_xor((int)(uint32_t)v, stride, kWave);
-          const uint32_t ohi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), stride, kWave);
-          const uint64_t o = ((uint64_t)ohi << 32) | olo;
-          const bool keep_min = ((lane & stride) == 0) == ((lane & size) == 0);  // lower lane of an ascending pair
-          v = keep_min ? (o < v ? o : v) : (o > v ? o : v);
-        }
-      if (lane < nc) chosen[lane] = (int32_t)(uint32_t)v;
-      if (buckets_out && lane < top_b) buckets_out[(int64_t)b * top_b + lane] = lane < nc ? (int32_t)(uint32_t)v : -1;
-    }
-    if (buckets_out)
-      for (int i = kWave + tid; i < top_b; i += 1024) buckets_out[(int64_t)b * top_b + i] = -1;
-  } else {
-    int n2 = 2;
-    while (n2 < nc) n2 <<= 1;
-    for (int i = nc + tid; i < n2; i += 1024) sorted[i] = ~0ull;
+  if (fast) {
+    // the n <= kFastCand candidates as ascending (~key, id) = score desc, id asc; the rank of each is the number
+    // of candidates before it, and ranks below top_b are the chosen buckets in rank order
+    if (tid == 0) sel_n = 0u;
     __syncthreads();
-    for (int size = 2; size <= n2; size <<= 1)
-      for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        for (int i = tid; i < (n2 >> 1); i += 1024) {
-          const int lo = 2 * i - (i & (stride - 1));
-          const int hi = lo + stride;
-          const bool up = (lo & size) == 0;
-          const uint64_t x = sorted[lo], y = sorted[hi];
-          if ((x > y) == up) {
-            sorted[lo] = y;
-            sorted[hi] = x;
-          }
-        }
-        __syncthreads();
+    for_keys([&](int i, uint32_t v) {
+      if (v != 0u && v >= fast_lo) sorted[atomicAdd(&sel_n, 1u)] = ((uint64_t)~v << 32) | (uint32_t)i;
+    });
+    __syncthreads();
+    const int n = (int)sel_n;
+    if (tid < n) {
+      const uint64_t me = sorted[tid];
+      int r = 0;
+#pragma unroll 8
+      for (int j = 0; j < n; ++j) r += sorted[j] < me ? 1 : 0;
+      if (r < top_b) {
+        chosen[r] = (int32_t)(uint32_t)me;
+        if (buckets_out) buckets_out[(int64_t)b * top_b + r] = (int32_t)(uint32_t)me;
       }
-    if (tid < nc) chosen[tid] = (int32_t)(uint32_t)sorted[tid];
-    if (buckets_out && tid < top_b)
-      buckets_out[(int64_t)b * top_b + tid] = tid < nc ? (int32_t)(uint32_t)sorted[tid] : -1;
+    }
+  } else {
+    const uint32_t kstar = prefix;  // with full: chosen = slots above kstar + `need` of the slots equal to it
+    uint32_t id_lim = 0xFFFFFFFFu;  // slots equal to kstar are chosen when their id is below this
+    if (full) {
+      int my_ties = 0, n_ties;
+      for_keys([&](int, uint32_t v) { my_ties += v == kstar ? 1 : 0; });
+      block_scan(my_ties, &n_ties);
+      if ((uint32_t)n_ties > need) {  // block-uniform: the smallest limit that admits `need` ties
+        int lo = 0, hi = nb;
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          int mine = 0, cnt;
+          for_keys([&](int i, uint32_t v) { mine += (v == kstar && i < mid) ? 1 : 0; });
+          block_scan(mine, &cnt);
+          if ((uint32_t)cnt >= need) hi = mid;
+          else lo = mid + 1;
+        }
+        id_lim = (uint32_t)lo;
+      }
+    }
+    // the chosen (key, id) pairs, unordered, then sorted: ascending (~key, id) = score desc, id asc
+    if (tid == 0) sel_n = 0u;
+    __syncthreads();
+    for_keys([&](int i, uint32_t v) {
+      const bool take = full ? (v > kstar || (v == kstar && (uint32_t)i < id_lim)) : v != 0u;
+      if (take) sorted[atomicAdd(&sel_n, 1u)] = ((uint64_t)~v << 32) | (uint32_t)i;
+    });
+    __syncthreads();
+    if (nc <= kWave) {
+      // up to 64 chosen: wave 0 sorts them in registers (lane l holds entry l), a bitonic network over lane pairs
+      // exchanged by shuffles, with no workgroup barrier
+      if (wave == 0) {
+        uint64_t v = lane < nc ? sorted[lane] : ~0ull;
+#pragma unroll
+        for (int size = 2; size <= kWave; size <<= 1)
+#pragma unroll
+          for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            const uint32_t olo = (uint32_t)__shfl_xor((int)(uint32_t)v, stride, kWave);
+            const uint32_t ohi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), stride, kWave);
+            const uint64_t o = ((uint64_t)ohi << 32) | olo;
+            const bool keep_min = ((lane & stride) == 0) == ((lane & size) == 0);  // lower lane of an ascending pair
+            v = keep_min ? (o < v ? o : v) : (o > v ? o : v);
+          }
+        if (lane < nc) chosen[lane] = (int32_t)(uint32_t)v;
+        if (buckets_out && lane < top_b) buckets_out[(int64_t)b * top_b + lane] = lane < nc ? (int32_t)(uint32_t)v : -1;
+      }
+      if (buckets_out)
+        for (int i = kWave + tid; i < top_b; i += 1024) buckets_out[(int64_t)b * top_b + i] = -1;
+    } else {
+      int n2 = 2;
+      while (n2 < nc) n2 <<= 1;
+      for (int i = nc + tid; i < n2; i += 1024) sorted[i] = ~0ull;
+      __syncthreads();
+      for (int size = 2; size <= n2; size <<= 1)
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+          for (int i = tid; i < (n2 >> 1); i += 1024) {
+            const int lo = 2 * i - (i & (stride - 1));
+            const int hi = lo + stride;
+            const bool up = (lo & size) == 0;
+            const uint64_t x = sorted[lo], y = sorted[hi];
+            if ((x > y) == up) {
+              sorted[lo] = y;
+              sorted[hi] = x;
+            }
+          }
+          __syncthreads();
+        }
+      if (tid < nc) chosen[tid] = (int32_t)(uint32_t)sorted[tid];
+      if (buckets_out && tid < top_b)
+        buckets_out[(int64_t)b * top_b + tid] = tid < nc ? (int32_t)(uint32_t)sorted[tid] : -1;
+    }
   }
   __syncthreads();
 
@@ -447,21 +498,10 @@ __global__ __launch_bounds__(1024) void k_choose_expand(const uint32_t* __restri
       tmp[atomicAdd(&bin_cur[bin_of(v)], 1)] = v;
     }
     __syncthreads();
-    int32_t e[kBinMax];
-#pragma unroll
-    for (int i = 0; i < kBinMax; ++i) e[i] = i < my_cnt ? tmp[my_start + i] : 0x7FFFFFFF;
-    // odd-even transposition sort of the bin in registers
-#pragma unroll
-    for (int r = 0; r < kBinMax; ++r)
-#pragma unroll
-      for (int i = r & 1; i + 1 < kBinMax; i += 2) {
-        const int32_t x = e[i], y = e[i + 1];
-        e[i] = x < y ? x : y;
-        e[i + 1] = x < y ? y : x;
-      }
-#pragma unroll
-    for (int i = 0; i < kBinMax; ++i)
-      if (i < my_cnt) out[my_start + i] = e[i];
+    // each bin sorted in registers, by a network as wide as the fullest bin of the wave needs
+    if (ballot(my_cnt > 8)) sort_bin<kBinMax>(tmp + my_start, my_cnt, out + my_start);
+    else if (ballot(my_cnt > 4)) sort_bin<8>(tmp + my_start, my_cnt, out + my_start);
+    else sort_bin<4>(tmp + my_start, my_cnt, out + my_start);
   } else {
     int n2 = 1;
     while (n2 < total) n2 <<= 1;

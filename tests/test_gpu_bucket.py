@@ -162,3 +162,31 @@ def test_choice_ties_long_rows_and_few_nonempty():
         np.testing.assert_array_equal(got[:10], ref_chosen)
         assert np.all(got[10:] == -1)
         np.testing.assert_array_equal(selected(idx2[b], nsel2[b].item()), np.arange(L2))
+
+
+@pytest.mark.parametrize("n_mid", [100, 1000])
+def test_choice_first_bin_candidates(n_mid):
+    """Singleton buckets with exact scores: 20 at 6.0, n_mid at 4.25 / 4.5 / 4.75 (heavy ties), the rest at 1.0.
+    With top_b = 32 the 32nd score lies in the bin [4, 5) of the first digit pass, which then holds 20 + n_mid
+    candidates: few enough to be ranked directly (100), or too many (1000), so that the remaining digit passes and
+    the tie limit decide. Either way the chosen ids, in rank order (score desc, id asc), match the oracle."""
+    L, d, nb, top = 3000, 4, 3000, 32
+    rng = np.random.default_rng(7 + n_mid)
+    vals = np.full(L, 1.0)
+    ids = rng.permutation(L)
+    vals[ids[:20]] = 6.0
+    vals[ids[20:20 + n_mid]] = rng.choice([4.25, 4.5, 4.75], n_mid)
+    k_np = np.zeros((L, d), dtype=np.float32)
+    k_np[:, 0] = vals
+    k = torch.as_tensor(k_np, device=DEV)
+    q = torch.tensor([[1.0, 0, 0, 0], [2.0, 0, 0, 0]], device=DEV)
+    assign = torch.arange(L, dtype=torch.int32, device=DEV)
+    reps, offsets, members = sa.sa_bucket_build(k, assign, nb)
+    idx, nsel, buckets = sa.sa_bucket_select(q, reps, offsets, members, L, top, 0, 0, cap=64, return_buckets=True)
+    torch.cuda.synchronize()
+    qf = q.double().cpu().numpy()
+    r32, off, mem = reps.cpu().numpy(), offsets.cpu().numpy().astype(np.int64), members.cpu().numpy().astype(np.int64)
+    for b in range(2):
+        ref_pos, ref_chosen, sc = O.bucket_select(qf[b], r32, off, mem, L - 1, top, 0, 0)
+        np.testing.assert_array_equal(buckets[b].cpu().numpy(), ref_chosen)
+        np.testing.assert_array_equal(selected(idx[b], nsel[b].item()), ref_pos)
