@@ -153,40 +153,86 @@ __global__ __launch_bounds__(256) void k_bucket_scores(const void* __restrict__ 
                                                        const int32_t* __restrict__ offsets, int nb,
                                                        uint32_t* __restrict__ keys) {
   extern __shared__ __attribute__((aligned(16))) float qs[];  // [B * d]
-  for (int i = threadIdx.x; i < B * d; i += blockDim.x) qs[i] = load_elem<QT>(q, i);
-  __syncthreads();
   // four lanes per bucket, sixteen buckets per wave: each lane takes every fourth group of four dims of its
   // bucket's representative, keeps it for all queries, and the four partial dot products meet in two lane swaps
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int qtr = lane & 3;
   const int bucket = (blockIdx.x * 4 + wave) * 16 + (lane >> 2);
   const bool in = bucket < nb;
-  const bool valid = in && offsets[bucket + 1] > offsets[bucket];
-  const float* r = reps + (int64_t)(in ? bucket : 0) * d;
+  const int bc = in ? bucket : 0;  // loads clamped to bucket 0 rather than predicated (no branch around them)
+  const int32_t o0 = offsets[bc], o1 = offsets[bc + 1];
+  const float* r = reps + (int64_t)bc * d;
+  // for d a multiple of 16 up to 16 * kRepRegs the lane's slice (dims 16 c + 4 qtr .. + 3) is loaded into registers
+  // here, before the queries are staged, so that the two loads overlap
+  constexpr int kRepRegs = 16;
+  const bool in_regs = (d & 15) == 0 && d <= 16 * kRepRegs;
+  float4 rv[kRepRegs];
+#pragma unroll
+  for (int c = 0; c < kRepRegs; ++c)
+    rv[c] = *reinterpret_cast<const float4*>(r + (in_regs && 16 * c < d ? 16 * c + 4 * qtr : 0));
+  // the queries into LDS: up to kStageRegs elements per thread are all loaded before any is stored, so their
+  // latencies overlap
+  constexpr int kStageRegs = 16;
+  const int n_q = B * d;
+  if (n_q <= kStageRegs * (int)blockDim.x) {
+    float v[kStageRegs];
+#pragma unroll
+    for (int m = 0; m < kStageRegs; ++m) {
+      const int i = threadIdx.x + m * blockDim.x;
+      v[m] = load_elem<QT>(q, i < n_q ? i : n_q - 1);  // clamped, not predicated: no branch, no wait per load
+    }
+#pragma unroll
+    for (int m = 0; m < kStageRegs; ++m) {
+      const int i = threadIdx.x + m * blockDim.x;
+      if (i < n_q) qs[i] = v[m];
+    }
+  } else {
+    for (int i = threadIdx.x; i < n_q; i += blockDim.x) qs[i] = load_elem<QT>(q, i);
+  }
+  __syncthreads();
   for (int b0 = 0; b0 < B; b0 += 8) {
     float acc[8];
+    const float* qrow[8];  // rows past the last query repeat it; their sums are not stored (no branches inside)
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc[u] = 0.f;
-    if ((d & 3) == 0) {
+    for (int u = 0; u < 8; ++u) {
+      acc[u] = 0.f;
+      qrow[u] = qs + (b0 + u < B ? b0 + u : B - 1) * d;
+    }
+    if (in_regs) {
+#pragma unroll
+      for (int c = 0; c < kRepRegs; ++c) {
+        if (16 * c < d) {
+          float4 qv[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) qv[u] = *reinterpret_cast<const float4*>(qrow[u] + 16 * c + 4 * qtr);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            acc[u] = fmaf(qv[u].x, rv[c].x, acc[u]);
+            acc[u] = fmaf(qv[u].y, rv[c].y, acc[u]);
+            acc[u] = fmaf(qv[u].z, rv[c].z, acc[u]);
+            acc[u] = fmaf(qv[u].w, rv[c].w, acc[u]);
+          }
+        }
+      }
+    } else if ((d & 3) == 0) {
+#pragma unroll 4
       for (int x = 4 * qtr; x < d; x += 16) {
         const float4 rv = *reinterpret_cast<const float4*>(r + x);
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          if (b0 + u < B) {
-            const float4 qv = *reinterpret_cast<const float4*>(qs + (b0 + u) * d + x);
-            acc[u] = fmaf(qv.x, rv.x, acc[u]);
-            acc[u] = fmaf(qv.y, rv.y, acc[u]);
-            acc[u] = fmaf(qv.z, rv.z, acc[u]);
-            acc[u] = fmaf(qv.w, rv.w, acc[u]);
-          }
+          const float4 qv = *reinterpret_cast<const float4*>(qrow[u] + x);
+          acc[u] = fmaf(qv.x, rv.x, acc[u]);
+          acc[u] = fmaf(qv.y, rv.y, acc[u]);
+          acc[u] = fmaf(qv.z, rv.z, acc[u]);
+          acc[u] = fmaf(qv.w, rv.w, acc[u]);
         }
       }
     } else {
+#pragma unroll 4
       for (int x = qtr; x < d; x += 4) {
         const float rv = r[x];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (b0 + u < B) acc[u] = fmaf(qs[(b0 + u) * d + x], rv, acc[u]);
+        for (int u = 0; u < 8; ++u) acc[u] = fmaf(qrow[u][x], rv, acc[u]);
       }
     }
 #pragma unroll
@@ -197,7 +243,7 @@ __global__ __launch_bounds__(256) void k_bucket_scores(const void* __restrict__ 
     if (qtr == 0 && in) {
 #pragma unroll
       for (int u = 0; u < 8; ++u)
-        if (b0 + u < B) keys[(int64_t)(b0 + u) * nb + bucket] = valid ? score_key(acc[u]) : 0u;
+        if (b0 + u < B) keys[(int64_t)(b0 + u) * nb + bucket] = o1 > o0 ? score_key(acc[u]) : 0u;
     }
   }
 }
