@@ -120,14 +120,63 @@ __device__ __forceinline__ Chunk chunk_of(int64_t L, int64_t chunk) {
   return c;
 }
 
-// Four keys at s (a multiple of 4; the row is padded to a multiple of 4 so the vector load stays inside it);
-// entries at or past s1 read as 0.
-__device__ __forceinline__ void load4(const uint32_t* __restrict__ row, int64_t s, int64_t s1, uint32_t (&v)[4]) {
-  const uint4 x = *reinterpret_cast<const uint4*>(row + s);
-  v[0] = s + 0 < s1 ? x.x : 0u;
-  v[1] = s + 1 < s1 ? x.y : 0u;
-  v[2] = s + 2 < s1 ? x.z : 0u;
-  v[3] = s + 3 < s1 ? x.w : 0u;
+// Key scans. A chunk is read in batches of 4 * kRThreads keys, four per thread (s a multiple of 4; the row is
+// padded to a multiple of 4 so the vector load stays inside it). Loads are never predicated: an address past the
+// chunk's end is clamped to the chunk's start and the value masked to 0 afterwards, so that all loads of a round
+// are in flight together (a load under a branch makes the compiler wait for it at the branch's end). The first
+// kPre batches are issued at kernel entry, before the record and histogram reads that precede the scan; later
+// batches go kRound per round trip. A chunk of at most kPre batches (the usual size) needs no second round.
+constexpr int kBatch = 4 * kRThreads;
+constexpr int kPre = 2;
+constexpr int kRound = 8;
+
+__device__ __forceinline__ uint4 load_batch(const uint32_t* __restrict__ row, const Chunk& c, int64_t bs) {
+  const int64_t s = bs + 4 * (int64_t)threadIdx.x;
+  return *reinterpret_cast<const uint4*>(row + (s < c.s1 ? s : c.s0));
+}
+__device__ __forceinline__ void unpack(const uint4& x, const Chunk& c, int64_t bs, uint32_t (&v)[4]) {
+  const int64_t s = bs + 4 * (int64_t)threadIdx.x;
+  v[0] = s + 0 < c.s1 ? x.x : 0u;
+  v[1] = s + 1 < c.s1 ? x.y : 0u;
+  v[2] = s + 2 < c.s1 ? x.z : 0u;
+  v[3] = s + 3 < c.s1 ? x.w : 0u;
+}
+struct PreKeys {
+  uint4 x[kPre];
+};
+__device__ __forceinline__ PreKeys preload(const uint32_t* __restrict__ row, const Chunk& c) {
+  PreKeys p;
+#pragma unroll
+  for (int h = 0; h < kPre; ++h) p.x[h] = load_batch(row, c, c.s0 + (int64_t)h * kBatch);
+  return p;
+}
+// f(bs, v) for every batch of the chunk in order (block-uniform calls: f may hold barriers).
+template <typename F>
+__device__ __forceinline__ void scan_chunk(const uint32_t* __restrict__ row, const Chunk& c, const PreKeys& p,
+                                           F&& f) {
+#pragma unroll
+  for (int h = 0; h < kPre; ++h) {
+    const int64_t bs = c.s0 + (int64_t)h * kBatch;
+    if (bs < c.s1) {
+      uint32_t v[4];
+      unpack(p.x[h], c, bs, v);
+      f(bs, v);
+    }
+  }
+  for (int64_t base = c.s0 + (int64_t)kPre * kBatch; base < c.s1; base += (int64_t)kRound * kBatch) {
+    uint4 x[kRound];
+#pragma unroll
+    for (int u = 0; u < kRound; ++u) x[u] = load_batch(row, c, base + (int64_t)u * kBatch);
+#pragma unroll
+    for (int u = 0; u < kRound; ++u) {
+      const int64_t bs = base + (int64_t)u * kBatch;
+      if (bs < c.s1) {
+        uint32_t v[4];
+        unpack(x[u], c, bs, v);
+        f(bs, v);
+      }
+    }
+  }
 }
 
 template <int PASS>
@@ -139,6 +188,9 @@ __global__ __launch_bounds__(kRThreads) void k_radix_hist(const uint32_t* __rest
   constexpr int nb = PASS == 2 ? 1024 : 2048;
   constexpr int shift = PASS == 0 ? 21 : (PASS == 1 ? 10 : 0);
   uint32_t* rec = recs + (size_t)b * kRecWords;
+  const Chunk c = chunk_of(L, chunk);
+  const uint32_t* row = keys + (int64_t)b * keys_ld;
+  const PreKeys pre = preload(row, c);
   for (int i = tid; i < kRBins; i += kRThreads) sh.hist[i] = 0u;
   uint32_t prefix = 0u, pmask = 0u;
   if (PASS == 1) {
@@ -162,15 +214,11 @@ __global__ __launch_bounds__(kRThreads) void k_radix_hist(const uint32_t* __rest
     pmask = (0x7FFu << 21) | (0x7FFu << 10);
   }
   __syncthreads();
-  const Chunk c = chunk_of(L, chunk);
-  const uint32_t* row = keys + (int64_t)b * keys_ld;
-  for (int64_t s = c.s0 + 4 * tid; s < c.s1; s += 4 * kRThreads) {
-    uint32_t v[4];
-    load4(row, s, c.s1, v);
+  scan_chunk(row, c, pre, [&](int64_t, const uint32_t (&v)[4]) {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       if (v[e] != 0u && (v[e] & pmask) == prefix) atomicAdd(&sh.hist[(v[e] >> shift) & (nb - 1)], 1u);
-  }
+  });
   __syncthreads();
   uint32_t* g = hist + ((size_t)PASS * B + b) * kRBins;
   for (int i = tid; i < nb; i += kRThreads) {
@@ -186,6 +234,9 @@ __global__ __launch_bounds__(kRThreads) void k_radix_count(const uint32_t* __res
   __shared__ RadixShared sh;
   const int b = blockIdx.y, tid = threadIdx.x;
   uint32_t* rec = recs + (size_t)b * kRecWords;
+  const Chunk c = chunk_of(L, chunk);
+  const uint32_t* row = keys + (int64_t)b * keys_ld;
+  const PreKeys pre = preload(row, c);
   KStar ks{rec[kRecOk] != 0u, 0u, 0u, rec[kRecNCand]};
   if (ks.ok) {
     const uint32_t need = (uint32_t)k - rec[kRecB0] - rec[kRecB1];
@@ -196,18 +247,14 @@ __global__ __launch_bounds__(kRThreads) void k_radix_count(const uint32_t* __res
   }
   store_rec(rec, kRecKStar, ks.kstar);
   store_rec(rec, kRecNeedEq, ks.need_eq);
-  const Chunk c = chunk_of(L, chunk);
-  const uint32_t* row = keys + (int64_t)b * keys_ld;
   uint32_t gt = 0, eq = 0;
-  for (int64_t s = c.s0 + 4 * tid; s < c.s1; s += 4 * kRThreads) {
-    uint32_t v[4];
-    load4(row, s, c.s1, v);
+  scan_chunk(row, c, pre, [&](int64_t, const uint32_t (&v)[4]) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       gt += v[e] > ks.kstar ? 1u : 0u;
       eq += (ks.ok && v[e] == ks.kstar) ? 1u : 0u;
     }
-  }
+  });
   uint32_t tg, te;
   block_excl_scan(sh, gt, &tg);
   block_excl_scan(sh, eq, &te);
@@ -228,6 +275,9 @@ __global__ __launch_bounds__(kRThreads) void k_radix_write(const uint32_t* __res
   const int b = blockIdx.y, j = blockIdx.x, tid = threadIdx.x;
   const int G = gridDim.x;
   const uint32_t* rec = recs + (size_t)b * kRecWords;
+  const Chunk c = chunk_of(L, chunk);
+  const uint32_t* row = keys + (int64_t)b * keys_ld;
+  const PreKeys pre = preload(row, c);
   const KStar ks{rec[kRecOk] != 0u, rec[kRecKStar], rec[kRecNeedEq], rec[kRecNCand]};
   // counts of the chunks before this one
   const uint32_t* cb = cnt + (int64_t)b * G * 2;
@@ -251,14 +301,9 @@ __global__ __launch_bounds__(kRThreads) void k_radix_write(const uint32_t* __res
     if (kp) kp[r] = Cand{key, (int32_t)pos};
   };
 
-  const Chunk c = chunk_of(L, chunk);
-  const uint32_t* row = keys + (int64_t)b * keys_ld;
   uint32_t run_gt = 0, run_eq = 0;  // entries of this chunk before the current batch
-  for (int64_t base = c.s0; base < c.s1; base += 4 * kRThreads) {
+  scan_chunk(row, c, pre, [&](int64_t base, const uint32_t (&v)[4]) {
     const int64_t s = base + 4 * tid;
-    uint32_t v[4];
-    if (s < c.s1) load4(row, s, c.s1, v);
-    else v[0] = v[1] = v[2] = v[3] = 0u;
     bool g[4], t[4];
     uint32_t lg = 0, lt = 0;
 #pragma unroll
@@ -283,7 +328,7 @@ __global__ __launch_bounds__(kRThreads) void k_radix_write(const uint32_t* __res
     }
     run_gt += tot >> 16;
     run_eq += tot & 0xFFFFu;
-  }
+  });
   if (j == 0) {
     const int take = ks.ok ? k : (int)ks.n_cand;
     if (out)
