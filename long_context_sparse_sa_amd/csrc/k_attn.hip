@@ -544,28 +544,44 @@ __global__ __launch_bounds__(kCombineThreads) void k_attn_combine(const float* _
   const bool act = dv < d_v;
   const float* ml = part_ml + bh * n_splits * 2;
   const float* po = part_o + bh * n_splits * d_v + (act ? dv : 0);
+  // the first kCombineBatch splits' partials and (max, sum) pairs, all requested before any is used: indices past
+  // the last split are clamped to it (loads are never predicated, so that they stay in flight together) and the
+  // duplicates are skipped below
   f32x4 v[kCombineBatch];
+  float mv[kCombineBatch], lv[kCombineBatch];
 #pragma unroll
-  for (int u = 0; u < kCombineBatch; ++u)
-    v[u] = act && u < n_splits ? *reinterpret_cast<const f32x4*>(po + (int64_t)u * d_v) : f32x4{};
+  for (int u = 0; u < kCombineBatch; ++u) {
+    const int i = u < n_splits ? u : n_splits - 1;
+    v[u] = *reinterpret_cast<const f32x4*>(po + (int64_t)i * d_v);
+    mv[u] = ml[2 * i];
+    lv[u] = ml[2 * i + 1];
+  }
   float M = -INFINITY;
-  for (int i = 0; i < n_splits; ++i) M = fmaxf(M, ml[2 * i]);
+#pragma unroll
+  for (int u = 0; u < kCombineBatch; ++u) M = u < n_splits ? fmaxf(M, mv[u]) : M;
+  for (int i = kCombineBatch; i < n_splits; ++i) M = fmaxf(M, ml[2 * i]);
   float Ls = 0.f;
   f32x4 acc = f32x4{};
   if (M != -INFINITY) {
-    for (int i = 0; i < n_splits; ++i) Ls += exp2f(ml[2 * i] - M) * ml[2 * i + 1];
-    for (int i0 = 0; i0 < n_splits; i0 += kCombineBatch) {
-      if (i0 > 0) {
 #pragma unroll
-        for (int u = 0; u < kCombineBatch; ++u)
-          v[u] = act && i0 + u < n_splits ? *reinterpret_cast<const f32x4*>(po + (int64_t)(i0 + u) * d_v) : f32x4{};
+    for (int u = 0; u < kCombineBatch; ++u) {
+      const float w = u < n_splits ? exp2f(mv[u] - M) : 0.f;
+      Ls += w * lv[u];
+      if (w > 0.f) acc += w * v[u];  // a split without rows has max -inf, weight 0, and unwritten partials
+    }
+    for (int i0 = kCombineBatch; i0 < n_splits; i0 += kCombineBatch) {
+#pragma unroll
+      for (int u = 0; u < kCombineBatch; ++u) {
+        const int i = i0 + u < n_splits ? i0 + u : n_splits - 1;
+        v[u] = *reinterpret_cast<const f32x4*>(po + (int64_t)i * d_v);
+        mv[u] = ml[2 * i];
+        lv[u] = ml[2 * i + 1];
       }
 #pragma unroll
       for (int u = 0; u < kCombineBatch; ++u) {
-        if (i0 + u < n_splits) {
-          const float w = exp2f(ml[2 * (i0 + u)] - M);
-          if (w > 0.f) acc += w * v[u];
-        }
+        const float w = i0 + u < n_splits ? exp2f(mv[u] - M) : 0.f;
+        Ls += w * lv[u];
+        if (w > 0.f) acc += w * v[u];
       }
     }
   }
