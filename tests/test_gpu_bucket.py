@@ -190,3 +190,30 @@ def test_choice_first_bin_candidates(n_mid):
         ref_pos, ref_chosen, sc = O.bucket_select(qf[b], r32, off, mem, L - 1, top, 0, 0)
         np.testing.assert_array_equal(buckets[b].cpu().numpy(), ref_chosen)
         np.testing.assert_array_equal(selected(idx[b], nsel[b].item()), ref_pos)
+
+
+def test_select_prefilled_workspace():
+    """The bucket search gives the same result whatever its workspace held before (all-ones bytes, a byte pattern,
+    zeros): every slot key it reads is written by the same call."""
+    wl, inp = _small_lsa(2)
+    reps, offsets, members = sa.sa_bucket_build(inp["k_idx"], inp["assign"], wl.n_buckets)
+    ws = torch.empty(1 << 22, dtype=torch.uint8, device=DEV)
+    res = []
+    for fill in (0xFF, 0x5A, 0x00):
+        ws.fill_(fill)
+        idx, nsel, buckets = sa.sa_bucket_select(inp["q_idx"], reps, offsets, members, wl.L, 32, 4, 128, cap=8192,
+                                                 return_buckets=True, ws=ws)
+        torch.cuda.synchronize()
+        res.append((idx.cpu(), nsel.cpu(), buckets.cpu()))
+    for r in res[1:]:
+        for a, b in zip(res[0], r):
+            assert torch.equal(a, b)
+    qf = to_f64(inp["q_idx"])
+    r32, off, mem = reps.cpu().numpy(), offsets.cpu().numpy().astype(np.int64), members.cpu().numpy().astype(np.int64)
+    ids = np.nonzero(np.diff(off) > 0)[0]
+    for b in range(wl.B):
+        ref_pos, ref_chosen, sc = O.bucket_select(qf[b], r32, off, mem, wl.L - 1, 32, 4, 128)
+        nband = band_compare(np.sort(res[0][2][b].numpy()), np.sort(ref_chosen), ids, sc[ids], 32)
+        if nband == 0:
+            np.testing.assert_array_equal(res[0][2][b].numpy(), ref_chosen)
+            np.testing.assert_array_equal(selected(res[0][0][b], res[0][1][b].item()), ref_pos)

@@ -211,3 +211,29 @@ def test_topk_radix_chunks_and_ties():
             assert np.unique(sc).size < sc.size / 4
         np.testing.assert_array_equal(selected(idx[b], nsel[b].item()), ref)
     assert nsel[2].item() == 2500 - 5 - 40 + 1
+
+
+@pytest.mark.parametrize("algo", ALGOS + [sa.SA_TOPK_AUTO])
+def test_topk_prefilled_workspace_and_outputs(algo):
+    """Whatever the workspace and the output buffers hold before the call (all-ones bytes, a byte pattern, zeros),
+    the selection is the same exact result: the kernels clear every counter, histogram and record they use, and idx
+    is overwritten in full, padding included. The calls run back to back on one workspace."""
+    B, H, d, L, kk, ld = 6, 64, 128, 40000, 700, 711
+    q, w, k = _inputs(5, B, H, d, L, "bf16", integer=True)
+    ts = [L - 1, 39000, 20000, 17000, 5000, 300]
+    t = torch.tensor(ts, dtype=torch.int32, device=DEV)
+    nbytes = sa.sa_select_topk_workspace(L, B, H, d, sa.SA_BF16, sa.SA_BF16, kk, algo)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=DEV)
+    qf, wf, kf = to_f64(q), w.double().cpu().numpy(), to_f64(k)
+    refs = [O.select_topk(qf[b], wf[b], kf, ts[b], kk, 3, 50)[0] for b in range(B)]
+    for fill in (0xFF, 0x5A, 0x00):
+        ws.fill_(fill)
+        idx = torch.full((B, ld), -7, dtype=torch.int32, device=DEV)
+        nsel = torch.full((B,), 12345, dtype=torch.int32, device=DEV)
+        sa.sa_select_topk(q, w, k, kk, n_sink=3, n_window=50, t=t, algo=algo, idx_ld=ld, ws=ws, out=(idx, nsel))
+        torch.cuda.synchronize()
+        for b in range(B):
+            n = nsel[b].item()
+            assert n == refs[b].size, (fill, b, n)
+            np.testing.assert_array_equal(selected(idx[b], n), refs[b])
+            assert torch.all(idx[b, n:] == -1), (fill, b)
