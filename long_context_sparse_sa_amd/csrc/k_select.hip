@@ -11,6 +11,8 @@
 //     when several candidates share it, radix passes over their positions keep the lowest ones.
 // Intermediate calls keep the k best and publish the k-th key as the next threshold. Bucket ranking (final_mode
 // 2) is the one caller that needs (key desc, position asc) order; it sorts its at most top_b ids in LDS.
+#include <atomic>
+
 #include "sa_device.h"
 #include "sa_internal.h"
 #include "sa_wave_select.h"
@@ -420,12 +422,16 @@ hipError_t launch_merge(int B, int k, const MergeIn& in, Cand* gather, int64_t g
   const int sort_bytes = out.final_mode == 2 ? 8 * n2 : 0;
   const int dyn = kLdsBytes - (int)sizeof(MergeShared) - 256;
   const int cap = (dyn - sort_bytes) / 8;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_merge),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, dyn);
+  // the dynamic LDS limit is raised once per device (host threads may race here: the call is idempotent)
+  static std::atomic<uint64_t> attr_set{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev >= 0 && dev < 64 ? 1ull << dev : 0ull;
+  if (bit == 0 || !(attr_set.load(std::memory_order_acquire) & bit)) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_merge), hipFuncAttributeMaxDynamicSharedMemorySize, dyn);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    attr_set.fetch_or(bit, std::memory_order_release);
   }
   hipLaunchKernelGGL(k_merge, dim3((unsigned)B), dim3(kMergeThreads), (size_t)dyn, st, k, in, gather, gather_cap,
                      out, cap);
