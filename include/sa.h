@@ -29,8 +29,10 @@
  *   - Arguments are validated on the host before any launch; a non-zero return means nothing was launched
  *     (except SA_ERR_HIP, which reports a failed launch). sa_last_error() gives a thread-local message.
  *   - Scratch memory ("workspace") is caller-owned device memory of at least the size the matching *_workspace
- *     query returns; the queries are pure host functions.
- *   - The library is stateless and thread-safe. Calls on different streams may overlap freely.
+ *     query returns; the queries are pure host functions. A workspace carries nothing from one call to the next:
+ *     its contents on entry do not matter, since the kernels clear whatever they accumulate into.
+ *   - The library is stateless and thread-safe. Calls on different streams may overlap, provided they share no
+ *     workspace and no output buffer.
  *   - `stream` is a hipStream_t passed as void*; NULL means the null stream.
  */
 #ifndef SA_H
