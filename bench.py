@@ -266,16 +266,20 @@ def cpu_baseline(wl, base, n_sample, min_seconds):
     else:
         kf = to_f64(base["k_idx"])
         qi, w = base["q_idx"], base["w"].double().cpu().numpy()
-    qi64 = [to_f64(qi[b]) for b in range(wl.B)]
-    q64 = [to_f64(q[b]) for b in range(wl.B)]
     prep = time.perf_counter() - t0
     ts = wl.t_positions()
     n = n_sample or (wl.B if wl.L <= 200_000 else 1)
     n = min(n, wl.B)
+    qi64, q64 = {}, {}  # per-query inputs decoded to fp64 on first use, outside the timed part
     done = 0
-    t0 = time.perf_counter()
+    dt = 0.0
     while True:
         b = done % n
+        if b not in q64:
+            t1 = time.perf_counter()
+            qi64[b], q64[b] = to_f64(qi[b]), to_f64(q[b])
+            prep += time.perf_counter() - t1
+        t0 = time.perf_counter()
         if wl.kind == "bucket":
             O.bucket_step(qi64[b], reps, off, mem, q64[b], kv, ts[b], wl.top_b, wl.n_sink, wl.n_window,
                           wl.softmax_scale, wl.d_qk, wl.d_v)
@@ -283,13 +287,15 @@ def cpu_baseline(wl, base, n_sample, min_seconds):
             O.dsa_step(qi64[b], w[b], kf, q64[b], kv, ts[b], wl.k_sparse, wl.n_sink, wl.n_window,
                        wl.softmax_scale, wl.d_qk, wl.d_v)
         done += 1
-        dt = time.perf_counter() - t0
+        dt += time.perf_counter() - t0
         if dt >= min_seconds:
             break
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    which = (f"queries 0..{done - 1} of {wl.name} ({wl.B} in all), each once" if done <= n else
+             f"queries 0..{n - 1} of {wl.name}, cycled: {done} query evaluations")
     return {"value": round(done / dt, 3), "unit": "queries/s", "cores": threads, "kind": "oracle",
-            "sample": f"queries 0..{n - 1} of {wl.name} cycled {done} times in total, full per-query path (score "
-                      f"all candidates, exact top-k, attention), fp64 numpy; {prep:.1f} s input decode not counted",
+            "sample": f"{which}; full per-query path (score all candidates, exact top-k, attention), fp64 numpy; "
+                      f"{prep:.1f} s input decode not counted",
             "seconds": round(dt, 2)}
 
 
