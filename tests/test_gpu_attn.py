@@ -141,3 +141,30 @@ def test_dense_reduction_bf16():
     """k >= |C|: reading every visible row equals dense softmax attention (oracle, fp64)."""
     L = 700
     _mfma_case(3, B=2, L=L, n_list=[L - 4 - 64] * 2, n_sink=4, n_window=64, d_v=576)
+
+
+@pytest.mark.parametrize("dtype,tol", [("bf16", 2e-2), ("f32", 1e-5)])
+def test_generic_separate_v(dtype, tol):
+    """A separate V cache (wider than K), several queries and heads, ragged read sets with t given: the generic
+    kernel against the oracle, and the lse within its own tolerance."""
+    B, H, d_qk, d_v, L = 4, 6, 64, 96, 3000
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    g = torch.Generator(device="cpu").manual_seed(21)
+    q = torch.randn((B, H, d_qk), generator=g).to(dt).to(DEV)
+    kv = torch.randn((L, d_qk), generator=g).to(dt).to(DEV)
+    v = torch.randn((L, d_v), generator=g).to(dt).to(DEV)
+    rng = np.random.default_rng(21)
+    ts = [L - 1, 1500, 40, 2999]
+    n_list = [300, 57, 0, 1000]
+    sels = [_rand_sparse(rng, ts[b], 3, 20, n_list[b]) for b in range(B)]
+    idx, nsel = _pack_idx(sels, max(n_list))
+    tt = torch.tensor(ts, dtype=torch.int32, device=DEV)
+    scale = 1 / math.sqrt(d_qk)
+    o, lse = sa.sa_sparse_attn(q, kv, idx, nsel, 3, 20, scale, t=tt, v=v, d_v=d_v, return_lse=True)
+    torch.cuda.synchronize()
+    qf, kvf, vf = to_f64(q), to_f64(kv), to_f64(v)
+    for b in range(B):
+        R = O.read_set(ts[b], 3, 20, sels[b])
+        oo, ol = O.sparse_attn(qf[b], kvf, R, scale, d_qk, d_v, v=vf)
+        np.testing.assert_allclose(o[b].double().cpu().numpy(), oo, atol=tol, rtol=0)
+        np.testing.assert_allclose(lse[b].double().cpu().numpy(), ol, atol=max(tol, 1e-4), rtol=0)
