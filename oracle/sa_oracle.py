@@ -27,7 +27,10 @@ Readings taken where the pages are silent:
   * a bucket representative is the fp64 mean of its member keys rounded once to fp32;
   * an empty read set yields o = 0 and lse = -inf.
 
-Every function below is pinned by tests under tests/ (test_oracle_*.py); none is "parity unpinned".
+Every function below is pinned by tests under tests/ (test_oracle_*.py) to something other than itself: the
+pages' printed eight-entry example, brute force on tiny inputs, closed forms, or a library routine on a special
+case. The two whole-step compositions (dsa_step, bucket_step) are pinned by routing the eight-entry example
+through them.
 """
 from __future__ import annotations
 
@@ -248,21 +251,25 @@ def merge_lse(parts):
 
 
 # ----------------------------------------------------------------------------------------------------------------
-# One decode/prefill step of the whole path for one query
+# One decode/prefill step of the whole path for one query: selection, read set, attention over it
 # ----------------------------------------------------------------------------------------------------------------
 
 
 def dsa_step(q_idx, w, k_idx, q, kv, t: int, k_sparse: int, n_sink: int, n_window: int, scale: float,
-             d_qk: int, d_v: int):
+             d_qk: int, d_v: int, v=None):
+    """Lightning-indexer top-k ([LongCat] DSA baseline section) plus sink and window ([LongCat] SI section), then
+    attention over the read set. Returns (ascending sparse positions, o [H, d_v], lse [H])."""
     sel, _, _ = select_topk(q_idx, w, k_idx, t, k_sparse, n_sink, n_window)
     R = read_set(t, n_sink, n_window, sel)
-    o, lse = sparse_attn(q, kv, R, scale, d_qk, d_v)
+    o, lse = sparse_attn(q, kv, R, scale, d_qk, d_v, v=v)
     return sel, o, lse
 
 
 def bucket_step(q_idx, reps32, offsets, members, q, kv, t: int, top_b: int, n_sink: int, n_window: int,
-                scale: float, d_qk: int, d_v: int):
+                scale: float, d_qk: int, d_v: int, v=None):
+    """Flat bucket search and expansion ([LSA-8] section 2, steps 3-4) plus sink and window, then attention over
+    the read set. Returns (ascending sparse positions, chosen bucket ids, o [H, d_v], lse [H])."""
     sel, chosen, _ = bucket_select(q_idx, reps32, offsets, members, t, top_b, n_sink, n_window)
     R = read_set(t, n_sink, n_window, sel)
-    o, lse = sparse_attn(q, kv, R, scale, d_qk, d_v)
+    o, lse = sparse_attn(q, kv, R, scale, d_qk, d_v, v=v)
     return sel, chosen, o, lse

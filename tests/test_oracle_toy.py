@@ -100,3 +100,41 @@ def test_lse_merge_of_the_two_buckets(toy):
     full = O.attention(q[None, :], K, V, SCALE)
     assert o[0, 0] == pytest.approx(g["derived"]["attn_dim0_full_read"], rel=1e-13)
     assert lse[0] == pytest.approx(full[1][0], rel=1e-14)
+
+
+def test_bucket_step_through_toy(toy):
+    """The whole Flat-bucket step (search, expansion, read set, attention) on the eight entries: bucket A alone gives
+    the printed 23.24, both buckets the printed 36.45, and q = (0, 1) picks bucket B (63.2422 by hand)."""
+    g, q, K, V = toy
+    reps, offsets, members = O.bucket_build(K, np.array([0, 0, 0, 0, 1, 1, 1, 1]), 2)
+    for qv, top_b, expect_pos, expect_chosen, key in [
+            ((1.0, 0.0), 1, [0, 1, 2, 3], [0], "attn_dim0_bucket_A_only"),
+            ((1.0, 0.0), 2, list(range(8)), [0, 1], "attn_dim0_full_read"),
+            ((0.0, 1.0), 1, [4, 5, 6, 7], [1], "attn_dim0_bucket_B_with_q_0_1")]:
+        qq = np.array(qv)
+        sel, chosen, o, lse = O.bucket_step(qq, reps, offsets, members, qq[None, :], K, 7, top_b, 0, 0, SCALE, 2,
+                                            2, v=V)
+        assert sel.tolist() == expect_pos and chosen.tolist() == expect_chosen
+        assert o[0, 0] == pytest.approx(g["derived"][key], rel=1e-13)
+        assert o[0, 1] == 0.0
+        # lse by hand: log of the sum of exp(q.k / sqrt(2)) over the rows read
+        assert lse[0] == pytest.approx(math.log(sum(math.exp(SCALE * float(np.dot(qq, K[s]))) for s in expect_pos)),
+                                       rel=1e-14)
+    # sink and window rows are read on top of the chosen bucket: sink {0} + window {7} + bucket A
+    sel, _, o, _ = O.bucket_step(q, reps, offsets, members, q[None, :], K, 7, 1, 1, 1, SCALE, 2, 2, v=V)
+    assert sel.tolist() == [1, 2, 3]
+    rows = [0, 1, 2, 3, 7]
+    z = np.array([SCALE * float(np.dot(q, K[s])) for s in rows])
+    e = np.exp(z - z.max())
+    assert o[0, 0] == pytest.approx(float(np.dot(e, V[rows, 0]) / e.sum()), rel=1e-13)
+
+
+def test_dsa_step_through_toy(toy):
+    """The whole DSA step with one indexer head (w = 1, q_idx = (1, 0)): top-4 reads bucket A (printed 23.24),
+    top-8 reads everything (printed 36.45)."""
+    g, q, K, V = toy
+    for k, key in [(4, "attn_dim0_bucket_A_only"), (8, "attn_dim0_full_read")]:
+        sel, o, lse = O.dsa_step(q[None, :], np.array([1.0]), K, q[None, :], K, 7, k, 0, 0, SCALE, 2, 2, v=V)
+        assert sel.tolist() == list(range(k))
+        assert o[0, 0] == pytest.approx(g["derived"][key], rel=1e-13)
+        assert abs(o[0, 0] - g["printed"][key]) < 0.005
