@@ -5,7 +5,6 @@ caller's), and calls the HIP library on torch's current stream. No step of the m
 """
 from __future__ import annotations
 
-import math
 from typing import Optional
 
 import torch
@@ -97,6 +96,28 @@ def sa_select_topk(q_idx, w, k_idx, k_sparse: int, n_sink: int = 0, n_window: in
     return idx, n_sel
 
 
+def sa_select_topk_scores(scores, k_sparse: int, n_sink: int = 0, n_window: int = 0, t=None,
+                          idx_ld: Optional[int] = None, ws=None, out=None, stream=None):
+    """(idx [B, idx_ld] ascending with -1 padding, n_sel [B]) of the top-k of caller-given fp32 scores [B, L]."""
+    _need_cuda(scores, t)
+    if scores.dtype != torch.float32 or scores.dim() != 2 or scores.stride(1) != 1:
+        raise ValueError("scores must be a 2-D fp32 tensor with unit column stride")
+    B, L = scores.shape
+    idx_ld = k_sparse if idx_ld is None else idx_ld
+    lib = _lib.load()
+    nbytes = lib.sa_select_topk_scores_workspace(L, B)
+    ws = _workspace(nbytes, scores.device, ws)
+    if out is None:
+        idx = torch.empty((B, idx_ld), dtype=torch.int32, device=scores.device)
+        n_sel = torch.empty((B,), dtype=torch.int32, device=scores.device)
+    else:
+        idx, n_sel = out
+    st = lib.sa_select_topk_scores(_ptr(scores), scores.stride(0), L, B, _ptr(t), k_sparse, n_sink, n_window,
+                                   _ptr(idx), idx.stride(0), _ptr(n_sel), _ptr(ws), nbytes, _stream(stream))
+    _lib.check("sa_select_topk_scores", st)
+    return idx, n_sel
+
+
 def sa_bucket_build(k_idx, assign, n_buckets: int, ws=None, stream=None):
     """(reps [NB, d] fp32, offsets [NB + 1] int32, members [L] int32) of the bucket directory."""
     _need_cuda(k_idx, assign)
@@ -136,16 +157,15 @@ def sa_sparse_attn_workspace(B, H, d_qk, d_v, max_rows, dtype) -> int:
     return int(_lib.load().sa_sparse_attn_workspace(B, H, d_qk, d_v, max_rows, dtype))
 
 
-def sa_sparse_attn(q, kv, idx=None, n_sel=None, n_sink: int = 0, n_window: int = 0, scale: Optional[float] = None,
-                   t=None, v=None, d_v: Optional[int] = None, return_lse: bool = False, ws=None, out=None,
-                   stream=None):
-    """o [B, H, d_v] (and lse [B, H]) of softmax attention over sink U window U idx[b, :n_sel[b]]."""
+def sa_sparse_attn(q, kv, idx, n_sel, n_sink: int, n_window: int, scale: float, t=None, v=None,
+                   d_v: Optional[int] = None, return_lse: bool = False, ws=None, out=None, stream=None):
+    """o [B, H, d_v] (and lse [B, H]) of softmax attention over sink U window U idx[b, :n_sel[b]] with logits
+    scale * q . K (the caller's scale; idx and n_sel may both be None for sink and window only)."""
     _need_cuda(q, kv, idx, n_sel, t, v)
     B, H, d_qk = q.shape
     L = kv.shape[0]
     if d_v is None:
         d_v = v.shape[1] if v is not None else d_qk
-    scale = 1.0 / math.sqrt(d_qk) if scale is None else scale
     idx_ld = idx.stride(0) if idx is not None else 0
     lib = _lib.load()
     max_rows = n_sink + n_window + idx_ld

@@ -9,10 +9,12 @@
 //  * k_attn_generic -- any widths, fp32 or bf16, one workgroup per (query, head), two passes (max/sum, then
 //    weighted V), fp32 throughout.
 //  * k_attn_mfma    -- bf16 latent of width 576 (V = first 512 or all 576 columns), 64 heads per workgroup
-//    (4 waves x 16 heads). Rows are gathered 32 at a time into LDS by asynchronous DMA (72 x 16-byte chunks per
-//    1152-byte row), S^T = K Q^T runs on 16x16x32 MFMA with the query heads register-resident, the online
-//    softmax runs in the log2 domain, and O^T = V^T P^T takes V through LDS transpose reads so that P never
-//    leaves registers. Rows are split over workgroups; k_attn_combine merges the splits by their (max, sum).
+//    (4 waves = 2 head blocks of 32 heads x 2 halves of the 576 dims). Rows are gathered 32 at a time into LDS
+//    by asynchronous DMA (72 x 16-byte chunks per 1152-byte row), S^T = K Q^T runs on the 32x32x16 bf16 MFMA with
+//    each wave's 32 query heads register-resident over its 288 dims (the two halves add their partial scores
+//    through LDS), the online softmax runs in the log2 domain, and O^T = V^T P^T takes V through LDS transpose
+//    reads so that P never leaves registers. Rows are split over workgroups; k_attn_combine merges the splits by
+//    their (max, sum).
 #include <math.h>
 
 #include "sa_device.h"
@@ -196,6 +198,10 @@ __device__ __forceinline__ i16x4 lds_read_tr16_at(uint32_t lds_addr) {
 __device__ __forceinline__ float halves_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_min(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float halves_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -415,17 +421,27 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
     for (int i = 0; i < kPrefV; ++i) vr[i] = v_frag(i);
 
     // register r of this lane holds row 8 (r / 4) + 4 hsel + r % 4 of head `head`. The softmax works on raw
-    // scores: log2-domain exponent = score * scale_log2 - m_use.
+    // scores: log2-domain exponent = score * scale_log2 - m_use. The tile's largest scaled score is the scale
+    // times the largest raw score, or times the smallest one when the scale is negative (a uniform choice).
+    // Rows past the split's end are pushed to the extreme that never wins, and their weights are zeroed below
+    // (so that a zero scale never meets an infinity).
+    const bool neg = scale_log2 < 0.f;
+    const int valid = decltype(partial)::value ? n_my - tile * kTileRows : kTileRows;
     if constexpr (decltype(partial)::value) {
-      const int valid = n_my - tile * kTileRows;
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (8 * (r >> 2) + 4 * hsel + (r & 3) >= valid) s[r] = -INFINITY;
+        if (8 * (r >> 2) + 4 * hsel + (r & 3) >= valid) s[r] = neg ? INFINITY : -INFINITY;
     }
     float mt = s[0];
+    if (!neg) {
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
-    mt = halves_max(mt);
+      for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
+      mt = halves_max(mt);
+    } else {
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mt = fminf(mt, s[r]);
+      mt = halves_min(mt);
+    }
     mt *= scale_log2;  // finite: row 0 of a tile is always valid
     // raise the reference only when this tile would exceed it by more than 2^kRescaleSlack
     const bool raise = mt > m_use + kRescaleSlack;
@@ -444,7 +460,11 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         // exponents are <= kRescaleSlack; results below 2^-126 flush to zero, far below bf16 resolution of the sum
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[8 * kk + e], scale_log2, -m_use));
+        float p = __builtin_amdgcn_exp2f(fmaf(s[8 * kk + e], scale_log2, -m_use));
+        if constexpr (decltype(partial)::value) {
+          const int r = 8 * kk + e;
+          p = 8 * (r >> 2) + 4 * hsel + (r & 3) >= valid ? 0.f : p;
+        }
         psum += p;
         pf[kk][e] = (__bf16)p;
       }
@@ -652,11 +672,11 @@ hipError_t launch_attn(const AttnArgs& a, const AttnPlan& p, void* ws, hipStream
     const size_t lds = sizeof(float) * ((size_t)a.d_qk + 2 * kGenThreads);
     dim3 grid((unsigned)a.H, (unsigned)a.B);
     if (a.dtype == 0)
-      hipLaunchKernelGGL(k_attn_generic<0>, grid, dim3(kGenThreads), lds, st, a.q, a.kv, a.v, a.kv_ld, a.v_ld, a.L,
+      SA_LAUNCH(k_attn_generic<0>, grid, dim3(kGenThreads), lds, st, a.q, a.kv, a.v, a.kv_ld, a.v_ld, a.L,
                          a.H, a.d_qk, a.d_v, a.t, a.idx, a.idx_ld, a.n_sel, a.n_sink, a.n_window, a.scale, a.out,
                          a.lse);
     else
-      hipLaunchKernelGGL(k_attn_generic<1>, grid, dim3(kGenThreads), lds, st, a.q, a.kv, a.v, a.kv_ld, a.v_ld, a.L,
+      SA_LAUNCH(k_attn_generic<1>, grid, dim3(kGenThreads), lds, st, a.q, a.kv, a.v, a.kv_ld, a.v_ld, a.L,
                          a.H, a.d_qk, a.d_v, a.t, a.idx, a.idx_ld, a.n_sel, a.n_sink, a.n_window, a.scale, a.out,
                          a.lse);
     return hipGetLastError();
@@ -672,16 +692,16 @@ hipError_t launch_attn(const AttnArgs& a, const AttnPlan& p, void* ws, hipStream
   const uint16_t* kv = reinterpret_cast<const uint16_t*>(a.kv);
   uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
   if (a.d_v == 576)
-    hipLaunchKernelGGL(k_attn_mfma<576>, grid, dim3(256), 0, st, q, kv, a.kv_ld, a.L, a.H, a.t, a.idx, a.idx_ld,
+    SA_LAUNCH(k_attn_mfma<576>, grid, dim3(256), 0, st, q, kv, a.kv_ld, a.L, a.H, a.t, a.idx, a.idx_ld,
                        a.n_sel, a.n_sink, a.n_window, sl2, p.n_splits, n_units, part_o, part_ml, out,
                        a.lse);
   else
-    hipLaunchKernelGGL(k_attn_mfma<512>, grid, dim3(256), 0, st, q, kv, a.kv_ld, a.L, a.H, a.t, a.idx, a.idx_ld,
+    SA_LAUNCH(k_attn_mfma<512>, grid, dim3(256), 0, st, q, kv, a.kv_ld, a.L, a.H, a.t, a.idx, a.idx_ld,
                        a.n_sel, a.n_sink, a.n_window, sl2, p.n_splits, n_units, part_o, part_ml, out,
                        a.lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_splits == 1) return e;
-  hipLaunchKernelGGL(k_attn_combine<1>, dim3((unsigned)(a.B * a.H)), dim3(kCombineThreads), 0, st, part_o, part_ml,
+  SA_LAUNCH(k_attn_combine<1>, dim3((unsigned)(a.B * a.H)), dim3(kCombineThreads), 0, st, part_o, part_ml,
                      p.n_splits, a.d_v, a.out, a.lse);
   return hipGetLastError();
 }

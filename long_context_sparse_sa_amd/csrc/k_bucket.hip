@@ -167,9 +167,11 @@ __global__ __launch_bounds__(256) void k_bucket_scores(const void* __restrict__ 
   constexpr int kRepRegs = 16;
   const bool in_regs = (d & 15) == 0 && d <= 16 * kRepRegs;
   float4 rv[kRepRegs];
+  if (in_regs) {  // uniform; slices past d repeat the first one (never used), so every load stays in the row
 #pragma unroll
-  for (int c = 0; c < kRepRegs; ++c)
-    rv[c] = *reinterpret_cast<const float4*>(r + (in_regs && 16 * c < d ? 16 * c + 4 * qtr : 0));
+    for (int c = 0; c < kRepRegs; ++c)
+      rv[c] = *reinterpret_cast<const float4*>(r + (16 * c < d ? 16 * c + 4 * qtr : 4 * qtr));
+  }
   // the queries into LDS: up to kStageRegs elements per thread are all loaded before any is stored, so their
   // latencies overlap
   constexpr int kStageRegs = 16;
@@ -591,19 +593,19 @@ hipError_t launch_bucket_build(const void* k, int k_dtype, int64_t k_ld, int64_t
                                int nb, float* reps, int32_t* offsets, int32_t* members, int32_t* counts,
                                int32_t* table, const BucketBuildPlan& p, hipStream_t st) {
   const int64_t tbl = p.n_chunks * (int64_t)nb;
-  hipLaunchKernelGGL(k_fill_i32, dim3(256), dim3(256), 0, st, counts, (int64_t)nb, 0);
-  if (tbl > 0) hipLaunchKernelGGL(k_fill_i32, dim3(1024), dim3(256), 0, st, table, tbl, 0);
-  if (L > 0) hipLaunchKernelGGL(k_count, dim3(1024), dim3(256), 0, st, assign, L, counts);
-  hipLaunchKernelGGL(k_offsets, dim3(1), dim3(1024), 0, st, counts, nb, offsets);
+  SA_LAUNCH(k_fill_i32, dim3(256), dim3(256), 0, st, counts, (int64_t)nb, 0);
+  if (tbl > 0) SA_LAUNCH(k_fill_i32, dim3(1024), dim3(256), 0, st, table, tbl, 0);
+  if (L > 0) SA_LAUNCH(k_count, dim3(1024), dim3(256), 0, st, assign, L, counts);
+  SA_LAUNCH(k_offsets, dim3(1), dim3(1024), 0, st, counts, nb, offsets);
   if (L > 0) {
-    hipLaunchKernelGGL(k_chunk_hist, dim3((unsigned)p.n_chunks), dim3(256), 0, st, assign, L, p.chunk, nb, table);
-    hipLaunchKernelGGL(k_chunk_scan, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, st, offsets, nb, p.n_chunks, table);
-    hipLaunchKernelGGL(k_scatter, dim3((unsigned)p.n_chunks), dim3(64), 0, st, assign, L, p.chunk, nb, table, members);
+    SA_LAUNCH(k_chunk_hist, dim3((unsigned)p.n_chunks), dim3(256), 0, st, assign, L, p.chunk, nb, table);
+    SA_LAUNCH(k_chunk_scan, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, st, offsets, nb, p.n_chunks, table);
+    SA_LAUNCH(k_scatter, dim3((unsigned)p.n_chunks), dim3(64), 0, st, assign, L, p.chunk, nb, table, members);
   }
   if (k_dtype == 0)
-    hipLaunchKernelGGL(k_reps<0>, dim3((unsigned)((nb + 3) / 4)), dim3(256), 0, st, k, k_ld, d, offsets, members, nb, reps);
+    SA_LAUNCH(k_reps<0>, dim3((unsigned)((nb + 3) / 4)), dim3(256), 0, st, k, k_ld, d, offsets, members, nb, reps);
   else
-    hipLaunchKernelGGL(k_reps<1>, dim3((unsigned)((nb + 3) / 4)), dim3(256), 0, st, k, k_ld, d, offsets, members, nb, reps);
+    SA_LAUNCH(k_reps<1>, dim3((unsigned)((nb + 3) / 4)), dim3(256), 0, st, k, k_ld, d, offsets, members, nb, reps);
   return hipGetLastError();
 }
 
@@ -616,12 +618,12 @@ hipError_t launch_bucket_select(const void* q, int q_dtype, int B, int d, const 
   const unsigned n_wg = (unsigned)((nb + 63) / 64);  // 64 buckets per workgroup
   const size_t lds = sizeof(float) * (size_t)B * d;
   if (q_dtype == 0)
-    hipLaunchKernelGGL(k_bucket_scores<0>, dim3(n_wg), dim3(256), lds, st, q, B, d, reps, offsets, nb, keys);
+    SA_LAUNCH(k_bucket_scores<0>, dim3(n_wg), dim3(256), lds, st, q, B, d, reps, offsets, nb, keys);
   else
-    hipLaunchKernelGGL(k_bucket_scores<1>, dim3(n_wg), dim3(256), lds, st, q, B, d, reps, offsets, nb, keys);
+    SA_LAUNCH(k_bucket_scores<1>, dim3(n_wg), dim3(256), lds, st, q, B, d, reps, offsets, nb, keys);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_choose_expand, dim3((unsigned)B), dim3(1024), 0, st, keys, nb, top_b, buckets_out, offsets,
+  SA_LAUNCH(k_choose_expand, dim3((unsigned)B), dim3(1024), 0, st, keys, nb, top_b, buckets_out, offsets,
                      members, L, t, n_sink, n_window, idx, cap, n_sel);
   return hipGetLastError();
 }

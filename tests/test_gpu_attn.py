@@ -67,7 +67,8 @@ def test_toy_decode_config_fp32(seed):
     np.testing.assert_allclose(lse[0].double().cpu().numpy(), ol, atol=1e-5, rtol=0)
 
 
-def _mfma_case(seed, B, L, n_list, n_sink, n_window, d_v, q_scale=1.0, t=None, H=128, idx_ld=None, ws_fill=None):
+def _mfma_case(seed, B, L, n_list, n_sink, n_window, d_v, q_scale=1.0, t=None, H=128, idx_ld=None, ws_fill=None,
+               scale=None):
     g = torch.Generator(device="cpu").manual_seed(seed)
     q = (torch.randn((B, H, 576), generator=g) * q_scale).to(torch.bfloat16).to(DEV)
     kv = torch.randn((L, 576), generator=g).to(torch.bfloat16).to(DEV)
@@ -77,7 +78,7 @@ def _mfma_case(seed, B, L, n_list, n_sink, n_window, d_v, q_scale=1.0, t=None, H
     idx_ld = max(1, max(n_list)) if idx_ld is None else idx_ld
     idx, nsel = _pack_idx(sels, idx_ld)
     tt = torch.tensor(ts, dtype=torch.int32, device=DEV)
-    scale = 1 / math.sqrt(576)
+    scale = 1 / math.sqrt(576) if scale is None else scale
     ws = None
     if ws_fill is not None:  # every workspace byte set, e.g. 0xFF: NaN in every float no kernel writes
         nb = sa.sa_sparse_attn_workspace(B, H, 576, d_v, n_sink + n_window + idx_ld, sa.SA_BF16)
@@ -126,6 +127,31 @@ def test_mfma_single_split_and_peaked():
 def test_mfma_short_prefix_t():
     # per-query t: sink and window overlap the whole visible prefix for early queries
     _mfma_case(2, B=3, L=5000, n_list=[0, 10, 300], n_sink=4, n_window=128, d_v=576, t=[2, 200, 4999])
+
+
+@pytest.mark.parametrize("scale", [0.0, -1 / math.sqrt(576), -0.2])
+def test_mfma_zero_and_negative_scale(scale):
+    # any finite scale is valid: a zero scale averages V over the read set (lse = ln |R|), a negative one prefers
+    # the rows least aligned with q; ragged read sets put masked rows in the last tile of each split
+    _mfma_case(7, B=3, L=6000, n_list=[1000, 45, 333], n_sink=4, n_window=128, d_v=576, scale=scale)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.3])
+def test_generic_zero_and_negative_scale(scale):
+    B, H, d, L = 2, 3, 64, 500
+    g = torch.Generator(device="cpu").manual_seed(8)
+    q = torch.randn((B, H, d), generator=g).to(DEV)
+    kv = torch.randn((L, d), generator=g).to(DEV)
+    rng = np.random.default_rng(8)
+    sels = [_rand_sparse(rng, L - 1, 2, 10, n) for n in (50, 7)]
+    idx, nsel = _pack_idx(sels, 50)
+    o, lse = sa.sa_sparse_attn(q, kv, idx, nsel, 2, 10, scale, return_lse=True)
+    torch.cuda.synchronize()
+    for b in range(B):
+        R = O.read_set(L - 1, 2, 10, sels[b])
+        oo, ol = O.sparse_attn(to_f64(q[b]), to_f64(kv), R, scale, d, d)
+        np.testing.assert_allclose(o[b].double().cpu().numpy(), oo, atol=1e-5, rtol=0)
+        np.testing.assert_allclose(lse[b].double().cpu().numpy(), ol, atol=1e-5, rtol=0)
 
 
 def test_mfma_empty_read_set():
