@@ -31,7 +31,8 @@
  *   - Scratch memory ("workspace") is caller-owned device memory of at least the size the matching *_workspace
  *     query returns; the queries are pure host functions. A workspace carries nothing from one call to the next:
  *     its contents on entry do not matter, since the kernels clear whatever they accumulate into.
- *   - The library is stateless and thread-safe. Calls on different streams may overlap, provided they share no
+ *   - The library keeps no state between calls (apart from the optional, thread-local instrumentation list at the
+ *     end of this header) and is thread-safe. Calls on different streams may overlap, provided they share no
  *     workspace and no output buffer.
  *   - `stream` is a hipStream_t passed as void*; NULL means the null stream.
  */
@@ -115,6 +116,25 @@ SA_API int sa_select_topk(const void* q, int q_dtype, const float* w, const void
                           void* ws, size_t ws_bytes, int algo, void* stream);
 
 /* ---------------------------------------------------------------------------------------------------------------
+ * sa_select_topk_scores -- the selection step of sa_select_topk on caller-given fp32 scores ([LongCat] DSA
+ * baseline section, arg-topK equation; SI section, sparse-part equation). It is the test mode of the selection
+ * (adversarial score patterns: signed zeros, subnormals, infinities, long runs of equal scores) and serves any
+ * caller whose scores come from elsewhere:
+ *     S_sparse,b = the min(k_sparse, |C_b|) positions s of C_b with the largest scores[b, s], ties to the LOWER s,
+ * where scores compare as fp32 values (-0 == +0; -inf is a valid score). Entries outside C_b are never read as
+ * candidates. NaN scores are outside the contract.
+ *   scores [B, scores_ld] fp32, scores_ld >= L, 16-byte aligned.      t [B] or NULL (t_b = L - 1).
+ *   idx    [B, idx_ld] int32 out, idx_ld >= k_sparse: ascending positions, then -1.   n_sel [B] int32 out.
+ *   1 <= k_sparse <= 16384; n_sink, n_window >= 0; L < 2^31.
+ *   ws / ws_bytes: at least sa_select_topk_scores_workspace(L, B) bytes (one key per position and query: this
+ *   call is given the full score matrix, so keeping its keys costs no more than the input).
+ * ------------------------------------------------------------------------------------------------------------- */
+SA_API size_t sa_select_topk_scores_workspace(int64_t L, int32_t B);
+SA_API int sa_select_topk_scores(const float* scores, int64_t scores_ld, int64_t L, int32_t B, const int32_t* t,
+                                 int32_t k_sparse, int32_t n_sink, int32_t n_window, int32_t* idx, int32_t idx_ld,
+                                 int32_t* n_sel, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------------------------------
  * sa_bucket_build -- the bucket directory of Latent Sparse Attention ([LSA-8] section 2, step 2: each bucket
  * keeps a representative vector and the positions of its members). Built once per cache.
  *   k        [L, d] index keys, leading dimension k_ld, dtype F32 or BF16
@@ -174,6 +194,17 @@ SA_API int sa_sparse_attn(const void* q, const void* kv, const void* v, int dtyp
                           const int32_t* idx, int32_t idx_ld, const int32_t* n_sel, int32_t n_sink,
                           int32_t n_window, float scale, void* out, float* lse, void* ws, size_t ws_bytes,
                           void* stream);
+
+/* ---------------------------------------------------------------------------------------------------------------
+ * Instrumentation (not part of the method): per-kernel timing of the calls above.
+ * sa_set_stage_events -- while a list is set on the calling thread, the library records events[i] (a hipEvent_t
+ *   created by the caller, passed as void*) on the call's stream right after its i-th kernel launch counted from
+ *   this call, for i < n; later launches record nothing. The array (host memory) and the events stay owned by the
+ *   caller and must stay valid while the list is set. sa_set_stage_events(NULL, 0) clears the list.
+ * sa_stage_events_used -- how many events of the current list have been recorded so far.
+ * ------------------------------------------------------------------------------------------------------------- */
+SA_API void sa_set_stage_events(void* const* events, int n);
+SA_API int sa_stage_events_used(void);
 
 #ifdef __cplusplus
 }

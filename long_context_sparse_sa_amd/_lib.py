@@ -30,6 +30,8 @@ SIGNATURES = {
     "sa_index_score": (INT, [P, INT, P, P, INT, I64, I64, I32, I32, I32, P, I64, I64, P, I64, P]),
     "sa_select_topk_workspace": (SZ, [I64, I32, I32, I32, INT, INT, I32, INT]),
     "sa_select_topk": (INT, [P, INT, P, P, INT, I64, I64, I32, I32, I32, P, I32, I32, I32, P, I32, P, P, SZ, INT, P]),
+    "sa_select_topk_scores_workspace": (SZ, [I64, I32]),
+    "sa_select_topk_scores": (INT, [P, I64, I64, I32, P, I32, I32, I32, P, I32, P, P, SZ, P]),
     "sa_bucket_build_workspace": (SZ, [I64, I32]),
     "sa_bucket_build": (INT, [P, INT, I64, I64, I32, P, I32, P, P, P, P, SZ, P]),
     "sa_bucket_select_workspace": (SZ, [I32, I32, I32]),
@@ -37,6 +39,8 @@ SIGNATURES = {
     "sa_sparse_attn_workspace": (SZ, [I32, I32, I32, I32, I64, INT]),
     "sa_sparse_attn": (INT, [P, P, P, INT, I64, I64, I64, I32, I32, I32, I32, P, P, I32, P, I32, I32, F32, P, P, P,
                              SZ, P]),
+    "sa_set_stage_events": (None, [P, INT]),
+    "sa_stage_events_used": (INT, []),
 }
 
 _lib = None

@@ -501,7 +501,7 @@ hipError_t launch_valu(const IndexerArgs& a, int64_t lo, int64_t hi, int mode, f
   const int64_t n = hi - lo;
   dim3 grid((unsigned)((n + kValuKeysPerWg - 1) / kValuKeysPerWg), (unsigned)a.B);
   const size_t lds = sizeof(float) * ((size_t)a.H * a.d + a.H);
-  hipLaunchKernelGGL((k_score_valu<QT, KT>), grid, dim3(256), lds, st, a.q, a.w, a.k, a.k_ld, a.L, a.H, a.d, a.t,
+  SA_LAUNCH((k_score_valu<QT, KT>), grid, dim3(256), lds, st, a.q, a.w, a.k, a.k_ld, a.L, a.H, a.d, a.t,
                      lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, cand, cand_ld, seg_cnt, a.clear,
                      a.clear_n);
   return hipGetLastError();
@@ -534,7 +534,7 @@ hipError_t launch_mfma(const IndexerArgs& a, int64_t lo, int64_t hi, int mode, f
   mfma_grid(a.B, NQ, n_tiles, &n_wg, &run);
   if (n_tiles < 1 || a.B < 1) return hipSuccess;
   dim3 grid((unsigned)n_wg, (unsigned)((a.B + NQ - 1) / NQ));
-  hipLaunchKernelGGL((k_score_mfma<NMT, FP8, NQ>), grid, dim3(64 * NQ), 0, st, a.q, a.w, a.k, a.k_ld, a.L, a.B, a.t,
+  SA_LAUNCH((k_score_mfma<NMT, FP8, NQ>), grid, dim3(64 * NQ), 0, st, a.q, a.w, a.k, a.k_ld, a.L, a.B, a.t,
                      lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, cand, cand_ld, seg_cnt, a.clear, a.clear_n);
   return hipGetLastError();
 }
@@ -601,7 +601,7 @@ hipError_t launch_stream_select(const IndexerArgs& a, int k, int n_sink, int n_w
   const int nq = 4;
   dim3 grid((unsigned)((a.B + nq - 1) / nq));
 #define SA_STREAM(NMT, F8, NQ)                                                                                  \
-  hipLaunchKernelGGL((k_stream_select<NMT, F8, NQ>), grid, dim3(64 * NQ), 0, st, a.q, a.w, a.k, a.k_ld, a.L, a.B, \
+  SA_LAUNCH((k_stream_select<NMT, F8, NQ>), grid, dim3(64 * NQ), 0, st, a.q, a.w, a.k, a.k_ld, a.L, a.B, \
                      a.t, k, n_sink, n_window, buf, buf_n, cap)
   if (a.H == 64) {
     if (fp8) SA_STREAM(2, true, 4); else SA_STREAM(2, false, 4);

@@ -340,7 +340,36 @@ __global__ __launch_bounds__(kRThreads) void k_radix_write(const uint32_t* __res
   }
 }
 
+// Keys of caller-given fp32 scores: grid (key blocks, queries); also zeroes the select's control words.
+__global__ __launch_bounds__(256) void k_keys_from_scores(const float* __restrict__ scores, int64_t scores_ld,
+                                                          int64_t L, const int32_t* __restrict__ t, int n_sink,
+                                                          int n_window, int64_t keys_ld, uint32_t* __restrict__ keys,
+                                                          uint32_t* __restrict__ ctl, int64_t ctl_words) {
+  const int b = blockIdx.y;
+  const int64_t nthr = (int64_t)gridDim.x * gridDim.y * blockDim.x;
+  for (int64_t i = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x; i < ctl_words; i += nthr)
+    ctl[i] = 0u;
+  const int64_t tb = t ? (int64_t)t[b] : L - 1;
+  const float* row = scores + (int64_t)b * scores_ld;
+  uint32_t* out = keys + (int64_t)b * keys_ld;
+  for (int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; s < keys_ld; s += (int64_t)gridDim.x * blockDim.x) {
+    const bool cand = s < L && s >= n_sink && s <= tb - n_window;
+    out[s] = cand ? score_key(row[s]) : 0u;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_keys_from_scores(const float* scores, int64_t scores_ld, int64_t L, int B, const int32_t* t,
+                                   int n_sink, int n_window, const RadixPlan& p, uint32_t* keys, uint32_t* ctl,
+                                   int64_t ctl_words, hipStream_t st) {
+  if (B == 0) return hipSuccess;
+  int64_t blocks = (p.keys_ld + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  SA_LAUNCH(k_keys_from_scores, dim3((unsigned)blocks, (unsigned)B), dim3(256), 0, st, scores, scores_ld, L, t,
+            n_sink, n_window, p.keys_ld, keys, ctl, ctl_words);
+  return hipGetLastError();
+}
 
 RadixPlan radix_plan(int B, int64_t L) {
   RadixPlan p{};
@@ -369,12 +398,12 @@ hipError_t launch_radix_select(int B, int64_t L, int k, const RadixPlan& p, cons
   uint32_t* hist = ctl;
   uint32_t* cnt = ctl + (size_t)3 * B * kRBins;
   uint32_t* recs = cnt + (size_t)2 * B * p.n_chunks;
-  hipLaunchKernelGGL(k_radix_hist<0>, grid, dim3(kRThreads), 0, st, keys, p.keys_ld, L, p.chunk, k, B, hist, recs);
-  hipLaunchKernelGGL(k_radix_hist<1>, grid, dim3(kRThreads), 0, st, keys, p.keys_ld, L, p.chunk, k, B, hist, recs);
-  hipLaunchKernelGGL(k_radix_hist<2>, grid, dim3(kRThreads), 0, st, keys, p.keys_ld, L, p.chunk, k, B, hist, recs);
-  hipLaunchKernelGGL(k_radix_count, grid, dim3(kRThreads), 0, st, keys, p.keys_ld, L, p.chunk, k, B, hist, recs,
+  SA_LAUNCH(k_radix_hist<0>, grid, dim3(kRThreads), 0, st, keys, p.keys_ld, L, p.chunk, k, B, hist, recs);
+  SA_LAUNCH(k_radix_hist<1>, grid, dim3(kRThreads), 0, st, keys, p.keys_ld, L, p.chunk, k, B, hist, recs);
+  SA_LAUNCH(k_radix_hist<2>, grid, dim3(kRThreads), 0, st, keys, p.keys_ld, L, p.chunk, k, B, hist, recs);
+  SA_LAUNCH(k_radix_count, grid, dim3(kRThreads), 0, st, keys, p.keys_ld, L, p.chunk, k, B, hist, recs,
                      cnt);
-  hipLaunchKernelGGL(k_radix_write, grid, dim3(kRThreads), 0, st, keys, p.keys_ld, L, p.chunk, k, B, recs, cnt, idx,
+  SA_LAUNCH(k_radix_write, grid, dim3(kRThreads), 0, st, keys, p.keys_ld, L, p.chunk, k, B, recs, cnt, idx,
                      idx_ld, n_sel, kept, thr_out);
   return hipGetLastError();
 }

@@ -433,7 +433,7 @@ hipError_t launch_merge(int B, int k, const MergeIn& in, Cand* gather, int64_t g
     if (e != hipSuccess) return e;
     attr_set.fetch_or(bit, std::memory_order_release);
   }
-  hipLaunchKernelGGL(k_merge, dim3((unsigned)B), dim3(kMergeThreads), (size_t)dyn, st, k, in, gather, gather_cap,
+  SA_LAUNCH(k_merge, dim3((unsigned)B), dim3(kMergeThreads), (size_t)dyn, st, k, in, gather, gather_cap,
                      out, cap);
   return hipGetLastError();
 }
@@ -450,7 +450,7 @@ hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t st) {
   if (n <= 0) return hipSuccess;
   const int64_t blocks64 = (n + 255) / 256;
   const unsigned blocks = (unsigned)(blocks64 < 1024 ? blocks64 : 1024);
-  hipLaunchKernelGGL(k_fill_u32, dim3(blocks), dim3(256), 0, st, p, n, v);
+  SA_LAUNCH(k_fill_u32, dim3(blocks), dim3(256), 0, st, p, n, v);
   return hipGetLastError();
 }
 

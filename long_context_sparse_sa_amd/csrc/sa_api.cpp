@@ -16,6 +16,11 @@ namespace {
 
 thread_local char g_err[512] = "";
 
+// Stage events (instrumentation): caller-created hipEvent_t handles, recorded one after each kernel launch.
+thread_local void* const* g_stage_ev = nullptr;
+thread_local int g_stage_n = 0;
+thread_local int g_stage_next = 0;
+
 int fail(int status, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
@@ -235,7 +240,19 @@ PerQueryWs carve_per_query(void* ws, const sa::IndexerArgs& a, int k) {
 
 }  // namespace
 
+void sa::stage_mark(hipStream_t st) {
+  if (g_stage_ev && g_stage_next < g_stage_n) (void)hipEventRecord((hipEvent_t)g_stage_ev[g_stage_next++], st);
+}
+
 extern "C" {
+
+SA_API void sa_set_stage_events(void* const* events, int n) {
+  g_stage_ev = n > 0 ? events : nullptr;
+  g_stage_n = n > 0 ? n : 0;
+  g_stage_next = 0;
+}
+
+SA_API int sa_stage_events_used(void) { return g_stage_next; }
 
 SA_API const char* sa_status_string(int s) {
   switch (s) {
@@ -418,6 +435,42 @@ SA_API int sa_select_topk(const void* q, int q_dtype, const float* w, const void
     if (e != hipSuccess) return hip_fail(e, "sa_select_topk (merge)");
   }
   return SA_OK;
+}
+
+// ---------------------------------------------------------------------------------------------------------------
+SA_API size_t sa_select_topk_scores_workspace(int64_t L, int32_t B) {
+  if (L < 1 || B < 0) return 0;
+  sa::IndexerArgs a{};
+  a.L = L;
+  a.B = B;
+  return carve_radix(nullptr, a).bytes;
+}
+
+SA_API int sa_select_topk_scores(const float* scores, int64_t scores_ld, int64_t L, int32_t B, const int32_t* t,
+                                 int32_t k_sparse, int32_t n_sink, int32_t n_window, int32_t* idx, int32_t idx_ld,
+                                 int32_t* n_sel, void* ws, size_t ws_bytes, void* stream) {
+  if (!scores || !idx || !n_sel) return fail(SA_ERR_NULL, "scores, idx and n_sel must be non-NULL");
+  if (L < 1 || L > 0x7FFFFFFFLL || B < 0) return fail(SA_ERR_SHAPE, "need 1 <= L < 2^31 and B >= 0");
+  if (scores_ld < L) return fail(SA_ERR_SHAPE, "scores_ld (%lld) < L (%lld)", (long long)scores_ld, (long long)L);
+  if (k_sparse < 1 || k_sparse > sa::merge_max_k())
+    return fail(SA_ERR_SHAPE, "k_sparse must be in [1, %d]", sa::merge_max_k());
+  if (idx_ld < k_sparse) return fail(SA_ERR_SHAPE, "idx_ld (%d) < k_sparse (%d)", idx_ld, k_sparse);
+  if (n_sink < 0 || n_window < 0) return fail(SA_ERR_SHAPE, "n_sink and n_window must be >= 0");
+  if (!aligned16(scores)) return fail(SA_ERR_ALIGN, "scores must be 16-byte aligned");
+  const size_t need = sa_select_topk_scores_workspace(L, B);
+  if (!ws || ws_bytes < need) return fail(SA_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  if (!aligned16(ws)) return fail(SA_ERR_ALIGN, "workspace must be 16-byte aligned");
+  if (B == 0) return SA_OK;
+  sa::IndexerArgs a{};
+  a.L = L;
+  a.B = B;
+  const RadixWs w2 = carve_radix(ws, a);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = sa::launch_keys_from_scores(scores, scores_ld, L, B, t, n_sink, n_window, w2.p, w2.keys, w2.ctl,
+                                             (int64_t)w2.ctl_words, s);
+  if (e != hipSuccess) return hip_fail(e, "sa_select_topk_scores (keys)");
+  e = sa::launch_radix_select(B, L, k_sparse, w2.p, w2.keys, w2.ctl, idx, idx_ld, n_sel, nullptr, nullptr, s);
+  return e == hipSuccess ? SA_OK : hip_fail(e, "sa_select_topk_scores (radix select)");
 }
 
 // ---------------------------------------------------------------------------------------------------------------

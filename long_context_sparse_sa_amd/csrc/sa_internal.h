@@ -7,6 +7,18 @@
 
 namespace sa {
 
+// Instrumentation: records the next event of the caller's stage-event list (sa_set_stage_events) on `st`, if a list
+// is set on this thread and not used up. Every kernel launch of the library is followed by one call.
+void stage_mark(hipStream_t st);
+
+#define SA_NTH_5(a, b, c, d, e, ...) e
+// A kernel launch followed by its stage mark (the fifth argument of hipLaunchKernelGGL is the stream).
+#define SA_LAUNCH(...)                                \
+  do {                                               \
+    hipLaunchKernelGGL(__VA_ARGS__);                 \
+    ::sa::stage_mark(SA_NTH_5(__VA_ARGS__, 0, 0, 0, 0, 0)); \
+  } while (0)
+
 struct IndexerArgs {
   const void* q;     // [B, H, d]
   int q_dtype;
@@ -113,6 +125,11 @@ size_t radix_ctl_words(int B, const RadixPlan& p);
 hipError_t launch_radix_select(int B, int64_t L, int k, const RadixPlan& p, const uint32_t* keys, uint32_t* ctl,
                                int32_t* idx, int idx_ld, int32_t* n_sel, Cand* kept, uint32_t* thr_out,
                                hipStream_t stream);
+// The radix select's keys from caller-given fp32 scores: keys[b * p.keys_ld + s] = score_key(scores[b, s]) for
+// candidates (n_sink <= s <= t_b - n_window), 0 otherwise; also zeroes ctl[0, ctl_words).
+hipError_t launch_keys_from_scores(const float* scores, int64_t scores_ld, int64_t L, int B, const int32_t* t,
+                                   int n_sink, int n_window, const RadixPlan& p, uint32_t* keys, uint32_t* ctl,
+                                   int64_t ctl_words, hipStream_t stream);
 
 // Streaming per-query selection for many queries (prefill chunk): one pass over each query's visible keys keeps
 // at most `cap` candidates per query in buf[b, :] (count in buf_n[b]) that contain the exact top-k.

@@ -26,7 +26,7 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported_and_bound(lib):
     names = declared_symbols()
-    assert len(names) == 12
+    assert sorted(names) == sorted(_lib.SIGNATURES)
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n

@@ -1,10 +1,14 @@
 """Parity at the full workload sizes, in the launch configuration bench.py times (the same entry points, default
 algorithm choices and workspace sizing), checked on sampled queries the oracle can compute one at a time.
 
-Workloads (sa_workloads.configs): 128K decode with 16 queries, the 32768-query prefill chunk, the 1M Flat bucket
-search and the 10M decode with e4m3 index keys. Selection follows the band rule of the selection tests; attention
-is checked on the read set the GPU selected, at the bf16 tolerance (2e-2 absolute), and the relative error is
-reported.
+Workloads (sa_workloads.configs): 128K decode with 16 queries (all checked), the 32768-query prefill chunk (a
+seeded sample of 16 queries, with the first and the last), the 1M Flat bucket search (all 8 queries) and the 10M
+decode with e4m3 index keys (all 4 queries). Selection follows the band rule of the selection tests. Attention is
+checked on the read set the GPU selected: max |o - oracle| within the bf16 tolerance (2e-2 absolute), lse within
+2e-3 absolute, and the relative L2 error within 1e-2. The last two make a dropped or doubled row tile fail: one
+32-row tile of about 2100 rows moves lse by about 0.015 and the output by about 10% relative, while bf16 rounding
+of the weights and of the output gives about 0.2%. The 128K decode is also run with queries scaled by 8, where the
+softmax is peaked and |o| is of order 1, so that the absolute tolerance is not loose against the output size.
 """
 import gc
 
@@ -21,6 +25,8 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
 ATTN_TOL = 2e-2
+LSE_TOL = 2e-3
+REL_L2_TOL = 1e-2
 
 
 def _free():
@@ -28,65 +34,90 @@ def _free():
     torch.cuda.empty_cache()
 
 
-def _scores_upto(k_dev, q64, w64, n, chunk=1 << 20):
-    """fp32 oracle scores of positions 0..n-1, decoding the stored keys one chunk at a time."""
-    out = []
+def _scores_upto(k_dev, queries, n, chunk=1 << 20):
+    """fp32 oracle scores of positions 0..n-1 for each (q [H, d], w [H]) in `queries`, decoding the stored keys
+    one chunk at a time (each chunk once for all queries)."""
+    out = [[] for _ in queries]
     for a in range(0, n, chunk):
         b = min(n, a + chunk)
         kf = to_f64(k_dev[a:b])
-        out.append(O.index_score_f32(q64, w64, kf, np.arange(b - a)))
+        for i, (q64, w64) in enumerate(queries):
+            out[i].append(O.index_score_f32(q64, w64, kf, np.arange(b - a)))
         del kf
-    return np.concatenate(out)
+    return [np.concatenate(o) for o in out]
 
 
-def _check_select(inp, wl, b, idx, n_sel):
-    t = wl.t_positions()[b]
-    q64, w64 = to_f64(inp["q_idx"][b]), inp["w"][b].double().cpu().numpy()
-    cand = O.candidate_positions(t, wl.n_sink, wl.n_window)
-    sc = _scores_upto(inp["k_idx"], q64, w64, t + 1)[cand]
-    ref = O.topk_positions(sc, cand, wl.k_sparse)
-    got = selected(idx[b], int(n_sel[b].item()))
-    band_compare(got, ref, cand, sc, wl.k_sparse)
-    return got
+def _check_select(inp, wl, sample, idx, n_sel):
+    ts = wl.t_positions()
+    queries = [(to_f64(inp["q_idx"][b]), inp["w"][b].double().cpu().numpy()) for b in sample]
+    scores = _scores_upto(inp["k_idx"], queries, max(ts[b] for b in sample) + 1)
+    got_all = {}
+    for i, b in enumerate(sample):
+        t = ts[b]
+        cand = O.candidate_positions(t, wl.n_sink, wl.n_window)
+        sc = scores[i][cand]
+        ref = O.topk_positions(sc, cand, wl.k_sparse)
+        got = selected(idx[b], int(n_sel[b].item()))
+        band_compare(got, ref, cand, sc, wl.k_sparse)
+        got_all[b] = got
+    return got_all
 
 
-def _check_attn(inp, wl, b, sel, out):
+def _check_attn(inp, wl, b, sel, out, lse, q=None):
     t = wl.t_positions()[b]
     R = O.read_set(t, wl.n_sink, wl.n_window, sel)
     rows = to_f64(inp["kv"][torch.as_tensor(R, device=inp["kv"].device)])
-    ref, _ = O.sparse_attn(to_f64(inp["q"][b]), rows, np.arange(R.size), wl.softmax_scale, wl.d_qk, wl.d_v)
+    qb = inp["q"][b] if q is None else q[b]
+    ref, ref_lse = O.sparse_attn(to_f64(qb), rows, np.arange(R.size), wl.softmax_scale, wl.d_qk, wl.d_v)
     got = out[b].double().cpu().numpy()
     err = np.abs(got - ref).max()
     rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
-    print(f"query {b}: |R| = {R.size}, max |o - oracle| = {err:.3e}, relative L2 = {rel:.3e}")
-    assert err <= ATTN_TOL, (b, err)
+    lse_err = np.abs(lse[b].double().cpu().numpy() - ref_lse).max()
+    print(f"query {b}: |R| = {R.size}, max |o| = {np.abs(ref).max():.3e}, max |o - oracle| = {err:.3e}, "
+          f"relative L2 = {rel:.3e}, max |lse - oracle| = {lse_err:.3e}")
+    assert err <= ATTN_TOL, ("max abs", b, err)
+    assert lse_err <= LSE_TOL, ("lse", b, lse_err)
+    assert rel <= REL_L2_TOL, ("relative L2", b, rel)
 
 
-def _run_dsa(wl, sample):
+def _run_dsa(wl, sample, peaked=False):
     inp = gen.make_inputs(wl, device=DEV)
     t = inp["t"]
     idx, n_sel = sa.sa_select_topk(inp["q_idx"], inp["w"], inp["k_idx"], wl.k_sparse, wl.n_sink, wl.n_window, t=t)
-    out = sa.sa_sparse_attn(inp["q"], inp["kv"], idx, n_sel, wl.n_sink, wl.n_window, wl.softmax_scale, t=t,
-                            d_v=wl.d_v)
+    out, lse = sa.sa_sparse_attn(inp["q"], inp["kv"], idx, n_sel, wl.n_sink, wl.n_window, wl.softmax_scale, t=t,
+                                 d_v=wl.d_v, return_lse=True)
     torch.cuda.synchronize()
+    sels = _check_select(inp, wl, sample, idx, n_sel)
     for b in sample:
-        sel = _check_select(inp, wl, b, idx, n_sel)
-        _check_attn(inp, wl, b, sel, out)
-    del inp, idx, n_sel, out
+        _check_attn(inp, wl, b, sels[b], out, lse)
+    if peaked:
+        # the same selection, queries x 8 (exact in bf16): a peaked softmax with |o| of order 1
+        q8 = inp["q"] * 8
+        out8, lse8 = sa.sa_sparse_attn(q8, inp["kv"], idx, n_sel, wl.n_sink, wl.n_window, wl.softmax_scale, t=t,
+                                       d_v=wl.d_v, return_lse=True)
+        torch.cuda.synchronize()
+        for b in sample:
+            _check_attn(inp, wl, b, sels[b], out8, lse8, q=q8)
+        del q8, out8, lse8
+    del inp, idx, n_sel, out, lse
     _free()
 
 
 def test_dsa_decode_128k_full():
-    _run_dsa(get_workload("dsa_decode_128k"), [0, 7, 15])
+    wl = get_workload("dsa_decode_128k")
+    _run_dsa(wl, list(range(wl.B)), peaked=True)
 
 
 def test_prefill_chunk_128k_sampled():
     wl = get_workload("prefill_chunk_128k")
-    _run_dsa(wl, [0, wl.B // 2 - 1, wl.B - 1])
+    rng = np.random.default_rng(2026)
+    sample = sorted({0, wl.B - 1, *rng.choice(np.arange(1, wl.B - 1), size=14, replace=False).tolist()})
+    _run_dsa(wl, sample)
 
 
 def test_decode_10m_fp8_full():
-    _run_dsa(get_workload("decode_10m_fp8"), [0])
+    wl = get_workload("decode_10m_fp8")
+    _run_dsa(wl, list(range(wl.B)))
 
 
 def test_lsa_flat_1m_full():
@@ -96,8 +127,8 @@ def test_lsa_flat_1m_full():
     reps, offsets, members = sa.sa_bucket_build(inp["k_idx"], inp["assign"], wl.n_buckets)
     idx, n_sel, buckets = sa.sa_bucket_select(inp["q_idx"], reps, offsets, members, wl.L, wl.top_b, wl.n_sink,
                                               wl.n_window, cap=8192, t=t, return_buckets=True)
-    out = sa.sa_sparse_attn(inp["q"], inp["kv"], idx, n_sel, wl.n_sink, wl.n_window, wl.softmax_scale, t=t,
-                            d_v=wl.d_v)
+    out, lse = sa.sa_sparse_attn(inp["q"], inp["kv"], idx, n_sel, wl.n_sink, wl.n_window, wl.softmax_scale, t=t,
+                                 d_v=wl.d_v, return_lse=True)
     torch.cuda.synchronize()
     # the directory: CSR bit-exact, representatives within 1e-6 relative
     ref_reps, ref_off, ref_mem = O.bucket_build(to_f64(inp["k_idx"]), inp["assign"].cpu().numpy(), wl.n_buckets)
@@ -106,11 +137,11 @@ def test_lsa_flat_1m_full():
     g = reps.cpu().numpy().astype(np.float64)
     r = ref_reps.astype(np.float64)
     assert np.all(np.abs(g - r) <= 1e-6 * np.maximum(np.abs(r), 1e-30) + 1e-30)
-    # selection and attention of sampled queries, with the same representatives on both sides
+    # selection and attention of every query, with the same representatives on both sides
     reps32 = reps.cpu().numpy()
     off_np, mem_np = offsets.cpu().numpy().astype(np.int64), members.cpu().numpy().astype(np.int64)
     ids = np.nonzero(np.diff(off_np) > 0)[0]
-    for b in (0, wl.B - 1):
+    for b in range(wl.B):
         tb = wl.t_positions()[b]
         q64 = to_f64(inp["q_idx"][b])
         ref_sel, ref_chosen, sc = O.bucket_select(q64, reps32, off_np, mem_np, tb, wl.top_b, wl.n_sink, wl.n_window)
@@ -127,6 +158,6 @@ def test_lsa_flat_1m_full():
         hi = max(lo, tb - wl.n_window + 1)
         exp = np.concatenate([mem_np[off_np[c]:off_np[c + 1]] for c in got_chosen])
         np.testing.assert_array_equal(got, np.sort(exp[(exp >= lo) & (exp < hi)]))
-        _check_attn(inp, wl, b, got, out)
-    del inp, reps, offsets, members, idx, n_sel, buckets, out
+        _check_attn(inp, wl, b, got, out, lse)
+    del inp, reps, offsets, members, idx, n_sel, buckets, out, lse
     _free()
