@@ -170,6 +170,26 @@ SA_API int sa_bucket_select(const void* q, int q_dtype, int32_t B, int32_t d, co
                             void* stream);
 
 /* ---------------------------------------------------------------------------------------------------------------
+ * sa_bucket_select_noalloc -- for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): sa_bucket_select with the same arguments minus the workspace,
+ * and the same result. Its scratch (one 4-byte key per (query, bucket)) lives in a static device array of the
+ * library instead of a caller workspace.
+ *   Limit: B * n_buckets <= sa_bucket_select_noalloc_max_keys() (2^21 keys, 8 MiB); a larger call returns
+ *   SA_ERR_WORKSPACE and launches nothing.
+ *   The array exists once per device, from when the library's device code is loaded there until the process
+ *   ends; the first call on a device looks its address up (hipGetSymbolAddress, with that device made current
+ *   for the lookup). No call allocates or frees memory.
+ *   Every call on one device shares that device's array and leaves its keys behind: calls that may overlap on one
+ *   device (different streams, or several host threads) race, and the caller must order them. Nothing in the
+ *   array has to start at zero: the kernels write every key they read.
+ * ------------------------------------------------------------------------------------------------------------- */
+SA_API int64_t sa_bucket_select_noalloc_max_keys(void);
+SA_API int sa_bucket_select_noalloc(const void* q, int q_dtype, int32_t B, int32_t d, const float* reps,
+                                    const int32_t* offsets, const int32_t* members, int32_t n_buckets, int64_t L,
+                                    const int32_t* t, int32_t top_b, int32_t n_sink, int32_t n_window, int32_t* idx,
+                                    int32_t cap, int32_t* n_sel, int32_t* buckets_out, void* stream);
+
+/* ---------------------------------------------------------------------------------------------------------------
  * sa_sparse_attn -- attention over the read set only ([LongCat] DSA baseline section, sparse-attention equation,
  * in MLA absorbed-MQA form: one cached latent row per position is shared by every query head):
  *     o[b,h,:] = sum_{s in R_b} softmax_s(scale * q[b,h,:] . K_s) * V_s,   lse[b,h] = log sum_{s in R_b} exp(...)

@@ -153,6 +153,29 @@ def sa_bucket_select(q_idx, reps, offsets, members, L: int, top_b: int, n_sink: 
     return (idx, n_sel, buckets) if return_buckets else (idx, n_sel)
 
 
+def sa_bucket_select_noalloc(q_idx, reps, offsets, members, L: int, top_b: int, n_sink: int = 0,
+                             n_window: int = 0, cap: int = 8192, t=None, return_buckets: bool = False, out=None,
+                             stream=None):
+    """sa_bucket_select without a workspace (the library's static scratch array); out = (idx, n_sel[, buckets])
+    preallocated by the caller, or None to have them allocated here."""
+    _need_cuda(q_idx, reps, offsets, members, t)
+    B, d = q_idx.shape
+    nb = reps.shape[0]
+    if out is None:
+        idx = torch.empty((B, cap), dtype=torch.int32, device=q_idx.device)
+        n_sel = torch.empty((B,), dtype=torch.int32, device=q_idx.device)
+        buckets = torch.empty((B, top_b), dtype=torch.int32, device=q_idx.device) if return_buckets else None
+    else:
+        idx, n_sel = out[0], out[1]
+        buckets = out[2] if return_buckets else None
+        cap = idx.stride(0)
+    st = _lib.load().sa_bucket_select_noalloc(_ptr(q_idx), _dtype(q_idx), B, d, _ptr(reps), _ptr(offsets),
+                                              _ptr(members), nb, L, _ptr(t), top_b, n_sink, n_window, _ptr(idx), cap,
+                                              _ptr(n_sel), _ptr(buckets), _stream(stream))
+    _lib.check("sa_bucket_select_noalloc", st)
+    return (idx, n_sel, buckets) if return_buckets else (idx, n_sel)
+
+
 def sa_sparse_attn_workspace(B, H, d_qk, d_v, max_rows, dtype) -> int:
     return int(_lib.load().sa_sparse_attn_workspace(B, H, d_qk, d_v, max_rows, dtype))
 

@@ -12,6 +12,8 @@
 //   query chooses the exact top-b (ties to the lower bucket id) and expands the chosen buckets' member ranges
 //   inside [sink end, window start), sorted ascending by binning the positions (a bitonic sort when the bins
 //   crowd).
+#include <mutex>
+
 #include "sa_device.h"
 #include "sa_internal.h"
 
@@ -610,6 +612,51 @@ hipError_t launch_bucket_build(const void* k, int k_dtype, int64_t k_ld, int64_t
 }
 
 int bucket_expand_max() { return kMaxExpand; }
+
+// ---- scratch of the no-allocation variant of the bucket search ---------------------------------------------------
+// One key per (query, bucket) in a static device array: each device that loads the library holds its own copy
+// until the process ends. Host code never passes `scratch` itself to a kernel (on the host it only names the
+// symbol): the device address comes from hipGetSymbolAddress, looked up once per device with that device current.
+constexpr int64_t kScratchWords = (int64_t)1 << 21;  // 8 MiB
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint32_t scratch[kScratchWords];
+
+int64_t bucket_scratch_words() { return kScratchWords; }
+
+hipError_t bucket_scratch(hipStream_t st, uint32_t** out) {
+  static std::mutex mu;
+  static uint32_t* ptrs[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e;
+  if (st) {
+    hipDevice_t d;
+    e = hipStreamGetDevice(st, &d);
+    if (e != hipSuccess) return e;
+    dev = (int)d;
+  } else {
+    e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    ptrs[dev] = static_cast<uint32_t*>(p);
+  }
+  *out = ptrs[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_bucket_select(const void* q, int q_dtype, int B, int d, const float* reps, const int32_t* offsets,
                                 const int32_t* members, int nb, int64_t L, const int32_t* t, int top_b, int n_sink,

@@ -508,11 +508,10 @@ SA_API size_t sa_bucket_select_workspace(int32_t B, int32_t n_buckets, int32_t t
   return align_up(c.off, 256);
 }
 
-SA_API int sa_bucket_select(const void* q, int q_dtype, int32_t B, int32_t d, const float* reps,
-                            const int32_t* offsets, const int32_t* members, int32_t n_buckets, int64_t L,
-                            const int32_t* t, int32_t top_b, int32_t n_sink, int32_t n_window, int32_t* idx,
-                            int32_t cap, int32_t* n_sel, int32_t* buckets_out, void* ws, size_t ws_bytes,
-                            void* stream) {
+namespace {
+int check_bucket_select(const void* q, int q_dtype, int32_t B, int32_t d, const float* reps,
+                        const int32_t* offsets, const int32_t* members, int32_t n_buckets, int64_t L, int32_t top_b,
+                        int32_t n_sink, int32_t n_window, int32_t* idx, int32_t cap, int32_t* n_sel) {
   if (!q || !reps || !offsets || !members || !idx || !n_sel) return fail(SA_ERR_NULL, "required pointer is NULL");
   if (q_dtype != SA_F32 && q_dtype != SA_BF16) return fail(SA_ERR_DTYPE, "bucket queries must be f32 or bf16");
   if (B < 0 || d < 1 || n_buckets < 1 || L < 1 || L > 0x7FFFFFFFLL) return fail(SA_ERR_SHAPE, "bad B, d, n_buckets or L");
@@ -520,6 +519,18 @@ SA_API int sa_bucket_select(const void* q, int q_dtype, int32_t B, int32_t d, co
   if (top_b < 1 || top_b > n_buckets || top_b > 1024) return fail(SA_ERR_SHAPE, "need 1 <= top_b <= min(n_buckets, 1024)");
   if (cap < 1 || cap > sa::bucket_expand_max()) return fail(SA_ERR_SHAPE, "cap must be in [1, %d]", sa::bucket_expand_max());
   if (n_sink < 0 || n_window < 0) return fail(SA_ERR_SHAPE, "n_sink and n_window must be >= 0");
+  return SA_OK;
+}
+}  // namespace
+
+SA_API int sa_bucket_select(const void* q, int q_dtype, int32_t B, int32_t d, const float* reps,
+                            const int32_t* offsets, const int32_t* members, int32_t n_buckets, int64_t L,
+                            const int32_t* t, int32_t top_b, int32_t n_sink, int32_t n_window, int32_t* idx,
+                            int32_t cap, int32_t* n_sel, int32_t* buckets_out, void* ws, size_t ws_bytes,
+                            void* stream) {
+  int st = check_bucket_select(q, q_dtype, B, d, reps, offsets, members, n_buckets, L, top_b, n_sink, n_window, idx,
+                               cap, n_sel);
+  if (st) return st;
   const size_t need = sa_bucket_select_workspace(B, n_buckets, top_b);
   if (!ws || ws_bytes < need) return fail(SA_ERR_WORKSPACE, "workspace needs %zu bytes", need);
   if (B == 0) return SA_OK;
@@ -528,6 +539,29 @@ SA_API int sa_bucket_select(const void* q, int q_dtype, int32_t B, int32_t d, co
   hipError_t e = sa::launch_bucket_select(q, q_dtype, B, d, reps, offsets, members, n_buckets, L, t, top_b, n_sink,
                                           n_window, idx, cap, n_sel, buckets_out, keys, (hipStream_t)stream);
   return e == hipSuccess ? SA_OK : hip_fail(e, "sa_bucket_select");
+}
+
+SA_API int64_t sa_bucket_select_noalloc_max_keys(void) { return sa::bucket_scratch_words(); }
+
+SA_API int sa_bucket_select_noalloc(const void* q, int q_dtype, int32_t B, int32_t d, const float* reps,
+                                    const int32_t* offsets, const int32_t* members, int32_t n_buckets, int64_t L,
+                                    const int32_t* t, int32_t top_b, int32_t n_sink, int32_t n_window, int32_t* idx,
+                                    int32_t cap, int32_t* n_sel, int32_t* buckets_out, void* stream) {
+  int st = check_bucket_select(q, q_dtype, B, d, reps, offsets, members, n_buckets, L, top_b, n_sink, n_window, idx,
+                               cap, n_sel);
+  if (st) return st;
+  if ((int64_t)B * n_buckets > sa::bucket_scratch_words())
+    return fail(SA_ERR_WORKSPACE,
+                "B * n_buckets = %lld exceeds the %lld keys of the static scratch array (use sa_bucket_select with a "
+                "workspace)",
+                (long long)B * n_buckets, (long long)sa::bucket_scratch_words());
+  if (B == 0) return SA_OK;
+  uint32_t* keys = nullptr;
+  hipError_t e = sa::bucket_scratch((hipStream_t)stream, &keys);
+  if (e != hipSuccess) return hip_fail(e, "sa_bucket_select_noalloc (scratch address)");
+  e = sa::launch_bucket_select(q, q_dtype, B, d, reps, offsets, members, n_buckets, L, t, top_b, n_sink, n_window,
+                               idx, cap, n_sel, buckets_out, keys, (hipStream_t)stream);
+  return e == hipSuccess ? SA_OK : hip_fail(e, "sa_bucket_select_noalloc");
 }
 
 // ---------------------------------------------------------------------------------------------------------------

@@ -148,6 +148,10 @@ hipError_t launch_bucket_build(const void* k, int k_dtype, int64_t k_ld, int64_t
                                int32_t* table, const BucketBuildPlan& plan, hipStream_t stream);
 
 int bucket_expand_max();
+// The no-allocation bucket search keeps its keys in a static device array of bucket_scratch_words() words;
+// bucket_scratch returns that array's address on the device of `stream` (looked up once per device).
+int64_t bucket_scratch_words();
+hipError_t bucket_scratch(hipStream_t stream, uint32_t** out);
 // Workspace of the Flat search: keys [B * n_buckets] (uint32, in a Cand-sized area), n_chosen [B],
 // gather [B * n_buckets], chosen [B * top_b].
 hipError_t launch_bucket_select(const void* q, int q_dtype, int B, int d, const float* reps, const int32_t* offsets,

@@ -170,3 +170,22 @@ def test_bucket_validation(lib):
     assert lib.sa_bucket_select(*bad) == WS
     bad = list(args); bad[2] = 0
     assert lib.sa_bucket_select(*bad) == OK
+
+
+def test_bucket_select_noalloc_validation(lib):
+    """The no-allocation variant validates like the workspace variant and rejects, before any HIP call, calls
+    whose keys do not fit its static scratch array."""
+    max_keys = lib.sa_bucket_select_noalloc_max_keys()
+    assert max_keys == 1 << 21
+    nb = 1 << 17
+    args = [A, BF16, max_keys // nb, 128, A, A, A, nb, 1 << 20, None, 32, 4, 128, A, 8192, A, None, None]
+    assert lib.sa_bucket_select_noalloc(*args[:13], None, *args[14:]) == NULL
+    bad = list(args); bad[1] = E4M3
+    assert lib.sa_bucket_select_noalloc(*bad) == DTYPE
+    bad = list(args); bad[10] = 0
+    assert lib.sa_bucket_select_noalloc(*bad) == SHAPE
+    bad = list(args); bad[2] = max_keys // nb + 1
+    assert lib.sa_bucket_select_noalloc(*bad) == WS
+    assert b"static scratch" in lib.sa_last_error()
+    bad = list(args); bad[2] = 0
+    assert lib.sa_bucket_select_noalloc(*bad) == OK  # nothing to do: no HIP call
