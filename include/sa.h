@@ -68,9 +68,12 @@ typedef enum {
   SA_TOPK_SPLIT_L = 1,   /* few queries: key range split over workgroups, thresholds refined by levels  */
   SA_TOPK_PER_QUERY = 2, /* many queries (prefill chunk): one streaming pass per query group             */
   SA_TOPK_RADIX = 3,     /* few queries: one key per position, radix select spread over workgroups      */
-  SA_TOPK_RADIX_LEVELS = 4 /* few queries over long caches: the radix select over a prefix of the
-                            * positions (at most half of them and at most 2^24 keys over all queries), then
-                            * key ranges in which only keys above the prefix's k-th key are kept, merged  */
+  SA_TOPK_RADIX_LEVELS = 4, /* few queries over long caches: the radix select over a prefix of the
+                             * positions (at most half of them and at most 2^24 keys over all queries), then
+                             * key ranges in which only keys above the prefix's k-th key are kept, merged  */
+  SA_TOPK_STREAM = 5       /* few queries: scores stay on chip; each launch over a range of positions derives a
+                            * proven lower bound of every query's k-th key from per-chunk statistics and emits
+                            * only the keys at or above it; one exact merge                                  */
 } sa_topk_algo;
 
 SA_API const char* sa_status_string(int status);
@@ -96,10 +99,13 @@ SA_API int sa_index_score(const void* q, int q_dtype, const float* w, const void
  * baseline section, arg-topK equation; SI section, sparse-part equation):
  *     S_sparse,b = the min(k_sparse, |C_b|) positions of C_b with the largest fp32 score I_{b,s}
  * where ties are broken towards the LOWER position. The score is the one sa_index_score defines (fp32).
- * SA_TOPK_SPLIT_L and SA_TOPK_PER_QUERY never write the full score matrix (only candidates that can still enter
- * the top-k leave the kernels); SA_TOPK_RADIX writes one 4-byte key per position and query to the workspace, and
- * SA_TOPK_RADIX_LEVELS does so for the positions of its prefix only. SA_TOPK_AUTO takes PER_QUERY for B >= 64,
- * RADIX while B * L <= 2^24, RADIX_LEVELS beyond.
+ * SA_TOPK_STREAM, SA_TOPK_SPLIT_L and SA_TOPK_PER_QUERY never write the full score matrix (only candidates that
+ * can still enter the top-k leave the kernels); SA_TOPK_RADIX writes one 4-byte key per position and query to the
+ * workspace, and SA_TOPK_RADIX_LEVELS does so for the positions of its prefix only. SA_TOPK_AUTO takes PER_QUERY
+ * for B >= 64 and STREAM below, when the MFMA scorer serves the shape (d = 128, H in {32, 64}, bf16 or e4m3);
+ * otherwise RADIX while B * L <= 2^24 and RADIX_LEVELS beyond. SA_TOPK_STREAM's launches wait, for a bounded
+ * number of polls, for one another's workgroups (which are sized to be resident together); whatever they see, the
+ * bound they use is a proven one, so the result never depends on the timing.
  *   idx    [B, idx_ld] int32, idx_ld >= k_sparse: S_sparse,b in ascending position order, then -1 padding.
  *   n_sel  [B] int32: |S_sparse,b|.
  *   The sink and window are not listed in idx; pass the same n_sink/n_window to sa_sparse_attn.
@@ -222,9 +228,13 @@ SA_API int sa_sparse_attn(const void* q, const void* kv, const void* v, int dtyp
  *   this call, for i < n; later launches record nothing. The array (host memory) and the events stay owned by the
  *   caller and must stay valid while the list is set. sa_set_stage_events(NULL, 0) clears the list.
  * sa_stage_events_used -- how many events of the current list have been recorded so far.
+ * sa_set_stream_spin_limit -- test knob of SA_TOPK_STREAM on the calling thread: how many times a workgroup polls
+ *   for the other workgroups' statistics before it goes on without them (negative: the library's default). A
+ *   small limit only makes the bound weaker and the merge larger; the result is the same.
  * ------------------------------------------------------------------------------------------------------------- */
 SA_API void sa_set_stage_events(void* const* events, int n);
 SA_API int sa_stage_events_used(void);
+SA_API void sa_set_stream_spin_limit(int polls);
 
 #ifdef __cplusplus
 }

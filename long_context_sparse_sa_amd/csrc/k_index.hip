@@ -9,6 +9,7 @@
 //    to bf16 on the way in) and shared by the workgroup's waves (four or eight queries: eight when B >= 8).
 // Both kernels either write the dense score row or emit only candidates whose score beats the caller's running
 // threshold, so a decode step never writes the [B, L] score matrix.
+#include <atomic>
 #include <type_traits>
 
 #include "sa_device.h"
@@ -276,6 +277,60 @@ __device__ __forceinline__ float score_tile(const char* tile, int lane, const bf
   return fold_halves(part0, part1);
 }
 
+// Walks the tiles 0 .. n_tiles-1 of a workgroup's run (tile i covers positions tile_start(i) .. + 63): every wave
+// calls on_tile(tile_in_lds, i) once per tile, in order, after the tile's keys have landed in LDS. bf16 keys arrive
+// by asynchronous DMA into NBUF LDS buffers (NBUF - 1 tiles in flight); e4m3 keys are loaded two tiles ahead into a
+// register ring, converted and committed to two LDS buffers. All waves of the workgroup must call it.
+template <bool E4M3, int NQ, int NBUF, typename TS, typename F>
+__device__ __forceinline__ void walk_tiles(const char* kbytes, int64_t ld_bytes, int64_t L, int64_t n_tiles,
+                                           TS tile_start, char (*tiles)[kTileBytes], int wave, int lane,
+                                           F&& on_tile) {
+  typedef KeyLoader<E4M3, NQ> KL;
+  constexpr int kDmaPerWave = KeyLoader<false, NQ>::kPerWave;
+  if constexpr (!E4M3) {
+    static_assert(NBUF == 4, "the waits below keep two tiles in flight behind the current one");
+    typename KL::Regs none;
+    KL::init(none, ld_bytes, wave, lane);
+    const int64_t n_pre = n_tiles < NBUF - 1 ? n_tiles : NBUF - 1;
+    for (int64_t p = 0; p < n_pre; ++p) KL::fetch(kbytes, ld_bytes, L, tile_start(p), tiles[p], wave, lane, none);
+    for (int64_t i = 0; i < n_tiles; ++i) {
+      const int64_t newer = n_tiles - 1 - i;
+      if (newer >= 2) wait_vmem_below<2 * kDmaPerWave>();
+      else if (newer == 1) wait_vmem_below<kDmaPerWave>();
+      else wait_vmem_below<0>();
+      lds_barrier();
+      if (i + NBUF - 1 < n_tiles)
+        KL::fetch(kbytes, ld_bytes, L, tile_start(i + NBUF - 1), tiles[(i + NBUF - 1) % NBUF], wave, lane, none);
+      on_tile(tiles[i % NBUF], i);
+    }
+  } else {
+    static_assert(NBUF == 2, "e4m3 tiles alternate between two LDS buffers");
+    typename KL::Regs ring[2];
+    if (n_tiles > 0) {
+      KL::fetch(kbytes, ld_bytes, L, tile_start(0), nullptr, wave, lane, ring[0]);
+      if (n_tiles > 1) KL::fetch(kbytes, ld_bytes, L, tile_start(1), nullptr, wave, lane, ring[1]);
+      KL::commit(ring[0], tiles[0], threadIdx.x);
+      if (n_tiles > 2) KL::fetch(kbytes, ld_bytes, L, tile_start(2), nullptr, wave, lane, ring[0]);
+    }
+    // tile i + 1 (ring slot (i + 1) % 2) goes to LDS while tile i is scored; its slot then takes tile i + 3.
+    // Unrolled by two so that ring slots and LDS buffers are compile-time (a runtime-indexed ring would live in
+    // scratch memory).
+    auto step = [&](int64_t i, auto P) {
+      constexpr int p = decltype(P)::value;
+      lds_barrier();
+      if (i + 1 < n_tiles) {
+        KL::commit(ring[1 - p], tiles[1 - p], threadIdx.x);
+        if (i + 3 < n_tiles) KL::fetch(kbytes, ld_bytes, L, tile_start(i + 3), nullptr, wave, lane, ring[1 - p]);
+      }
+      on_tile(tiles[p], i);
+    };
+    for (int64_t i = 0; i < n_tiles; i += 2) {
+      step(i, std::integral_constant<int, 0>{});
+      if (i + 1 < n_tiles) step(i + 1, std::integral_constant<int, 1>{});
+    }
+  }
+}
+
 // Split-L scoring: workgroup = NQ waves = NQ queries. Each of the gridDim.x workgroups of a query group scores a
 // contiguous run of the 64-position tiles of [lo, hi), with its queries in registers. bf16 keys arrive by
 // asynchronous DMA into four LDS buffers (three tiles in flight); e4m3 keys are loaded two tiles ahead into a
@@ -296,7 +351,6 @@ __global__ __launch_bounds__(64 * NQ) void k_score_mfma(const void* __restrict__
   typedef KeyLoader<E4M3, NQ> KL;
   constexpr int kNBuf = E4M3 ? 2 : 4;
   constexpr int kStage = 512;
-  constexpr int kDmaPerWave = KeyLoader<false, NQ>::kPerWave;
   __shared__ __attribute__((aligned(1024))) char tiles[kNBuf][kTileBytes];
   __shared__ Cand staged[NQ][kStage];
   const int lane = lane_id();
@@ -355,46 +409,8 @@ __global__ __launch_bounds__(64 * NQ) void k_score_mfma(const void* __restrict__
     }
   };
 
-  if constexpr (!E4M3) {
-    typename KL::Regs none;
-    KL::init(none, ld_bytes, wave, lane);
-    const int64_t n_pre = n_tiles < kNBuf - 1 ? n_tiles : kNBuf - 1;
-    for (int64_t p = 0; p < n_pre; ++p) KL::fetch(kbytes, ld_bytes, L, tile_start(p), tiles[p], wave, lane, none);
-    for (int64_t i = 0; i < n_tiles; ++i) {
-      const int64_t newer = n_tiles - 1 - i;
-      if (newer >= 2) wait_vmem_below<2 * kDmaPerWave>();
-      else if (newer == 1) wait_vmem_below<kDmaPerWave>();
-      else wait_vmem_below<0>();
-      lds_barrier();
-      if (i + kNBuf - 1 < n_tiles)
-        KL::fetch(kbytes, ld_bytes, L, tile_start(i + kNBuf - 1), tiles[(i + kNBuf - 1) % kNBuf], wave, lane, none);
-      process_tile(tiles[i % kNBuf], tile_start(i));
-    }
-  } else {
-    typename KL::Regs ring[2];
-    if (n_tiles > 0) {
-      KL::fetch(kbytes, ld_bytes, L, tile_start(0), nullptr, wave, lane, ring[0]);
-      if (n_tiles > 1) KL::fetch(kbytes, ld_bytes, L, tile_start(1), nullptr, wave, lane, ring[1]);
-      KL::commit(ring[0], tiles[0], threadIdx.x);
-      if (n_tiles > 2) KL::fetch(kbytes, ld_bytes, L, tile_start(2), nullptr, wave, lane, ring[0]);
-    }
-    // tile i + 1 (ring slot (i + 1) % 2) goes to LDS while tile i is scored; its slot then takes tile i + 3.
-    // Unrolled by two so that ring slots and LDS buffers are compile-time (a runtime-indexed ring would live in
-    // scratch memory).
-    auto step = [&](int64_t i, auto P) {
-      constexpr int p = decltype(P)::value;
-      lds_barrier();
-      if (i + 1 < n_tiles) {
-        KL::commit(ring[1 - p], tiles[1 - p], threadIdx.x);
-        if (i + 3 < n_tiles) KL::fetch(kbytes, ld_bytes, L, tile_start(i + 3), nullptr, wave, lane, ring[1 - p]);
-      }
-      process_tile(tiles[p], tile_start(i));
-    };
-    for (int64_t i = 0; i < n_tiles; i += 2) {
-      step(i, std::integral_constant<int, 0>{});
-      if (i + 1 < n_tiles) step(i + 1, std::integral_constant<int, 1>{});
-    }
-  }
+  walk_tiles<E4M3, NQ, kNBuf>(kbytes, ld_bytes, L, n_tiles, tile_start, tiles, wave, lane,
+                              [&](const char* tile, int64_t i) { process_tile(tile, tile_start(i)); });
   if (active && mode == kScoreEmit) {
     if (n_emit > 0) flush();
     if (lane == 0) seg_cnt[(int64_t)b * gridDim.x + blockIdx.x] = (uint32_t)n_out;
@@ -494,6 +510,222 @@ __global__ __launch_bounds__(64 * NQ) void k_stream_select(const void* __restric
   if (active && lane == 0) buf_n[b] = n;
 }
 
+
+// ---- streaming selection for few queries ---------------------------------------------------------------------------
+// One launch scores a range of positions for every query. Workgroup = NQ waves = NQ queries scoring a run of at most
+// stream_wg_keys / NQ positions, whose keys stay in LDS (the score matrix never leaves the chip). Each query wave then
+//   1. publishes one statistic of its chunk: x = the m-th largest of its 64 per-lane maxima, so that at least m keys
+//      of the chunk are >= x;
+//   2. waits, a bounded number of polls, for the other workgroups of the launch to publish theirs (the grid is
+//      sized to be co-resident, so they normally have; after the last poll it goes on with whatever is published);
+//   3. takes T = the r-th largest published x with r = ceil(k / m): r chunks hold at least m keys >= T each, so at
+//      least k candidates score >= T and T is a lower bound of the k-th key, whatever subset was seen. The bound of
+//      the earlier launches of the call (thr[b]) is a lower bound too; the larger one is used;
+//   4. emits its keys >= T, in position order, to its own segment of the merge's input.
+// Workgroup 0 of each query group also takes the same statistic over every slot of the call so far and stores it in
+// thr[b] for the next launch. No key per (query, position) is written to memory.
+// keys per workgroup in LDS, over its NQ queries: 32 KB, or 16 KB where four bf16 DMA buffers (64 KB) are staged
+// for only four queries, so that two such workgroups share a CU
+constexpr int stream_wg_keys(bool e4m3, int nq) { return (!e4m3 && nq == 4) ? 4096 : 8192; }
+constexpr int kStreamMaxWgs = 512;    // workgroups per query group and launch (eight slots per lane)
+constexpr int kStreamTopCap = 1024;   // kept statistics of earlier launches per query (r <= 512 of them are needed)
+
+struct StreamArgs {
+  int64_t lo, hi;        // positions of this launch
+  int n_sink, n_window;
+  int k, m;              // k of the selection; m of the published statistic (1..64)
+  uint32_t* pub;         // [B, pub_ld], zero at the first launch: slots (this launch's workgroup w owns slot slot0 + w)
+                         // and, from word flag0 of the first query row of each group, one flag per workgroup
+  int64_t flag0;
+  int64_t pub_ld;
+  int slot0;
+  uint32_t* thr;         // [B] lower bound carried between launches
+  uint32_t* top;         // [B, kStreamTopCap + 1]: count, then the largest statistics of the earlier launches
+  int first;             // first launch of the call: thr and top are not read
+  int last;              // last launch of the call: thr and top are not written
+  Cand* cand;            // [B, cand_ld]: segment j at cand + j * seg_cap
+  int64_t cand_ld, seg_cap;
+  uint32_t* seg_cnt;     // [B, seg_ld]
+  int64_t seg_ld;
+  int spin_limit;        // polls of the other workgroups' slots before going on without them
+};
+
+// The r-th largest (r >= 1) of the values v[j] (j < NV, lanes x registers) of the wave, or 0 when fewer than r are
+// nonzero: the largest x with at least r values >= x, found bit by bit.
+template <int NV>
+__device__ __forceinline__ uint32_t wave_rth_largest(const uint32_t (&v)[NV], int r) {
+  uint32_t prefix = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = prefix | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) cnt += __popcll(ballot(v[j] >= c));
+    prefix = cnt >= r ? c : prefix;
+  }
+  return prefix;
+}
+
+// Descending bitonic sort of one value per lane across the wave.
+__device__ __forceinline__ uint32_t wave_sort_desc(uint32_t v, int lane) {
+#pragma unroll
+  for (int size = 2; size <= kWave; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const uint32_t o = (uint32_t)__shfl_xor((int)v, stride, kWave);
+      const bool lower = (lane & stride) == 0;       // this lane holds the lower index of the pair
+      const bool desc = (lane & size) == 0;          // this block sorts descending (the last one: all lanes)
+      const uint32_t hi = v > o ? v : o, lo = v > o ? o : v;
+      v = (lower == desc) ? hi : lo;
+    }
+  }
+  return v;
+}
+
+template <int NMT, bool E4M3, int NQ>
+__global__ __launch_bounds__(64 * NQ) void k_score_stream(const void* __restrict__ q, const float* __restrict__ w,
+                                                          const void* __restrict__ k, int64_t k_ld, int64_t L, int B,
+                                                          const int32_t* __restrict__ t, StreamArgs a) {
+  constexpr int kNBuf = E4M3 ? 2 : 4;
+  constexpr int kRun = stream_wg_keys(E4M3, NQ) / NQ;  // keys of one query in LDS
+  constexpr int kSlotRegs = kStreamMaxWgs / kWave;
+  __shared__ __attribute__((aligned(1024))) char tiles[kNBuf][kTileBytes];
+  __shared__ uint32_t keys_s[NQ][kRun];
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int b = blockIdx.y * NQ + wave;
+  const bool active = b < B;
+  const int n_wg = gridDim.x, wg = blockIdx.x;
+  const int64_t tiles_total = (a.hi - a.lo + kTileKeys - 1) / kTileKeys;
+  const int64_t run = (tiles_total + n_wg - 1) / n_wg;  // <= kRun / 64 (the host plans it so)
+  const int64_t first_tile = (int64_t)wg * run;
+  const int64_t left = tiles_total - first_tile;
+  const int n_tiles = (int)(left < 0 ? 0 : (left < run ? left : run));
+  auto tile_start = [&](int64_t i) { return a.lo + (first_tile + i) * kTileKeys; };
+  const char* kbytes = reinterpret_cast<const char*>(k);
+  const int64_t ld_bytes = k_ld * (E4M3 ? 1 : 2);
+
+  bf16x8 qa[NMT][kSteps];
+  float wv[NMT][16];
+  int64_t tb = L - 1;
+  if (active) {
+    tb = t ? (int64_t)t[b] : L - 1;
+    load_query<NMT, E4M3>(q, w, b, lane, qa, wv);
+  }
+  // the query and weight loads complete before the first tile copy is issued: the compiler then knows them done,
+  // instead of waiting for them inside the tile loop, where its vmcnt waits would also drain the copies in flight
+  wait_vmem();
+  walk_tiles<E4M3, NQ, kNBuf>(kbytes, ld_bytes, L, n_tiles, tile_start, tiles, wave, lane,
+                              [&](const char* tile, int64_t i) {
+                                if (!active) return;
+                                const float score = score_tile<NMT>(tile, lane, qa, wv);
+                                const int64_t s = tile_start(i) + lane;
+                                const bool cand = s < a.hi && is_candidate(s, tb, a.n_sink, a.n_window);
+                                keys_s[wave][i * kTileKeys + lane] = cand ? score_key(score) : 0u;
+                              });
+  // 1. the chunk's statistic (each lane reads back only the keys it wrote itself)
+  uint32_t lmax = 0;
+  for (int i = 0; i < n_tiles; ++i) {
+    const uint32_t key = keys_s[wave][i * kTileKeys + lane];
+    lmax = key > lmax ? key : lmax;
+  }
+  const uint32_t x = (uint32_t)__shfl((int)wave_sort_desc(lmax, lane), a.m - 1, kWave);
+  // Cross-workgroup data goes through device-coherent single accesses (agent-scope atomics: they bypass the
+  // per-XCD L2 caches, which are not coherent with one another), never through fences, which would write back and
+  // invalidate a whole L2 under the other workgroups' tile copies.
+  uint32_t* slots = a.pub + (int64_t)(active ? b : 0) * a.pub_ld;
+  if (active && lane == 0) __hip_atomic_store(slots + a.slot0 + wg, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  wait_vmem();  // the slot store has completed (is visible device-wide) before the workgroup raises its flag
+  __syncthreads();
+
+  // 2. per workgroup and launch, a flag word (the last pub_ld - slots words of the group's first query row) says
+  // that its waves' slots are all written: wave 0 raises it, then polls, a bounded number of times, the flags of
+  // every workgroup of the launch in its group; then every wave reads its query's slots (a slot never written reads
+  // 0, which the bound ignores: the slots and flags of a call start at zero)
+  uint32_t* flags = a.pub + (int64_t)(blockIdx.y * NQ) * a.pub_ld + a.flag0;
+  if (wave == 0) {
+    if (lane == 0) __hip_atomic_store(flags + a.slot0 + wg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int it = 0; it < a.spin_limit; ++it) {
+      bool up = true;
+#pragma unroll
+      for (int j = 0; j < kSlotRegs; ++j) {
+        const int i = j * kWave + lane;
+        if (i < n_wg) up = up && __hip_atomic_load(flags + a.slot0 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+      }
+      if (__all(up)) break;
+      __builtin_amdgcn_s_sleep(4);
+    }
+  }
+  __syncthreads();
+  if (!active) return;  // no barrier follows
+  uint32_t xs[kSlotRegs];
+#pragma unroll
+  for (int j = 0; j < kSlotRegs; ++j) {
+    const int i = j * kWave + lane;
+    xs[j] = i < n_wg ? __hip_atomic_load(slots + a.slot0 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+  }
+
+  // 3. the lower bound of the k-th key
+  const int r = (a.k + a.m - 1) / a.m;
+  uint32_t T = wave_rth_largest(xs, r);
+  if (!a.first) {
+    const uint32_t prev = __hip_atomic_load(a.thr + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    T = prev > T ? prev : T;
+  }
+  if (wg == 0 && !a.last) {
+    // the same statistic over every slot of the call so far, for the next launch: the r-th largest of the union is
+    // the r-th largest of (the r largest of the earlier launches' slots, kept in top[b]) and this launch's slots;
+    // the values >= it are kept as the new top[b] (only this wave touches top[b])
+    constexpr int kTopRegs = kStreamTopCap / kWave;
+    uint32_t* tp = a.top + (int64_t)b * (kStreamTopCap + 1);
+    const int tn = a.first ? 0 : (int)tp[0];
+    uint32_t ys[kTopRegs];
+#pragma unroll
+    for (int j = 0; j < kTopRegs; ++j) {
+      const int i = j * kWave + lane;
+      ys[j] = i < tn ? tp[1 + i] : 0u;
+    }
+    uint32_t u = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t c = u | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int j = 0; j < kSlotRegs; ++j) cnt += __popcll(ballot(xs[j] >= c));
+#pragma unroll
+      for (int j = 0; j < kTopRegs; ++j) cnt += __popcll(ballot(ys[j] >= c));
+      u = cnt >= r ? c : u;
+    }
+    wait_vmem();  // every load of top[b] has returned before it is overwritten
+    int n = 0;
+    auto keep = [&](uint32_t v) {
+      const bool f = v != 0u && v >= u;
+      const uint64_t mk = ballot(f);
+      const int o = n + lanes_below(mk);
+      if (f && o < kStreamTopCap) tp[1 + o] = v;
+      n += __popcll(mk);
+    };
+#pragma unroll
+    for (int j = 0; j < kSlotRegs; ++j) keep(xs[j]);
+#pragma unroll
+    for (int j = 0; j < kTopRegs; ++j) keep(ys[j]);
+    if (lane == 0) {
+      tp[0] = (uint32_t)(n < kStreamTopCap ? n : kStreamTopCap);  // ties beyond the cap change no r-th value
+      __hip_atomic_store(a.thr + b, u > T ? u : T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+
+  // 4. emission of the keys >= T in position order
+  Cand* seg = a.cand + (int64_t)b * a.cand_ld + (int64_t)(a.slot0 + wg) * a.seg_cap;
+  int n_out = 0;
+  for (int i = 0; i < n_tiles; ++i) {
+    const uint32_t key = keys_s[wave][i * kTileKeys + lane];
+    const bool emit = key != 0u && key >= T;
+    const uint64_t mk = ballot(emit);
+    if (emit) seg[n_out + lanes_below(mk)] = Cand{key, (int32_t)(tile_start(i) + lane)};
+    n_out += __popcll(mk);
+  }
+  if (lane == 0) a.seg_cnt[(int64_t)b * a.seg_ld + a.slot0 + wg] = (uint32_t)n_out;
+}
+
 template <int QT, int KT>
 hipError_t launch_valu(const IndexerArgs& a, int64_t lo, int64_t hi, int mode, float* scores, int64_t scores_ld,
                        int n_sink, int n_window, const uint32_t* thr, Cand* cand, int64_t cand_ld,
@@ -590,6 +822,117 @@ hipError_t launch_score(const IndexerArgs& a, int64_t lo, int64_t hi, int mode, 
 }
 
 bool stream_select_supported(const IndexerArgs& a) { return score_uses_mfma(a); }
+
+bool stream_supported(const IndexerArgs& a) { return score_uses_mfma(a); }
+
+StreamPlan stream_plan(const IndexerArgs& a, int64_t end) {
+  StreamPlan p{};
+  p.nq = a.B >= 8 ? 8 : 4;
+  p.run_keys = stream_wg_keys(a.q_dtype == 2, p.nq) / p.nq;
+  p.end = end;
+  // launch ranges hold whole runs, so the workgroup count of all launches together does not depend on how many
+  // workgroups one launch has; the first query row of each group also holds one flag per workgroup
+  p.slots = (end + p.run_keys - 1) / p.run_keys;
+  p.pub_ld = 2 * p.slots;
+  p.top_words = kStreamTopCap + 1;
+  return p;
+}
+
+namespace {
+// Workgroups of one k_score_stream instance resident on the current device at once (cached per device).
+template <int NMT, bool E4M3, int NQ>
+hipError_t stream_resident(int* out) {
+  static std::atomic<int> cache[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *out = c;
+      return hipSuccess;
+    }
+  }
+  int per_cu = 0, cus = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k_score_stream<NMT, E4M3, NQ>),
+                                                   64 * NQ, 0);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int r = per_cu * cus > 0 ? per_cu * cus : 1;
+  if (dev >= 0 && dev < 64) cache[dev].store(r, std::memory_order_relaxed);
+  *out = r;
+  return hipSuccess;
+}
+
+template <int NMT, bool E4M3, int NQ>
+hipError_t launch_stream_t(const IndexerArgs& a, int k, int n_sink, int n_window, const StreamPlan& p, uint32_t* pub,
+                           uint32_t* thr, uint32_t* top, uint32_t* seg_cnt, Cand* cand, int spin_limit,
+                           hipStream_t st) {
+  int resident = 0;
+  hipError_t e = stream_resident<NMT, E4M3, NQ>(&resident);
+  if (e != hipSuccess) return e;
+  const int groups = (a.B + NQ - 1) / NQ;
+  int n_wg = resident / groups;
+  n_wg = n_wg < 1 ? 1 : (n_wg > kStreamMaxWgs ? kStreamMaxWgs : n_wg);
+  const int64_t range = (int64_t)n_wg * p.run_keys;
+  // statistic: the m-th largest lane maximum of each chunk, m chosen so that about 2k keys of a launch's range
+  // reach the bound (at most 64 lanes; at least k / n_wg so that r = ceil(k / m) chunks can exist)
+  int m = (int)((2 * (int64_t)k + n_wg - 1) / n_wg);
+  m = m < 1 ? 1 : (m > 64 ? 64 : m);
+  StreamArgs sa{};
+  sa.n_sink = n_sink;
+  sa.n_window = n_window;
+  sa.k = k;
+  sa.m = m;
+  sa.pub = pub;
+  sa.pub_ld = p.pub_ld;
+  sa.flag0 = p.slots;
+  sa.thr = thr;
+  sa.top = top;
+  sa.cand = cand;
+  sa.cand_ld = p.slots * (int64_t)p.run_keys;
+  sa.seg_cap = p.run_keys;
+  sa.seg_cnt = seg_cnt;
+  sa.seg_ld = p.slots;
+  sa.spin_limit = spin_limit;
+  e = launch_fill_u32(pub, (int64_t)a.B * p.pub_ld, 0u, st);  // slots and counters of the call start at zero
+  if (e != hipSuccess) return e;
+  int slot0 = 0;
+  for (int64_t lo = 0; lo < p.end; lo += range) {
+    const int64_t hi = lo + range < p.end ? lo + range : p.end;
+    const int wgs = (int)((hi - lo + p.run_keys - 1) / p.run_keys);
+    sa.lo = lo;
+    sa.hi = hi;
+    sa.slot0 = slot0;
+    sa.first = lo == 0;
+    sa.last = hi >= p.end;
+    SA_LAUNCH((k_score_stream<NMT, E4M3, NQ>), dim3((unsigned)wgs, (unsigned)groups), dim3(64 * NQ), 0, st, a.q, a.w,
+              a.k, a.k_ld, a.L, a.B, a.t, sa);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    slot0 += wgs;
+  }
+  return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_stream_decode(const IndexerArgs& a, int k, int n_sink, int n_window, const StreamPlan& p,
+                                uint32_t* pub, uint32_t* thr, uint32_t* top, uint32_t* seg_cnt, Cand* cand,
+                                int spin_limit, hipStream_t st) {
+  if (!score_uses_mfma(a) || a.B < 1) return a.B < 1 ? hipSuccess : hipErrorInvalidValue;
+  const bool fp8 = a.q_dtype == 2;
+#define SA_STREAMD(NMT, F8, NQ) \
+  return launch_stream_t<NMT, F8, NQ>(a, k, n_sink, n_window, p, pub, thr, top, seg_cnt, cand, spin_limit, st)
+  if (p.nq == 8) {
+    if (a.H == 64) { if (fp8) SA_STREAMD(2, true, 8); else SA_STREAMD(2, false, 8); }
+    else { if (fp8) SA_STREAMD(1, true, 8); else SA_STREAMD(1, false, 8); }
+  } else {
+    if (a.H == 64) { if (fp8) SA_STREAMD(2, true, 4); else SA_STREAMD(2, false, 4); }
+    else { if (fp8) SA_STREAMD(1, true, 4); else SA_STREAMD(1, false, 4); }
+  }
+#undef SA_STREAMD
+}
 
 hipError_t launch_stream_select(const IndexerArgs& a, int k, int n_sink, int n_window, Cand* buf, int32_t* buf_n,
                                 int cap, hipStream_t st) {

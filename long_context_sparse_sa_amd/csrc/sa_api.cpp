@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -20,6 +21,10 @@ thread_local char g_err[512] = "";
 thread_local void* const* g_stage_ev = nullptr;
 thread_local int g_stage_n = 0;
 thread_local int g_stage_next = 0;
+
+// Test knob of the streaming selection: polls of the other workgroups' statistics (negative: the default).
+thread_local int g_stream_spin = -1;
+constexpr int kStreamSpinDefault = 4096;
 
 int fail(int status, const char* fmt, ...) {
   va_list ap;
@@ -97,11 +102,23 @@ constexpr int64_t kAutoRadixMaxKeys = (int64_t)1 << 24;  // B * L up to which fe
 int resolve_algo(int algo, const sa::IndexerArgs& a) {
   if (algo != SA_TOPK_AUTO) return algo;
   if (a.B >= kAutoPerQueryMinB && sa::stream_select_supported(a)) return SA_TOPK_PER_QUERY;
-  // few queries: writing one key per position and selecting over all of them with every workgroup beats the
-  // level-by-level thresholds until the key buffer gets large; beyond that the radix select takes a prefix and
-  // its k-th key prunes the rest (measured faster than thresholds refined over geometric levels from 16K)
+  // few queries on the MFMA scorer: the streaming bound keeps every score on chip
+  if (sa::stream_supported(a)) return SA_TOPK_STREAM;
+  // other shapes (the VALU scorer): one key per position and a radix select over all of them while the key
+  // buffer is small; beyond that the radix select takes a prefix and its k-th key prunes the rest
   return (int64_t)a.B * a.L <= kAutoRadixMaxKeys ? SA_TOPK_RADIX : SA_TOPK_RADIX_LEVELS;
 }
+
+struct StreamWs {
+  sa::StreamPlan p;  // the on-chip part over [0, first)
+  uint32_t* thr;
+  uint32_t* top;
+  uint32_t* pub;
+  uint32_t* seg_cnt;
+  sa::Cand* cand;
+  sa::Cand* gather;
+  size_t bytes;
+};
 
 struct RadixWs {
   sa::RadixPlan p;
@@ -121,6 +138,7 @@ RadixWs carve_radix(void* ws, const sa::IndexerArgs& a) {
   w.bytes = align_up(c.off, 256);
   return w;
 }
+
 
 // Level boundaries of the split-L algorithm: [0, first), [first, 8 first), ... up to L. The first level holds at least
 // 4 k positions so that the first threshold already prunes.
@@ -219,6 +237,41 @@ RadixLevelsWs carve_radix_levels(void* ws, const sa::IndexerArgs& a, int k) {
   return w;
 }
 
+// SA_TOPK_STREAM: the positions [0, first) are scored on chip by the streaming kernel (first = min(L, 2^20));
+// beyond them, key ranges [first, 8 first), ... emit only keys above the exact k-th key kept so far, as in the
+// level algorithm, each followed by a merge.
+constexpr int64_t kStreamFirst = (int64_t)1 << 20;
+
+struct StreamAll {
+  StreamWs s;
+  int64_t first;
+  std::vector<int64_t> lv;  // key ranges after the on-chip part (empty when it covers the cache)
+  SplitLWs l;
+  size_t bytes;
+};
+
+StreamAll carve_stream(void* ws, const sa::IndexerArgs& a, int k) {
+  StreamAll w{};
+  w.first = std::min(a.L, kStreamFirst);
+  StreamWs& st = w.s;
+  st.p = sa::stream_plan(a, w.first);
+  Carver c(ws);
+  st.thr = c.take<uint32_t>(a.B);
+  st.top = c.take<uint32_t>((size_t)a.B * st.p.top_words);
+  st.pub = c.take<uint32_t>((size_t)a.B * st.p.pub_ld);
+  st.seg_cnt = c.take<uint32_t>((size_t)a.B * st.p.slots);
+  st.cand = c.take<sa::Cand>((size_t)a.B * st.p.slots * st.p.run_keys);
+  st.gather = c.take<sa::Cand>((size_t)a.B * st.p.slots * st.p.run_keys);
+  st.bytes = align_up(c.off, 256);
+  w.bytes = st.bytes;
+  if (w.first < a.L) {
+    w.lv = levels_after(w.first, a.L);
+    w.l = carve_levels(ws ? static_cast<char*>(ws) + st.bytes : nullptr, a, k, w.lv, false);
+    w.bytes += w.l.bytes;
+  }
+  return w;
+}
+
 struct PerQueryWs {
   sa::Cand* buf;
   int32_t* buf_n;
@@ -253,6 +306,8 @@ SA_API void sa_set_stage_events(void* const* events, int n) {
 }
 
 SA_API int sa_stage_events_used(void) { return g_stage_next; }
+
+SA_API void sa_set_stream_spin_limit(int polls) { g_stream_spin = polls; }
 
 SA_API const char* sa_status_string(int s) {
   switch (s) {
@@ -295,6 +350,7 @@ SA_API size_t sa_select_topk_workspace(int64_t L, int32_t B, int32_t H, int32_t 
   const sa::IndexerArgs a = make_indexer(nullptr, q_dtype, nullptr, nullptr, k_dtype, d, L, B, H, d, nullptr);
   const int alg = resolve_algo(algo, a);
   if (alg == SA_TOPK_PER_QUERY) return carve_per_query(nullptr, a, k_sparse).bytes;
+  if (alg == SA_TOPK_STREAM) return carve_stream(nullptr, a, k_sparse).bytes;
   if (alg == SA_TOPK_RADIX) return carve_radix(nullptr, a).bytes;
   if (alg == SA_TOPK_RADIX_LEVELS) return carve_radix_levels(nullptr, a, k_sparse).bytes;
   return carve_split_l(nullptr, a, k_sparse).bytes;
@@ -311,11 +367,13 @@ SA_API int sa_select_topk(const void* q, int q_dtype, const float* w, const void
     return fail(SA_ERR_SHAPE, "k_sparse must be in [1, %d]", sa::merge_max_k());
   if (idx_ld < k_sparse) return fail(SA_ERR_SHAPE, "idx_ld (%d) < k_sparse (%d)", idx_ld, k_sparse);
   if (n_sink < 0 || n_window < 0) return fail(SA_ERR_SHAPE, "n_sink and n_window must be >= 0");
-  if (algo < SA_TOPK_AUTO || algo > SA_TOPK_RADIX_LEVELS) return fail(SA_ERR_SHAPE, "unknown algo %d", algo);
+  if (algo < SA_TOPK_AUTO || algo > SA_TOPK_STREAM) return fail(SA_ERR_SHAPE, "unknown algo %d", algo);
   const sa::IndexerArgs a = make_indexer(q, q_dtype, w, k, k_dtype, k_ld, L, B, H, d, t);
   const int alg = resolve_algo(algo, a);
   if (alg == SA_TOPK_PER_QUERY && !sa::stream_select_supported(a))
     return fail(SA_ERR_UNSUPPORTED, "the per-query algorithm needs d = 128, H in {32, 64} and bf16 or e4m3 inputs");
+  if (alg == SA_TOPK_STREAM && !sa::stream_supported(a))
+    return fail(SA_ERR_UNSUPPORTED, "the streaming algorithm needs d = 128, H in {32, 64} and bf16 or e4m3 inputs");
   const size_t need = sa_select_topk_workspace(L, B, H, d, q_dtype, k_dtype, k_sparse, alg);
   if (!ws || ws_bytes < need) return fail(SA_ERR_WORKSPACE, "workspace needs %zu bytes", need);
   if (!aligned16(ws)) return fail(SA_ERR_ALIGN, "workspace must be 16-byte aligned");
@@ -337,6 +395,58 @@ SA_API int sa_select_topk(const void* q, int q_dtype, const float* w, const void
     out.n_sel = n_sel;
     e = sa::launch_merge(B, k_sparse, in, w2.gather, w2.cap, out, s);
     return e == hipSuccess ? SA_OK : hip_fail(e, "sa_select_topk (final merge)");
+  }
+  if (alg == SA_TOPK_STREAM) {
+    // the on-chip part: scoring launches that emit only keys at or above a proven lower bound of the k-th key
+    const StreamAll w2 = carve_stream(ws, a, k_sparse);
+    const bool whole = w2.first >= L;
+    e = sa::launch_stream_decode(a, k_sparse, n_sink, n_window, w2.s.p, w2.s.pub, w2.s.thr, w2.s.top, w2.s.seg_cnt,
+                                 w2.s.cand, g_stream_spin >= 0 ? g_stream_spin : kStreamSpinDefault, s);
+    if (e != hipSuccess) return hip_fail(e, "sa_select_topk (stream score)");
+    // its exact top-k: the final selection, or the kept list and its k-th key for the key ranges after it
+    sa::MergeIn in{};
+    in.cand = w2.s.cand;
+    in.cand_ld = w2.s.p.slots * (int64_t)w2.s.p.run_keys;
+    in.seg_cnt = w2.s.seg_cnt;
+    in.n_seg = (int)w2.s.p.slots;
+    in.seg_cap = w2.s.p.run_keys;
+    sa::MergeOut out{};
+    out.final_mode = whole ? 1 : 0;
+    out.kept_out = whole ? nullptr : w2.l.kept;
+    out.kept_n_out = whole ? nullptr : w2.l.kept_n;
+    out.thr_out = whole ? nullptr : w2.l.thr;
+    out.idx = idx;
+    out.idx_ld = idx_ld;
+    out.n_sel = n_sel;
+    e = sa::launch_merge(B, k_sparse, in, w2.s.gather, (int64_t)w2.s.p.slots * w2.s.p.run_keys, out, s);
+    if (e != hipSuccess) return hip_fail(e, "sa_select_topk (stream merge)");
+    for (size_t i = 0; i + 1 < w2.lv.size(); ++i) {
+      const int64_t lo = w2.lv[i], hi = w2.lv[i + 1];
+      e = sa::launch_score(a, lo, hi, sa::kScoreEmit, nullptr, 0, n_sink, n_window, w2.l.thr, w2.l.cand,
+                           w2.l.cand_ld, w2.l.seg_cnt, s);
+      if (e != hipSuccess) return hip_fail(e, "sa_select_topk (score)");
+      sa::MergeIn li{};
+      li.kept = w2.l.kept;
+      li.kept_ld = k_sparse;
+      li.kept_n = w2.l.kept_n;
+      li.cand = w2.l.cand;
+      li.cand_ld = w2.l.cand_ld;
+      const sa::EmitPlan ep = sa::score_emit_plan(a, lo, hi);
+      li.seg_cnt = w2.l.seg_cnt;
+      li.n_seg = ep.n_seg;
+      li.seg_cap = ep.seg_cap;
+      sa::MergeOut lo_{};
+      lo_.final_mode = i + 2 == w2.lv.size() ? 1 : 0;
+      lo_.kept_out = w2.l.kept;
+      lo_.kept_n_out = w2.l.kept_n;
+      lo_.thr_out = w2.l.thr;
+      lo_.idx = idx;
+      lo_.idx_ld = idx_ld;
+      lo_.n_sel = n_sel;
+      e = sa::launch_merge(B, k_sparse, li, w2.l.gather, w2.l.gather_cap, lo_, s);
+      if (e != hipSuccess) return hip_fail(e, "sa_select_topk (merge)");
+    }
+    return SA_OK;
   }
   if (alg == SA_TOPK_RADIX) {
     // every position's key into the workspace (0 for positions outside the candidate range), then the radix

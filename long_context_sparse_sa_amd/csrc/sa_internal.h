@@ -131,6 +131,26 @@ hipError_t launch_keys_from_scores(const float* scores, int64_t scores_ld, int64
                                    int n_sink, int n_window, const RadixPlan& p, uint32_t* keys, uint32_t* ctl,
                                    int64_t ctl_words, hipStream_t stream);
 
+// Streaming selection for few queries (decode): launches over co-resident ranges of positions; each keeps its keys
+// on chip, publishes per-chunk statistics, derives a lower bound T of each query's k-th key from them and emits only
+// keys >= T into per-workgroup segments (one segment per workgroup and launch) for a final merge.
+struct StreamPlan {
+  int64_t end;       // positions [0, end) are scored
+  int nq;            // queries per workgroup
+  int run_keys;      // positions per workgroup (a multiple of 64) = segment capacity
+  int64_t slots;     // workgroups (= statistics slots = segments) per query over all launches
+  int64_t pub_ld;    // words per query row of the statistics area: the slots and a group counter
+  int top_words;     // words per query of the kept-statistics sketch
+};
+bool stream_supported(const IndexerArgs& a);
+StreamPlan stream_plan(const IndexerArgs& a, int64_t end);
+// pub [B, p.pub_ld] 32-bit slots and counters (zeroed by the call's first launch); thr [B]; top [B, p.top_words];
+// seg_cnt [B, p.slots]; cand [B, p.slots * p.run_keys]. spin_limit: polls of the other workgroups' publication
+// before going on without them.
+hipError_t launch_stream_decode(const IndexerArgs& a, int k, int n_sink, int n_window, const StreamPlan& p,
+                                uint32_t* pub, uint32_t* thr, uint32_t* top, uint32_t* seg_cnt, Cand* cand,
+                                int spin_limit, hipStream_t stream);
+
 // Streaming per-query selection for many queries (prefill chunk): one pass over each query's visible keys keeps
 // at most `cap` candidates per query in buf[b, :] (count in buf_n[b]) that contain the exact top-k.
 bool stream_select_supported(const IndexerArgs& a);

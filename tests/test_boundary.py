@@ -102,15 +102,32 @@ def test_select_topk_workspace_sizes(lib):
 
 
 def test_select_topk_auto_choices(lib):
-    # up to 2^24 keys over all queries AUTO takes the plain radix select (one key per position)
-    r = lib.sa_select_topk_workspace(131072, 16, 64, 128, BF16, BF16, 2048, 3)
+    # few queries on the MFMA scorer shapes: AUTO takes the streaming algorithm (5), whose workspace reserves, for
+    # the first min(L, 2^20) positions scored on chip, one 8-byte candidate slot per position for the emitted
+    # segments and as many for the merge's overflow (only candidates at or above the bound are ever written), plus
+    # per-workgroup statistics; beyond 2^20 positions, the emission levels' candidate areas
+    for L, B, dt in [(131072, 16, BF16), (10_000_000, 4, E4M3), (1000, 1, BF16)]:
+        s = lib.sa_select_topk_workspace(L, B, 64, 128, dt, dt, 2048, 5)
+        assert lib.sa_select_topk_workspace(L, B, 64, 128, dt, dt, 2048, 0) == s
+        first = min(L, 1 << 20)
+        assert B * first * 16 <= s
+        if L <= 1 << 20:
+            assert s < B * (L + 2048) * 16 + B * (L // 512 + 2) * 12 + B * 1025 * 4 + (1 << 20)
+        else:
+            assert s < B * L * 16 + (64 << 20)
+    # many queries: the per-query streaming select (2)
+    assert lib.sa_select_topk_workspace(131072, 64, 64, 128, BF16, BF16, 2048, 0) == \
+        lib.sa_select_topk_workspace(131072, 64, 64, 128, BF16, BF16, 2048, 2)
+    # shapes the MFMA scorer does not serve (fp32 here): the radix select over one key per position up to 2^24
+    # keys over all queries ...
+    r = lib.sa_select_topk_workspace(131072, 16, 64, 128, F32, F32, 2048, 3)
     assert r >= 16 * 131072 * 4
-    assert lib.sa_select_topk_workspace(131072, 16, 64, 128, BF16, BF16, 2048, 0) == r
-    # beyond that, the radix select over a prefix of at most 2^24 / B positions, then emission levels
+    assert lib.sa_select_topk_workspace(131072, 16, 64, 128, F32, F32, 2048, 0) == r
+    # ... and beyond that the radix select over a prefix of at most 2^24 / B positions, then emission levels
     L, B = 10_000_000, 4
-    w = lib.sa_select_topk_workspace(L, B, 64, 128, E4M3, E4M3, 2048, 4)
-    assert lib.sa_select_topk_workspace(L, B, 64, 128, E4M3, E4M3, 2048, 0) == w
-    prefix = (1 << 24) // B // 512 * 512
+    w = lib.sa_select_topk_workspace(L, B, 4, 32, F32, F32, 2048, 4)
+    assert lib.sa_select_topk_workspace(L, B, 4, 32, F32, F32, 2048, 0) == w
+    prefix = (1 << 24) // B // 256 * 256
     assert B * prefix * 4 <= w < B * L * 4 + B * (L - prefix) * 16 + (64 << 20)
     # a cache too short to split is selected whole by the radix part
     assert lib.sa_select_topk_workspace(600, 1, 64, 128, BF16, BF16, 100, 4) > 0

@@ -52,7 +52,7 @@ def test_index_score_dense(dtype, H, d):
         assert np.all(err <= 1e-5 * mag[vis] + 1e-30), (b, err.max())
 
 
-ALGOS = [sa.SA_TOPK_SPLIT_L, sa.SA_TOPK_PER_QUERY, sa.SA_TOPK_RADIX, sa.SA_TOPK_RADIX_LEVELS]
+ALGOS = [sa.SA_TOPK_SPLIT_L, sa.SA_TOPK_PER_QUERY, sa.SA_TOPK_RADIX, sa.SA_TOPK_RADIX_LEVELS, sa.SA_TOPK_STREAM]
 
 
 @pytest.mark.parametrize("algo", ALGOS)
@@ -91,7 +91,7 @@ def test_topk_heads32_integer_exact(algo):
         np.testing.assert_array_equal(selected(idx[b], nsel[b].item()), ref)
 
 
-@pytest.mark.parametrize("algo", [sa.SA_TOPK_RADIX, sa.SA_TOPK_RADIX_LEVELS, sa.SA_TOPK_SPLIT_L])
+@pytest.mark.parametrize("algo", [sa.SA_TOPK_RADIX, sa.SA_TOPK_RADIX_LEVELS, sa.SA_TOPK_SPLIT_L, sa.SA_TOPK_STREAM])
 def test_topk_single_query(algo):
     """B = 1: the radix select spreads one query over its largest number of chunks."""
     B, H, d, L, kk = 1, 64, 128, 200000, 1000
@@ -172,7 +172,7 @@ def test_topk_valu_path_levels():
         band_compare(selected(idx[b], nsel[b].item()), ref, cand, sc, kk)
 
 
-@pytest.mark.parametrize("algo", [sa.SA_TOPK_SPLIT_L, sa.SA_TOPK_RADIX_LEVELS])
+@pytest.mark.parametrize("algo", [sa.SA_TOPK_SPLIT_L, sa.SA_TOPK_RADIX_LEVELS, sa.SA_TOPK_STREAM])
 def test_topk_rising_scores_many_emits(algo):
     """Scores rise with position (with runs of equal bf16 keys): every later key range emits almost all of its
     positions, so the merges overflow LDS and run from the gather buffer; ties resolve to lower positions."""
@@ -237,3 +237,56 @@ def test_topk_prefilled_workspace_and_outputs(algo):
             assert n == refs[b].size, (fill, b, n)
             np.testing.assert_array_equal(selected(idx[b], n), refs[b])
             assert torch.all(idx[b, n:] == -1), (fill, b)
+
+
+def _exact_check(q, w, k, kk, n_sink, n_window, ts, idx, nsel):
+    qf, wf, kf = to_f64(q), w.double().cpu().numpy(), to_f64(k)
+    for b in range(q.shape[0]):
+        ref, sc, cand = O.select_topk(qf[b], wf[b], kf, ts[b], kk, n_sink, n_window)
+        np.testing.assert_array_equal(selected(idx[b], nsel[b].item()), ref)
+
+
+@pytest.mark.parametrize("spin", [0, 1])
+def test_topk_stream_bound_without_waiting(spin):
+    """The streaming select with its wait cut to `spin` polls (a test knob set from the host): workgroups go on with
+    whatever statistics are published by then, so their bounds are weaker and more keys reach the merge, but the
+    selection is the same. Integer scores (exact, heavy ties), three launches of 16 queries, per-query t."""
+    B, H, d, L, kk = 16, 64, 128, 300000, 2048
+    q, w, k = _inputs(21, B, H, d, L, "bf16", integer=True)
+    ts = [L - 1 - 7919 * b for b in range(B)]
+    t = torch.tensor(ts, dtype=torch.int32, device=DEV)
+    lib = sa.load()
+    lib.sa_set_stream_spin_limit(spin)
+    try:
+        idx, nsel = sa.sa_select_topk(q, w, k, kk, n_sink=4, n_window=128, t=t, algo=sa.SA_TOPK_STREAM)
+        torch.cuda.synchronize()
+    finally:
+        lib.sa_set_stream_spin_limit(-1)
+    _exact_check(q, w, k, kk, 4, 128, ts, idx, nsel)
+
+
+def test_topk_stream_launches_carry_the_bound_fp8():
+    """Few queries (four per workgroup) over more positions than one launch's resident workgroups cover: later
+    launches start from the bound of the earlier ones. e4m3 integer inputs: exact scores."""
+    B, H, d, L, kk = 3, 64, 128, 1_300_000, 2048
+    q, w, k = _inputs(22, B, H, d, L, "e4m3", integer=True)
+    ts = [L - 1, L - 1 - 250_000, 700_000]
+    t = torch.tensor(ts, dtype=torch.int32, device=DEV)
+    idx, nsel = sa.sa_select_topk(q, w, k, kk, n_sink=4, n_window=128, t=t, algo=sa.SA_TOPK_STREAM)
+    torch.cuda.synchronize()
+    _exact_check(q, w, k, kk, 4, 128, ts, idx, nsel)
+
+
+def test_topk_stream_repeated_calls_one_workspace():
+    """Calls in a row on one workspace with different data: the statistics slots of a call are cleared by its merge
+    and tagged with the call's nonce, so no call sees another's."""
+    B, H, d, L, kk = 9, 64, 128, 140000, 1000
+    ws = None
+    for seed in (30, 31, 32):
+        q, w, k = _inputs(seed, B, H, d, L, "bf16", integer=True)
+        if ws is None:
+            ws = torch.empty(sa.sa_select_topk_workspace(L, B, H, d, sa.SA_BF16, sa.SA_BF16, kk, sa.SA_TOPK_STREAM),
+                             dtype=torch.uint8, device=DEV)
+        idx, nsel = sa.sa_select_topk(q, w, k, kk, n_sink=2, n_window=16, algo=sa.SA_TOPK_STREAM, ws=ws)
+        torch.cuda.synchronize()
+        _exact_check(q, w, k, kk, 2, 16, [L - 1] * B, idx, nsel)
