@@ -273,3 +273,57 @@ def bucket_step(q_idx, reps32, offsets, members, q, kv, t: int, top_b: int, n_si
     R = read_set(t, n_sink, n_window, sel)
     o, lse = sparse_attn(q, kv, R, scale, d_qk, d_v, v=v)
     return sel, chosen, o, lse
+
+
+# ----------------------------------------------------------------------------------------------------------------
+# Hierarchical indexing, coarse to fine ([LongCat] section "Mechanism 3: hierarchical indexing (HI)": the cache is
+# cut into pages of P positions and each page into sub-blocks of B positions; each sub-block keeps the per-dimension
+# mean of its index keys; a page scores the indexer equation summed over its sub-blocks' mean keys; the M best pages
+# are recalled and the token-level top-k runs over their positions only).
+# Readings where the section is silent:
+#   * the mean of a sub-block is over its cached positions (the last one may be partial), computed in fp64 and
+#     stored in bf16, the dtype the keys are scored in (rounded to nearest even through fp32, see round_bf16);
+#   * query t sees the pages whose first position is <= t; a page's score sums over all its sub-blocks as cached;
+#   * pages are ranked by (fp32 page score desc, page id asc); the token stage ranks the sink/window-budget
+#     candidates inside the recalled pages exactly like the flat selection.
+# ----------------------------------------------------------------------------------------------------------------
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """The stored value of an fp64 mean: rounded to fp32 (nearest even), then to bf16 (nearest even on the upper 16
+    bits), returned as fp64. This equals one direct rounding to bf16 except when the fp64 value lies within half an
+    fp32 ulp of a bf16 midpoint, which needs member keys whose magnitudes differ by more than 2^24."""
+    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def hi_means(k: np.ndarray, B: int) -> np.ndarray:
+    """Sub-block mean keys [ceil(L / B), d] (bf16 values as fp64)."""
+    L, d = k.shape
+    n = (L + B - 1) // B
+    out = np.zeros((n, d), dtype=np.float64)
+    for i in range(n):
+        out[i] = k[i * B:min(L, (i + 1) * B)].mean(axis=0)
+    return round_bf16(out)
+
+
+def hi_page_scores(q: np.ndarray, w: np.ndarray, means: np.ndarray, sub_per_page: int, t: int, P: int):
+    """fp32 page scores of one query over its visible pages 0 .. floor(t / P): sum over the page's sub-blocks of
+    sum_j w_j ReLU(q_j . mean_n), in fp64, rounded once. Returns (scores32, page ids)."""
+    n_pages = t // P + 1
+    per_sub = index_score(q, w, means, np.arange(means.shape[0]))      # the indexer equation on each mean key
+    sc = np.array([per_sub[p * sub_per_page:(p + 1) * sub_per_page].sum() for p in range(n_pages)])
+    return sc.astype(np.float32), np.arange(n_pages, dtype=np.int64)
+
+
+def hi_select(q, w, k, means, t: int, P: int, B: int, M: int, k_sparse: int, n_sink: int, n_window: int):
+    """Two-stage selection of one query. Returns (ascending sparse positions, chosen pages ascending, page scores,
+    candidate positions of the token stage, their fp32 scores)."""
+    psc, pids = hi_page_scores(q, w, means, P // B, t, P)
+    pages = topk_positions(psc, pids, M)
+    cand = candidate_positions(t, n_sink, n_window)
+    cand = cand[np.isin(cand // P, pages)]
+    sc = index_score_f32(q, w, k, cand)
+    return topk_positions(sc, cand, k_sparse), pages, psc, cand, sc
