@@ -3,13 +3,16 @@
  *
  * The path has three steps, each a call below:
  *   score   an indexer scores every cached position           (sa_index_score, inside sa_select_topk)
- *   select  exact top-k plus sink/window positions             (sa_select_topk; sa_bucket_select for buckets)
+ *   select  exact top-k plus sink/window positions             (sa_select_topk; sa_bucket_select for buckets;
+ *                                                               sa_hi_select for the coarse-to-fine search)
  *   attend  softmax attention over only the gathered rows      (sa_sparse_attn)
  *
  * Sources (web pages; cited by title and section):
  *   [LongCat]  "LongCat Sparse Attention (LSA) deep-dive" (pinghaoyang.com.cn): section "DSA baseline: how the
  *              lightning indexer works" (indexer equation I_{t,s}, arg-topK equation, sparse-attention equation);
- *              section "Mechanism 1: streaming-aware indexing (SI)" (budget decomposition equations; HFA kernel).
+ *              section "Mechanism 1: streaming-aware indexing (SI)" (budget decomposition equations; HFA kernel);
+ *              section "Mechanism 3: hierarchical indexing (HI)" (sub-block mean keys, page scores, top-M pages,
+ *              token top-k inside them).
  *   [LSA-8]    "LSA sparse attention: does it save memory? eight QKV entries" (alphalab.site): section 2 (the four
  *              steps of Latent Sparse Attention: index keys, buckets with a representative and member positions,
  *              Flat search over representatives, read selected rows plus sink plus window); sections 3-4 (the
@@ -194,6 +197,41 @@ SA_API int sa_bucket_select_noalloc(const void* q, int q_dtype, int32_t B, int32
                                     const int32_t* offsets, const int32_t* members, int32_t n_buckets, int64_t L,
                                     const int32_t* t, int32_t top_b, int32_t n_sink, int32_t n_window, int32_t* idx,
                                     int32_t cap, int32_t* n_sel, int32_t* buckets_out, void* stream);
+
+/* ---------------------------------------------------------------------------------------------------------------
+ * sa_hi_build -- the mean keys of the coarse-to-fine index ([LongCat] HI section: every sub-block of B consecutive
+ * cached positions keeps the mean of their index keys).
+ *   k      [L, k_ld] bf16 index keys (d <= k_ld).
+ *   means  [ceil(L / sub_block), d] bf16 out, contiguous: means[n, x] = mean of k[s, x] over the cached positions
+ *          s of sub-block n (the last block may be partial); summed in fp64, divided once, rounded to fp32 and
+ *          then to bf16, to nearest even both times. Built once per cache (or per appended block); reused by
+ *          every sa_hi_select on it.
+ *
+ * sa_hi_select -- coarse-to-fine top-k ([LongCat] HI section, with the indexer equation of the DSA baseline
+ * section applied to the mean keys):
+ *   page p (positions [p P, (p+1) P), P = page_len) has score  PS_b(p) = sum over the sub-blocks n of page p of
+ *   sum_h w[b,h] relu(q[b,h,:] . means[n,:]), each sub-block term evaluated as sa_index_score evaluates one position
+ *   (fp32 accumulation). Query b sees pages whose first position is <= t_b; the n_pages_keep (= M) best visible
+ *   pages are recalled (ties: lower page id; fewer if fewer are visible). The token stage then returns the exact
+ *   top-k_sparse, as sa_select_topk defines it, of the candidates C_b (outside sink and window) that lie in the
+ *   recalled pages.
+ *   q, w, k, k_ld, L, B, H, d, t: as sa_index_score; bf16 q and k, d = 128, H in {32, 64}.
+ *   means    the output of sa_hi_build for this cache and sub_block.
+ *   page_len a multiple of 64 and of sub_block, page_len / sub_block a power of two <= 64; at most 2^17 pages.
+ *   n_pages_keep in [1, 1024].  k_sparse in [1, 16384] and <= idx_ld.
+ *   idx, idx_ld, n_sel: as sa_select_topk (ascending positions, -1 padding).
+ *   pages_out [B, n_pages_keep] int32 or NULL: the recalled pages, ascending, -1 padding.
+ *   ws / ws_bytes: at least sa_hi_select_workspace(L, B, sub_block, page_len, n_pages_keep, k_sparse) bytes.
+ * ------------------------------------------------------------------------------------------------------------- */
+SA_API int sa_hi_build(const void* k, int k_dtype, int64_t k_ld, int64_t L, int32_t d, int32_t sub_block,
+                       void* means, void* stream);
+SA_API size_t sa_hi_select_workspace(int64_t L, int32_t B, int32_t sub_block, int32_t page_len, int32_t n_pages_keep,
+                                     int32_t k_sparse);
+SA_API int sa_hi_select(const void* q, int q_dtype, const float* w, const void* k, int k_dtype, int64_t k_ld,
+                        int64_t L, int32_t B, int32_t H, int32_t d, const int32_t* t, const void* means,
+                        int32_t sub_block, int32_t page_len, int32_t n_pages_keep, int32_t k_sparse, int32_t n_sink,
+                        int32_t n_window, int32_t* idx, int32_t idx_ld, int32_t* n_sel, int32_t* pages_out,
+                        void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------------------------------
  * sa_sparse_attn -- attention over the read set only ([LongCat] DSA baseline section, sparse-attention equation,

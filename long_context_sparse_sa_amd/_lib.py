@@ -38,6 +38,10 @@ SIGNATURES = {
     "sa_bucket_select": (INT, [P, INT, I32, I32, P, P, P, I32, I64, P, I32, I32, I32, P, I32, P, P, P, SZ, P]),
     "sa_bucket_select_noalloc_max_keys": (I64, []),
     "sa_bucket_select_noalloc": (INT, [P, INT, I32, I32, P, P, P, I32, I64, P, I32, I32, I32, P, I32, P, P, P]),
+    "sa_hi_build": (INT, [P, INT, I64, I64, I32, I32, P, P]),
+    "sa_hi_select_workspace": (SZ, [I64, I32, I32, I32, I32, I32]),
+    "sa_hi_select": (INT, [P, INT, P, P, INT, I64, I64, I32, I32, I32, P, P, I32, I32, I32, I32, I32, I32, P, I32, P,
+                           P, P, SZ, P]),
     "sa_sparse_attn_workspace": (SZ, [I32, I32, I32, I32, I64, INT]),
     "sa_sparse_attn": (INT, [P, P, P, INT, I64, I64, I64, I32, I32, I32, I32, P, P, I32, P, I32, I32, F32, P, P, P,
                              SZ, P]),

@@ -176,6 +176,50 @@ def sa_bucket_select_noalloc(q_idx, reps, offsets, members, L: int, top_b: int, 
     return (idx, n_sel, buckets) if return_buckets else (idx, n_sel)
 
 
+def sa_hi_build(k_idx, sub_block: int, out=None, stream=None):
+    """Mean index keys [ceil(L / sub_block), d] (bf16) of consecutive sub-blocks of the cache's index keys."""
+    _need_cuda(k_idx)
+    L, d = k_idx.shape
+    n_sub = (L + sub_block - 1) // sub_block
+    means = torch.empty((n_sub, d), dtype=torch.bfloat16, device=k_idx.device) if out is None else out
+    if means.shape != (n_sub, d) or means.dtype != torch.bfloat16 or not means.is_contiguous():
+        raise ValueError(f"out must be a contiguous bf16 tensor of shape {(n_sub, d)}")
+    st = _lib.load().sa_hi_build(_ptr(k_idx), _dtype(k_idx), _rows(k_idx), L, d, sub_block, _ptr(means),
+                                 _stream(stream))
+    _lib.check("sa_hi_build", st)
+    return means
+
+
+def sa_hi_select_workspace(L, B, sub_block, page_len, n_pages_keep, k_sparse) -> int:
+    return int(_lib.load().sa_hi_select_workspace(L, B, sub_block, page_len, n_pages_keep, k_sparse))
+
+
+def sa_hi_select(q_idx, w, k_idx, means, sub_block: int, page_len: int, n_pages_keep: int, k_sparse: int,
+                 n_sink: int = 0, n_window: int = 0, t=None, idx_ld: Optional[int] = None, return_pages=False,
+                 ws=None, out=None, stream=None):
+    """(idx [B, idx_ld] ascending with -1 padding, n_sel [B][, pages [B, n_pages_keep]]) of the two-stage search."""
+    _need_cuda(q_idx, w, k_idx, means, t)
+    B, H, d = q_idx.shape
+    L = k_idx.shape[0]
+    if not means.is_contiguous() or means.shape != ((L + sub_block - 1) // sub_block, d):
+        raise ValueError("means must be the contiguous output of sa_hi_build for this cache and sub_block")
+    idx_ld = k_sparse if idx_ld is None else idx_ld
+    lib = _lib.load()
+    nbytes = lib.sa_hi_select_workspace(L, B, sub_block, page_len, n_pages_keep, k_sparse)
+    ws = _workspace(nbytes, q_idx.device, ws)
+    if out is None:
+        idx = torch.empty((B, idx_ld), dtype=torch.int32, device=q_idx.device)
+        n_sel = torch.empty((B,), dtype=torch.int32, device=q_idx.device)
+    else:
+        idx, n_sel = out
+    pages = torch.empty((B, n_pages_keep), dtype=torch.int32, device=q_idx.device) if return_pages else None
+    st = lib.sa_hi_select(_ptr(q_idx), _dtype(q_idx), _ptr(w), _ptr(k_idx), _dtype(k_idx), _rows(k_idx), L, B, H, d,
+                          _ptr(t), _ptr(means), sub_block, page_len, n_pages_keep, k_sparse, n_sink, n_window,
+                          _ptr(idx), idx.stride(0), _ptr(n_sel), _ptr(pages), _ptr(ws), nbytes, _stream(stream))
+    _lib.check("sa_hi_select", st)
+    return (idx, n_sel, pages) if return_pages else (idx, n_sel)
+
+
 def sa_sparse_attn_workspace(B, H, d_qk, d_v, max_rows, dtype) -> int:
     return int(_lib.load().sa_sparse_attn_workspace(B, H, d_qk, d_v, max_rows, dtype))
 

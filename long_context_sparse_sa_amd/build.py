@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 OUT = os.path.join(HERE, "libsa.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["sa_api.cpp", "k_index.hip", "k_select.hip", "k_radix.hip", "k_bucket.hip", "k_attn.hip"]
+SOURCES = ["sa_api.cpp", "k_index.hip", "k_select.hip", "k_radix.hip", "k_bucket.hip", "k_attn.hip", "k_hi.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
@@ -30,7 +30,8 @@ FLAGS = [
 # Per-source extra flags. The attention and indexer kernels keep their MFMA accumulators in VGPRs: their
 # epilogues (online-softmax rescale; ReLU and head weights) work on them with VALU instructions, and the default
 # AGPR form copies them between the two register files on every tile.
-EXTRA = {"k_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "k_index.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"k_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "k_index.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "k_hi.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:

@@ -344,12 +344,13 @@ __global__ __launch_bounds__(kRThreads) void k_radix_write(const uint32_t* __res
 __global__ __launch_bounds__(256) void k_keys_from_scores(const float* __restrict__ scores, int64_t scores_ld,
                                                           int64_t L, const int32_t* __restrict__ t, int n_sink,
                                                           int n_window, int64_t keys_ld, uint32_t* __restrict__ keys,
-                                                          uint32_t* __restrict__ ctl, int64_t ctl_words) {
+                                                          uint32_t* __restrict__ ctl, int64_t ctl_words,
+                                                          int64_t t_default, int t_div) {
   const int b = blockIdx.y;
   const int64_t nthr = (int64_t)gridDim.x * gridDim.y * blockDim.x;
   for (int64_t i = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x; i < ctl_words; i += nthr)
     ctl[i] = 0u;
-  const int64_t tb = t ? (int64_t)t[b] : L - 1;
+  const int64_t tb = (t ? (int64_t)t[b] : t_default) / t_div;
   const float* row = scores + (int64_t)b * scores_ld;
   uint32_t* out = keys + (int64_t)b * keys_ld;
   for (int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; s < keys_ld; s += (int64_t)gridDim.x * blockDim.x) {
@@ -362,12 +363,13 @@ __global__ __launch_bounds__(256) void k_keys_from_scores(const float* __restric
 
 hipError_t launch_keys_from_scores(const float* scores, int64_t scores_ld, int64_t L, int B, const int32_t* t,
                                    int n_sink, int n_window, const RadixPlan& p, uint32_t* keys, uint32_t* ctl,
-                                   int64_t ctl_words, hipStream_t st) {
+                                   int64_t ctl_words, hipStream_t st, int64_t t_default, int t_div) {
   if (B == 0) return hipSuccess;
   int64_t blocks = (p.keys_ld + 255) / 256;
   if (blocks > 1024) blocks = 1024;
   SA_LAUNCH(k_keys_from_scores, dim3((unsigned)blocks, (unsigned)B), dim3(256), 0, st, scores, scores_ld, L, t,
-            n_sink, n_window, p.keys_ld, keys, ctl, ctl_words);
+            n_sink, n_window, p.keys_ld, keys, ctl, ctl_words, t_default < 0 ? L - 1 : t_default,
+            t_div < 1 ? 1 : t_div);
   return hipGetLastError();
 }
 

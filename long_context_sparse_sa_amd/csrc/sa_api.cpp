@@ -584,6 +584,124 @@ SA_API int sa_select_topk_scores(const float* scores, int64_t scores_ld, int64_t
 }
 
 // ---------------------------------------------------------------------------------------------------------------
+namespace {
+
+struct HiWs {
+  int64_t n_sub, n_pages;
+  float* page_scores;  // [B, n_pages]
+  RadixWs r;           // the top-M page select over them
+  int32_t* pages;      // [B, M] when the caller passes none
+  int32_t* n_pg;       // [B]
+  PerQueryWs f;        // token-stage buffers
+  size_t bytes;
+};
+
+HiWs carve_hi(void* ws, int64_t L, int32_t B, int32_t sub, int32_t page_len, int32_t M, int32_t k) {
+  HiWs w{};
+  w.n_sub = (L + sub - 1) / sub;
+  w.n_pages = (L + page_len - 1) / page_len;
+  Carver c(ws);
+  w.page_scores = c.take<float>((size_t)B * w.n_pages);
+  sa::IndexerArgs pa{};
+  pa.B = B;
+  pa.L = w.n_pages;
+  const size_t r_off = align_up(c.off, 256);
+  w.r = carve_radix(ws ? static_cast<char*>(ws) + r_off : nullptr, pa);
+  c.off = r_off + w.r.bytes;
+  w.pages = c.take<int32_t>((size_t)B * M);
+  w.n_pg = c.take<int32_t>(B);
+  sa::IndexerArgs fa{};
+  fa.B = B;
+  const size_t f_off = align_up(c.off, 256);
+  w.f = carve_per_query(ws ? static_cast<char*>(ws) + f_off : nullptr, fa, k);
+  c.off = f_off + w.f.bytes;
+  w.bytes = align_up(c.off, 256);
+  return w;
+}
+
+int check_hi_shape(int32_t sub, int32_t page_len, int32_t M, int64_t L) {
+  if (sub < 1 || page_len < 64 || page_len % 64 != 0 || page_len % sub != 0)
+    return fail(SA_ERR_SHAPE, "need page_len a multiple of 64 and of sub_block");
+  const int32_t g = page_len / sub;
+  if (g > 64 || (g & (g - 1)) != 0) return fail(SA_ERR_SHAPE, "page_len / sub_block must be a power of two <= 64");
+  if (M < 1 || M > sa::kHiMaxPages) return fail(SA_ERR_SHAPE, "n_pages_keep must be in [1, %d]", sa::kHiMaxPages);
+  if ((L + page_len - 1) / page_len > sa::kHiMaxCachePages)
+    return fail(SA_ERR_SHAPE, "the cache has more than %lld pages", (long long)sa::kHiMaxCachePages);
+  return SA_OK;
+}
+
+}  // namespace
+
+SA_API int sa_hi_build(const void* k, int k_dtype, int64_t k_ld, int64_t L, int32_t d, int32_t sub_block,
+                       void* means, void* stream) {
+  if (!k || !means) return fail(SA_ERR_NULL, "k and means must be non-NULL");
+  if (k_dtype != SA_BF16) return fail(SA_ERR_DTYPE, "the hierarchical index takes bf16 keys");
+  if (L < 1 || L > 0x7FFFFFFFLL || d < 1 || sub_block < 1 || k_ld < d) return fail(SA_ERR_SHAPE, "bad L, d, sub_block or k_ld");
+  if (!aligned16(k) || !aligned16(means)) return fail(SA_ERR_ALIGN, "k and means must be 16-byte aligned");
+  hipError_t e = sa::launch_hi_means(static_cast<const uint16_t*>(k), k_ld, L, d, sub_block,
+                                     static_cast<uint16_t*>(means), (hipStream_t)stream);
+  return e == hipSuccess ? SA_OK : hip_fail(e, "sa_hi_build");
+}
+
+SA_API size_t sa_hi_select_workspace(int64_t L, int32_t B, int32_t sub_block, int32_t page_len, int32_t n_pages_keep,
+                                     int32_t k_sparse) {
+  if (L < 1 || B < 0 || sub_block < 1 || page_len < 1 || n_pages_keep < 1 || k_sparse < 1) return 0;
+  return carve_hi(nullptr, L, B, sub_block, page_len, n_pages_keep, k_sparse).bytes;
+}
+
+SA_API int sa_hi_select(const void* q, int q_dtype, const float* w, const void* k, int k_dtype, int64_t k_ld,
+                        int64_t L, int32_t B, int32_t H, int32_t d, const int32_t* t, const void* means,
+                        int32_t sub_block, int32_t page_len, int32_t n_pages_keep, int32_t k_sparse, int32_t n_sink,
+                        int32_t n_window, int32_t* idx, int32_t idx_ld, int32_t* n_sel, int32_t* pages_out,
+                        void* ws, size_t ws_bytes, void* stream) {
+  int st = check_indexer(q, q_dtype, w, k, k_dtype, k_ld, L, B, H, d);
+  if (st) return st;
+  if (!means || !idx || !n_sel) return fail(SA_ERR_NULL, "means, idx and n_sel must be non-NULL");
+  const sa::IndexerArgs a = make_indexer(q, q_dtype, w, k, k_dtype, k_ld, L, B, H, d, t);
+  if (!sa::hi_fine_supported(a)) return fail(SA_ERR_UNSUPPORTED, "the hierarchical index needs bf16, d = 128, H in {32, 64}");
+  if ((st = check_hi_shape(sub_block, page_len, n_pages_keep, L))) return st;
+  if (k_sparse < 1 || k_sparse > sa::merge_max_k()) return fail(SA_ERR_SHAPE, "k_sparse must be in [1, %d]", sa::merge_max_k());
+  if (idx_ld < k_sparse) return fail(SA_ERR_SHAPE, "idx_ld (%d) < k_sparse (%d)", idx_ld, k_sparse);
+  if (n_sink < 0 || n_window < 0) return fail(SA_ERR_SHAPE, "n_sink and n_window must be >= 0");
+  if (!aligned16(means)) return fail(SA_ERR_ALIGN, "means must be 16-byte aligned");
+  const size_t need = sa_hi_select_workspace(L, B, sub_block, page_len, n_pages_keep, k_sparse);
+  if (!ws || ws_bytes < need) return fail(SA_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  if (!aligned16(ws)) return fail(SA_ERR_ALIGN, "workspace must be 16-byte aligned");
+  if (B == 0) return SA_OK;
+  const HiWs w2 = carve_hi(ws, L, B, sub_block, page_len, n_pages_keep, k_sparse);
+  hipStream_t s = (hipStream_t)stream;
+  // stage 1: page scores over the mean keys, then the top-M visible pages per query (ascending page ids)
+  sa::IndexerArgs m = a;
+  m.k = means;
+  m.k_ld = d;
+  m.L = w2.n_sub;
+  hipError_t e = sa::launch_page_scores(m, page_len / sub_block, page_len, L, w2.page_scores, w2.n_pages, s);
+  if (e != hipSuccess) return hip_fail(e, "sa_hi_select (page scores)");
+  int32_t* pages = pages_out ? pages_out : w2.pages;
+  e = sa::launch_keys_from_scores(w2.page_scores, w2.n_pages, w2.n_pages, B, t, 0, 0, w2.r.p, w2.r.keys, w2.r.ctl,
+                                  (int64_t)w2.r.ctl_words, s, L - 1, page_len);
+  if (e != hipSuccess) return hip_fail(e, "sa_hi_select (page keys)");
+  e = sa::launch_radix_select(B, w2.n_pages, n_pages_keep, w2.r.p, w2.r.keys, w2.r.ctl, pages, n_pages_keep,
+                              w2.n_pg, nullptr, nullptr, s);
+  if (e != hipSuccess) return hip_fail(e, "sa_hi_select (page select)");
+  // stage 2: the token top-k inside the recalled pages, then the final merge
+  e = sa::launch_hi_fine(a, pages, n_pages_keep, w2.n_pg, page_len, w2.n_pages, k_sparse, n_sink, n_window, w2.f.buf,
+                         w2.f.buf_n, w2.f.cap, s);
+  if (e != hipSuccess) return hip_fail(e, "sa_hi_select (token stage)");
+  sa::MergeIn in{};
+  in.kept = w2.f.buf;
+  in.kept_ld = w2.f.cap;
+  in.kept_n = w2.f.buf_n;
+  sa::MergeOut out{};
+  out.final_mode = 1;
+  out.idx = idx;
+  out.idx_ld = idx_ld;
+  out.n_sel = n_sel;
+  e = sa::launch_merge(B, k_sparse, in, w2.f.gather, w2.f.cap, out, s);
+  return e == hipSuccess ? SA_OK : hip_fail(e, "sa_hi_select (merge)");
+}
+
+// ---------------------------------------------------------------------------------------------------------------
 SA_API size_t sa_bucket_build_workspace(int64_t L, int32_t n_buckets) {
   if (L < 0 || n_buckets < 1) return 0;
   const sa::BucketBuildPlan p = sa::bucket_build_plan(L, n_buckets);

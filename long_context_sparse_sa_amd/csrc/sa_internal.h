@@ -41,7 +41,7 @@ struct Cand {
   int32_t pos;
 };
 
-enum ScoreMode { kScoreDense = 0, kScoreEmit = 1, kScoreAll = 2 };
+enum ScoreMode { kScoreDense = 0, kScoreEmit = 1, kScoreAll = 2, kScorePage = 3 };
 
 // Positions handled by one workgroup of the scoring kernel chosen for these arguments.
 int score_keys_per_wg(const IndexerArgs& a);
@@ -127,9 +127,11 @@ hipError_t launch_radix_select(int B, int64_t L, int k, const RadixPlan& p, cons
                                hipStream_t stream);
 // The radix select's keys from caller-given fp32 scores: keys[b * p.keys_ld + s] = score_key(scores[b, s]) for
 // candidates (n_sink <= s <= t_b - n_window), 0 otherwise; also zeroes ctl[0, ctl_words).
+// With t_div > 1 (page selection), entry s is a candidate when s <= (t_b / t_div) - n_window, t_b from t or
+// t_default.
 hipError_t launch_keys_from_scores(const float* scores, int64_t scores_ld, int64_t L, int B, const int32_t* t,
                                    int n_sink, int n_window, const RadixPlan& p, uint32_t* keys, uint32_t* ctl,
-                                   int64_t ctl_words, hipStream_t stream);
+                                   int64_t ctl_words, hipStream_t stream, int64_t t_default = -1, int t_div = 1);
 
 // Streaming selection for few queries (decode): launches over co-resident ranges of positions; each keeps its keys
 // on chip, publishes per-chunk statistics, derives a lower bound T of each query's k-th key from them and emits only
@@ -150,6 +152,26 @@ StreamPlan stream_plan(const IndexerArgs& a, int64_t end);
 hipError_t launch_stream_decode(const IndexerArgs& a, int k, int n_sink, int n_window, const StreamPlan& p,
                                 uint32_t* pub, uint32_t* thr, uint32_t* top, uint32_t* seg_cnt, Cand* cand,
                                 int spin_limit, hipStream_t stream);
+
+// ---- hierarchical index ------------------------------------------------------------------------------------------
+// Sub-block mean keys: means[n, 0:d] = bf16(float(fp64 sum of k[n B + i, 0:d] over the block's cached positions /
+// their count)) for n < ceil(L / B); keys bf16.
+hipError_t launch_hi_means(const uint16_t* k, int64_t k_ld, int64_t L, int d, int sub, uint16_t* means,
+                           hipStream_t stream);
+// Page scores over the mean keys m (m.k = means, m.L = their count, m.t = the queries' token t): scores[b, p] = sum
+// of the indexer score of the page_subs mean keys of page p (page_subs a power of two <= 64), -inf when the page's
+// first position p * page_len is past t_b (t_b = tok_L - 1 without t).
+hipError_t launch_page_scores(const IndexerArgs& m, int page_subs, int page_len, int64_t tok_L, float* scores,
+                              int64_t scores_ld, hipStream_t stream);
+// Token stage: per query, its recalled pages pages[b, 0:n_pages[b]) (ascending); four queries per workgroup walk the
+// union of their pages and each keeps, in buf[b, 0:cap), candidates (in its pages, inside the sink/window budget)
+// that contain its exact top-k, in ascending position order; buf_n[b] their count.
+constexpr int kHiMaxPages = 1024;          // recalled pages per query
+constexpr int64_t kHiMaxCachePages = 1 << 17;  // pages of the cache
+bool hi_fine_supported(const IndexerArgs& a);
+hipError_t launch_hi_fine(const IndexerArgs& a, const int32_t* pages, int pages_ld, const int32_t* n_pages,
+                          int page_len, int64_t n_cache_pages, int k, int n_sink, int n_window, Cand* buf,
+                          int32_t* buf_n, int cap, hipStream_t stream);
 
 // Streaming per-query selection for many queries (prefill chunk): one pass over each query's visible keys keeps
 // at most `cap` candidates per query in buf[b, :] (count in buf_n[b]) that contain the exact top-k.

@@ -1,0 +1,253 @@
+// MFMA building blocks of the lightning-indexer scorers (LongCat Sparse Attention deep-dive, DSA baseline section,
+// indexer equation): staged key tiles, register-resident query fragments, and the score of a 64-position tile,
+// I(b, s) = sum_j w[b, j] * ReLU(q[b, j, :] . k[s, :]), for d = 128 and 32 * NMT heads.
+#pragma once
+
+#include <type_traits>
+
+#include "sa_device.h"
+
+namespace sa {
+namespace tile {
+
+constexpr int kTileKeys = 64;
+
+// NMT = H / 32 head tiles per query, d = 128. The dot products always run on the bf16 32x32x16 MFMA, whose sums
+// are exact for these operands. E4M3-stored keys and queries are converted exactly to bf16 on the way into LDS
+// and registers: the fp8 MFMA is not used because its internal accumulation loses about 2^-15 of the sum of
+// |products|, which would move scores by more than the selection tolerance.
+//
+// LDS key tile: 64 positions x 256 bytes of bf16; the 16-byte chunk c of position n is stored at chunk
+// c ^ (n % 16) so that the 32 lanes reading one chunk column spread over the banks.
+constexpr int kTileRowBytes = 256;
+constexpr int kTileChunks = 16;
+constexpr int kTileBytes = kTileKeys * kTileRowBytes;
+constexpr int kSteps = 8;  // MFMA k-steps of 16 dims
+
+__device__ __forceinline__ int tile_off(int n, int c) { return n * kTileRowBytes + 16 * (c ^ (n % kTileChunks)); }
+
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+
+// Exact E4M3 -> bf16 of the four bytes of `packed`.
+__device__ __forceinline__ bf16x4 e4m3x4_to_bf16(int packed) {
+  const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(packed, 1.0f, false);
+  const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(packed, 1.0f, true);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3);
+}
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(int a, int b) {
+  return __builtin_shufflevector(e4m3x4_to_bf16(a), e4m3x4_to_bf16(b), 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+template <bool E4M3, int NW>
+struct KeyLoader;
+
+// bf16 keys: the stored 256-byte rows go straight to LDS by asynchronous DMA (16 KB = 16 wave instructions).
+// Each lane's byte offset inside a tile is computed once (init); a tile then costs one address add per copy,
+// except a tile that runs past row L - 1, which clamps its rows (rows past the end are never scored, the clamp
+// keeps the copy in bounds).
+template <int NW>
+struct KeyLoader<false, NW> {
+  static constexpr int kPerWave = 16 / NW;
+  struct Regs {
+    int64_t off[kPerWave];
+  };
+  static __device__ __forceinline__ void init(Regs& r, int64_t ld_bytes, int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < kPerWave; ++j) {
+      const int slot = (wave * kPerWave + j) * 64 + lane;
+      const int n = slot / kTileChunks;
+      const int c = (slot % kTileChunks) ^ (n % kTileChunks);
+      r.off[j] = n * ld_bytes + c * 16;
+    }
+  }
+  static __device__ __forceinline__ void fetch(const char* kbytes, int64_t ld_bytes, int64_t L, int64_t s0,
+                                               char* tile, int wave, int lane, Regs& r) {
+    const char* base = kbytes + s0 * ld_bytes;
+    if (s0 + kTileKeys <= L) {
+#pragma unroll
+      for (int j = 0; j < kPerWave; ++j) dma16(base + r.off[j], tile + (wave * kPerWave + j) * 1024);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kPerWave; ++j) {
+        const int slot = (wave * kPerWave + j) * 64 + lane;
+        const int n = slot / kTileChunks;
+        const int c = (slot % kTileChunks) ^ (n % kTileChunks);
+        const int64_t row = (s0 + n < L ? s0 + n : L - 1) - s0;
+        dma16(base + row * ld_bytes + c * 16, tile + (wave * kPerWave + j) * 1024);
+      }
+    }
+  }
+  static __device__ __forceinline__ void commit(const Regs&, char*, int) {}
+};
+
+// e4m3 keys: each thread loads BPT stored bytes of one position and writes them as 2 BPT bytes of bf16.
+template <int NW>
+struct KeyLoader<true, NW> {
+  static constexpr int BPT = 8192 / (64 * NW);      // raw bytes per thread (32 or 16)
+  static constexpr int TPK = 128 / BPT;             // threads per position
+  struct Regs {
+    int4 part[BPT / 16];
+  };
+  static __device__ __forceinline__ void init(Regs&, int64_t, int, int) {}
+  static __device__ __forceinline__ void fetch(const char* kbytes, int64_t ld_bytes, int64_t L, int64_t s0, char*,
+                                               int, int, Regs& r) {
+    const int tid = threadIdx.x;
+    int64_t s = s0 + tid / TPK;
+    s = s < L ? s : L - 1;
+    const int4* src = reinterpret_cast<const int4*>(kbytes + s * ld_bytes + BPT * (tid % TPK));
+#pragma unroll
+    for (int p = 0; p < BPT / 16; ++p) r.part[p] = src[p];
+  }
+  static __device__ __forceinline__ void commit(const Regs& r, char* tile, int tid) {
+    const int n = tid / TPK, c0 = (BPT / 8) * (tid % TPK);
+#pragma unroll
+    for (int p = 0; p < BPT / 16; ++p) {
+      *reinterpret_cast<bf16x8*>(tile + tile_off(n, c0 + 2 * p)) = e4m3x8_to_bf16(r.part[p].x, r.part[p].y);
+      *reinterpret_cast<bf16x8*>(tile + tile_off(n, c0 + 2 * p + 1)) = e4m3x8_to_bf16(r.part[p].z, r.part[p].w);
+    }
+  }
+};
+
+// Query fragments (A operand, head = 32 * mt + lane % 32, dims 16 ks + 8 (lane / 32) ..) and the head weights in
+// the accumulator layout (this lane's 16 values of tile mt belong to heads 32 mt + 8 (r / 4) + 4 (lane / 32) + r % 4).
+template <int NMT, bool E4M3>
+__device__ __forceinline__ void load_query(const void* q, const float* w, int64_t b, int lane,
+                                           bf16x8 (&qa)[NMT][kSteps], float (&wv)[NMT][16]) {
+  constexpr int H = 32 * NMT;
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt) {
+    const int64_t e0 = (b * H + 32 * mt + (lane & 31)) * 128 + (lane >> 5) * 8;
+#pragma unroll
+    for (int ks = 0; ks < kSteps; ++ks) {
+      if constexpr (E4M3) {
+        const int2 raw = *reinterpret_cast<const int2*>(reinterpret_cast<const char*>(q) + e0 + ks * 16);
+        qa[mt][ks] = e4m3x8_to_bf16(raw.x, raw.y);
+      } else {
+        qa[mt][ks] = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint16_t*>(q) + e0 + ks * 16);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) wv[mt][r] = w[b * H + 32 * mt + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)];
+  }
+}
+
+// ReLU as one integer max: a negative float (or -0) has a negative int image and becomes +0; other values pass.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// Scores of the 64 positions of a tile: lane l returns the score of position l of the tile.
+// The eight key fragments of a 32-position half sit in a register ring: the half-0 fragments are read up front
+// and each slot is refilled with the matching half-1 fragment as soon as its MFMAs are issued, so every LDS read
+// has eight MFMA pairs to land. The half-1 MFMAs are interleaved with the half-0 ReLU-weighted head sum (two MFMAs,
+// then eight VALU instructions, per k-step), so the matrix unit and the VALU work at the same time.
+template <int NMT>
+__device__ __forceinline__ float score_tile(const char* tile, int lane, const bf16x8 (&qa)[NMT][kSteps],
+                                           const float (&wv)[NMT][16]) {
+  static_assert(NMT * 16 % kSteps == 0, "head-sum chunks must divide evenly over the k-steps");
+  constexpr int kChunk = NMT * 16 / kSteps;  // half-0 accumulator elements folded per half-1 k-step
+  const int hs = lane >> 5;
+  auto frag = [&](int nt, int ks) {
+    return *reinterpret_cast<const bf16x8*>(tile + tile_off(32 * nt + (lane & 31), 2 * ks + hs));
+  };
+  bf16x8 fr[kSteps];
+#pragma unroll
+  for (int ks = 0; ks < kSteps; ++ks) fr[ks] = frag(0, ks);
+  f32x16 acc0[NMT], acc1[NMT];
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt) {
+    acc0[mt] = f32x16{};
+    acc1[mt] = f32x16{};
+  }
+  // half 0
+#pragma unroll
+  for (int ks = 0; ks < kSteps; ++ks) {
+    const bf16x8 bk = fr[ks];
+    fr[ks] = frag(1, ks);
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) acc0[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt][ks], bk, acc0[mt], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // half 1, with the half-0 head sum in the MFMA shadow
+  float part0 = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < kSteps; ++ks) {
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) acc1[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt][ks], fr[ks], acc1[mt], 0, 0, 0);
+#pragma unroll
+    for (int e = 0; e < kChunk; ++e) {
+      const int idx = ks * kChunk + e;
+      part0 = fmaf(wv[idx / 16][idx % 16], relu(acc0[idx / 16][idx % 16]), part0);
+    }
+  }
+#pragma unroll
+  for (int ks = 0; ks < kSteps; ++ks) {
+    __builtin_amdgcn_sched_group_barrier(0x008, NMT, 0);       // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 2 * kChunk, 0);  // VALU
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  float part1 = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) part1 = fmaf(wv[mt][r], relu(acc1[mt][r]), part1);
+  // part0 / part1 hold the half-0 / half-1 sums over this lane's heads; lanes l and l ^ 32 cover the two head
+  // halves of the same position
+  return fold_halves(part0, part1);
+}
+
+// Walks the tiles 0 .. n_tiles-1 of a workgroup's run (tile i covers positions tile_start(i) .. + 63): every wave
+// calls on_tile(tile_in_lds, i) once per tile, in order, after the tile's keys have landed in LDS. bf16 keys arrive
+// by asynchronous DMA into NBUF LDS buffers (NBUF - 1 tiles in flight); e4m3 keys are loaded two tiles ahead into a
+// register ring, converted and committed to two LDS buffers. All waves of the workgroup must call it.
+template <bool E4M3, int NQ, int NBUF, typename TS, typename F>
+__device__ __forceinline__ void walk_tiles(const char* kbytes, int64_t ld_bytes, int64_t L, int64_t n_tiles,
+                                           TS tile_start, char (*tiles)[kTileBytes], int wave, int lane,
+                                           F&& on_tile) {
+  typedef KeyLoader<E4M3, NQ> KL;
+  constexpr int kDmaPerWave = KeyLoader<false, NQ>::kPerWave;
+  if constexpr (!E4M3) {
+    static_assert(NBUF == 4, "the waits below keep two tiles in flight behind the current one");
+    typename KL::Regs none;
+    KL::init(none, ld_bytes, wave, lane);
+    const int64_t n_pre = n_tiles < NBUF - 1 ? n_tiles : NBUF - 1;
+    for (int64_t p = 0; p < n_pre; ++p) KL::fetch(kbytes, ld_bytes, L, tile_start(p), tiles[p], wave, lane, none);
+    for (int64_t i = 0; i < n_tiles; ++i) {
+      const int64_t newer = n_tiles - 1 - i;
+      if (newer >= 2) wait_vmem_below<2 * kDmaPerWave>();
+      else if (newer == 1) wait_vmem_below<kDmaPerWave>();
+      else wait_vmem_below<0>();
+      lds_barrier();
+      if (i + NBUF - 1 < n_tiles)
+        KL::fetch(kbytes, ld_bytes, L, tile_start(i + NBUF - 1), tiles[(i + NBUF - 1) % NBUF], wave, lane, none);
+      on_tile(tiles[i % NBUF], i);
+    }
+  } else {
+    static_assert(NBUF == 2, "e4m3 tiles alternate between two LDS buffers");
+    typename KL::Regs ring[2];
+    if (n_tiles > 0) {
+      KL::fetch(kbytes, ld_bytes, L, tile_start(0), nullptr, wave, lane, ring[0]);
+      if (n_tiles > 1) KL::fetch(kbytes, ld_bytes, L, tile_start(1), nullptr, wave, lane, ring[1]);
+      KL::commit(ring[0], tiles[0], threadIdx.x);
+      if (n_tiles > 2) KL::fetch(kbytes, ld_bytes, L, tile_start(2), nullptr, wave, lane, ring[0]);
+    }
+    // tile i + 1 (ring slot (i + 1) % 2) goes to LDS while tile i is scored; its slot then takes tile i + 3.
+    // Unrolled by two so that ring slots and LDS buffers are compile-time (a runtime-indexed ring would live in
+    // scratch memory).
+    auto step = [&](int64_t i, auto P) {
+      constexpr int p = decltype(P)::value;
+      lds_barrier();
+      if (i + 1 < n_tiles) {
+        KL::commit(ring[1 - p], tiles[1 - p], threadIdx.x);
+        if (i + 3 < n_tiles) KL::fetch(kbytes, ld_bytes, L, tile_start(i + 3), nullptr, wave, lane, ring[1 - p]);
+      }
+      on_tile(tiles[p], i);
+    };
+    for (int64_t i = 0; i < n_tiles; i += 2) {
+      step(i, std::integral_constant<int, 0>{});
+      if (i + 1 < n_tiles) step(i + 1, std::integral_constant<int, 1>{});
+    }
+  }
+}
+
+}  // namespace tile
+}  // namespace sa

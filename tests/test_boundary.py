@@ -206,3 +206,40 @@ def test_bucket_select_noalloc_validation(lib):
     assert b"static scratch" in lib.sa_last_error()
     bad = list(args); bad[2] = 0
     assert lib.sa_bucket_select_noalloc(*bad) == OK  # nothing to do: no HIP call
+
+
+def hi(lib, **kw):
+    a = dict(q=A, qd=BF16, w=A, k=A, kd=BF16, k_ld=128, L=131072, B=4, H=64, d=128, t=None, means=A, sub=8, P=128,
+             M=64, kk=2048, ns=4, nw=128, idx=A, idx_ld=2048, nsel=A, pages=None, ws=A, wsb=None)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = lib.sa_hi_select_workspace(a["L"], a["B"], a["sub"], a["P"], a["M"], a["kk"])
+    return lib.sa_hi_select(a["q"], a["qd"], a["w"], a["k"], a["kd"], a["k_ld"], a["L"], a["B"], a["H"], a["d"],
+                            a["t"], a["means"], a["sub"], a["P"], a["M"], a["kk"], a["ns"], a["nw"], a["idx"],
+                            a["idx_ld"], a["nsel"], a["pages"], a["ws"], a["wsb"], None)
+
+
+def test_hi_validation(lib):
+    assert hi(lib, means=None) == NULL
+    assert hi(lib, idx=None) == NULL
+    assert hi(lib, qd=E4M3, kd=E4M3) == UNSUP          # the token stage reads bf16 keys
+    assert hi(lib, H=48) == UNSUP
+    assert hi(lib, P=96) == SHAPE                      # pages are whole 64-position tiles
+    assert hi(lib, P=128, sub=3) == SHAPE              # sub-blocks tile the page
+    assert hi(lib, P=128, sub=1) == SHAPE              # 128 sub-blocks per page: more than one tile of means
+    assert hi(lib, M=0) == SHAPE
+    assert hi(lib, M=1025) == SHAPE
+    assert hi(lib, L=(1 << 17) * 128 + 1) == SHAPE     # more pages than the token stage's bitmap holds
+    assert hi(lib, kk=0) == SHAPE
+    assert hi(lib, idx_ld=100) == SHAPE
+    assert hi(lib, means=MIS) == ALIGN
+    assert hi(lib, ws=None) == WS
+    need = lib.sa_hi_select_workspace(131072, 4, 8, 128, 64, 2048)
+    assert hi(lib, wsb=need - 1) == WS
+    assert hi(lib, B=0) == OK
+    # the workspace holds the page scores, the page select's keys and the token stage's buffers
+    assert need >= 4 * 1024 * 4 * 2 + 2 * 4 * (4 * 2048 + 64) * 8
+    assert lib.sa_hi_build(None, BF16, 128, 1000, 128, 8, A, None) == NULL
+    assert lib.sa_hi_build(A, E4M3, 128, 1000, 128, 8, A, None) == DTYPE
+    assert lib.sa_hi_build(A, BF16, 64, 1000, 128, 8, A, None) == SHAPE
+    assert lib.sa_hi_build(A, BF16, 128, 1000, 128, 0, A, None) == SHAPE
