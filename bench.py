@@ -3,7 +3,8 @@
 
 A step is one pass of the whole path over one batch: indexer scoring fused with exact top-k selection
 (sa_select_topk), then sparse attention over sink + window + selected latent rows (sa_sparse_attn); for the
-bucket workload the selection is the Flat bucket search (sa_bucket_select). Inputs are synthetic, seeded and
+bucket workload the selection is the Flat bucket search (sa_bucket_select), for the coarse-to-fine workload the
+two-stage page-then-token search (sa_hi_select; its mean keys are built once per cache, outside the step). Inputs are synthetic, seeded and
 already resident in HBM; several independent copies of the caches rotate so that the measured traffic comes from
 HBM rather than the 256 MB Infinity Cache.
 
@@ -33,6 +34,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill_chunk_128k")
+    ap.add_argument("--L", type=int, default=0, help="override the workload's cache length (positions)")
     ap.add_argument("--rotate-bytes", type=float, default=1.2e9, help="total bytes of rotated cache copies")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -133,7 +135,7 @@ def main():
         return
     lib = sa.load()
     dev = "cuda"
-    wl = get_workload(args.workload)
+    wl = get_workload(args.workload, **({"L": args.L} if args.L else {}))
     torch.manual_seed(0)
     copy_gbps = copy_bandwidth_gbps(torch)
 
@@ -150,7 +152,18 @@ def main():
     stream = torch.cuda.current_stream()
     t = base["t"]
     is_bucket = wl.kind == "bucket"
-    if is_bucket:
+    is_hi = wl.kind == "hi"
+    if is_hi:
+        build_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        build_ev[0].record()
+        hi_means = [sa.sa_hi_build(c["k_idx"], wl.sub_block) for c in copies]
+        build_ev[1].record()
+        torch.cuda.synchronize()
+        build_ms = build_ev[0].elapsed_time(build_ev[1]) / len(copies)
+        idx_ld = wl.k_sparse
+        hi_ws = torch.empty(sa.sa_hi_select_workspace(wl.L, wl.B, wl.sub_block, wl.page_len, wl.n_pages_keep,
+                                                      wl.k_sparse), dtype=torch.uint8, device=dev)
+    elif is_bucket:
         dirs = []
         build_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         build_ev[0].record()
@@ -184,6 +197,9 @@ def main():
                                       t.data_ptr(), wl.top_b, wl.n_sink, wl.n_window, idx.data_ptr(), cap,
                                       n_sel.data_ptr(), None, bws.data_ptr(), bws.numel(), stream.cuda_stream)
             sa.api._lib.check("sa_bucket_select", st)
+        elif is_hi:
+            sa.sa_hi_select(c["q_idx"], c["w"], c["k_idx"], hi_means[i % n_copies], wl.sub_block, wl.page_len,
+                            wl.n_pages_keep, wl.k_sparse, wl.n_sink, wl.n_window, t=t, ws=hi_ws, out=(idx, n_sel))
         else:
             sa.sa_select_topk(c["q_idx"], c["w"], c["k_idx"], wl.k_sparse, wl.n_sink, wl.n_window, t=t, ws=sel_ws,
                               out=(idx, n_sel))
@@ -270,6 +286,9 @@ def main():
                                     "hbm_frac": round(rep_bytes / t_sel / 1e9 / perf.PEAK_HBM_GBPS, 4),
                                     "kernel_ms": [round(x, 4) for x in sel_kernels]}}
         keys_per_s = n_keys / t_sel
+    elif is_hi:
+        sel_roof, keys_per_s, hi_info = hi_roofline(sa, wl, copies[0], hi_means[0], t, sel_kernels, t_sel)
+        t_sel_k = sel_roof["launch_ms"] * 1e-3
     else:
         pairs = sum(max(0, tb - wl.n_window - wl.n_sink + 1) for tb in wl.t_positions())
         i_flops = perf.indexer_flops(pairs, wl.H_I, wl.d_I)
@@ -319,11 +338,67 @@ def main():
     }
     if is_bucket:
         res["bucket_build_ms_per_cache"] = round(build_ms, 3)
+    if is_hi:
+        res["config"].update(sub_block=wl.sub_block, page_len=wl.page_len, n_pages_keep=wl.n_pages_keep)
+        res["hi"] = {**hi_info, "means_build_ms_per_cache": round(build_ms, 3)}
 
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, base, args.cpu_seconds)
     res["host"] = {**host_info(), "gpu": torch.cuda.get_device_name(0)}
     print(json.dumps(res))
+
+
+HI_KERNELS = ["k_score_mfma (page scores)", "k_keys_from_scores (pages)", "k_radix_hist<0>", "k_radix_hist<1>",
+              "k_radix_hist<2>", "k_radix_count", "k_radix_write", "k_hi_fine", "k_merge"]
+
+
+def hi_roofline(sa, wl, c, means, t, sel_kernels, t_sel):
+    """Roofline of the coarse-to-fine select's longest kernel. Algorithmic work: the page scorer scores every
+    visible sub-block mean key of every query; the token stage scores, per query, the candidates inside its
+    recalled pages (counted from the pages one extra call returns)."""
+    import numpy as np
+    assert len(sel_kernels) == len(HI_KERNELS), sel_kernels
+    from sa_workloads import perf
+    _, _, pages = sa.sa_hi_select(c["q_idx"], c["w"], c["k_idx"], means, wl.sub_block, wl.page_len,
+                                  wl.n_pages_keep, wl.k_sparse, wl.n_sink, wl.n_window, t=t, return_pages=True)
+    pages = pages.cpu().numpy().astype(np.int64)
+    P, g = wl.page_len, wl.page_len // wl.sub_block
+    n_sub = (wl.L + wl.sub_block - 1) // wl.sub_block
+    ts = np.asarray(wl.t_positions(), dtype=np.int64)
+    page_pairs = int(np.minimum(n_sub, (ts // P + 1) * g).sum())
+    # candidates of query b inside page p: [max(pP, n_sink), min(pP + P - 1, L - 1, t_b - n_window)]
+    lo = np.maximum(pages * P, wl.n_sink)
+    hi = np.minimum(np.minimum(pages * P + P - 1, wl.L - 1), (ts - wl.n_window)[:, None])
+    token_pairs = int(np.where(pages >= 0, np.maximum(0, hi - lo + 1), 0).sum())
+    flat_pairs = int(np.maximum(0, ts - wl.n_window - wl.n_sink + 1).sum())
+    peak = perf.PEAK_TFLOPS["bf16"]
+    work = {"k_score_mfma (page scores)": perf.indexer_flops(page_pairs, wl.H_I, wl.d_I),
+            "k_hi_fine": perf.indexer_flops(token_pairs, wl.H_I, wl.d_I)}
+    kernels = {}
+    for name, ms in zip(HI_KERNELS, sel_kernels):
+        kernels[name] = {"ms": round(ms, 4)}
+        if name in work:
+            kernels[name]["tflops"] = round(work[name] / (ms * 1e-3) / 1e12, 1)
+            kernels[name]["mfma_frac"] = round(work[name] / (ms * 1e-3) / 1e12 / peak, 4)
+    j = int(np.argmax(sel_kernels))
+    name, ms = HI_KERNELS[j], sel_kernels[j]
+    if name in work:
+        tf = work[name] / (ms * 1e-3) / 1e12
+        roof = {"kernel": name, "bound": "mfma", "achieved": round(tf, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(tf / peak, 4), "algorithmic_flops_per_launch": work[name]}
+    else:
+        roof = {"kernel": name, "bound": "hbm", "achieved": None, "peak": perf.PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": None}
+    all_flops = work["k_score_mfma (page scores)"] + work["k_hi_fine"]
+    roof.update({"traffic": None, "launch_ms": round(ms, 4),
+                 "entry_point": {"name": "sa_hi_select", "ms": round(t_sel * 1e3, 4),
+                                 "mfma_frac": round(all_flops / t_sel / 1e12 / peak, 4),
+                                 "kernel_ms": [round(x, 4) for x in sel_kernels]}})
+    info = {"kernels": kernels, "sub_block_keys_scored": page_pairs, "token_pairs_scored": token_pairs,
+            "flat_equivalent_pairs": flat_pairs,
+            "token_gather_gbps": round(token_pairs * wl.d_I * 2 / (sel_kernels[HI_KERNELS.index("k_hi_fine")]
+                                                                    * 1e-3) / 1e9, 1)}
+    return roof, flat_pairs / t_sel, info
 
 
 def measured_traffic(workload: str):
@@ -366,6 +441,10 @@ def cpu_baseline(wl, base, min_seconds):
         kf = to_f64(base["k_idx"])
         reps, off, mem = O.bucket_build(kf, base["assign"].cpu().numpy(), wl.n_buckets)
         qi = base["q_idx"]
+    elif wl.kind == "hi":
+        kf = to_f64(base["k_idx"])
+        means = O.hi_means(kf, wl.sub_block)       # once per cache, as on the GPU: not timed
+        qi, w = base["q_idx"], base["w"].double().cpu().numpy()
     else:
         kf = to_f64(base["k_idx"])
         qi, w = base["q_idx"], base["w"].double().cpu().numpy()
@@ -388,7 +467,10 @@ def cpu_baseline(wl, base, min_seconds):
             qi64[b], q64[b] = to_f64(qi[b]), to_f64(q[b])
             prep += time.perf_counter() - t1
         t0 = time.perf_counter()
-        if wl.kind == "bucket":
+        if wl.kind == "hi":
+            O.hi_step(qi64[b], w[b], kf, means, q64[b], kv, ts[b], wl.page_len, wl.sub_block, wl.n_pages_keep,
+                      wl.k_sparse, wl.n_sink, wl.n_window, wl.softmax_scale, wl.d_qk, wl.d_v)
+        elif wl.kind == "bucket":
             O.bucket_step(qi64[b], reps, off, mem, q64[b], kv, ts[b], wl.top_b, wl.n_sink, wl.n_window,
                           wl.softmax_scale, wl.d_qk, wl.d_v)
         else:
@@ -401,14 +483,14 @@ def cpu_baseline(wl, base, min_seconds):
             break
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     mean_pairs = sum(pairs_of(tb) for tb in ts) / len(ts)
-    causal = wl.kind != "bucket" and len(set(ts)) > 1
+    causal = wl.kind == "dsa" and len(set(ts)) > 1
     value = pairs_done / dt / mean_pairs if causal else done / dt
     which = f"{len(sample)} seeded queries of {wl.name} ({wl.B} in all, first and last included), cycled: " \
             f"{done} query evaluations"
     how = (f"; rate per scored pair ({pairs_done} pairs) divided by the mean {mean_pairs:.0f} pairs per query "
            "(extrapolated by pair count)") if causal else ""
     return {"value": round(value, 3), "unit": "queries/s", "cores": threads, "kind": "oracle",
-            "sample": f"{which}; full per-query path (score all candidates, exact top-k, attention), fp64 numpy"
+            "sample": f"{which}; full per-query path ({'page scores, top pages, token top-k inside them' if wl.kind == 'hi' else 'score all candidates, exact top-k'}, attention), fp64 numpy"
                       f"{how}; {prep:.1f} s input decode not counted",
             "extrapolated": causal, "seconds": round(dt, 2)}
 

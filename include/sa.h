@@ -217,8 +217,8 @@ SA_API int sa_bucket_select_noalloc(const void* q, int q_dtype, int32_t B, int32
  *   recalled pages.
  *   q, w, k, k_ld, L, B, H, d, t: as sa_index_score; bf16 q and k, d = 128, H in {32, 64}.
  *   means    the output of sa_hi_build for this cache and sub_block.
- *   page_len a multiple of 64 and of sub_block, page_len / sub_block a power of two <= 64; at most 2^17 pages.
- *   n_pages_keep in [1, 1024].  k_sparse in [1, 16384] and <= idx_ld.
+ *   page_len a multiple of 64 and of sub_block, page_len / sub_block a power of two <= 64.
+ *   n_pages_keep in [1, 2^20].  k_sparse in [1, 16384] and <= idx_ld.
  *   idx, idx_ld, n_sel: as sa_select_topk (ascending positions, -1 padding).
  *   pages_out [B, n_pages_keep] int32 or NULL: the recalled pages, ascending, -1 padding.
  *   ws / ws_bytes: at least sa_hi_select_workspace(L, B, sub_block, page_len, n_pages_keep, k_sparse) bytes.

@@ -592,7 +592,10 @@ struct HiWs {
   RadixWs r;           // the top-M page select over them
   int32_t* pages;      // [B, M] when the caller passes none
   int32_t* n_pg;       // [B]
-  PerQueryWs f;        // token-stage buffers
+  sa::HiFinePlan f;    // the token stage's parts
+  sa::Cand* seg;       // [B, n_parts, seg_cap] its candidate segments
+  uint32_t* seg_cnt;   // [B, n_parts]
+  sa::Cand* gather;    // [B, n_parts * k] the merge's overflow
   size_t bytes;
 };
 
@@ -610,23 +613,20 @@ HiWs carve_hi(void* ws, int64_t L, int32_t B, int32_t sub, int32_t page_len, int
   c.off = r_off + w.r.bytes;
   w.pages = c.take<int32_t>((size_t)B * M);
   w.n_pg = c.take<int32_t>(B);
-  sa::IndexerArgs fa{};
-  fa.B = B;
-  const size_t f_off = align_up(c.off, 256);
-  w.f = carve_per_query(ws ? static_cast<char*>(ws) + f_off : nullptr, fa, k);
-  c.off = f_off + w.f.bytes;
+  w.f = sa::hi_fine_plan(L, B, page_len, k);
+  w.seg = c.take<sa::Cand>((size_t)B * w.f.n_parts * w.f.seg_cap);
+  w.seg_cnt = c.take<uint32_t>((size_t)B * w.f.n_parts);
+  w.gather = c.take<sa::Cand>((size_t)B * w.f.n_parts * k);
   w.bytes = align_up(c.off, 256);
   return w;
 }
 
-int check_hi_shape(int32_t sub, int32_t page_len, int32_t M, int64_t L) {
+int check_hi_shape(int32_t sub, int32_t page_len, int32_t M) {
   if (sub < 1 || page_len < 64 || page_len % 64 != 0 || page_len % sub != 0)
     return fail(SA_ERR_SHAPE, "need page_len a multiple of 64 and of sub_block");
   const int32_t g = page_len / sub;
   if (g > 64 || (g & (g - 1)) != 0) return fail(SA_ERR_SHAPE, "page_len / sub_block must be a power of two <= 64");
   if (M < 1 || M > sa::kHiMaxPages) return fail(SA_ERR_SHAPE, "n_pages_keep must be in [1, %d]", sa::kHiMaxPages);
-  if ((L + page_len - 1) / page_len > sa::kHiMaxCachePages)
-    return fail(SA_ERR_SHAPE, "the cache has more than %lld pages", (long long)sa::kHiMaxCachePages);
   return SA_OK;
 }
 
@@ -659,7 +659,7 @@ SA_API int sa_hi_select(const void* q, int q_dtype, const float* w, const void* 
   if (!means || !idx || !n_sel) return fail(SA_ERR_NULL, "means, idx and n_sel must be non-NULL");
   const sa::IndexerArgs a = make_indexer(q, q_dtype, w, k, k_dtype, k_ld, L, B, H, d, t);
   if (!sa::hi_fine_supported(a)) return fail(SA_ERR_UNSUPPORTED, "the hierarchical index needs bf16, d = 128, H in {32, 64}");
-  if ((st = check_hi_shape(sub_block, page_len, n_pages_keep, L))) return st;
+  if ((st = check_hi_shape(sub_block, page_len, n_pages_keep))) return st;
   if (k_sparse < 1 || k_sparse > sa::merge_max_k()) return fail(SA_ERR_SHAPE, "k_sparse must be in [1, %d]", sa::merge_max_k());
   if (idx_ld < k_sparse) return fail(SA_ERR_SHAPE, "idx_ld (%d) < k_sparse (%d)", idx_ld, k_sparse);
   if (n_sink < 0 || n_window < 0) return fail(SA_ERR_SHAPE, "n_sink and n_window must be >= 0");
@@ -685,19 +685,21 @@ SA_API int sa_hi_select(const void* q, int q_dtype, const float* w, const void* 
                               w2.n_pg, nullptr, nullptr, s);
   if (e != hipSuccess) return hip_fail(e, "sa_hi_select (page select)");
   // stage 2: the token top-k inside the recalled pages, then the final merge
-  e = sa::launch_hi_fine(a, pages, n_pages_keep, w2.n_pg, page_len, w2.n_pages, k_sparse, n_sink, n_window, w2.f.buf,
-                         w2.f.buf_n, w2.f.cap, s);
+  e = sa::launch_hi_fine(a, pages, n_pages_keep, w2.n_pg, page_len, k_sparse, n_sink, n_window, w2.f, w2.seg,
+                         w2.seg_cnt, s);
   if (e != hipSuccess) return hip_fail(e, "sa_hi_select (token stage)");
   sa::MergeIn in{};
-  in.kept = w2.f.buf;
-  in.kept_ld = w2.f.cap;
-  in.kept_n = w2.f.buf_n;
+  in.cand = w2.seg;
+  in.cand_ld = (int64_t)w2.f.n_parts * w2.f.seg_cap;
+  in.seg_cnt = w2.seg_cnt;
+  in.n_seg = w2.f.n_parts;
+  in.seg_cap = w2.f.seg_cap;
   sa::MergeOut out{};
   out.final_mode = 1;
   out.idx = idx;
   out.idx_ld = idx_ld;
   out.n_sel = n_sel;
-  e = sa::launch_merge(B, k_sparse, in, w2.f.gather, w2.f.cap, out, s);
+  e = sa::launch_merge(B, k_sparse, in, w2.gather, (int64_t)w2.f.n_parts * k_sparse, out, s);
   return e == hipSuccess ? SA_OK : hip_fail(e, "sa_hi_select (merge)");
 }
 

@@ -106,6 +106,9 @@ __device__ __forceinline__ void wait_vmem() { wait_vmem_below<0>(); }
 // Data copied into LDS asynchronously must be waited for (wait_vmem*) by each wave before the barrier.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// This wave's LDS (and scalar-memory) operations complete; the memory clobber keeps accesses from moving across.
+__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 // 16-byte asynchronous copy global -> LDS: lane i of the wave writes lds_base + 16 * i.
 //
 // Issued from inline asm on purpose. When the compiler sees a global->LDS copy it cannot tell which LDS bytes

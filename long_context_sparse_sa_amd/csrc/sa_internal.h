@@ -163,15 +163,22 @@ hipError_t launch_hi_means(const uint16_t* k, int64_t k_ld, int64_t L, int d, in
 // first position p * page_len is past t_b (t_b = tok_L - 1 without t).
 hipError_t launch_page_scores(const IndexerArgs& m, int page_subs, int page_len, int64_t tok_L, float* scores,
                               int64_t scores_ld, hipStream_t stream);
-// Token stage: per query, its recalled pages pages[b, 0:n_pages[b]) (ascending); four queries per workgroup walk the
-// union of their pages and each keeps, in buf[b, 0:cap), candidates (in its pages, inside the sink/window budget)
-// that contain its exact top-k, in ascending position order; buf_n[b] their count.
-constexpr int kHiMaxPages = 1024;          // recalled pages per query
-constexpr int64_t kHiMaxCachePages = 1 << 17;  // pages of the cache
+// Token stage: per query, its recalled pages pages[b, 0:n_pages[b]) (ascending). The cache's pages are cut into
+// n_parts ranges of part_pages page ids; one wave per (query, part) keeps, in segment seg[(b n_parts + part)
+// seg_cap ...] with seg_cnt[b n_parts + part] entries, at most k candidates (in its pages, inside the sink/window
+// budget, ascending positions) that contain the part's exact top-k: the merge's segment input.
+constexpr int kHiMaxPages = 1 << 20;            // recalled pages per query (the size of the page list only)
+constexpr int64_t kHiTargetWaves = 1536;        // (query, part) waves wanted at the least
+struct HiFinePlan {
+  int n_parts;
+  int part_pages;
+  int64_t seg_cap;
+};
+HiFinePlan hi_fine_plan(int64_t L, int B, int page_len, int k);
 bool hi_fine_supported(const IndexerArgs& a);
 hipError_t launch_hi_fine(const IndexerArgs& a, const int32_t* pages, int pages_ld, const int32_t* n_pages,
-                          int page_len, int64_t n_cache_pages, int k, int n_sink, int n_window, Cand* buf,
-                          int32_t* buf_n, int cap, hipStream_t stream);
+                          int page_len, int k, int n_sink, int n_window, const HiFinePlan& p, Cand* seg,
+                          uint32_t* seg_cnt, hipStream_t stream);
 
 // Streaming per-query selection for many queries (prefill chunk): one pass over each query's visible keys keeps
 // at most `cap` candidates per query in buf[b, :] (count in buf_n[b]) that contain the exact top-k.

@@ -140,15 +140,14 @@ __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__flo
 // and each slot is refilled with the matching half-1 fragment as soon as its MFMAs are issued, so every LDS read
 // has eight MFMA pairs to land. The half-1 MFMAs are interleaved with the half-0 ReLU-weighted head sum (two MFMAs,
 // then eight VALU instructions, per k-step), so the matrix unit and the VALU work at the same time.
-template <int NMT>
-__device__ __forceinline__ float score_tile(const char* tile, int lane, const bf16x8 (&qa)[NMT][kSteps],
-                                           const float (&wv)[NMT][16]) {
+//
+// frag(nt, ks) gives this lane's B fragment of k-step ks in half nt: position 32 nt + lane % 32, dims
+// 16 ks + 8 (lane / 32) .. + 7. score_tile reads them from an LDS tile; score_frags takes any source.
+template <int NMT, typename FR>
+__device__ __forceinline__ float score_frags(FR&& frag, const bf16x8 (&qa)[NMT][kSteps],
+                                            const float (&wv)[NMT][16]) {
   static_assert(NMT * 16 % kSteps == 0, "head-sum chunks must divide evenly over the k-steps");
   constexpr int kChunk = NMT * 16 / kSteps;  // half-0 accumulator elements folded per half-1 k-step
-  const int hs = lane >> 5;
-  auto frag = [&](int nt, int ks) {
-    return *reinterpret_cast<const bf16x8*>(tile + tile_off(32 * nt + (lane & 31), 2 * ks + hs));
-  };
   bf16x8 fr[kSteps];
 #pragma unroll
   for (int ks = 0; ks < kSteps; ++ks) fr[ks] = frag(0, ks);
@@ -195,9 +194,49 @@ __device__ __forceinline__ float score_tile(const char* tile, int lane, const bf
   return fold_halves(part0, part1);
 }
 
+template <int NMT>
+__device__ __forceinline__ float score_tile(const char* tile, int lane, const bf16x8 (&qa)[NMT][kSteps],
+                                           const float (&wv)[NMT][16]) {
+  const int hs = lane >> 5;
+  return score_frags<NMT>(
+      [&](int nt, int ks) {
+        return *reinterpret_cast<const bf16x8*>(tile + tile_off(32 * nt + (lane & 31), 2 * ks + hs));
+      },
+      qa, wv);
+}
+
+// The B fragments of the 64-position tile at s0 straight from global memory into registers (rows past L - 1 are
+// clamped to it; they are never scored). Plain loads: the compiler places the waits before their first use.
+__device__ __forceinline__ void load_frags(const char* kbytes, int64_t ld_bytes, int64_t L, int64_t s0, int lane,
+                                           bf16x8 (&f)[2][kSteps]) {
+  const int hs = lane >> 5;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    int64_t row = s0 + 32 * nt + (lane & 31);
+    row = row < L ? row : L - 1;
+    const char* p = kbytes + row * ld_bytes + 16 * hs;
+#pragma unroll
+    for (int ks = 0; ks < kSteps; ++ks) f[nt][ks] = *reinterpret_cast<const bf16x8*>(p + 32 * ks);
+  }
+}
+
+// Waits until at most min(newer, MAXN) tiles of PER copies each are outstanding (vmcnt takes an immediate).
+template <int MAXN, int PER>
+__device__ __forceinline__ void wait_tiles_newer(int64_t newer) {
+  if constexpr (MAXN > 0) {
+    if (newer >= MAXN) {
+      wait_vmem_below<MAXN * PER>();
+      return;
+    }
+    wait_tiles_newer<MAXN - 1, PER>(newer);
+  } else {
+    wait_vmem_below<0>();
+  }
+}
+
 // Walks the tiles 0 .. n_tiles-1 of a workgroup's run (tile i covers positions tile_start(i) .. + 63): every wave
 // calls on_tile(tile_in_lds, i) once per tile, in order, after the tile's keys have landed in LDS. bf16 keys arrive
-// by asynchronous DMA into NBUF LDS buffers (NBUF - 1 tiles in flight); e4m3 keys are loaded two tiles ahead into a
+// by asynchronous DMA into NBUF >= 3 LDS buffers (NBUF - 1 tiles in flight); e4m3 keys are loaded two tiles ahead into a
 // register ring, converted and committed to two LDS buffers. All waves of the workgroup must call it.
 template <bool E4M3, int NQ, int NBUF, typename TS, typename F>
 __device__ __forceinline__ void walk_tiles(const char* kbytes, int64_t ld_bytes, int64_t L, int64_t n_tiles,
@@ -206,16 +245,16 @@ __device__ __forceinline__ void walk_tiles(const char* kbytes, int64_t ld_bytes,
   typedef KeyLoader<E4M3, NQ> KL;
   constexpr int kDmaPerWave = KeyLoader<false, NQ>::kPerWave;
   if constexpr (!E4M3) {
-    static_assert(NBUF == 4, "the waits below keep two tiles in flight behind the current one");
+    // at tile i's wait, tiles i+1 .. i+NBUF-2 may still be in flight; after the barrier (every wave is done with
+    // tile i-1) tile i+NBUF-1 goes into tile i-1's buffer, so NBUF-1 tiles are in flight while tile i is scored
+    static_assert(NBUF >= 3 && (NBUF - 2) * kDmaPerWave < 64, "the wait counts must fit the vmcnt field");
     typename KL::Regs none;
     KL::init(none, ld_bytes, wave, lane);
     const int64_t n_pre = n_tiles < NBUF - 1 ? n_tiles : NBUF - 1;
     for (int64_t p = 0; p < n_pre; ++p) KL::fetch(kbytes, ld_bytes, L, tile_start(p), tiles[p], wave, lane, none);
     for (int64_t i = 0; i < n_tiles; ++i) {
       const int64_t newer = n_tiles - 1 - i;
-      if (newer >= 2) wait_vmem_below<2 * kDmaPerWave>();
-      else if (newer == 1) wait_vmem_below<kDmaPerWave>();
-      else wait_vmem_below<0>();
+      wait_tiles_newer<NBUF - 2, kDmaPerWave>(newer);
       lds_barrier();
       if (i + NBUF - 1 < n_tiles)
         KL::fetch(kbytes, ld_bytes, L, tile_start(i + NBUF - 1), tiles[(i + NBUF - 1) % NBUF], wave, lane, none);

@@ -327,3 +327,13 @@ def hi_select(q, w, k, means, t: int, P: int, B: int, M: int, k_sparse: int, n_s
     cand = cand[np.isin(cand // P, pages)]
     sc = index_score_f32(q, w, k, cand)
     return topk_positions(sc, cand, k_sparse), pages, psc, cand, sc
+
+
+def hi_step(q_idx, w, k_idx, means, q, kv, t: int, P: int, B: int, M: int, k_sparse: int, n_sink: int,
+            n_window: int, scale: float, d_qk: int, d_v: int, v=None):
+    """Coarse-to-fine selection ([LongCat] HI section) plus sink and window, then attention over the read set.
+    Returns (ascending sparse positions, recalled pages, o [H, d_v], lse [H])."""
+    sel, pages, _, _, _ = hi_select(q_idx, w, k_idx, means, t, P, B, M, k_sparse, n_sink, n_window)
+    R = read_set(t, n_sink, n_window, sel)
+    o, lse = sparse_attn(q, kv, R, scale, d_qk, d_v, v=v)
+    return sel, pages, o, lse

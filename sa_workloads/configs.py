@@ -16,7 +16,7 @@ from typing import Optional
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str                 # "dsa" (lightning indexer + top-k) or "bucket" (Flat bucket search)
+    kind: str                 # "dsa" (lightning indexer + top-k), "hi" (coarse-to-fine) or "bucket" (Flat search)
     L: int                    # cached positions
     B: int                    # queries
     # indexer
@@ -29,6 +29,10 @@ class Workload:
     n_buckets: int = 0
     top_b: int = 0
     key_noise: float = 0.3    # k = centre[assign] + key_noise * N(0, 1)
+    # coarse-to-fine index: sub-block mean keys, pages of sub-blocks, pages recalled per query
+    sub_block: int = 0
+    page_len: int = 0
+    n_pages_keep: int = 0
     # selection budget
     n_sink: int = 0
     n_window: int = 0
@@ -72,6 +76,16 @@ WORKLOADS = {
     "lsa_flat_1m": Workload(
         name="lsa_flat_1m", kind="bucket", L=1 << 20, B=8, d_I=128, idx_dtype="bf16", n_buckets=16384, top_b=32,
         n_sink=4, n_window=128),
+    # A prefill chunk of 2048 queries at the end of a causal 1M sequence (the query length of the LongCat
+    # deep-dive's HI-versus-flat table), selected by the coarse-to-fine index: sub-blocks of 8, pages of 128, the
+    # best 1024 pages recalled per query (the settings of that section), then the top 2048 inside them.
+    "hi_prefill_1m": Workload(
+        name="hi_prefill_1m", kind="hi", L=1 << 20, B=2048, H_I=64, d_I=128, idx_dtype="bf16", k_sparse=2048,
+        sub_block=8, page_len=128, n_pages_keep=1024, causal_chunk=True),
+    # The same chunk selected by the flat indexer (every visible position scored): the table's other column.
+    "flat_prefill_1m": Workload(
+        name="flat_prefill_1m", kind="dsa", L=1 << 20, B=2048, H_I=64, d_I=128, idx_dtype="bf16", k_sparse=2048,
+        causal_chunk=True),
     # 10M-token decode with fp8 E4M3 index keys and queries, fp32 accumulation; 4 queries.
     "decode_10m_fp8": Workload(
         name="decode_10m_fp8", kind="dsa", L=10_000_000, B=4, H_I=64, d_I=128, idx_dtype="e4m3", k_sparse=2048,

@@ -228,8 +228,7 @@ def test_hi_validation(lib):
     assert hi(lib, P=128, sub=3) == SHAPE              # sub-blocks tile the page
     assert hi(lib, P=128, sub=1) == SHAPE              # 128 sub-blocks per page: more than one tile of means
     assert hi(lib, M=0) == SHAPE
-    assert hi(lib, M=1025) == SHAPE
-    assert hi(lib, L=(1 << 17) * 128 + 1) == SHAPE     # more pages than the token stage's bitmap holds
+    assert hi(lib, M=(1 << 20) + 1) == SHAPE
     assert hi(lib, kk=0) == SHAPE
     assert hi(lib, idx_ld=100) == SHAPE
     assert hi(lib, means=MIS) == ALIGN

@@ -90,3 +90,18 @@ def test_recall_limits_candidates_to_pages(seed):
     # the recalled pages are the 5 best page scores (ties to lower ids), checked by brute-force rank counting
     order = sorted(range(psc.size), key=lambda p: (-float(psc[p]), p))
     assert sorted(order[:5]) == pages.tolist()
+
+
+def test_hi_step_with_every_page_recalled_is_the_dsa_step():
+    # the whole-step composition reduces to the flat step when every visible page is recalled
+    rng = np.random.default_rng(7)
+    q_idx, w, k = _rand(7, 300)
+    q = rng.standard_normal((2, 16))
+    kv = rng.standard_normal((300, 16))
+    means = O.hi_means(k, 4)
+    sel, pages, o, lse = O.hi_step(q_idx, w, k, means, q, kv, 250, 16, 4, 1000, 30, 2, 10, 0.25, 16, 8)
+    sel2, o2, lse2 = O.dsa_step(q_idx, w, k, q, kv, 250, 30, 2, 10, 0.25, 16, 8)
+    np.testing.assert_array_equal(sel, sel2)
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(lse, lse2)
+    assert pages.tolist() == list(range(250 // 16 + 1))
