@@ -13,6 +13,8 @@ the definitions. Sources, cited by page title and section:
       - section "Mechanism 1: streaming-aware indexing (SI)", sub-section on the budget: the selected set is the
         disjoint union of sink, sliding window and the top-K of the indexer over the remaining positions;
         sub-section on the HFA kernel: partial attentions merge exactly by log-sum-exp rescaling.
+  [LCA]     "long-context attention" lecture (tju-yxq.github.io): sections "Qwen Sparse Attention" (QSA) and "MiniMax
+            Sparse Attention" (MSA), and the read-budget table of its budget calculator.
   [LSA-8]   "LSA sparse attention: does it save memory? eight QKV entries" (alphalab.site)
       - section 2: Latent Sparse Attention's four steps (index keys; buckets keeping a representative vector and
         member positions; Flat search over representatives; read the chosen rows plus sink plus window);
@@ -337,3 +339,67 @@ def hi_step(q_idx, w, k_idx, means, q, kv, t: int, P: int, B: int, M: int, k_spa
     R = read_set(t, n_sink, n_window, sel)
     o, lse = sparse_attn(q, kv, R, scale, d_qk, d_v, v=v)
     return sel, pages, o, lse
+
+
+
+# ----------------------------------------------------------------------------------------------------------------
+# Block-granular indexers ([LCA] QSA and MSA sections; per-mechanism read budgets in its budget table).
+# Readings where the lecture is silent:
+#   QSA * a micro-block is b consecutive positions (b = 4 in the release configuration); its pooled index key is
+#         the mean of its keys, computed and stored as hi_means does (fp64, rounded through fp32 to bf16);
+#       * the normalisation and position encoding the model applies to pooled keys are learned transforms, not
+#         part of this path: a caller applies them to the pooled keys before selecting;
+#       * a micro-block enters the ranking once all its positions are <= t; it scores the indexer equation on its
+#         pooled key; the k_blocks best (fp32 score desc, block id asc) expand to their b positions;
+#       * the visible positions of the unfinished micro-block (t+1 mod b of them) are read directly;
+#       * the release budget of 2048 tokens is k_blocks = 2048 / b micro-blocks.
+#   MSA * the indexer heads form G equal groups (one per GQA group; a group's query heads share its selection);
+#         group g's token score is the indexer equation over its own heads, one index key per position;
+#       * a block is c consecutive positions (c = 128); its score is the largest visible token score in it;
+#       * the block holding t (the local block) is always read; the k_b - 1 best earlier blocks (fp32 score
+#         desc, block id asc) complete the group's k_b blocks (16 x 128 = 2048 positions, the table's per-group
+#         budget); the local block is read only up to t.
+# ----------------------------------------------------------------------------------------------------------------
+
+
+def qsa_pool(k: np.ndarray, b: int) -> np.ndarray:
+    """Pooled index keys of the micro-blocks of b positions (bf16 values as fp64); the last may be partial."""
+    return hi_means(k, b)
+
+
+def qsa_select(q, w, pooled, t: int, b: int, k_blocks: int):
+    """QSA read set of one query. Returns (ascending positions: chosen micro-blocks expanded, then the tail;
+    chosen block ids ascending; fp32 scores of the complete blocks)."""
+    n_complete = (t + 1) // b
+    blocks = np.arange(n_complete, dtype=np.int64)
+    sc = index_score_f32(q, w, pooled, blocks)
+    chosen = topk_positions(sc, blocks, k_blocks)
+    expanded = (chosen[:, None] * b + np.arange(b, dtype=np.int64)[None, :]).reshape(-1)
+    tail = np.arange(n_complete * b, t + 1, dtype=np.int64)
+    return np.concatenate([expanded, tail]), chosen, sc
+
+
+def msa_block_scores(q, w, k, t: int, G: int, c: int):
+    """Per group g: fp32 block scores of the blocks before the local block (max of their token scores)."""
+    H = q.shape[0]
+    hg = H // G
+    local = t // c
+    out = []
+    for g in range(G):
+        tok = index_score_f32(q[g * hg:(g + 1) * hg], w[g * hg:(g + 1) * hg], k, np.arange(local * c))
+        out.append(tok.reshape(local, c).max(axis=1) if local > 0 else np.zeros(0, dtype=np.float32))
+    return out
+
+
+def msa_select(q, w, k, t: int, G: int, c: int, k_b: int):
+    """MSA read sets of one query, one per group. Returns a list over groups of (ascending positions, chosen block
+    ids ascending with the local block last, fp32 block scores of the earlier blocks)."""
+    local = t // c
+    res = []
+    for bsc in msa_block_scores(q, w, k, t, G, c):
+        chosen = topk_positions(bsc, np.arange(local, dtype=np.int64), k_b - 1)
+        blocks = np.concatenate([chosen, [local]]).astype(np.int64)
+        pos = np.concatenate([(chosen[:, None] * c + np.arange(c)[None, :]).reshape(-1),
+                              np.arange(local * c, t + 1)]).astype(np.int64)
+        res.append((pos, blocks, bsc))
+    return res
