@@ -4,7 +4,8 @@
  * The path has three steps, each a call below:
  *   score   an indexer scores every cached position           (sa_index_score, inside sa_select_topk)
  *   select  exact top-k plus sink/window positions             (sa_select_topk; sa_bucket_select for buckets;
- *                                                               sa_hi_select for the coarse-to-fine search)
+ *                                                               sa_hi_select for the coarse-to-fine search;
+ *                                                               sa_qsa_select / sa_msa_select for blocks)
  *   attend  softmax attention over only the gathered rows      (sa_sparse_attn)
  *
  * Sources (web pages; cited by title and section):
@@ -13,6 +14,10 @@
  *              section "Mechanism 1: streaming-aware indexing (SI)" (budget decomposition equations; HFA kernel);
  *              section "Mechanism 3: hierarchical indexing (HI)" (sub-block mean keys, page scores, top-M pages,
  *              token top-k inside them).
+ *   [LCA]      "long-context attention" lecture (tju-yxq.github.io): sections "Qwen Sparse Attention" (QSA: index keys
+ *              pooled over micro-blocks, micro-blocks expanded to raw positions, the unfinished micro-block read
+ *              directly) and "MiniMax Sparse Attention" (MSA: block max of token scores, per-group top-k blocks, the
+ *              local block always kept); the per-mechanism read budgets of its budget table.
  *   [LSA-8]    "LSA sparse attention: does it save memory? eight QKV entries" (alphalab.site): section 2 (the four
  *              steps of Latent Sparse Attention: index keys, buckets with a representative and member positions,
  *              Flat search over representatives, read selected rows plus sink plus window); sections 3-4 (the
@@ -232,6 +237,46 @@ SA_API int sa_hi_select(const void* q, int q_dtype, const float* w, const void* 
                         int32_t sub_block, int32_t page_len, int32_t n_pages_keep, int32_t k_sparse, int32_t n_sink,
                         int32_t n_window, int32_t* idx, int32_t idx_ld, int32_t* n_sel, int32_t* pages_out,
                         void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------------------------------
+ * sa_qsa_pool -- pooled index keys of micro-blocks of `block` consecutive positions ([LCA] QSA section): the mean
+ * of their keys, computed exactly as sa_hi_build computes sub-block means (bf16 out, [ceil(L / block), d]). The
+ * learned normalisation and position encoding a model applies to pooled keys are not part of this library: a
+ * caller applies them to `pooled` before sa_qsa_select.
+ *
+ * sa_qsa_select -- micro-block selection ([LCA] QSA section): query b ranks the micro-blocks whose positions are
+ * all <= t_b by the indexer equation (as sa_index_score) on their pooled keys, keeps the k_blocks best (ties: lower
+ * block), and reads them whole, then the visible positions of its unfinished micro-block ((t_b + 1) mod block of
+ * them, read directly).
+ *   q [B, H, d] bf16, w [B, H] fp32, pooled [ceil(L / block), d] bf16 contiguous (d a multiple of 8), t as
+ *   sa_index_score (positions of the L-position cache).
+ *   idx [B, idx_ld] int32 out: ascending positions, -1 padding; idx_ld >= k_blocks * block + block - 1.
+ *   n_sel [B] int32 out.   k_blocks in [1, 16384].
+ *   ws / ws_bytes: at least sa_qsa_select_workspace(L, B, H, d, block, k_blocks) bytes.
+ *
+ * sa_msa_select -- per-group block selection ([LCA] MSA section): the H indexer heads form G equal groups; for
+ * (query b, group g) the token score is the indexer equation over the group's heads, a block of `block` positions
+ * scores the largest token score in it, the block holding t_b (the local block) is always read, and the
+ * k_blocks - 1 best earlier blocks (ties: lower block) complete the group's blocks.
+ *   q, w, k, k_ld, L, B, H, d, t: as sa_index_score; d = 128, H / G in {32, 64}, bf16 or e4m3.
+ *   block a multiple of 64.   k_blocks >= 1.
+ *   idx [B * G, idx_ld] int32 out (row b * G + g): ascending positions (chosen blocks whole, then the local block up
+ *   to t_b), -1 padding; idx_ld >= k_blocks * block.   n_sel [B * G] int32 out.
+ *   ws / ws_bytes: at least sa_msa_select_workspace(L, B, G, block, k_blocks) bytes.
+ *   For the attention step, row b * G + g is a query whose heads are group g's query heads (sa_sparse_attn with
+ *   B * G queries of H_q / G heads each).
+ * ------------------------------------------------------------------------------------------------------------- */
+SA_API int sa_qsa_pool(const void* k, int k_dtype, int64_t k_ld, int64_t L, int32_t d, int32_t block, void* pooled,
+                       void* stream);
+SA_API size_t sa_qsa_select_workspace(int64_t L, int32_t B, int32_t H, int32_t d, int32_t block, int32_t k_blocks);
+SA_API int sa_qsa_select(const void* q, int q_dtype, const float* w, const void* pooled, int64_t L, int32_t B,
+                         int32_t H, int32_t d, const int32_t* t, int32_t block, int32_t k_blocks, int32_t* idx,
+                         int32_t idx_ld, int32_t* n_sel, void* ws, size_t ws_bytes, void* stream);
+SA_API size_t sa_msa_select_workspace(int64_t L, int32_t B, int32_t G, int32_t block, int32_t k_blocks);
+SA_API int sa_msa_select(const void* q, int q_dtype, const float* w, const void* k, int k_dtype, int64_t k_ld,
+                         int64_t L, int32_t B, int32_t H, int32_t d, int32_t G, const int32_t* t, int32_t block,
+                         int32_t k_blocks, int32_t* idx, int32_t idx_ld, int32_t* n_sel, void* ws, size_t ws_bytes,
+                         void* stream);
 
 /* ---------------------------------------------------------------------------------------------------------------
  * sa_sparse_attn -- attention over the read set only ([LongCat] DSA baseline section, sparse-attention equation,

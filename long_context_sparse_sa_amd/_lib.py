@@ -42,6 +42,11 @@ SIGNATURES = {
     "sa_hi_select_workspace": (SZ, [I64, I32, I32, I32, I32, I32]),
     "sa_hi_select": (INT, [P, INT, P, P, INT, I64, I64, I32, I32, I32, P, P, I32, I32, I32, I32, I32, I32, P, I32, P,
                            P, P, SZ, P]),
+    "sa_qsa_pool": (INT, [P, INT, I64, I64, I32, I32, P, P]),
+    "sa_qsa_select_workspace": (SZ, [I64, I32, I32, I32, I32, I32]),
+    "sa_qsa_select": (INT, [P, INT, P, P, I64, I32, I32, I32, P, I32, I32, P, I32, P, P, SZ, P]),
+    "sa_msa_select_workspace": (SZ, [I64, I32, I32, I32, I32]),
+    "sa_msa_select": (INT, [P, INT, P, P, INT, I64, I64, I32, I32, I32, I32, P, I32, I32, P, I32, P, P, SZ, P]),
     "sa_sparse_attn_workspace": (SZ, [I32, I32, I32, I32, I64, INT]),
     "sa_sparse_attn": (INT, [P, P, P, INT, I64, I64, I64, I32, I32, I32, I32, P, P, I32, P, I32, I32, F32, P, P, P,
                              SZ, P]),

@@ -220,6 +220,65 @@ def sa_hi_select(q_idx, w, k_idx, means, sub_block: int, page_len: int, n_pages_
     return (idx, n_sel, pages) if return_pages else (idx, n_sel)
 
 
+def sa_qsa_pool(k_idx, block: int, out=None, stream=None):
+    """Pooled index keys [ceil(L / block), d] (bf16): the mean of each micro-block's keys."""
+    _need_cuda(k_idx)
+    L, d = k_idx.shape
+    n = (L + block - 1) // block
+    pooled = torch.empty((n, d), dtype=torch.bfloat16, device=k_idx.device) if out is None else out
+    if pooled.shape != (n, d) or pooled.dtype != torch.bfloat16 or not pooled.is_contiguous():
+        raise ValueError(f"out must be a contiguous bf16 tensor of shape {(n, d)}")
+    st = _lib.load().sa_qsa_pool(_ptr(k_idx), _dtype(k_idx), _rows(k_idx), L, d, block, _ptr(pooled),
+                                 _stream(stream))
+    _lib.check("sa_qsa_pool", st)
+    return pooled
+
+
+def sa_qsa_select(q_idx, w, pooled, L: int, block: int, k_blocks: int, t=None, idx_ld: Optional[int] = None,
+                  ws=None, out=None, stream=None):
+    """(idx [B, idx_ld] ascending with -1 padding, n_sel [B]): chosen micro-blocks expanded, then the tail."""
+    _need_cuda(q_idx, w, pooled, t)
+    B, H, d = q_idx.shape
+    if not pooled.is_contiguous() or pooled.shape != ((L + block - 1) // block, d):
+        raise ValueError("pooled must be the contiguous output of sa_qsa_pool for this cache and block")
+    idx_ld = k_blocks * block + block - 1 if idx_ld is None else idx_ld
+    lib = _lib.load()
+    nbytes = lib.sa_qsa_select_workspace(L, B, H, d, block, k_blocks)
+    ws = _workspace(nbytes, q_idx.device, ws)
+    if out is None:
+        idx = torch.empty((B, idx_ld), dtype=torch.int32, device=q_idx.device)
+        n_sel = torch.empty((B,), dtype=torch.int32, device=q_idx.device)
+    else:
+        idx, n_sel = out
+    st = lib.sa_qsa_select(_ptr(q_idx), _dtype(q_idx), _ptr(w), _ptr(pooled), L, B, H, d, _ptr(t), block, k_blocks,
+                           _ptr(idx), idx.stride(0), _ptr(n_sel), _ptr(ws), nbytes, _stream(stream))
+    _lib.check("sa_qsa_select", st)
+    return idx, n_sel
+
+
+def sa_msa_select(q_idx, w, k_idx, G: int, block: int, k_blocks: int, t=None, idx_ld: Optional[int] = None,
+                  ws=None, out=None, stream=None):
+    """(idx [B * G, idx_ld] ascending with -1 padding, n_sel [B * G]): per (query, group) the chosen blocks whole,
+    then the local block up to t."""
+    _need_cuda(q_idx, w, k_idx, t)
+    B, H, d = q_idx.shape
+    L = k_idx.shape[0]
+    idx_ld = k_blocks * block if idx_ld is None else idx_ld
+    lib = _lib.load()
+    nbytes = lib.sa_msa_select_workspace(L, B, G, block, k_blocks)
+    ws = _workspace(nbytes, q_idx.device, ws)
+    if out is None:
+        idx = torch.empty((B * G, idx_ld), dtype=torch.int32, device=q_idx.device)
+        n_sel = torch.empty((B * G,), dtype=torch.int32, device=q_idx.device)
+    else:
+        idx, n_sel = out
+    st = lib.sa_msa_select(_ptr(q_idx), _dtype(q_idx), _ptr(w), _ptr(k_idx), _dtype(k_idx), _rows(k_idx), L, B, H,
+                           d, G, _ptr(t), block, k_blocks, _ptr(idx), idx.stride(0), _ptr(n_sel), _ptr(ws), nbytes,
+                           _stream(stream))
+    _lib.check("sa_msa_select", st)
+    return idx, n_sel
+
+
 def sa_sparse_attn_workspace(B, H, d_qk, d_v, max_rows, dtype) -> int:
     return int(_lib.load().sa_sparse_attn_workspace(B, H, d_qk, d_v, max_rows, dtype))
 

@@ -154,11 +154,24 @@ __global__ __launch_bounds__(64 * NQ) void k_score_mfma(const void* __restrict__
   };
   auto process_tile = [&](const char* tile, int64_t s0) {
     if (!active || s0 >= hi) return;
+    // block maxima rank only the blocks before the one holding t (page_len is the block length, a multiple of 64,
+    // so a tile lies in one block)
+    if (mode == kScoreBlockMax && s0 / page_len >= tb / page_len) return;
     if (mode == kScoreEmit && n_emit > kStage - kTileKeys) flush();
     const float score = score_tile<NMT>(tile, lane, qa, wv);
     const int64_t s = s0 + lane;  // lane order is position order
     const bool in_range = s < hi;
-    if (mode == kScorePage) {
+    if (mode == kScoreBlockMax) {
+      // every position of a block before the local one is visible; the block's key is the max of its scores'
+      // keys (score_key is order-preserving), combined over its tiles with an atomic max
+      uint32_t kv = in_range ? score_key(score) : 0u;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const uint32_t x = __shfl_xor(kv, o, kWave);
+        kv = x > kv ? x : kv;
+      }
+      if (lane == 0) atomicMax(reinterpret_cast<uint32_t*>(scores) + (int64_t)b * scores_ld + s0 / page_len, kv);
+    } else if (mode == kScorePage) {
       // the rows are the sub-block mean keys of the hierarchical index; page p = rows [p G, (p + 1) G) (G divides
       // the 64 rows of a tile, tiles start at multiples of 64): its score sums theirs, rows past the last add 0
       float v = in_range ? score : 0.f;
@@ -611,6 +624,24 @@ hipError_t launch_page_scores(const IndexerArgs& m, int page_subs, int page_len,
   }
   if (wide) return launch_mfma<1, false, 8>(m, 0, m.L, kScorePage, scores, scores_ld, 0, 0, nullptr, nullptr, 0, nullptr, st, page_subs, page_len, tok_L);
   return launch_mfma<1, false, 4>(m, 0, m.L, kScorePage, scores, scores_ld, 0, 0, nullptr, nullptr, 0, nullptr, st, page_subs, page_len, tok_L);
+}
+
+hipError_t launch_block_max(const IndexerArgs& a, int block, uint32_t* keys, int64_t keys_ld, hipStream_t st) {
+  if (!score_uses_mfma(a) || block < kTileKeys || block % kTileKeys != 0) return hipErrorInvalidValue;
+  if (a.B < 1 || a.L < 1) return hipSuccess;
+  float* out = reinterpret_cast<float*>(keys);  // the block-max mode writes uint32 keys through the scores pointer
+  const bool wide = a.B >= 8;
+  const bool fp8 = a.q_dtype == 2;
+  if (a.H == 64) {
+    if (fp8) return wide ? launch_mfma<2, true, 8>(a, 0, a.L, kScoreBlockMax, out, keys_ld, 0, 0, nullptr, nullptr, 0, nullptr, st, 1, block, a.L)
+                         : launch_mfma<2, true, 4>(a, 0, a.L, kScoreBlockMax, out, keys_ld, 0, 0, nullptr, nullptr, 0, nullptr, st, 1, block, a.L);
+    return wide ? launch_mfma<2, false, 8>(a, 0, a.L, kScoreBlockMax, out, keys_ld, 0, 0, nullptr, nullptr, 0, nullptr, st, 1, block, a.L)
+                : launch_mfma<2, false, 4>(a, 0, a.L, kScoreBlockMax, out, keys_ld, 0, 0, nullptr, nullptr, 0, nullptr, st, 1, block, a.L);
+  }
+  if (fp8) return wide ? launch_mfma<1, true, 8>(a, 0, a.L, kScoreBlockMax, out, keys_ld, 0, 0, nullptr, nullptr, 0, nullptr, st, 1, block, a.L)
+                       : launch_mfma<1, true, 4>(a, 0, a.L, kScoreBlockMax, out, keys_ld, 0, 0, nullptr, nullptr, 0, nullptr, st, 1, block, a.L);
+  return wide ? launch_mfma<1, false, 8>(a, 0, a.L, kScoreBlockMax, out, keys_ld, 0, 0, nullptr, nullptr, 0, nullptr, st, 1, block, a.L)
+              : launch_mfma<1, false, 4>(a, 0, a.L, kScoreBlockMax, out, keys_ld, 0, 0, nullptr, nullptr, 0, nullptr, st, 1, block, a.L);
 }
 
 bool stream_supported(const IndexerArgs& a) { return score_uses_mfma(a); }

@@ -704,6 +704,147 @@ SA_API int sa_hi_select(const void* q, int q_dtype, const float* w, const void* 
 }
 
 // ---------------------------------------------------------------------------------------------------------------
+namespace {
+
+struct QsaWs {
+  int64_t Lp;        // pooled rows
+  int32_t* tq;       // [B] last complete micro-block
+  int32_t* blk;      // [B, k_blocks] chosen micro-blocks
+  int32_t* n_blk;    // [B]
+  void* sel;         // the flat selection's workspace
+  size_t sel_bytes;
+  size_t bytes;
+};
+
+QsaWs carve_qsa(void* ws, int64_t L, int32_t B, int32_t H, int32_t d, int32_t b, int32_t kb) {
+  QsaWs w{};
+  w.Lp = (L + b - 1) / b;
+  Carver c(ws);
+  w.tq = c.take<int32_t>(B);
+  w.blk = c.take<int32_t>((size_t)B * kb);
+  w.n_blk = c.take<int32_t>(B);
+  w.sel_bytes = sa_select_topk_workspace(w.Lp, B, H, d, SA_BF16, SA_BF16, kb, SA_TOPK_AUTO);
+  w.sel = c.take<char>(w.sel_bytes);
+  w.bytes = align_up(c.off, 256);
+  return w;
+}
+
+struct MsaWs {
+  int64_t n_blocks;
+  int32_t* tq;       // [B G] t of each (query, group)
+  RadixWs r;         // block keys and the select's control words
+  int32_t* blk;      // [B G, k_blocks - 1] chosen earlier blocks
+  int32_t* n_blk;    // [B G]
+  size_t bytes;
+};
+
+MsaWs carve_msa(void* ws, int64_t L, int32_t B, int32_t G, int32_t c, int32_t kb) {
+  MsaWs w{};
+  w.n_blocks = (L + c - 1) / c;
+  const int32_t Bp = B * G;
+  Carver cv(ws);
+  w.tq = cv.take<int32_t>(Bp);
+  sa::IndexerArgs pa{};
+  pa.B = Bp;
+  pa.L = w.n_blocks;
+  const size_t r_off = align_up(cv.off, 256);
+  w.r = carve_radix(ws ? static_cast<char*>(ws) + r_off : nullptr, pa);
+  cv.off = r_off + w.r.bytes;
+  w.blk = cv.take<int32_t>((size_t)Bp * (kb > 1 ? kb - 1 : 1));
+  w.n_blk = cv.take<int32_t>(Bp);
+  w.bytes = align_up(cv.off, 256);
+  return w;
+}
+
+}  // namespace
+
+SA_API int sa_qsa_pool(const void* k, int k_dtype, int64_t k_ld, int64_t L, int32_t d, int32_t block, void* pooled,
+                       void* stream) {
+  return sa_hi_build(k, k_dtype, k_ld, L, d, block, pooled, stream);
+}
+
+SA_API size_t sa_qsa_select_workspace(int64_t L, int32_t B, int32_t H, int32_t d, int32_t block, int32_t k_blocks) {
+  if (L < 1 || B < 0 || H < 1 || d < 1 || block < 1 || k_blocks < 1) return 0;
+  return carve_qsa(nullptr, L, B, H, d, block, k_blocks).bytes;
+}
+
+SA_API int sa_qsa_select(const void* q, int q_dtype, const float* w, const void* pooled, int64_t L, int32_t B,
+                         int32_t H, int32_t d, const int32_t* t, int32_t block, int32_t k_blocks, int32_t* idx,
+                         int32_t idx_ld, int32_t* n_sel, void* ws, size_t ws_bytes, void* stream) {
+  if (block < 1 || L < 1) return fail(SA_ERR_SHAPE, "need block >= 1 and L >= 1");
+  const int64_t Lp = (L + block - 1) / block;
+  int st = check_indexer(q, q_dtype, w, pooled, q_dtype, d, Lp, B, H, d);
+  if (st) return st;
+  if (q_dtype != SA_BF16) return fail(SA_ERR_DTYPE, "the pooled keys are bf16: q must be bf16 too");
+  if (!idx || !n_sel) return fail(SA_ERR_NULL, "idx and n_sel must be non-NULL");
+  if (k_blocks < 1 || k_blocks > sa::merge_max_k())
+    return fail(SA_ERR_SHAPE, "k_blocks must be in [1, %d]", sa::merge_max_k());
+  if ((int64_t)idx_ld < (int64_t)k_blocks * block + block - 1)
+    return fail(SA_ERR_SHAPE, "idx_ld must hold k_blocks * block + block - 1 positions");
+  const size_t need = sa_qsa_select_workspace(L, B, H, d, block, k_blocks);
+  if (!ws || ws_bytes < need) return fail(SA_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  if (!aligned16(ws)) return fail(SA_ERR_ALIGN, "workspace must be 16-byte aligned");
+  if (B == 0) return SA_OK;
+  const QsaWs w2 = carve_qsa(ws, L, B, H, d, block, k_blocks);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = sa::launch_block_t(t, B, 1, L, block, w2.tq, s);
+  if (e != hipSuccess) return hip_fail(e, "sa_qsa_select (bounds)");
+  // the flat selection over the pooled keys, each query bounded by its last complete micro-block
+  st = sa_select_topk(q, q_dtype, w, pooled, SA_BF16, d, Lp, B, H, d, w2.tq, k_blocks, 0, 0, w2.blk, k_blocks,
+                      w2.n_blk, w2.sel, w2.sel_bytes, SA_TOPK_AUTO, stream);
+  if (st) return st;
+  e = sa::launch_qsa_expand(w2.blk, k_blocks, w2.n_blk, t, B, L, block, idx, idx_ld, n_sel, s);
+  return e == hipSuccess ? SA_OK : hip_fail(e, "sa_qsa_select (expand)");
+}
+
+SA_API size_t sa_msa_select_workspace(int64_t L, int32_t B, int32_t G, int32_t block, int32_t k_blocks) {
+  if (L < 1 || B < 0 || G < 1 || block < 1 || k_blocks < 1) return 0;
+  return carve_msa(nullptr, L, B, G, block, k_blocks).bytes;
+}
+
+SA_API int sa_msa_select(const void* q, int q_dtype, const float* w, const void* k, int k_dtype, int64_t k_ld,
+                         int64_t L, int32_t B, int32_t H, int32_t d, int32_t G, const int32_t* t, int32_t block,
+                         int32_t k_blocks, int32_t* idx, int32_t idx_ld, int32_t* n_sel, void* ws, size_t ws_bytes,
+                         void* stream) {
+  int st = check_indexer(q, q_dtype, w, k, k_dtype, k_ld, L, B, H, d);
+  if (st) return st;
+  if (!idx || !n_sel) return fail(SA_ERR_NULL, "idx and n_sel must be non-NULL");
+  if (G < 1 || H % G != 0) return fail(SA_ERR_SHAPE, "G must divide H");
+  if (block < 64 || block % 64 != 0) return fail(SA_ERR_SHAPE, "block must be a multiple of 64");
+  if (k_blocks < 1) return fail(SA_ERR_SHAPE, "k_blocks must be >= 1");
+  if ((int64_t)B * G > 0x7FFFFFFF / 2) return fail(SA_ERR_SHAPE, "too many (query, group) pairs");
+  if ((int64_t)idx_ld < (int64_t)k_blocks * block) return fail(SA_ERR_SHAPE, "idx_ld must hold k_blocks * block");
+  const sa::IndexerArgs probe = make_indexer(q, q_dtype, w, k, k_dtype, k_ld, L, B * G, H / G, d, nullptr);
+  if (!sa::score_uses_mfma(probe))
+    return fail(SA_ERR_UNSUPPORTED, "the block indexer needs d = 128, H / G in {32, 64} and bf16 or e4m3 inputs");
+  const size_t need = sa_msa_select_workspace(L, B, G, block, k_blocks);
+  if (!ws || ws_bytes < need) return fail(SA_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  if (!aligned16(ws)) return fail(SA_ERR_ALIGN, "workspace must be 16-byte aligned");
+  if (B == 0) return SA_OK;
+  const MsaWs w2 = carve_msa(ws, L, B, G, block, k_blocks);
+  const int32_t Bp = B * G;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = sa::launch_block_t(t, B, G, L, 1, w2.tq, s);
+  if (e != hipSuccess) return hip_fail(e, "sa_msa_select (bounds)");
+  // zero the block keys and the select's control words (one contiguous range), then the block maxima
+  const size_t words = (size_t)((reinterpret_cast<char*>(w2.r.keys + (size_t)Bp * w2.r.p.keys_ld) -
+                                 reinterpret_cast<char*>(w2.r.ctl)) / 4);
+  e = sa::launch_fill_u32(w2.r.ctl, (int64_t)words, 0u, s);
+  if (e != hipSuccess) return hip_fail(e, "sa_msa_select (clear)");
+  const sa::IndexerArgs a = make_indexer(q, q_dtype, w, k, k_dtype, k_ld, L, Bp, H / G, d, w2.tq);
+  e = sa::launch_block_max(a, block, w2.r.keys, w2.r.p.keys_ld, s);
+  if (e != hipSuccess) return hip_fail(e, "sa_msa_select (block maxima)");
+  if (k_blocks > 1) {
+    e = sa::launch_radix_select(Bp, w2.n_blocks, k_blocks - 1, w2.r.p, w2.r.keys, w2.r.ctl, w2.blk, k_blocks - 1,
+                                w2.n_blk, nullptr, nullptr, s);
+    if (e != hipSuccess) return hip_fail(e, "sa_msa_select (block select)");
+  }
+  e = sa::launch_msa_expand(k_blocks > 1 ? w2.blk : nullptr, k_blocks > 1 ? k_blocks - 1 : 1,
+                            k_blocks > 1 ? w2.n_blk : nullptr, w2.tq, Bp, block, idx, idx_ld, n_sel, s);
+  return e == hipSuccess ? SA_OK : hip_fail(e, "sa_msa_select (expand)");
+}
+
+// ---------------------------------------------------------------------------------------------------------------
 SA_API size_t sa_bucket_build_workspace(int64_t L, int32_t n_buckets) {
   if (L < 0 || n_buckets < 1) return 0;
   const sa::BucketBuildPlan p = sa::bucket_build_plan(L, n_buckets);

@@ -41,7 +41,7 @@ struct Cand {
   int32_t pos;
 };
 
-enum ScoreMode { kScoreDense = 0, kScoreEmit = 1, kScoreAll = 2, kScorePage = 3 };
+enum ScoreMode { kScoreDense = 0, kScoreEmit = 1, kScoreAll = 2, kScorePage = 3, kScoreBlockMax = 4 };
 
 // Positions handled by one workgroup of the scoring kernel chosen for these arguments.
 int score_keys_per_wg(const IndexerArgs& a);
@@ -179,6 +179,23 @@ bool hi_fine_supported(const IndexerArgs& a);
 hipError_t launch_hi_fine(const IndexerArgs& a, const int32_t* pages, int pages_ld, const int32_t* n_pages,
                           int page_len, int k, int n_sink, int n_window, const HiFinePlan& p, Cand* seg,
                           uint32_t* seg_cnt, hipStream_t stream);
+
+// Block-granular indexers (k_blocks.hip and the MFMA scorer's block-max mode).
+// keys[b * keys_ld + n] = max over positions s of block n (positions [n c, (n + 1) c)) of score_key(I(b, s)), for
+// the blocks before the one holding t_b; the other entries are left as they are (zero them first). c is a
+// multiple of 64. The MFMA scorer shapes only.
+hipError_t launch_block_max(const IndexerArgs& a, int block, uint32_t* keys, int64_t keys_ld, hipStream_t stream);
+// t_out[b * reps + r] = t ? t[b] : L - 1 (r < reps), then, with div > 1, max(0, (t + 1) / div - 1): the last complete
+// micro-block of query b (clamped to 0 when there is none).
+hipError_t launch_block_t(const int32_t* t, int B, int reps, int64_t L, int div, int32_t* t_out, hipStream_t stream);
+// Micro-blocks of b positions to positions: the chosen blocks blk[q, 0:min(n_blk[q], kb)) (ascending), expanded,
+// then the unfinished block's visible positions; no block when query q has no complete block.
+hipError_t launch_qsa_expand(const int32_t* blk, int kb, const int32_t* n_blk, const int32_t* t, int B, int64_t L,
+                             int b, int32_t* idx, int idx_ld, int32_t* n_sel, hipStream_t stream);
+// Blocks of c positions to positions: the chosen earlier blocks blk[q, 0:n_blk[q]) (ascending; n_blk NULL: none)
+// expanded, then the local block up to t[q].
+hipError_t launch_msa_expand(const int32_t* blk, int blk_ld, const int32_t* n_blk, const int32_t* t, int B, int c,
+                             int32_t* idx, int idx_ld, int32_t* n_sel, hipStream_t stream);
 
 // Streaming per-query selection for many queries (prefill chunk): one pass over each query's visible keys keeps
 // at most `cap` candidates per query in buf[b, :] (count in buf_n[b]) that contain the exact top-k.

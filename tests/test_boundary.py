@@ -242,3 +242,45 @@ def test_hi_validation(lib):
     assert lib.sa_hi_build(A, E4M3, 128, 1000, 128, 8, A, None) == DTYPE
     assert lib.sa_hi_build(A, BF16, 64, 1000, 128, 8, A, None) == SHAPE
     assert lib.sa_hi_build(A, BF16, 128, 1000, 128, 0, A, None) == SHAPE
+
+
+def test_qsa_msa_validation(lib):
+    B, H, d, L = 4, 64, 128, 100_000
+    need_q = lib.sa_qsa_select_workspace(L, B, H, d, 4, 512)
+    assert need_q > 0
+
+    def qsa(**kw):
+        a = dict(q=A, qd=BF16, w=A, pooled=A, L=L, B=B, H=H, d=d, t=None, block=4, kb=512, idx=A,
+                 idx_ld=512 * 4 + 3, nsel=A, ws=A, wsb=need_q)
+        a.update(kw)
+        return lib.sa_qsa_select(a["q"], a["qd"], a["w"], a["pooled"], a["L"], a["B"], a["H"], a["d"], a["t"],
+                                 a["block"], a["kb"], a["idx"], a["idx_ld"], a["nsel"], a["ws"], a["wsb"], None)
+
+    assert qsa(idx=None) == NULL
+    assert qsa(pooled=None) == NULL
+    assert qsa(qd=E4M3) == DTYPE                   # pooled keys are bf16
+    assert qsa(block=0) == SHAPE
+    assert qsa(kb=0) == SHAPE
+    assert qsa(idx_ld=512 * 4 + 2) == SHAPE        # the tail needs up to block - 1 more entries
+    assert qsa(wsb=need_q - 1) == WS
+    assert qsa(B=0, wsb=lib.sa_qsa_select_workspace(L, 0, H, d, 4, 512)) == OK
+
+    need_m = lib.sa_msa_select_workspace(L, B, 2, 128, 16)
+    assert need_m > 0
+
+    def msa(**kw):
+        a = dict(q=A, qd=BF16, w=A, k=A, kd=BF16, k_ld=d, L=L, B=B, H=H, d=d, G=2, t=None, block=128, kb=16, idx=A,
+                 idx_ld=16 * 128, nsel=A, ws=A, wsb=need_m)
+        a.update(kw)
+        return lib.sa_msa_select(a["q"], a["qd"], a["w"], a["k"], a["kd"], a["k_ld"], a["L"], a["B"], a["H"],
+                                 a["d"], a["G"], a["t"], a["block"], a["kb"], a["idx"], a["idx_ld"], a["nsel"],
+                                 a["ws"], a["wsb"], None)
+
+    assert msa(idx=None) == NULL
+    assert msa(G=3) == SHAPE                       # G must divide H
+    assert msa(block=100) == SHAPE
+    assert msa(kb=0) == SHAPE
+    assert msa(idx_ld=16 * 128 - 1) == SHAPE
+    assert msa(G=4) == UNSUP                       # 16 heads per group: no MFMA scorer shape
+    assert msa(wsb=need_m - 1) == WS
+    assert msa(B=0) == OK
