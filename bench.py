@@ -153,7 +153,21 @@ def main():
     t = base["t"]
     is_bucket = wl.kind == "bucket"
     is_hi = wl.kind == "hi"
-    if is_hi:
+    is_blocks = wl.kind in ("qsa", "msa")
+    # attention queries: MSA reads one set per (query, group), each group's query heads forming one attention query
+    G_att = wl.groups if wl.kind == "msa" else 1
+    B_att, H_att = wl.B * G_att, wl.H // G_att
+    t_attq = t.repeat_interleave(G_att) if G_att > 1 else t
+    if wl.kind == "qsa":
+        pooled = [sa.sa_qsa_pool(c["k_idx"], wl.block) for c in copies]
+        idx_ld = wl.k_blocks * wl.block + wl.block - 1
+        blk_ws = torch.empty(lib.sa_qsa_select_workspace(wl.L, wl.B, wl.H_I, wl.d_I, wl.block, wl.k_blocks),
+                             dtype=torch.uint8, device=dev)
+    elif wl.kind == "msa":
+        idx_ld = wl.k_blocks * wl.block
+        blk_ws = torch.empty(lib.sa_msa_select_workspace(wl.L, wl.B, wl.groups, wl.block, wl.k_blocks),
+                             dtype=torch.uint8, device=dev)
+    elif is_hi:
         build_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         build_ev[0].record()
         hi_means = [sa.sa_hi_build(c["k_idx"], wl.sub_block) for c in copies]
@@ -182,11 +196,11 @@ def main():
         sel_ws = torch.empty(sa.sa_select_topk_workspace(wl.L, wl.B, wl.H_I, wl.d_I, qd, qd, wl.k_sparse),
                              dtype=torch.uint8, device=dev)
     max_rows = wl.n_sink + wl.n_window + idx_ld
-    attn_ws_bytes = sa.sa_sparse_attn_workspace(wl.B, wl.H, wl.d_qk, wl.d_v, max_rows, sa.api._dtype(base["q"]))
+    attn_ws_bytes = sa.sa_sparse_attn_workspace(B_att, H_att, wl.d_qk, wl.d_v, max_rows, sa.api._dtype(base["q"]))
     attn_ws = torch.empty(max(attn_ws_bytes, 256), dtype=torch.uint8, device=dev)
-    idx = torch.empty((wl.B, idx_ld), dtype=torch.int32, device=dev)
-    n_sel = torch.empty((wl.B,), dtype=torch.int32, device=dev)
-    out = torch.empty((wl.B, wl.H, wl.d_v), dtype=base["q"].dtype, device=dev)
+    idx = torch.empty((B_att, idx_ld), dtype=torch.int32, device=dev)
+    n_sel = torch.empty((B_att,), dtype=torch.int32, device=dev)
+    out = torch.empty((B_att, H_att, wl.d_v), dtype=base["q"].dtype, device=dev)
 
     def select(i):
         c = copies[i % n_copies]
@@ -197,6 +211,12 @@ def main():
                                       t.data_ptr(), wl.top_b, wl.n_sink, wl.n_window, idx.data_ptr(), cap,
                                       n_sel.data_ptr(), None, bws.data_ptr(), bws.numel(), stream.cuda_stream)
             sa.api._lib.check("sa_bucket_select", st)
+        elif wl.kind == "qsa":
+            sa.sa_qsa_select(c["q_idx"], c["w"], pooled[i % n_copies], wl.L, wl.block, wl.k_blocks, t=t, ws=blk_ws,
+                             out=(idx, n_sel))
+        elif wl.kind == "msa":
+            sa.sa_msa_select(c["q_idx"], c["w"], c["k_idx"], wl.groups, wl.block, wl.k_blocks, t=t, ws=blk_ws,
+                             out=(idx, n_sel))
         elif is_hi:
             sa.sa_hi_select(c["q_idx"], c["w"], c["k_idx"], hi_means[i % n_copies], wl.sub_block, wl.page_len,
                             wl.n_pages_keep, wl.k_sparse, wl.n_sink, wl.n_window, t=t, ws=hi_ws, out=(idx, n_sel))
@@ -206,8 +226,9 @@ def main():
 
     def attend(i):
         c = copies[i % n_copies]
-        sa.sa_sparse_attn(c["q"], c["kv"], idx, n_sel, wl.n_sink, wl.n_window, wl.softmax_scale, t=t, d_v=wl.d_v,
-                          ws=attn_ws, out=out)
+        q_att = c["q"].view(B_att, H_att, wl.d_qk) if G_att > 1 else c["q"]
+        sa.sa_sparse_attn(q_att, c["kv"], idx, n_sel, wl.n_sink, wl.n_window, wl.softmax_scale, t=t_attq,
+                          d_v=wl.d_v, ws=attn_ws, out=out)
 
     # ---------------- warmup + timed steps ------------------------------------------------------------------------
     for i in range(args.warmup):
@@ -254,15 +275,15 @@ def main():
 
     nsel = n_sel.cpu().tolist()
     rows_total = 0
-    for b, tb in enumerate(wl.t_positions()):
+    for b, tb in enumerate([tt for tt in wl.t_positions() for _ in range(G_att)]):
         ns = min(wl.n_sink, tb + 1)
         w0 = max(ns, tb - wl.n_window + 1)
         rows_total += ns + max(0, tb + 1 - w0) + max(0, nsel[b])
     width = max(wl.d_qk, wl.d_v)
-    a_bytes = perf.attn_bytes(rows_total, wl.B, wl.H, wl.d_qk, wl.d_v, width, wl.attn_dtype)
-    a_flops = perf.attn_flops(rows_total, wl.H, wl.d_qk, wl.d_v)
+    a_bytes = perf.attn_bytes(rows_total, B_att, H_att, wl.d_qk, wl.d_v, width, wl.attn_dtype)
+    a_flops = perf.attn_flops(rows_total, H_att, wl.d_qk, wl.d_v)
     # which kernels serve the workload (the same conditions the library applies)
-    attn_mfma = wl.attn_dtype == "bf16" and wl.d_qk == 576 and wl.d_v in (512, 576) and wl.H % 64 == 0
+    attn_mfma = wl.attn_dtype == "bf16" and wl.d_qk == 576 and wl.d_v in (512, 576) and H_att % 64 == 0
     idx_mfma = wl.idx_dtype in ("bf16", "e4m3") and wl.d_I == 128 and wl.H_I in (32, 64)
     t_att_k = att_kernels[0] * 1e-3  # the gather kernel (a split combine, if any, follows it)
     att_name = ("k_attn_mfma" if attn_mfma else "k_attn_generic")
@@ -289,6 +310,26 @@ def main():
     elif is_hi:
         sel_roof, keys_per_s, hi_info = hi_roofline(sa, wl, copies[0], hi_means[0], t, sel_kernels, t_sel)
         t_sel_k = sel_roof["launch_ms"] * 1e-3
+    elif is_blocks:
+        # scored (query, key) pairs: QSA scores each query's complete micro-blocks' pooled keys, MSA every
+        # position before each query's local block (all indexer heads over the groups)
+        ts_ = wl.t_positions()
+        if wl.kind == "qsa":
+            pairs = sum((tb + 1) // wl.block for tb in ts_)
+        else:
+            pairs = sum((tb // wl.block) * wl.block for tb in ts_)
+        i_flops = perf.indexer_flops(pairs, wl.H_I, wl.d_I)
+        peak = perf.PEAK_TFLOPS["bf16"]
+        t_sel_k = max(sel_kernels) * 1e-3
+        tf = i_flops / t_sel_k / 1e12
+        sel_roof = {"kernel": "scorer (the select call's longest kernel)", "bound": "mfma", "achieved": round(tf, 1),
+                    "peak": peak, "unit": "TFLOP/s", "frac": round(tf / peak, 4), "traffic": None,
+                    "algorithmic_flops_per_launch": i_flops, "launch_ms": round(t_sel_k * 1e3, 4),
+                    "entry_point": {"name": f"sa_{wl.kind}_select", "ms": round(t_sel * 1e3, 4),
+                                    "mfma_frac": round(i_flops / t_sel / 1e12 / peak, 4),
+                                    "kernel_ms": [round(x, 4) for x in sel_kernels]}}
+        flat_pairs = sum(max(0, tb - wl.n_window - wl.n_sink + 1) for tb in ts_)
+        keys_per_s = flat_pairs / t_sel
     else:
         pairs = sum(max(0, tb - wl.n_window - wl.n_sink + 1) for tb in wl.t_positions())
         i_flops = perf.indexer_flops(pairs, wl.H_I, wl.d_I)
@@ -338,6 +379,8 @@ def main():
     }
     if is_bucket:
         res["bucket_build_ms_per_cache"] = round(build_ms, 3)
+    if is_blocks:
+        res["config"].update(block=wl.block, k_blocks=wl.k_blocks, groups=wl.groups)
     if is_hi:
         res["config"].update(sub_block=wl.sub_block, page_len=wl.page_len, n_pages_keep=wl.n_pages_keep)
         res["hi"] = {**hi_info, "means_build_ms_per_cache": round(build_ms, 3)}
@@ -424,6 +467,12 @@ def measured_traffic(workload: str):
     return {k: v["read_bytes"] + v["write_bytes"] for k, v in rec.get("kernels", {}).items()}
 
 
+STEP_DESC = {"hi": "page scores, top pages, token top-k inside them",
+             "qsa": "pooled-key scores of the complete micro-blocks, top micro-blocks expanded plus the tail",
+             "msa": "per-group token scores, block maxima, top blocks plus the local block",
+             "bucket": "bucket scores, top buckets expanded"}
+
+
 def cpu_baseline(wl, base, min_seconds):
     """The oracle as it stands, timed on the host cores over a bounded sample of the same workload: a seeded
     sample of queries (with the first and the last), cycled until min_seconds have passed. For causal workloads the
@@ -444,6 +493,10 @@ def cpu_baseline(wl, base, min_seconds):
     elif wl.kind == "hi":
         kf = to_f64(base["k_idx"])
         means = O.hi_means(kf, wl.sub_block)       # once per cache, as on the GPU: not timed
+        qi, w = base["q_idx"], base["w"].double().cpu().numpy()
+    elif wl.kind == "qsa":
+        kf = to_f64(base["k_idx"])
+        pooled = O.qsa_pool(kf, wl.block)          # once per cache, as on the GPU: not timed
         qi, w = base["q_idx"], base["w"].double().cpu().numpy()
     else:
         kf = to_f64(base["k_idx"])
@@ -467,7 +520,14 @@ def cpu_baseline(wl, base, min_seconds):
             qi64[b], q64[b] = to_f64(qi[b]), to_f64(q[b])
             prep += time.perf_counter() - t1
         t0 = time.perf_counter()
-        if wl.kind == "hi":
+        if wl.kind == "qsa":
+            R, _, _ = O.qsa_select(qi64[b], w[b], pooled, ts[b], wl.block, wl.k_blocks)
+            O.sparse_attn(q64[b], kv, R, wl.softmax_scale, wl.d_qk, wl.d_v)
+        elif wl.kind == "msa":
+            Hg = wl.H // wl.groups
+            for g, (R, _, _) in enumerate(O.msa_select(qi64[b], w[b], kf, ts[b], wl.groups, wl.block, wl.k_blocks)):
+                O.sparse_attn(q64[b][g * Hg:(g + 1) * Hg], kv, R, wl.softmax_scale, wl.d_qk, wl.d_v)
+        elif wl.kind == "hi":
             O.hi_step(qi64[b], w[b], kf, means, q64[b], kv, ts[b], wl.page_len, wl.sub_block, wl.n_pages_keep,
                       wl.k_sparse, wl.n_sink, wl.n_window, wl.softmax_scale, wl.d_qk, wl.d_v)
         elif wl.kind == "bucket":
@@ -490,7 +550,7 @@ def cpu_baseline(wl, base, min_seconds):
     how = (f"; rate per scored pair ({pairs_done} pairs) divided by the mean {mean_pairs:.0f} pairs per query "
            "(extrapolated by pair count)") if causal else ""
     return {"value": round(value, 3), "unit": "queries/s", "cores": threads, "kind": "oracle",
-            "sample": f"{which}; full per-query path ({'page scores, top pages, token top-k inside them' if wl.kind == 'hi' else 'score all candidates, exact top-k'}, attention), fp64 numpy"
+            "sample": f"{which}; full per-query path ({STEP_DESC.get(wl.kind, 'score all candidates, exact top-k')}, attention), fp64 numpy"
                       f"{how}; {prep:.1f} s input decode not counted",
             "extrapolated": causal, "seconds": round(dt, 2)}
 

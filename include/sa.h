@@ -259,7 +259,7 @@ SA_API int sa_hi_select(const void* q, int q_dtype, const float* w, const void* 
  * scores the largest token score in it, the block holding t_b (the local block) is always read, and the
  * k_blocks - 1 best earlier blocks (ties: lower block) complete the group's blocks.
  *   q, w, k, k_ld, L, B, H, d, t: as sa_index_score; d = 128, H / G in {32, 64}, bf16 or e4m3.
- *   block a multiple of 64.   k_blocks >= 1.
+ *   block a multiple of 64.   k_blocks in [1, 16385].
  *   idx [B * G, idx_ld] int32 out (row b * G + g): ascending positions (chosen blocks whole, then the local block up
  *   to t_b), -1 padding; idx_ld >= k_blocks * block.   n_sel [B * G] int32 out.
  *   ws / ws_bytes: at least sa_msa_select_workspace(L, B, G, block, k_blocks) bytes.

@@ -706,6 +706,11 @@ SA_API int sa_hi_select(const void* q, int q_dtype, const float* w, const void* 
 // ---------------------------------------------------------------------------------------------------------------
 namespace {
 
+// The flat selection over pooled keys: few queries over a short pooled cache (up to 2^16 micro-blocks) take the
+// split-L algorithm, whose first key range already prunes the rest (measured faster there than the streaming
+// bound, which needs many workgroups per query to become tight); otherwise the library's own choice.
+int qsa_algo(int64_t Lp, int32_t B) { return (B < 64 && Lp <= (1 << 16)) ? SA_TOPK_SPLIT_L : SA_TOPK_AUTO; }
+
 struct QsaWs {
   int64_t Lp;        // pooled rows
   int32_t* tq;       // [B] last complete micro-block
@@ -723,7 +728,7 @@ QsaWs carve_qsa(void* ws, int64_t L, int32_t B, int32_t H, int32_t d, int32_t b,
   w.tq = c.take<int32_t>(B);
   w.blk = c.take<int32_t>((size_t)B * kb);
   w.n_blk = c.take<int32_t>(B);
-  w.sel_bytes = sa_select_topk_workspace(w.Lp, B, H, d, SA_BF16, SA_BF16, kb, SA_TOPK_AUTO);
+  w.sel_bytes = sa_select_topk_workspace(w.Lp, B, H, d, SA_BF16, SA_BF16, kb, qsa_algo(w.Lp, B));
   w.sel = c.take<char>(w.sel_bytes);
   w.bytes = align_up(c.off, 256);
   return w;
@@ -731,8 +736,10 @@ QsaWs carve_qsa(void* ws, int64_t L, int32_t B, int32_t H, int32_t d, int32_t b,
 
 struct MsaWs {
   int64_t n_blocks;
+  int64_t keys_ld;
   int32_t* tq;       // [B G] t of each (query, group)
-  RadixWs r;         // block keys and the select's control words
+  uint32_t* keys;    // [B G, keys_ld] block keys (0: not ranked)
+  sa::Cand* gather;  // [B G, n_blocks] the merge's overflow
   int32_t* blk;      // [B G, k_blocks - 1] chosen earlier blocks
   int32_t* n_blk;    // [B G]
   size_t bytes;
@@ -741,15 +748,12 @@ struct MsaWs {
 MsaWs carve_msa(void* ws, int64_t L, int32_t B, int32_t G, int32_t c, int32_t kb) {
   MsaWs w{};
   w.n_blocks = (L + c - 1) / c;
+  w.keys_ld = (w.n_blocks + 63) / 64 * 64;
   const int32_t Bp = B * G;
   Carver cv(ws);
   w.tq = cv.take<int32_t>(Bp);
-  sa::IndexerArgs pa{};
-  pa.B = Bp;
-  pa.L = w.n_blocks;
-  const size_t r_off = align_up(cv.off, 256);
-  w.r = carve_radix(ws ? static_cast<char*>(ws) + r_off : nullptr, pa);
-  cv.off = r_off + w.r.bytes;
+  w.keys = cv.take<uint32_t>((size_t)Bp * w.keys_ld);
+  w.gather = cv.take<sa::Cand>((size_t)Bp * w.n_blocks);
   w.blk = cv.take<int32_t>((size_t)Bp * (kb > 1 ? kb - 1 : 1));
   w.n_blk = cv.take<int32_t>(Bp);
   w.bytes = align_up(cv.off, 256);
@@ -791,7 +795,7 @@ SA_API int sa_qsa_select(const void* q, int q_dtype, const float* w, const void*
   if (e != hipSuccess) return hip_fail(e, "sa_qsa_select (bounds)");
   // the flat selection over the pooled keys, each query bounded by its last complete micro-block
   st = sa_select_topk(q, q_dtype, w, pooled, SA_BF16, d, Lp, B, H, d, w2.tq, k_blocks, 0, 0, w2.blk, k_blocks,
-                      w2.n_blk, w2.sel, w2.sel_bytes, SA_TOPK_AUTO, stream);
+                      w2.n_blk, w2.sel, w2.sel_bytes, qsa_algo(Lp, B), stream);
   if (st) return st;
   e = sa::launch_qsa_expand(w2.blk, k_blocks, w2.n_blk, t, B, L, block, idx, idx_ld, n_sel, s);
   return e == hipSuccess ? SA_OK : hip_fail(e, "sa_qsa_select (expand)");
@@ -811,7 +815,8 @@ SA_API int sa_msa_select(const void* q, int q_dtype, const float* w, const void*
   if (!idx || !n_sel) return fail(SA_ERR_NULL, "idx and n_sel must be non-NULL");
   if (G < 1 || H % G != 0) return fail(SA_ERR_SHAPE, "G must divide H");
   if (block < 64 || block % 64 != 0) return fail(SA_ERR_SHAPE, "block must be a multiple of 64");
-  if (k_blocks < 1) return fail(SA_ERR_SHAPE, "k_blocks must be >= 1");
+  if (k_blocks < 1 || k_blocks - 1 > sa::merge_max_k())
+    return fail(SA_ERR_SHAPE, "k_blocks must be in [1, %d]", sa::merge_max_k() + 1);
   if ((int64_t)B * G > 0x7FFFFFFF / 2) return fail(SA_ERR_SHAPE, "too many (query, group) pairs");
   if ((int64_t)idx_ld < (int64_t)k_blocks * block) return fail(SA_ERR_SHAPE, "idx_ld must hold k_blocks * block");
   const sa::IndexerArgs probe = make_indexer(q, q_dtype, w, k, k_dtype, k_ld, L, B * G, H / G, d, nullptr);
@@ -826,17 +831,25 @@ SA_API int sa_msa_select(const void* q, int q_dtype, const float* w, const void*
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = sa::launch_block_t(t, B, G, L, 1, w2.tq, s);
   if (e != hipSuccess) return hip_fail(e, "sa_msa_select (bounds)");
-  // zero the block keys and the select's control words (one contiguous range), then the block maxima
-  const size_t words = (size_t)((reinterpret_cast<char*>(w2.r.keys + (size_t)Bp * w2.r.p.keys_ld) -
-                                 reinterpret_cast<char*>(w2.r.ctl)) / 4);
-  e = sa::launch_fill_u32(w2.r.ctl, (int64_t)words, 0u, s);
+  // zero the block keys, then the block maxima, then the k_blocks - 1 best earlier blocks of each row (one exact
+  // merge over the row's block keys: the keys are few, one per block)
+  e = sa::launch_fill_u32(w2.keys, (int64_t)Bp * w2.keys_ld, 0u, s);
   if (e != hipSuccess) return hip_fail(e, "sa_msa_select (clear)");
   const sa::IndexerArgs a = make_indexer(q, q_dtype, w, k, k_dtype, k_ld, L, Bp, H / G, d, w2.tq);
-  e = sa::launch_block_max(a, block, w2.r.keys, w2.r.p.keys_ld, s);
+  e = sa::launch_block_max(a, block, w2.keys, w2.keys_ld, s);
   if (e != hipSuccess) return hip_fail(e, "sa_msa_select (block maxima)");
   if (k_blocks > 1) {
-    e = sa::launch_radix_select(Bp, w2.n_blocks, k_blocks - 1, w2.r.p, w2.r.keys, w2.r.ctl, w2.blk, k_blocks - 1,
-                                w2.n_blk, nullptr, nullptr, s);
+    sa::MergeIn in{};
+    in.slot_key = w2.keys;
+    in.slot_ld = w2.keys_ld;
+    in.n_slots = w2.n_blocks;
+    in.slot_pos0 = 0;
+    sa::MergeOut out{};
+    out.final_mode = 1;
+    out.idx = w2.blk;
+    out.idx_ld = k_blocks - 1;
+    out.n_sel = w2.n_blk;
+    e = sa::launch_merge(Bp, k_blocks - 1, in, w2.gather, w2.n_blocks, out, s);
     if (e != hipSuccess) return hip_fail(e, "sa_msa_select (block select)");
   }
   e = sa::launch_msa_expand(k_blocks > 1 ? w2.blk : nullptr, k_blocks > 1 ? k_blocks - 1 : 1,

@@ -16,7 +16,8 @@ from typing import Optional
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str                 # "dsa" (lightning indexer + top-k), "hi" (coarse-to-fine) or "bucket" (Flat search)
+    kind: str                 # "dsa" (lightning indexer + top-k), "hi" (coarse-to-fine), "qsa" / "msa" (block
+                              # indexers) or "bucket" (Flat search)
     L: int                    # cached positions
     B: int                    # queries
     # indexer
@@ -29,6 +30,10 @@ class Workload:
     n_buckets: int = 0
     top_b: int = 0
     key_noise: float = 0.3    # k = centre[assign] + key_noise * N(0, 1)
+    # block-granular indexers: micro-block / block length, blocks kept, indexer head groups (MSA)
+    block: int = 0
+    k_blocks: int = 0
+    groups: int = 1
     # coarse-to-fine index: sub-block mean keys, pages of sub-blocks, pages recalled per query
     sub_block: int = 0
     page_len: int = 0
@@ -86,6 +91,16 @@ WORKLOADS = {
     "flat_prefill_1m": Workload(
         name="flat_prefill_1m", kind="dsa", L=1 << 20, B=2048, H_I=64, d_I=128, idx_dtype="bf16", k_sparse=2048,
         causal_chunk=True),
+    # The 128K decode with QSA micro-blocks: index keys pooled over 4 positions, 512 micro-blocks (the release
+    # budget of 2048 tokens) plus the unfinished micro-block's tail ("long-context attention" lecture, QSA section).
+    "qsa_decode_128k": Workload(
+        name="qsa_decode_128k", kind="qsa", L=131072, B=16, H_I=64, d_I=128, idx_dtype="bf16", block=4,
+        k_blocks=512),
+    # The 128K decode with MSA blocks: two groups of 32 indexer heads (each group's 64 query heads share its
+    # selection), blocks of 128, 16 blocks per group including the local block (the lecture's MSA settings).
+    "msa_decode_128k": Workload(
+        name="msa_decode_128k", kind="msa", L=131072, B=16, H_I=64, d_I=128, idx_dtype="bf16", block=128,
+        k_blocks=16, groups=2),
     # 10M-token decode with fp8 E4M3 index keys and queries, fp32 accumulation; 4 queries.
     "decode_10m_fp8": Workload(
         name="decode_10m_fp8", kind="dsa", L=10_000_000, B=4, H_I=64, d_I=128, idx_dtype="e4m3", k_sparse=2048,

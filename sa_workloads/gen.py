@@ -81,7 +81,7 @@ def make_inputs(wl, device="cpu", seed: int = None, parts: Iterable[str] = ("ind
         "t": torch.tensor(wl.t_positions(), dtype=torch.int32, device=device),
     }
     if "index" in parts:
-        if wl.kind in ("dsa", "hi"):
+        if wl.kind in ("dsa", "hi", "qsa", "msa"):
             out["q_idx"] = normal((wl.B, wl.H_I, wl.d_I), seed, "q_idx", device, wl.idx_dtype)
             if wl.w_dist == "uniform":
                 out["w"] = uniform((wl.B, wl.H_I), seed, "w", device)
