@@ -15,6 +15,8 @@ the definitions. Sources, cited by page title and section:
         sub-section on the HFA kernel: partial attentions merge exactly by log-sum-exp rescaling.
   [LCA]     "long-context attention" lecture (tju-yxq.github.io): sections "Qwen Sparse Attention" (QSA) and "MiniMax
             Sparse Attention" (MSA), and the read-budget table of its budget calculator.
+  [XH]      news page on the open-sourcing of LSA (x-headline.com, 2026-11-04): key facts and the section on its
+            principle (keys clustered into a tree-shaped latent structure; the query scans cluster centres only).
   [LSA-8]   "LSA sparse attention: does it save memory? eight QKV entries" (alphalab.site)
       - section 2: Latent Sparse Attention's four steps (index keys; buckets keeping a representative vector and
         member positions; Flat search over representatives; read the chosen rows plus sink plus window);
@@ -205,6 +207,41 @@ def bucket_select(q, reps32, offsets, members, t: int, top_b: int, n_sink: int, 
     fixed = np.union1d(sink_positions(t, n_sink), window_positions(t, n_window))
     pos = np.setdiff1d(pos, fixed)
     return np.sort(pos), chosen, sc
+
+
+def tree_select(q, levels, reps32, offsets, members, t: int, keeps, top_b: int, n_sink: int, n_window: int):
+    """Tree search over buckets ([LSA-8] section 2, step 3: the Tree variant searches level by level, keeping
+    candidates as it goes; [XH] principle section: hierarchical clustering, the query scans cluster centres only).
+
+    Readings where the pages are silent: the tree is an input like the Flat buckets' assignment (its depth and
+    fan-out come from the caller's clustering); levels[l] = (reps_l [n_l, d] fp32, child_off_l [n_l + 1]): node i of
+    level l has the nodes child_off_l[i] .. child_off_l[i+1]-1 of the next level as children (the last internal
+    level's children are buckets); a node's representative is the mean of the keys of every position under it,
+    rounded once to fp32 (as a bucket's); at level l the query keeps its keeps[l] best candidate nodes that have
+    children (q . rep in fp32, ties to the lower id), and their children are the next level's candidates; at the
+    bucket level the top_b best non-empty candidate buckets expand as in the Flat search.
+    Returns (ascending sparse positions, chosen bucket ids in (score desc, id asc) order, per-level kept ids)."""
+    cand = np.arange(np.asarray(levels[0][0]).shape[0], dtype=np.int64)
+    kept_levels = []
+    for (reps_l, child_off_l), keep in zip(levels, keeps):
+        child_off_l = np.asarray(child_off_l, dtype=np.int64)
+        sc = bucket_scores_f32(q, reps_l).astype(np.float64)
+        ids = cand[np.diff(child_off_l)[cand] > 0]
+        kept = np.sort(ids[np.lexsort((ids, -sc[ids]))][:min(keep, ids.size)])
+        kept_levels.append(kept)
+        cand = (np.concatenate([np.arange(child_off_l[c], child_off_l[c + 1]) for c in kept]).astype(np.int64)
+                if kept.size else np.zeros(0, dtype=np.int64))
+    sc = bucket_scores_f32(q, reps32)
+    counts = np.diff(offsets)
+    ids = cand[counts[cand] > 0]
+    s64 = sc.astype(np.float64)[ids]
+    chosen = ids[np.lexsort((ids, -s64))][:min(top_b, ids.size)]
+    pos = (np.concatenate([members[offsets[c]:offsets[c + 1]] for c in chosen]) if chosen.size
+           else np.zeros(0, dtype=np.int64))
+    pos = pos[pos <= t]
+    fixed = np.union1d(sink_positions(t, n_sink), window_positions(t, n_window))
+    pos = np.setdiff1d(pos, fixed)
+    return np.sort(pos), chosen, kept_levels
 
 
 # ----------------------------------------------------------------------------------------------------------------
