@@ -3,7 +3,8 @@
  *
  * The path has three steps, each a call below:
  *   score   an indexer scores every cached position           (sa_index_score, inside sa_select_topk)
- *   select  exact top-k plus sink/window positions             (sa_select_topk; sa_bucket_select for buckets;
+ *   select  exact top-k plus sink/window positions             (sa_select_topk; sa_bucket_select and
+ *                                                               sa_bucket_tree_select for buckets;
  *                                                               sa_hi_select for the coarse-to-fine search;
  *                                                               sa_qsa_select / sa_msa_select for blocks)
  *   attend  softmax attention over only the gathered rows      (sa_sparse_attn)
@@ -18,6 +19,8 @@
  *              pooled over micro-blocks, micro-blocks expanded to raw positions, the unfinished micro-block read
  *              directly) and "MiniMax Sparse Attention" (MSA: block max of token scores, per-group top-k blocks, the
  *              local block always kept); the per-mechanism read budgets of its budget table.
+ *   [XH]       news page on the open-sourcing of LSA (x-headline.com, 2026-11-04): key facts and principle section
+ *              (keys clustered into a tree; the query scans cluster centres only).
  *   [LSA-8]    "LSA sparse attention: does it save memory? eight QKV entries" (alphalab.site): section 2 (the four
  *              steps of Latent Sparse Attention: index keys, buckets with a representative and member positions,
  *              Flat search over representatives, read selected rows plus sink plus window); sections 3-4 (the
@@ -197,6 +200,33 @@ SA_API int sa_bucket_select(const void* q, int q_dtype, int32_t B, int32_t d, co
  *   device (different streams, or several host threads) race, and the caller must order them. Nothing in the
  *   array has to start at zero: the kernels write every key they read.
  * ------------------------------------------------------------------------------------------------------------- */
+/* ---------------------------------------------------------------------------------------------------------------
+ * sa_bucket_tree_select -- Tree bucket search ([LSA-8] section 2, step 3: the Tree variant searches level by level,
+ * keeping candidates; [XH] principle section: keys clustered hierarchically, the query scans cluster centres only).
+ * The cluster tree is an input, as the Flat buckets' assignment is. Level l (l = 0 .. n_levels-1, root first) has
+ * level_n[l] nodes; node i of level l has as children the nodes level_child_off[l][i] .. level_child_off[l][i+1]-1
+ * of level l+1 (the buckets for the last level), so siblings are numbered contiguously. A node's representative
+ * level_reps[l][i] (fp32 [level_n[l], d]) is the mean of the keys of every position under it (sa_bucket_build with
+ * each position assigned to its level-l ancestor writes exactly that). For each query: every root node is scored
+ * (q . rep, fp32, as sa_bucket_select scores a bucket, bit-identically), the level_keep[l] best nodes that have
+ * children are kept (ties to the lower id), their children are scored, and so on; at the bucket level the top_b
+ * best non-empty candidate buckets are chosen and expanded exactly as sa_bucket_select does.
+ *   level_reps, level_child_off: HOST arrays of n_levels DEVICE pointers; level_n, level_keep: HOST arrays.
+ *   1 <= n_levels <= 8; 1 <= level_keep[l] <= 16384. Child offsets outside the next level are undefined behaviour.
+ *   q, reps, offsets, members, n_buckets, L, t, top_b, n_sink, n_window, idx, cap, n_sel, buckets_out: as
+ *   sa_bucket_select.
+ *   ws / ws_bytes: at least sa_bucket_tree_select_workspace(B, n_levels, level_n, level_keep, n_buckets) bytes.
+ * ------------------------------------------------------------------------------------------------------------- */
+SA_API size_t sa_bucket_tree_select_workspace(int32_t B, int32_t n_levels, const int32_t* level_n,
+                                              const int32_t* level_keep, int32_t n_buckets);
+SA_API int sa_bucket_tree_select(const void* q, int q_dtype, int32_t B, int32_t d, int32_t n_levels,
+                                 const float* const* level_reps, const int32_t* const* level_child_off,
+                                 const int32_t* level_n, const int32_t* level_keep, const float* reps,
+                                 const int32_t* offsets, const int32_t* members, int32_t n_buckets, int64_t L,
+                                 const int32_t* t, int32_t top_b, int32_t n_sink, int32_t n_window, int32_t* idx,
+                                 int32_t cap, int32_t* n_sel, int32_t* buckets_out, void* ws, size_t ws_bytes,
+                                 void* stream);
+
 SA_API int64_t sa_bucket_select_noalloc_max_keys(void);
 SA_API int sa_bucket_select_noalloc(const void* q, int q_dtype, int32_t B, int32_t d, const float* reps,
                                     const int32_t* offsets, const int32_t* members, int32_t n_buckets, int64_t L,

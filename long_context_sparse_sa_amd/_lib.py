@@ -36,6 +36,9 @@ SIGNATURES = {
     "sa_bucket_build": (INT, [P, INT, I64, I64, I32, P, I32, P, P, P, P, SZ, P]),
     "sa_bucket_select_workspace": (SZ, [I32, I32, I32]),
     "sa_bucket_select": (INT, [P, INT, I32, I32, P, P, P, I32, I64, P, I32, I32, I32, P, I32, P, P, P, SZ, P]),
+    "sa_bucket_tree_select_workspace": (SZ, [I32, I32, P, P, I32]),
+    "sa_bucket_tree_select": (INT, [P, INT, I32, I32, I32, P, P, P, P, P, P, P, I32, I64, P, I32, I32, I32, P, I32, P,
+                                    P, P, SZ, P]),
     "sa_bucket_select_noalloc_max_keys": (I64, []),
     "sa_bucket_select_noalloc": (INT, [P, INT, I32, I32, P, P, P, I32, I64, P, I32, I32, I32, P, I32, P, P, P]),
     "sa_hi_build": (INT, [P, INT, I64, I64, I32, I32, P, P]),

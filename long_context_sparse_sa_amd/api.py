@@ -153,6 +153,36 @@ def sa_bucket_select(q_idx, reps, offsets, members, L: int, top_b: int, n_sink: 
     return (idx, n_sel, buckets) if return_buckets else (idx, n_sel)
 
 
+def sa_bucket_tree_select(q_idx, levels, reps, offsets, members, L: int, top_b: int, n_sink: int = 0,
+                          n_window: int = 0, t=None, cap: int = 8192, return_buckets=False, ws=None, out=None,
+                          stream=None):
+    """Tree search over a cluster tree. levels: list, root first, of (reps_l [n_l, d] fp32, child_off_l [n_l + 1]
+    int32, keep_l). Returns (idx [B, cap], n_sel [B][, buckets [B, top_b]]) as sa_bucket_select."""
+    import ctypes
+    _need_cuda(q_idx, reps, offsets, members, t, *[x for lv in levels for x in lv[:2]])
+    B, d = q_idx.shape
+    nl = len(levels)
+    lib = _lib.load()
+    rp = (ctypes.c_void_p * nl)(*[lv[0].data_ptr() for lv in levels])
+    cp = (ctypes.c_void_p * nl)(*[lv[1].data_ptr() for lv in levels])
+    ln = (ctypes.c_int32 * nl)(*[int(lv[0].shape[0]) for lv in levels])
+    lk = (ctypes.c_int32 * nl)(*[int(lv[2]) for lv in levels])
+    n_buckets = reps.shape[0]
+    nbytes = lib.sa_bucket_tree_select_workspace(B, nl, ln, lk, n_buckets)
+    ws = _workspace(nbytes, q_idx.device, ws)
+    if out is None:
+        idx = torch.empty((B, cap), dtype=torch.int32, device=q_idx.device)
+        n_sel = torch.empty((B,), dtype=torch.int32, device=q_idx.device)
+    else:
+        idx, n_sel = out
+    buckets = torch.empty((B, top_b), dtype=torch.int32, device=q_idx.device) if return_buckets else None
+    st = lib.sa_bucket_tree_select(_ptr(q_idx), _dtype(q_idx), B, d, nl, rp, cp, ln, lk, _ptr(reps), _ptr(offsets),
+                                   _ptr(members), n_buckets, L, _ptr(t), top_b, n_sink, n_window, _ptr(idx),
+                                   idx.stride(0), _ptr(n_sel), _ptr(buckets), _ptr(ws), nbytes, _stream(stream))
+    _lib.check("sa_bucket_tree_select", st)
+    return (idx, n_sel, buckets) if return_buckets else (idx, n_sel)
+
+
 def sa_bucket_select_noalloc(q_idx, reps, offsets, members, L: int, top_b: int, n_sink: int = 0,
                              n_window: int = 0, cap: int = 8192, t=None, return_buckets: bool = False, out=None,
                              stream=None):

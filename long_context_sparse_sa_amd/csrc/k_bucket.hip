@@ -252,6 +252,54 @@ __global__ __launch_bounds__(256) void k_bucket_scores(const void* __restrict__ 
   }
 }
 
+// Tree search, one level down: for query b and its kept node kept[b, i] (i < n_kept[b]), scores every child
+// (the next level's nodes child_off[node] .. child_off[node + 1] - 1) and writes its slot key into keys[b * n_next
+// + child] (0 for a child without members or children); slots of children of unkept nodes keep their (zero) value.
+// Four lanes per child; each lane sums the same dims in the same order as k_bucket_scores (dims 16 c + 4 quarter
+// .. + 3, ascending c, then two lane swaps), so a node's score is bit-identical to the Flat search's.
+template <int QT>
+__global__ __launch_bounds__(256) void k_tree_children(const void* __restrict__ q, int d,
+                                                       const int32_t* __restrict__ kept, int keep_ld,
+                                                       const int32_t* __restrict__ n_kept,
+                                                       const int32_t* __restrict__ child_off,
+                                                       const float* __restrict__ reps,
+                                                       const int32_t* __restrict__ offsets, int n_next,
+                                                       uint32_t* __restrict__ keys) {
+  extern __shared__ __attribute__((aligned(16))) float qrow[];  // [d]
+  const int b = blockIdx.y, i = blockIdx.x;
+  int nk = n_kept[b];
+  nk = nk < 0 ? 0 : (nk > keep_ld ? keep_ld : nk);
+  if (i >= nk) return;
+  const int node = kept[(int64_t)b * keep_ld + i];
+  const int c0 = child_off[node], c1 = child_off[node + 1];
+  for (int x = threadIdx.x; x < d; x += blockDim.x) qrow[x] = load_elem<QT>(q, (int64_t)b * d + x);
+  __syncthreads();
+  const int qtr = threadIdx.x & 3;
+  for (int base = c0; base < c1; base += (int)blockDim.x / 4) {
+    const int child = base + (int)threadIdx.x / 4;
+    const bool in = child < c1;
+    const int cc = in ? child : c0;  // every lane of a quad takes part in the swaps below
+    const float* r = reps + (int64_t)cc * d;
+    float acc = 0.f;
+    if ((d & 3) == 0) {
+      for (int x = 4 * qtr; x < d; x += 16) {
+        const float4 rv = *reinterpret_cast<const float4*>(r + x);
+        const float4 qv = *reinterpret_cast<const float4*>(qrow + x);
+        acc = fmaf(qv.x, rv.x, acc);
+        acc = fmaf(qv.y, rv.y, acc);
+        acc = fmaf(qv.z, rv.z, acc);
+        acc = fmaf(qv.w, rv.w, acc);
+      }
+    } else {
+      for (int x = qtr; x < d; x += 4) acc = fmaf(qrow[x], r[x], acc);
+    }
+    acc += __shfl_xor(acc, 1, kWave);
+    acc += __shfl_xor(acc, 2, kWave);
+    if (qtr == 0 && in)
+      keys[(int64_t)b * n_next + child] = offsets[child + 1] > offsets[child] ? score_key(acc) : 0u;
+  }
+}
+
 // Expansion: the kept positions of a chosen bucket form the sub-range of its (ascending) member list inside
 // [lo, hi) with lo = end of the sink and hi = start of the window (which also excludes positions after t).
 __device__ __forceinline__ int lower_bound(const int32_t* a, int n, int32_t x) {
@@ -656,6 +704,41 @@ hipError_t bucket_scratch(hipStream_t st, uint32_t** out) {
   }
   *out = ptrs[dev];
   return hipSuccess;
+}
+
+hipError_t launch_bucket_scores(const void* q, int q_dtype, int B, int d, const float* reps, const int32_t* offsets,
+                                int nb, uint32_t* keys, hipStream_t st) {
+  const unsigned n_wg = (unsigned)((nb + 63) / 64);  // 64 buckets per workgroup
+  const size_t lds = sizeof(float) * (size_t)B * d;
+  if (q_dtype == 0)
+    SA_LAUNCH(k_bucket_scores<0>, dim3(n_wg), dim3(256), lds, st, q, B, d, reps, offsets, nb, keys);
+  else
+    SA_LAUNCH(k_bucket_scores<1>, dim3(n_wg), dim3(256), lds, st, q, B, d, reps, offsets, nb, keys);
+  return hipGetLastError();
+}
+
+hipError_t launch_tree_children(const void* q, int q_dtype, int B, int d, const int32_t* kept, int keep_ld,
+                                const int32_t* n_kept, const int32_t* child_off, const float* reps,
+                                const int32_t* offsets, int n_next, uint32_t* keys, hipStream_t st) {
+  if (B < 1 || keep_ld < 1) return hipSuccess;
+  const dim3 grid((unsigned)keep_ld, (unsigned)B);
+  const size_t lds = sizeof(float) * (size_t)d;
+  if (q_dtype == 0)
+    SA_LAUNCH(k_tree_children<0>, grid, dim3(256), lds, st, q, d, kept, keep_ld, n_kept, child_off, reps, offsets,
+              n_next, keys);
+  else
+    SA_LAUNCH(k_tree_children<1>, grid, dim3(256), lds, st, q, d, kept, keep_ld, n_kept, child_off, reps, offsets,
+              n_next, keys);
+  return hipGetLastError();
+}
+
+hipError_t launch_bucket_choose(const uint32_t* keys, int B, int nb, int top_b, int32_t* buckets_out,
+                                const int32_t* offsets, const int32_t* members, int64_t L, const int32_t* t,
+                                int n_sink, int n_window, int32_t* idx, int cap, int32_t* n_sel, hipStream_t st) {
+  if (B < 1) return hipSuccess;
+  SA_LAUNCH(k_choose_expand, dim3((unsigned)B), dim3(1024), 0, st, keys, nb, top_b, buckets_out, offsets,
+                     members, L, t, n_sink, n_window, idx, cap, n_sel);
+  return hipGetLastError();
 }
 
 hipError_t launch_bucket_select(const void* q, int q_dtype, int B, int d, const float* reps, const int32_t* offsets,

@@ -925,6 +925,110 @@ SA_API int sa_bucket_select(const void* q, int q_dtype, int32_t B, int32_t d, co
   return e == hipSuccess ? SA_OK : hip_fail(e, "sa_bucket_select");
 }
 
+namespace {
+
+constexpr int kTreeMaxLevels = 8;
+
+struct TreeWs {
+  uint32_t* keys[kTreeMaxLevels + 1];  // slot keys of each level's nodes; the last entry is the bucket level
+  int32_t* kept[kTreeMaxLevels];       // [B, keep_l] the kept node ids (ascending)
+  int32_t* n_kept[kTreeMaxLevels];     // [B]
+  sa::Cand* gather;                    // [B, max n_l] the merge's overflow
+  size_t bytes;
+};
+
+TreeWs carve_tree(void* ws, int32_t B, int32_t n_levels, const int32_t* level_n, const int32_t* level_keep,
+                  int32_t n_buckets) {
+  TreeWs w{};
+  Carver c(ws);
+  int64_t most = 1;
+  for (int l = 0; l < n_levels; ++l) {
+    w.keys[l] = c.take<uint32_t>((size_t)B * level_n[l]);
+    w.kept[l] = c.take<int32_t>((size_t)B * level_keep[l]);
+    w.n_kept[l] = c.take<int32_t>(B);
+    most = level_n[l] > most ? level_n[l] : most;
+  }
+  w.keys[n_levels] = c.take<uint32_t>((size_t)B * n_buckets);
+  w.gather = c.take<sa::Cand>((size_t)B * most);
+  w.bytes = align_up(c.off, 256);
+  return w;
+}
+
+int check_tree(int32_t n_levels, const float* const* level_reps, const int32_t* const* level_child_off,
+               const int32_t* level_n, const int32_t* level_keep) {
+  if (n_levels < 1 || n_levels > kTreeMaxLevels)
+    return fail(SA_ERR_SHAPE, "n_levels must be in [1, %d]", kTreeMaxLevels);
+  if (!level_reps || !level_child_off || !level_n || !level_keep)
+    return fail(SA_ERR_NULL, "the level arrays must be non-NULL");
+  for (int l = 0; l < n_levels; ++l) {
+    if (!level_reps[l] || !level_child_off[l]) return fail(SA_ERR_NULL, "level %d: NULL reps or child offsets", l);
+    if (level_n[l] < 1) return fail(SA_ERR_SHAPE, "level %d has no nodes", l);
+    if (level_keep[l] < 1 || level_keep[l] > sa::merge_max_k())
+      return fail(SA_ERR_SHAPE, "level %d: keep must be in [1, %d]", l, sa::merge_max_k());
+    if (!aligned16(level_reps[l])) return fail(SA_ERR_ALIGN, "level %d: reps must be 16-byte aligned", l);
+  }
+  return SA_OK;
+}
+
+}  // namespace
+
+SA_API size_t sa_bucket_tree_select_workspace(int32_t B, int32_t n_levels, const int32_t* level_n,
+                                              const int32_t* level_keep, int32_t n_buckets) {
+  if (B < 0 || n_levels < 1 || n_levels > kTreeMaxLevels || !level_n || !level_keep || n_buckets < 1) return 0;
+  for (int l = 0; l < n_levels; ++l)
+    if (level_n[l] < 1 || level_keep[l] < 1) return 0;
+  return carve_tree(nullptr, B, n_levels, level_n, level_keep, n_buckets).bytes;
+}
+
+SA_API int sa_bucket_tree_select(const void* q, int q_dtype, int32_t B, int32_t d, int32_t n_levels,
+                                 const float* const* level_reps, const int32_t* const* level_child_off,
+                                 const int32_t* level_n, const int32_t* level_keep, const float* reps,
+                                 const int32_t* offsets, const int32_t* members, int32_t n_buckets, int64_t L,
+                                 const int32_t* t, int32_t top_b, int32_t n_sink, int32_t n_window, int32_t* idx,
+                                 int32_t cap, int32_t* n_sel, int32_t* buckets_out, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  int st = check_bucket_select(q, q_dtype, B, d, reps, offsets, members, n_buckets, L, top_b, n_sink, n_window, idx,
+                               cap, n_sel);
+  if (st) return st;
+  if ((st = check_tree(n_levels, level_reps, level_child_off, level_n, level_keep))) return st;
+  const size_t need = sa_bucket_tree_select_workspace(B, n_levels, level_n, level_keep, n_buckets);
+  if (!ws || ws_bytes < need) return fail(SA_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  if (!aligned16(ws)) return fail(SA_ERR_ALIGN, "workspace must be 16-byte aligned");
+  if (B == 0) return SA_OK;
+  const TreeWs w2 = carve_tree(ws, B, n_levels, level_n, level_keep, n_buckets);
+  hipStream_t s = (hipStream_t)stream;
+  // the root level: every node scored (a node without children is an empty slot)
+  hipError_t e = sa::launch_bucket_scores(q, q_dtype, B, d, level_reps[0], level_child_off[0], level_n[0],
+                                          w2.keys[0], s);
+  if (e != hipSuccess) return hip_fail(e, "sa_bucket_tree_select (root scores)");
+  for (int l = 0; l < n_levels; ++l) {
+    // keep the best nodes of this level (ascending ids), then score their children one level down
+    sa::MergeIn in{};
+    in.slot_key = w2.keys[l];
+    in.slot_ld = level_n[l];
+    in.n_slots = level_n[l];
+    in.slot_pos0 = 0;
+    sa::MergeOut out{};
+    out.final_mode = 1;
+    out.idx = w2.kept[l];
+    out.idx_ld = level_keep[l];
+    out.n_sel = w2.n_kept[l];
+    e = sa::launch_merge(B, level_keep[l], in, w2.gather, level_n[l], out, s);
+    if (e != hipSuccess) return hip_fail(e, "sa_bucket_tree_select (keep)");
+    const bool last = l + 1 == n_levels;
+    const int32_t n_next = last ? n_buckets : level_n[l + 1];
+    e = sa::launch_fill_u32(w2.keys[l + 1], (int64_t)B * n_next, 0u, s);
+    if (e != hipSuccess) return hip_fail(e, "sa_bucket_tree_select (clear)");
+    e = sa::launch_tree_children(q, q_dtype, B, d, w2.kept[l], level_keep[l], w2.n_kept[l], level_child_off[l],
+                                 last ? reps : level_reps[l + 1], last ? offsets : level_child_off[l + 1], n_next,
+                                 w2.keys[l + 1], s);
+    if (e != hipSuccess) return hip_fail(e, "sa_bucket_tree_select (children)");
+  }
+  e = sa::launch_bucket_choose(w2.keys[n_levels], B, n_buckets, top_b, buckets_out, offsets, members, L, t, n_sink,
+                               n_window, idx, cap, n_sel, s);
+  return e == hipSuccess ? SA_OK : hip_fail(e, "sa_bucket_tree_select (choose)");
+}
+
 SA_API int64_t sa_bucket_select_noalloc_max_keys(void) { return sa::bucket_scratch_words(); }
 
 SA_API int sa_bucket_select_noalloc(const void* q, int q_dtype, int32_t B, int32_t d, const float* reps,

@@ -220,6 +220,18 @@ int64_t bucket_scratch_words();
 hipError_t bucket_scratch(hipStream_t stream, uint32_t** out);
 // Workspace of the Flat search: keys [B * n_buckets] (uint32, in a Cand-sized area), n_chosen [B],
 // gather [B * n_buckets], chosen [B * top_b].
+// The Flat search's two steps on their own: slot keys of every bucket (0 for empty ones), then the choice of the
+// top_b non-zero slots and their expansion.
+hipError_t launch_bucket_scores(const void* q, int q_dtype, int B, int d, const float* reps, const int32_t* offsets,
+                                int nb, uint32_t* keys, hipStream_t stream);
+hipError_t launch_bucket_choose(const uint32_t* keys, int B, int nb, int top_b, int32_t* buckets_out,
+                                const int32_t* offsets, const int32_t* members, int64_t L, const int32_t* t,
+                                int n_sink, int n_window, int32_t* idx, int cap, int32_t* n_sel, hipStream_t stream);
+// Tree search one level down: the children of each query's kept nodes get their slot keys in keys [B, n_next]
+// (bit-identical to launch_bucket_scores for the same representative); other slots are left as they are.
+hipError_t launch_tree_children(const void* q, int q_dtype, int B, int d, const int32_t* kept, int keep_ld,
+                                const int32_t* n_kept, const int32_t* child_off, const float* reps,
+                                const int32_t* offsets, int n_next, uint32_t* keys, hipStream_t stream);
 hipError_t launch_bucket_select(const void* q, int q_dtype, int B, int d, const float* reps, const int32_t* offsets,
                                 const int32_t* members, int n_buckets, int64_t L, const int32_t* t, int top_b,
                                 int n_sink, int n_window, int32_t* idx, int cap, int32_t* n_sel,

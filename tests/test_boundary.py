@@ -284,3 +284,33 @@ def test_qsa_msa_validation(lib):
     assert msa(G=4) == UNSUP                       # 16 heads per group: no MFMA scorer shape
     assert msa(wsb=need_m - 1) == WS
     assert msa(B=0) == OK
+
+
+def test_bucket_tree_validation(lib):
+    import ctypes
+    nb, B = 4096, 8
+    ln = (ctypes.c_int32 * 2)(64, 512)
+    lk = (ctypes.c_int32 * 2)(8, 64)
+    need = lib.sa_bucket_tree_select_workspace(B, 2, ln, lk, nb)
+    assert need >= B * (64 + 512 + nb) * 4
+    rp = (ctypes.c_void_p * 2)(A, A)
+    cp = (ctypes.c_void_p * 2)(A, A)
+
+    def tree(**kw):
+        a = dict(q=A, qd=F32, B=B, d=128, nl=2, rp=rp, cp=cp, ln=ln, lk=lk, reps=A, off=A, mem=A, nb=nb, L=1 << 20,
+                 t=None, top_b=32, ns=4, nw=128, idx=A, cap=8192, nsel=A, bo=None, ws=A, wsb=need)
+        a.update(kw)
+        return lib.sa_bucket_tree_select(a["q"], a["qd"], a["B"], a["d"], a["nl"], a["rp"], a["cp"], a["ln"], a["lk"],
+                                         a["reps"], a["off"], a["mem"], a["nb"], a["L"], a["t"], a["top_b"], a["ns"],
+                                         a["nw"], a["idx"], a["cap"], a["nsel"], a["bo"], a["ws"], a["wsb"], None)
+
+    assert tree(nl=0) == SHAPE
+    assert tree(nl=9) == SHAPE
+    assert tree(rp=None) == NULL
+    assert tree(rp=(ctypes.c_void_p * 2)(A, None)) == NULL
+    assert tree(lk=(ctypes.c_int32 * 2)(8, 0)) == SHAPE
+    assert tree(ln=(ctypes.c_int32 * 2)(0, 512)) == SHAPE
+    assert tree(rp=(ctypes.c_void_p * 2)(A, MIS)) == ALIGN
+    assert tree(top_b=0) == SHAPE                  # the Flat search's own checks apply
+    assert tree(wsb=need - 1) == WS
+    assert tree(B=0, wsb=lib.sa_bucket_tree_select_workspace(0, 2, ln, lk, nb)) == OK
