@@ -181,15 +181,32 @@ def main():
         dirs = []
         build_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         build_ev[0].record()
+        is_tree = wl.tree_fan > 0
+        tree_levels = []
         for c in copies:
             dirs.append(sa.sa_bucket_build(c["k_idx"], c["assign"], wl.n_buckets))
         build_ev[1].record()
+        torch.cuda.synchronize()
+        for c in copies:
+            if is_tree:  # one parent level: parent of bucket c = c // fan (siblings numbered contiguously)
+                n_top = (wl.n_buckets + wl.tree_fan - 1) // wl.tree_fan
+                parent = torch.arange(wl.n_buckets, device=dev, dtype=torch.int32) // wl.tree_fan
+                top_reps, _, _ = sa.sa_bucket_build(c["k_idx"], parent[c["assign"].long()], n_top)
+                child_off = torch.clamp(torch.arange(n_top + 1, device=dev, dtype=torch.int32) * wl.tree_fan,
+                                        max=wl.n_buckets).to(torch.int32)
+                tree_levels.append([(top_reps, child_off, wl.tree_keep)])
         torch.cuda.synchronize()
         build_ms = build_ev[0].elapsed_time(build_ev[1]) / len(copies)
         cap = 8192
         idx_ld = cap
         bws = torch.empty(lib.sa_bucket_select_workspace(wl.B, wl.n_buckets, wl.top_b), dtype=torch.uint8,
                           device=dev)
+        if is_tree:
+            import ctypes
+            n_top = tree_levels[0][0][0].shape[0]
+            tree_ws = torch.empty(lib.sa_bucket_tree_select_workspace(
+                wl.B, 1, (ctypes.c_int32 * 1)(n_top), (ctypes.c_int32 * 1)(wl.tree_keep), wl.n_buckets),
+                dtype=torch.uint8, device=dev)
     else:
         idx_ld = wl.k_sparse
         qd = sa.api._dtype(base["q_idx"])
@@ -204,7 +221,11 @@ def main():
 
     def select(i):
         c = copies[i % n_copies]
-        if is_bucket:
+        if is_bucket and is_tree:
+            reps, offsets, members = dirs[i % n_copies]
+            sa.sa_bucket_tree_select(c["q_idx"], tree_levels[i % n_copies], reps, offsets, members, wl.L, wl.top_b,
+                                     wl.n_sink, wl.n_window, t=t, cap=cap, ws=tree_ws, out=(idx, n_sel))
+        elif is_bucket:
             reps, offsets, members = dirs[i % n_copies]
             st = lib.sa_bucket_select(c["q_idx"].data_ptr(), sa.api._dtype(c["q_idx"]), wl.B, wl.d_I,
                                       reps.data_ptr(), offsets.data_ptr(), members.data_ptr(), wl.n_buckets, wl.L,
@@ -295,7 +316,22 @@ def main():
                  "entry_point": {"name": "sa_sparse_attn", "ms": round(t_att * 1e3, 4),
                                  "hbm_frac": round(a_bytes / t_att / 1e9 / perf.PEAK_HBM_GBPS, 4),
                                  "kernel_ms": [round(x, 4) for x in att_kernels]}}
-    if is_bucket:
+    if is_bucket and is_tree:
+        # representatives read: every root node once (shared by the queries), and each query's kept nodes'
+        # children; the longest kernel of the call is reported
+        n_top = tree_levels[0][0][0].shape[0]
+        rep_bytes = (n_top + wl.B * wl.tree_keep * wl.tree_fan) * wl.d_I * 4
+        n_keys = wl.B * (n_top + wl.tree_keep * wl.tree_fan)
+        t_sel_k = max(sel_kernels) * 1e-3
+        sel_roof = {"kernel": "the select call's longest kernel", "bound": "hbm",
+                    "achieved": round(rep_bytes / t_sel_k / 1e9, 1), "peak": perf.PEAK_HBM_GBPS, "unit": "GB/s",
+                    "frac": round(rep_bytes / t_sel_k / 1e9 / perf.PEAK_HBM_GBPS, 4), "traffic": None,
+                    "algorithmic_bytes_per_launch": rep_bytes, "launch_ms": round(t_sel_k * 1e3, 4),
+                    "entry_point": {"name": "sa_bucket_tree_select", "ms": round(t_sel * 1e3, 4),
+                                    "hbm_frac": round(rep_bytes / t_sel / 1e9 / perf.PEAK_HBM_GBPS, 4),
+                                    "kernel_ms": [round(x, 4) for x in sel_kernels]}}
+        keys_per_s = n_keys / t_sel
+    elif is_bucket:
         n_keys = wl.B * wl.n_buckets
         rep_bytes = wl.n_buckets * wl.d_I * 4
         t_sel_k = sel_kernels[0] * 1e-3
@@ -379,6 +415,8 @@ def main():
     }
     if is_bucket:
         res["bucket_build_ms_per_cache"] = round(build_ms, 3)
+        if is_tree:
+            res["config"].update(tree_fan=wl.tree_fan, tree_keep=wl.tree_keep)
     if is_blocks:
         res["config"].update(block=wl.block, k_blocks=wl.k_blocks, groups=wl.groups)
     if is_hi:
@@ -471,6 +509,7 @@ STEP_DESC = {"hi": "page scores, top pages, token top-k inside them",
              "qsa": "pooled-key scores of the complete micro-blocks, top micro-blocks expanded plus the tail",
              "msa": "per-group token scores, block maxima, top blocks plus the local block",
              "bucket": "bucket scores, top buckets expanded"}
+STEP_DESC_TREE = "parent-node scores, kept parents' bucket scores, top buckets expanded"
 
 
 def cpu_baseline(wl, base, min_seconds):
@@ -488,8 +527,14 @@ def cpu_baseline(wl, base, min_seconds):
     q = base["q"]
     if wl.kind == "bucket":
         kf = to_f64(base["k_idx"])
-        reps, off, mem = O.bucket_build(kf, base["assign"].cpu().numpy(), wl.n_buckets)
+        assign = base["assign"].cpu().numpy()
+        reps, off, mem = O.bucket_build(kf, assign, wl.n_buckets)
         qi = base["q_idx"]
+        if wl.tree_fan:  # the parent level, built once per cache as on the GPU: not timed
+            import numpy as np
+            n_top = (wl.n_buckets + wl.tree_fan - 1) // wl.tree_fan
+            top_reps, _, _ = O.bucket_build(kf, assign // wl.tree_fan, n_top)
+            levels = [(top_reps, np.minimum(np.arange(n_top + 1) * wl.tree_fan, wl.n_buckets))]
     elif wl.kind == "hi":
         kf = to_f64(base["k_idx"])
         means = O.hi_means(kf, wl.sub_block)       # once per cache, as on the GPU: not timed
@@ -530,6 +575,11 @@ def cpu_baseline(wl, base, min_seconds):
         elif wl.kind == "hi":
             O.hi_step(qi64[b], w[b], kf, means, q64[b], kv, ts[b], wl.page_len, wl.sub_block, wl.n_pages_keep,
                       wl.k_sparse, wl.n_sink, wl.n_window, wl.softmax_scale, wl.d_qk, wl.d_v)
+        elif wl.kind == "bucket" and wl.tree_fan:
+            R0, _, _ = O.tree_select(qi64[b], levels, reps, off, mem, ts[b], [wl.tree_keep], wl.top_b, wl.n_sink,
+                                     wl.n_window)
+            O.sparse_attn(q64[b], kv, O.read_set(ts[b], wl.n_sink, wl.n_window, R0), wl.softmax_scale, wl.d_qk,
+                          wl.d_v)
         elif wl.kind == "bucket":
             O.bucket_step(qi64[b], reps, off, mem, q64[b], kv, ts[b], wl.top_b, wl.n_sink, wl.n_window,
                           wl.softmax_scale, wl.d_qk, wl.d_v)
@@ -550,7 +600,7 @@ def cpu_baseline(wl, base, min_seconds):
     how = (f"; rate per scored pair ({pairs_done} pairs) divided by the mean {mean_pairs:.0f} pairs per query "
            "(extrapolated by pair count)") if causal else ""
     return {"value": round(value, 3), "unit": "queries/s", "cores": threads, "kind": "oracle",
-            "sample": f"{which}; full per-query path ({STEP_DESC.get(wl.kind, 'score all candidates, exact top-k')}, attention), fp64 numpy"
+            "sample": f"{which}; full per-query path ({STEP_DESC_TREE if wl.tree_fan else STEP_DESC.get(wl.kind, 'score all candidates, exact top-k')}, attention), fp64 numpy"
                       f"{how}; {prep:.1f} s input decode not counted",
             "extrapolated": causal, "seconds": round(dt, 2)}
 

@@ -29,6 +29,8 @@ class Workload:
     # bucket directory
     n_buckets: int = 0
     top_b: int = 0
+    tree_fan: int = 0         # Tree search: buckets per parent node (one parent level), parents kept per query
+    tree_keep: int = 0
     key_noise: float = 0.3    # k = centre[assign] + key_noise * N(0, 1)
     # block-granular indexers: micro-block / block length, blocks kept, indexer head groups (MSA)
     block: int = 0
@@ -81,6 +83,12 @@ WORKLOADS = {
     "lsa_flat_1m": Workload(
         name="lsa_flat_1m", kind="bucket", L=1 << 20, B=8, d_I=128, idx_dtype="bf16", n_buckets=16384, top_b=32,
         n_sink=4, n_window=128),
+    # The Tree search over the same directory: one parent level of 128 nodes over 128 buckets each; each query keeps
+    # its 8 best parents and chooses its top 32 buckets among their 1024 children (fan-out and beam are readings:
+    # the pages give neither).
+    "lsa_tree_1m": Workload(
+        name="lsa_tree_1m", kind="bucket", L=1 << 20, B=8, d_I=128, idx_dtype="bf16", n_buckets=16384, top_b=32,
+        n_sink=4, n_window=128, tree_fan=128, tree_keep=8),
     # A prefill chunk of 2048 queries at the end of a causal 1M sequence (the query length of the LongCat
     # deep-dive's HI-versus-flat table), selected by the coarse-to-fine index: sub-blocks of 8, pages of 128, the
     # best 1024 pages recalled per query (the settings of that section), then the top 2048 inside them.
