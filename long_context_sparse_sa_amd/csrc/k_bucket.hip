@@ -49,87 +49,210 @@ __global__ void k_fill_i32(int32_t* p, int64_t n, int32_t v) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
 }
 
-__global__ void k_count(const int32_t* __restrict__ assign, int64_t L, int32_t* __restrict__ counts) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < L; i += (int64_t)gridDim.x * blockDim.x)
-    atomicAdd(&counts[assign[i]], 1);
-}
+// Single-workgroup exclusive scan: offsets[c] = sum_{c' < c} counts[c'], offsets[nb] = total. Each thread takes a
+// contiguous run of counts (up to kRun of them held in registers, all loaded before any is used), the run sums are
+// scanned in LDS, and each thread writes its run's offsets from the registers.
+constexpr int kRun = 32;
 
-// Single-workgroup exclusive scan: offsets[c] = sum_{c' < c} counts[c'], offsets[nb] = total.
 __global__ __launch_bounds__(1024) void k_offsets(const int32_t* __restrict__ counts, int nb, int32_t* __restrict__ offsets) {
   __shared__ int32_t part[1024];
   const int tid = threadIdx.x;
   const int per = (nb + 1023) / 1024;
   const int lo = tid * per, hi = lo + per < nb ? lo + per : nb;
+  int32_t v[kRun];
   int32_t s = 0;
-  for (int i = lo; i < hi; ++i) s += counts[i];
+  if (per <= kRun) {
+#pragma unroll
+    for (int u = 0; u < kRun; ++u) v[u] = lo + u < hi ? counts[lo + u] : 0;
+#pragma unroll
+    for (int u = 0; u < kRun; ++u) s += v[u];
+  } else {
+    for (int i = lo; i < hi; ++i) s += counts[i];
+  }
   part[tid] = s;
   __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {
-    const int32_t v = tid >= off ? part[tid - off] : 0;
+    const int32_t x = tid >= off ? part[tid - off] : 0;
     __syncthreads();
-    part[tid] += v;
+    part[tid] += x;
     __syncthreads();
   }
   int32_t run = tid > 0 ? part[tid - 1] : 0;
-  for (int i = lo; i < hi; ++i) {
-    offsets[i] = run;
-    run += counts[i];
+  if (per <= kRun) {
+#pragma unroll
+    for (int u = 0; u < kRun; ++u)
+      if (lo + u < hi) {
+        offsets[lo + u] = run;
+        run += v[u];
+      }
+  } else {
+    for (int i = lo; i < hi; ++i) {
+      offsets[i] = run;
+      run += counts[i];
+    }
   }
   if (tid == 1023) offsets[nb] = part[1023];
 }
 
-__global__ void k_chunk_hist(const int32_t* __restrict__ assign, int64_t L, int64_t chunk, int nb,
-                             int32_t* __restrict__ table) {
+// Per-chunk bucket histogram: table[chunk][c] = number of positions of the chunk in bucket c. With nb <= kLdsBuckets
+// the histogram is built with LDS atomics and the row is written whole (no clearing needed); otherwise with global
+// atomics into a row the caller zeroed.
+constexpr int kLdsBuckets = 16384;
+
+template <bool LDS>
+__global__ __launch_bounds__(256) void k_chunk_hist(const int32_t* __restrict__ assign, int64_t L, int64_t chunk, int nb,
+                                                    int32_t* __restrict__ table) {
   const int64_t c = blockIdx.x;
   const int64_t lo = c * chunk, hi = lo + chunk < L ? lo + chunk : L;
-  for (int64_t i = lo + threadIdx.x; i < hi; i += blockDim.x) atomicAdd(&table[c * nb + assign[i]], 1);
-}
-
-// table[chunk][c] <- offsets[c] + sum of the bucket's counts in earlier chunks
-__global__ void k_chunk_scan(const int32_t* __restrict__ offsets, int nb, int64_t n_chunks, int32_t* __restrict__ table) {
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= nb) return;
-  int32_t run = offsets[c];
-  for (int64_t ch = 0; ch < n_chunks; ++ch) {
-    const int32_t v = table[ch * nb + c];
-    table[ch * nb + c] = run;
-    run += v;
+  int32_t* row = table + c * nb;
+  if constexpr (LDS) {
+    __shared__ int32_t hist[kLdsBuckets];
+    for (int i = threadIdx.x; i < nb; i += blockDim.x) hist[i] = 0;
+    __syncthreads();
+    constexpr int kStage = 16;
+    for (int64_t i0 = lo; i0 < hi; i0 += kStage * (int64_t)blockDim.x) {
+      int32_t v[kStage];
+#pragma unroll
+      for (int u = 0; u < kStage; ++u) {
+        const int64_t i = i0 + u * (int64_t)blockDim.x + threadIdx.x;
+        v[u] = i < hi ? assign[i] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < kStage; ++u)
+        if (v[u] >= 0) atomicAdd(&hist[v[u]], 1);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < nb; i += blockDim.x) row[i] = hist[i];
+  } else {
+    for (int64_t i = lo + threadIdx.x; i < hi; i += blockDim.x) atomicAdd(&row[assign[i]], 1);
   }
 }
 
-// Stable scatter: one wave walks its chunk in ascending position order, 64 positions at a time. A lane's slot in
-// its bucket is the bucket's running start plus the number of lower lanes with the same bucket.
-__global__ __launch_bounds__(64) void k_scatter(const int32_t* __restrict__ assign, int64_t L, int64_t chunk, int nb,
-                                                int32_t* __restrict__ table, int32_t* __restrict__ members) {
+// Column scan, one thread per bucket: table[chunk][c] <- the bucket's count in earlier chunks (exclusive), and
+// counts[c] <- its total. Sixteen rows are loaded before any is used, so that the loads overlap.
+__global__ __launch_bounds__(256) void k_chunk_scan(int nb, int64_t n_chunks, int32_t* __restrict__ table,
+                                                    int32_t* __restrict__ counts) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= nb) return;
+  constexpr int kBatch = 16;
+  int32_t run = 0;
+  for (int64_t ch0 = 0; ch0 < n_chunks; ch0 += kBatch) {
+    int32_t v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) v[u] = ch0 + u < n_chunks ? table[(ch0 + u) * nb + c] : 0;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (ch0 + u < n_chunks) table[(ch0 + u) * nb + c] = run;
+      run += v[u];
+    }
+  }
+  counts[c] = run;
+}
+
+constexpr int kScatterStage = 4096;  // positions of a chunk staged in LDS (the LDS path requires chunk <= this)
+
+// Stable scatter: one workgroup per chunk. With nb <= kLdsBuckets the chunk's cursors (offsets[c] + the bucket's
+// count in earlier chunks) sit in LDS; one wave then walks the chunk in ascending position order, 64 positions at a
+// time: a lane's slot in its bucket is the cursor plus the number of lower lanes with the same bucket, and the
+// highest such lane advances the cursor. Otherwise the cursors stay in the table row (global memory).
+template <bool LDS>
+__global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ assign, int64_t L, int64_t chunk, int nb,
+                                                 const int32_t* __restrict__ offsets, int32_t* __restrict__ table,
+                                                 int32_t* __restrict__ members) {
   const int64_t c = blockIdx.x;
-  const int lane = threadIdx.x;
   const int64_t lo = c * chunk, hi = lo + chunk < L ? lo + chunk : L;
   int32_t* row = table + c * nb;
+  __shared__ int32_t cur_lds[LDS ? kLdsBuckets : 1];
+  __shared__ int32_t asg[LDS ? kScatterStage : 1];  // the chunk's assignments, so the ordered walk never waits on HBM
+  __shared__ int32_t tag[LDS ? kLdsBuckets : 1];    // per-bucket scratch of the duplicate test below
+  if constexpr (LDS) {
+    // staged sixteen entries per thread at a time: every load of a batch is in flight before any is stored
+    constexpr int kStage = 16;
+    const int n_pos = (int)(hi - lo);
+    for (int i0 = 0; i0 < nb; i0 += kStage * (int)blockDim.x) {
+      int32_t v[kStage];
+#pragma unroll
+      for (int u = 0; u < kStage; ++u) {
+        const int i = i0 + u * (int)blockDim.x + (int)threadIdx.x;
+        const int ic = i < nb ? i : nb - 1;
+        v[u] = offsets[ic] + row[ic];
+      }
+#pragma unroll
+      for (int u = 0; u < kStage; ++u) {
+        const int i = i0 + u * (int)blockDim.x + (int)threadIdx.x;
+        if (i < nb) cur_lds[i] = v[u];
+      }
+    }
+    for (int i0 = 0; i0 < n_pos; i0 += kStage * (int)blockDim.x) {
+      int32_t v[kStage];
+#pragma unroll
+      for (int u = 0; u < kStage; ++u) {
+        const int i = i0 + u * (int)blockDim.x + (int)threadIdx.x;
+        v[u] = assign[lo + (i < n_pos ? i : n_pos - 1)];
+      }
+#pragma unroll
+      for (int u = 0; u < kStage; ++u) {
+        const int i = i0 + u * (int)blockDim.x + (int)threadIdx.x;
+        if (i < n_pos) asg[i] = v[u];
+      }
+    }
+    __syncthreads();
+  } else {
+    for (int i = threadIdx.x; i < nb; i += blockDim.x) row[i] += offsets[i];
+    __syncthreads();
+  }
+  if (threadIdx.x >= kWave) return;
+  const int lane = threadIdx.x;
+  const uint64_t below = (1ull << lane) - 1ull;
+  // (the cursors are addressed through the arrays themselves, not a pointer that may point to either memory: a
+  // generic pointer makes every cursor access a flat instruction that waits for the member stores)
   for (int64_t base = lo; base < hi; base += kWave) {
     const int64_t s = base + lane;
     const bool valid = s < hi;
-    const int a = valid ? assign[s] : -1;
+    const int a = valid ? (LDS ? asg[s - lo] : assign[s]) : -1;
+    // rank among the lanes of this step with the same bucket: a lane whose bucket no other lane holds has rank 0
+    // and is the last. Duplicates are found by each lane writing its id to its bucket's tag and reading it back
+    // (one writer per bucket wins); only the buckets of the lanes that lost are then matched lane by lane.
     int rank = 0;
     bool last = valid;
-    for (int j = 0; j < kWave; ++j) {
-      const int other = __shfl(a, j, kWave);
-      if (other == a) {
-        if (j < lane) ++rank;
-        if (j > lane) last = false;
+    uint64_t dup;
+    if constexpr (LDS) {
+      if (valid) tag[a] = lane;
+      __builtin_amdgcn_wave_barrier();
+      const int w = valid ? tag[a] : lane;
+      dup = ballot(w != lane);
+    } else {
+      dup = ballot(valid);  // without the LDS tags every bucket of the step is matched
+    }
+    while (dup) {
+      const int leader = __builtin_ctzll(dup);
+      const int v = __builtin_amdgcn_readlane(a, leader);
+      const bool same = valid && a == v;
+      const uint64_t m = ballot(same);
+      if (same) {
+        rank = __popcll(m & below);
+        last = (m >> lane) == 1ull;
       }
+      dup &= ~m;
     }
     int32_t start = 0;
-    if (valid) start = row[a];
+    if (valid) start = LDS ? cur_lds[a] : row[a];
     if (valid) members[start + rank] = (int32_t)s;
-    wait_vmem();
+    if constexpr (!LDS) wait_vmem();
     __builtin_amdgcn_wave_barrier();
-    if (last) row[a] = start + rank + 1;
-    wait_vmem();
+    if (last) {
+      if constexpr (LDS) cur_lds[a] = start + rank + 1;
+      else row[a] = start + rank + 1;
+    }
+    if constexpr (!LDS) wait_vmem();
     __builtin_amdgcn_wave_barrier();
   }
 }
 
-// One wave per bucket: rep = (float)(sum of member keys in fp64 / count).
+// One wave per bucket: rep = (float)(sum of member keys in fp64 / count). Each lane owns two dims of a 128-dim
+// slice (one 4-byte load per bf16 member row, two for fp32). The member positions come 64 at a time in one load
+// and are broadcast with readlane, so sixteen member rows are requested before any is summed, none waiting on an
+// index load.
 template <int KT>
 __global__ __launch_bounds__(256) void k_reps(const void* __restrict__ k, int64_t k_ld, int d,
                                               const int32_t* __restrict__ offsets, const int32_t* __restrict__ members,
@@ -138,12 +261,45 @@ __global__ __launch_bounds__(256) void k_reps(const void* __restrict__ k, int64_
   const int lane = lane_id();
   if (bucket >= nb) return;
   const int lo = offsets[bucket], hi = offsets[bucket + 1];
-  for (int x0 = 0; x0 < d; x0 += kWave) {
-    const int x = x0 + lane;
-    double sum = 0.0;
-    if (x < d)
-      for (int i = lo; i < hi; ++i) sum += (double)load_elem<KT>(k, (int64_t)members[i] * k_ld + x);
-    if (x < d) reps[(int64_t)bucket * d + x] = hi > lo ? (float)(sum / (double)(hi - lo)) : 0.f;
+  constexpr int kBatch = 16;
+  for (int x0 = 0; x0 < d; x0 += 2 * kWave) {
+    const int x = x0 + 2 * lane;
+    const bool has0 = x < d, has1 = x + 1 < d;
+    double s0 = 0.0, s1 = 0.0;
+    for (int i0 = lo; i0 < hi; i0 += kWave) {
+      const int nm = hi - i0 < kWave ? hi - i0 : kWave;
+      const int mi = members[i0 + (lane < nm ? lane : 0)];
+      for (int u0 = 0; u0 < nm; u0 += kBatch) {
+        float a0[kBatch], a1[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int m = __builtin_amdgcn_readlane(mi, u0 + u < nm ? u0 + u : 0);  // clamped; not summed
+          const int64_t e = (int64_t)m * k_ld + (has0 ? x : 0);
+          if constexpr (KT == 1) {
+            if (has1 && ((k_ld | x) & 1) == 0) {  // both bf16 of the pair in one aligned 4-byte load
+              const uint32_t pr = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(k) + e);
+              a0[u] = __uint_as_float(pr << 16);
+              a1[u] = __uint_as_float(pr & 0xFFFF0000u);
+            } else {
+              a0[u] = load_elem<KT>(k, e);
+              a1[u] = has1 ? load_elem<KT>(k, e + 1) : 0.f;
+            }
+          } else {
+            a0[u] = load_elem<KT>(k, e);
+            a1[u] = has1 ? load_elem<KT>(k, e + 1) : 0.f;
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+          if (u0 + u < nm) {
+            s0 += (double)a0[u];
+            s1 += (double)a1[u];
+          }
+      }
+    }
+    const double n = (double)(hi - lo);
+    if (has0) reps[(int64_t)bucket * d + x] = hi > lo ? (float)(s0 / n) : 0.f;
+    if (has1) reps[(int64_t)bucket * d + x + 1] = hi > lo ? (float)(s1 / n) : 0.f;
   }
 }
 
@@ -643,14 +799,26 @@ hipError_t launch_bucket_build(const void* k, int k_dtype, int64_t k_ld, int64_t
                                int nb, float* reps, int32_t* offsets, int32_t* members, int32_t* counts,
                                int32_t* table, const BucketBuildPlan& p, hipStream_t st) {
   const int64_t tbl = p.n_chunks * (int64_t)nb;
-  SA_LAUNCH(k_fill_i32, dim3(256), dim3(256), 0, st, counts, (int64_t)nb, 0);
-  if (tbl > 0) SA_LAUNCH(k_fill_i32, dim3(1024), dim3(256), 0, st, table, tbl, 0);
-  if (L > 0) SA_LAUNCH(k_count, dim3(1024), dim3(256), 0, st, assign, L, counts);
+  const bool lds = nb <= kLdsBuckets && p.chunk <= kScatterStage;
+  if (L > 0) {
+    if (lds) {
+      SA_LAUNCH(k_chunk_hist<true>, dim3((unsigned)p.n_chunks), dim3(256), 0, st, assign, L, p.chunk, nb, table);
+    } else {
+      SA_LAUNCH(k_fill_i32, dim3(1024), dim3(256), 0, st, table, tbl, 0);
+      SA_LAUNCH(k_chunk_hist<false>, dim3((unsigned)p.n_chunks), dim3(256), 0, st, assign, L, p.chunk, nb, table);
+    }
+    SA_LAUNCH(k_chunk_scan, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, st, nb, p.n_chunks, table, counts);
+  } else {
+    SA_LAUNCH(k_fill_i32, dim3(256), dim3(256), 0, st, counts, (int64_t)nb, 0);
+  }
   SA_LAUNCH(k_offsets, dim3(1), dim3(1024), 0, st, counts, nb, offsets);
   if (L > 0) {
-    SA_LAUNCH(k_chunk_hist, dim3((unsigned)p.n_chunks), dim3(256), 0, st, assign, L, p.chunk, nb, table);
-    SA_LAUNCH(k_chunk_scan, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, st, offsets, nb, p.n_chunks, table);
-    SA_LAUNCH(k_scatter, dim3((unsigned)p.n_chunks), dim3(64), 0, st, assign, L, p.chunk, nb, table, members);
+    if (lds)
+      SA_LAUNCH(k_scatter<true>, dim3((unsigned)p.n_chunks), dim3(256), 0, st, assign, L, p.chunk, nb, offsets, table,
+                members);
+    else
+      SA_LAUNCH(k_scatter<false>, dim3((unsigned)p.n_chunks), dim3(256), 0, st, assign, L, p.chunk, nb, offsets,
+                table, members);
   }
   if (k_dtype == 0)
     SA_LAUNCH(k_reps<0>, dim3((unsigned)((nb + 3) / 4)), dim3(256), 0, st, k, k_ld, d, offsets, members, nb, reps);
