@@ -35,6 +35,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill_chunk_128k")
     ap.add_argument("--L", type=int, default=0, help="override the workload's cache length (positions)")
+    ap.add_argument("--B", type=int, default=0, help="override the workload's number of queries")
     ap.add_argument("--rotate-bytes", type=float, default=1.2e9, help="total bytes of rotated cache copies")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -135,7 +136,8 @@ def main():
         return
     lib = sa.load()
     dev = "cuda"
-    wl = get_workload(args.workload, **({"L": args.L} if args.L else {}))
+    over = {k: v for k, v in (("L", args.L), ("B", args.B)) if v}
+    wl = get_workload(args.workload, **over)
     torch.manual_seed(0)
     copy_gbps = copy_bandwidth_gbps(torch)
 

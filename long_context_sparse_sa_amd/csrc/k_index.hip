@@ -697,15 +697,10 @@ hipError_t launch_stream_t(const IndexerArgs& a, int k, int n_sink, int n_window
   int n_wg = resident / groups;
   n_wg = n_wg < 1 ? 1 : (n_wg > kStreamMaxWgs ? kStreamMaxWgs : n_wg);
   const int64_t range = (int64_t)n_wg * p.run_keys;
-  // statistic: the m-th largest lane maximum of each chunk, m chosen so that about 2k keys of a launch's range
-  // reach the bound (at most 64 lanes; at least k / n_wg so that r = ceil(k / m) chunks can exist)
-  int m = (int)((2 * (int64_t)k + n_wg - 1) / n_wg);
-  m = m < 1 ? 1 : (m > 64 ? 64 : m);
   StreamArgs sa{};
   sa.n_sink = n_sink;
   sa.n_window = n_window;
   sa.k = k;
-  sa.m = m;
   sa.pub = pub;
   sa.pub_ld = p.pub_ld;
   sa.flag0 = p.slots;
@@ -723,6 +718,12 @@ hipError_t launch_stream_t(const IndexerArgs& a, int k, int n_sink, int n_window
   for (int64_t lo = 0; lo < p.end; lo += range) {
     const int64_t hi = lo + range < p.end ? lo + range : p.end;
     const int wgs = (int)((hi - lo + p.run_keys - 1) / p.run_keys);
+    // statistic: the m-th largest lane maximum of each chunk, m chosen from this launch's workgroup count so that
+    // about 2k keys of its range reach the bound (at most 64 lanes; at least k / wgs so that r = ceil(k / m)
+    // chunks can exist)
+    int m = (int)((2 * (int64_t)k + wgs - 1) / wgs);
+    m = m < 1 ? 1 : (m > 64 ? 64 : m);
+    sa.m = m;
     sa.lo = lo;
     sa.hi = hi;
     sa.slot0 = slot0;
