@@ -393,9 +393,9 @@ def main():
                                     "kernel_ms": [round(x, 4) for x in sel_kernels]}}
         keys_per_s = pairs / t_sel
     traffic = measured_traffic(wl.name)
-    if traffic:
-        sel_roof["traffic"] = traffic.get(sel_roof["kernel"])
-        attn_roof["traffic"] = traffic.get(attn_roof["kernel"])
+    if traffic:  # per dispatch of the roofline's kernel (its name up to the first space)
+        sel_roof["traffic"] = traffic.get(sel_roof["kernel"].split(" ")[0])
+        attn_roof["traffic"] = traffic.get(attn_roof["kernel"].split(" ")[0])
     dominant, other = (sel_roof, attn_roof) if t_sel_k >= t_att_k else (attn_roof, sel_roof)
 
     res = {
