@@ -8,7 +8,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libsa.so")
+# SA_LIB_PATH selects another build of the same library (for instance one whose host code carries the address and
+# undefined-behaviour sanitizers); the default is the in-tree build.
+LIB_PATH = os.environ.get("SA_LIB_PATH") or os.path.join(HERE, "libsa.so")
 
 SA_F32, SA_BF16, SA_E4M3 = 0, 1, 2
 SA_TOPK_AUTO, SA_TOPK_SPLIT_L, SA_TOPK_PER_QUERY, SA_TOPK_RADIX, SA_TOPK_RADIX_LEVELS, SA_TOPK_STREAM = 0, 1, 2, 3, 4, 5
