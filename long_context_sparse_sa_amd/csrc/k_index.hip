@@ -304,8 +304,9 @@ __global__ __launch_bounds__(64 * NQ) void k_stream_select(const void* __restric
 // stream_wg_keys / NQ positions, whose keys stay in LDS (the score matrix never leaves the chip). Each query wave then
 //   1. publishes one statistic of its chunk: x = the m-th largest of its 64 per-lane maxima, so that at least m keys
 //      of the chunk are >= x;
-//   2. waits, a bounded number of polls, for the other workgroups of the launch to publish theirs (the grid is
-//      sized to be co-resident, so they normally have; after the last poll it goes on with whatever is published);
+//   2. polls its query's slots, a bounded number of times, until the other workgroups of the launch have published
+//      theirs (the grid is sized to be co-resident, so they normally have; after the last poll it goes on with
+//      whatever is published);
 //   3. takes T = the r-th largest published x with r = ceil(k / m): r chunks hold at least m keys >= T each, so at
 //      least k candidates score >= T and T is a lower bound of the k-th key, whatever subset was seen. The bound of
 //      the earlier launches of the call (thr[b]) is a lower bound too; the larger one is used;
@@ -323,8 +324,6 @@ struct StreamArgs {
   int n_sink, n_window;
   int k, m;              // k of the selection; m of the published statistic (1..64)
   uint32_t* pub;         // [B, pub_ld], zero at the first launch: slots (this launch's workgroup w owns slot slot0 + w)
-                         // and, from word flag0 of the first query row of each group, one flag per workgroup
-  int64_t flag0;
   int64_t pub_ld;
   int slot0;
   uint32_t* thr;         // [B] lower bound carried between launches
@@ -340,6 +339,7 @@ struct StreamArgs {
 
 // The r-th largest (r >= 1) of the values v[j] (j < NV, lanes x registers) of the wave, or 0 when fewer than r are
 // nonzero: the largest x with at least r values >= x, found bit by bit.
+// Branch-free: zero values never count (every candidate threshold c is >= 1).
 template <int NV>
 __device__ __forceinline__ uint32_t wave_rth_largest(const uint32_t (&v)[NV], int r) {
   uint32_t prefix = 0;
@@ -351,22 +351,6 @@ __device__ __forceinline__ uint32_t wave_rth_largest(const uint32_t (&v)[NV], in
     prefix = cnt >= r ? c : prefix;
   }
   return prefix;
-}
-
-// Descending bitonic sort of one value per lane across the wave.
-__device__ __forceinline__ uint32_t wave_sort_desc(uint32_t v, int lane) {
-#pragma unroll
-  for (int size = 2; size <= kWave; size <<= 1) {
-#pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const uint32_t o = (uint32_t)__shfl_xor((int)v, stride, kWave);
-      const bool lower = (lane & stride) == 0;       // this lane holds the lower index of the pair
-      const bool desc = (lane & size) == 0;          // this block sorts descending (the last one: all lanes)
-      const uint32_t hi = v > o ? v : o, lo = v > o ? o : v;
-      v = (lower == desc) ? hi : lo;
-    }
-  }
-  return v;
 }
 
 template <int NMT, bool E4M3, int NQ>
@@ -410,51 +394,68 @@ __global__ __launch_bounds__(64 * NQ) void k_score_stream(const void* __restrict
                                 const bool cand = s < a.hi && is_candidate(s, tb, a.n_sink, a.n_window);
                                 keys_s[wave][i * kTileKeys + lane] = cand ? score_key(score) : 0u;
                               });
-  // 1. the chunk's statistic (each lane reads back only the keys it wrote itself)
+  // 1. the chunk's statistic (each lane reads back only the keys it wrote itself, all requested at once). It is
+  // published as at least 1, so that a written slot is never 0: a published 1 only lowers the bound to 1, which no
+  // candidate's key is below (key 0 marks "no candidate"), so every candidate is then emitted and the result is
+  // still exact.
+  constexpr int kKeysPerLane = kRun / kTileKeys;
+  uint32_t mine[kKeysPerLane];
+#pragma unroll
+  for (int i = 0; i < kKeysPerLane; ++i) mine[i] = i < n_tiles ? keys_s[wave][i * kTileKeys + lane] : 0u;
   uint32_t lmax = 0;
-  for (int i = 0; i < n_tiles; ++i) {
-    const uint32_t key = keys_s[wave][i * kTileKeys + lane];
-    lmax = key > lmax ? key : lmax;
-  }
-  const uint32_t x = (uint32_t)__shfl((int)wave_sort_desc(lmax, lane), a.m - 1, kWave);
-  // Cross-workgroup data goes through device-coherent single accesses (agent-scope atomics: they bypass the
-  // per-XCD L2 caches, which are not coherent with one another), never through fences, which would write back and
-  // invalidate a whole L2 under the other workgroups' tile copies.
-  uint32_t* slots = a.pub + (int64_t)(active ? b : 0) * a.pub_ld;
-  if (active && lane == 0) __hip_atomic_store(slots + a.slot0 + wg, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  wait_vmem();  // the slot store has completed (is visible device-wide) before the workgroup raises its flag
-  __syncthreads();
-
-  // 2. per workgroup and launch, a flag word (the last pub_ld - slots words of the group's first query row) says
-  // that its waves' slots are all written: wave 0 raises it, then polls, a bounded number of times, the flags of
-  // every workgroup of the launch in its group; then every wave reads its query's slots (a slot never written reads
-  // 0, which the bound ignores: the slots and flags of a call start at zero)
-  uint32_t* flags = a.pub + (int64_t)(blockIdx.y * NQ) * a.pub_ld + a.flag0;
-  if (wave == 0) {
-    if (lane == 0) __hip_atomic_store(flags + a.slot0 + wg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (int it = 0; it < a.spin_limit; ++it) {
-      bool up = true;
 #pragma unroll
-      for (int j = 0; j < kSlotRegs; ++j) {
-        const int i = j * kWave + lane;
-        if (i < n_wg) up = up && __hip_atomic_load(flags + a.slot0 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
-      }
-      if (__all(up)) break;
-      __builtin_amdgcn_s_sleep(4);
-    }
-  }
-  __syncthreads();
+  for (int i = 0; i < kKeysPerLane; ++i) lmax = mine[i] > lmax ? mine[i] : lmax;
+  const uint32_t lm[1] = {lmax};
+  uint32_t x = wave_rth_largest(lm, a.m);
+  x = x > 1u ? x : 1u;
   if (!active) return;  // no barrier follows
+
+  // 2. this wave's query row: publish the statistic, then poll the launch's slots (a bounded number of times) until
+  // every workgroup's is written; slots still unwritten read 0, which the bound ignores (the slots of a call start
+  // at zero). Cross-workgroup data goes through device-coherent single accesses (agent-scope atomics: they bypass
+  // the per-XCD L2 caches, which are not coherent with one another), never through fences, which would write back
+  // and invalidate a whole L2 under the other workgroups' tile copies. The wave's own slot is taken from x.
+  uint32_t* slots = a.pub + (int64_t)b * a.pub_ld + a.slot0;
+  if (lane == 0) __hip_atomic_store(slots + wg, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // Launches of at most 128 workgroups (the usual case) keep their slots in two registers per lane; the loads of one
+  // poll are issued together (clamped addresses) and slots past the launch's count are 0.
+  constexpr int kFewRegs = 2;
+  const bool few = n_wg <= kFewRegs * kWave;
   uint32_t xs[kSlotRegs];
+  for (int it = 0;; ++it) {
+    uint32_t v[kSlotRegs];
 #pragma unroll
-  for (int j = 0; j < kSlotRegs; ++j) {
-    const int i = j * kWave + lane;
-    xs[j] = i < n_wg ? __hip_atomic_load(slots + a.slot0 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+    for (int j = 0; j < kFewRegs; ++j) {
+      const int i = j * kWave + lane;
+      v[j] = __hip_atomic_load(slots + (i < n_wg ? i : n_wg - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (!few) {
+#pragma unroll
+      for (int j = kFewRegs; j < kSlotRegs; ++j) {
+        const int i = j * kWave + lane;
+        v[j] = __hip_atomic_load(slots + (i < n_wg ? i : n_wg - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    bool up = true;
+#pragma unroll
+    for (int j = 0; j < kSlotRegs; ++j) {
+      const int i = j * kWave + lane;
+      xs[j] = (i >= n_wg || (few && j >= kFewRegs)) ? 0u : (i == wg ? x : v[j]);
+      up = up && (i >= n_wg || xs[j] != 0u);
+    }
+    if (__all(up) || it >= a.spin_limit) break;
+    __builtin_amdgcn_s_sleep(4);
   }
 
   // 3. the lower bound of the k-th key
   const int r = (a.k + a.m - 1) / a.m;
-  uint32_t T = wave_rth_largest(xs, r);
+  uint32_t T;
+  if (few) {
+    const uint32_t x2[kFewRegs] = {xs[0], xs[1]};
+    T = wave_rth_largest(x2, r);
+  } else {
+    T = wave_rth_largest(xs, r);
+  }
   if (!a.first) {
     const uint32_t prev = __hip_atomic_load(a.thr + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     T = prev > T ? prev : T;
@@ -504,8 +505,9 @@ __global__ __launch_bounds__(64 * NQ) void k_score_stream(const void* __restrict
   // 4. emission of the keys >= T in position order
   Cand* seg = a.cand + (int64_t)b * a.cand_ld + (int64_t)(a.slot0 + wg) * a.seg_cap;
   int n_out = 0;
-  for (int i = 0; i < n_tiles; ++i) {
-    const uint32_t key = keys_s[wave][i * kTileKeys + lane];
+#pragma unroll
+  for (int i = 0; i < kKeysPerLane; ++i) {
+    const uint32_t key = mine[i];  // 0 past the last tile
     const bool emit = key != 0u && key >= T;
     const uint64_t mk = ballot(emit);
     if (emit) seg[n_out + lanes_below(mk)] = Cand{key, (int32_t)(tile_start(i) + lane)};
@@ -654,7 +656,7 @@ StreamPlan stream_plan(const IndexerArgs& a, int64_t end) {
   // launch ranges hold whole runs, so the workgroup count of all launches together does not depend on how many
   // workgroups one launch has; the first query row of each group also holds one flag per workgroup
   p.slots = (end + p.run_keys - 1) / p.run_keys;
-  p.pub_ld = 2 * p.slots;
+  p.pub_ld = p.slots;
   p.top_words = kStreamTopCap + 1;
   return p;
 }
@@ -703,7 +705,6 @@ hipError_t launch_stream_t(const IndexerArgs& a, int k, int n_sink, int n_window
   sa.k = k;
   sa.pub = pub;
   sa.pub_ld = p.pub_ld;
-  sa.flag0 = p.slots;
   sa.thr = thr;
   sa.top = top;
   sa.cand = cand;

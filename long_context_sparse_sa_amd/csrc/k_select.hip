@@ -7,7 +7,9 @@
 //     batch), so inputs in ascending position order give outputs in ascending position order without a sort;
 //   * keys and positions live in LDS, or in the gather buffer in global memory when they do not fit; the storage
 //     is a compile-time choice, so every access is a plain LDS or global load;
-//   * the bits all keys share are skipped; 8-bit radix passes with eight privatized histograms find the k-th key;
+//   * segments are gathered a chunk at a time, every entry located by a binary search over the segment offsets, so
+//     that all loads of a chunk are in flight together;
+//   * the bits all keys share are skipped; 12-bit radix passes find the k-th key;
 //     when several candidates share it, radix passes over their positions keep the lowest ones.
 // Intermediate calls keep the k best and publish the k-th key as the next threshold. Bucket ranking (final_mode
 // 2) is the one caller that needs (key desc, position asc) order; it sorts its at most top_b ids in LDS.
@@ -22,10 +24,11 @@ namespace {
 
 constexpr int kMergeThreads = 1024;
 constexpr int kMergeWaves = kMergeThreads / kWave;
-constexpr int kHistCopies = 2;         // privatized histograms (by wave parity)
-constexpr int kDigitBits = 11;        // radix digit width: 2048 bins spread clustered keys thinly
+constexpr int kHistCopies = 1;
+constexpr int kDigitBits = 12;  // radix digit width: two passes cover the 24 bits that keys near one binade differ in
 constexpr int kBins = 1 << kDigitBits;
-static_assert(kBins == 2 * 1024, "the digit search gives each of the 1024 threads two bins");
+constexpr int kBinsPerThread = kBins / 1024;
+static_assert(kBinsPerThread * 1024 == kBins, "the digit search gives each of the 1024 threads whole bins");
 constexpr int kRounds = 16;  // rounds of 1024 entries compacted per batch
 constexpr int kBatch = kRounds * kMergeThreads;
 constexpr int kMaxSortK = 16384;
@@ -35,8 +38,7 @@ struct MergeShared {
   union {
     uint32_t hist[kHistCopies][kBins];  // selection passes
     struct {
-      int32_t off[kMergeThreads];  // gather: output offset and count of each segment of a chunk
-      int32_t cnt[kMergeThreads];
+      int32_t off[kMergeThreads];  // gather: offset of each segment of a chunk in the chunk's concatenation
     } seg;
   } u;
   uint64_t masks[kRounds][kMergeWaves];
@@ -45,6 +47,8 @@ struct MergeShared {
   int32_t batch_total;
   uint32_t digit, before, in_bin;
   uint32_t kmin, kmax;
+  uint32_t small_n, small_key;  // small-bin finish: entries listed, the k-th key and position found
+  int32_t small_pos;
 };
 
 // Order-preserving compaction of one batch: entry r * 1024 + tid (r < kRounds) is flagged by f[r]. Returns the
@@ -108,7 +112,7 @@ __device__ __forceinline__ void note_minmax(uint32_t& lmin, uint32_t& lmax, uint
 // (descending for keys, ascending for positions). Key passes (kPos false) count the keys matching (prefix, mask);
 // position passes count the positions matching (prefix, mask) among entries whose key equals kstar. Loads are
 // unconditional (clamped index) and batched four per thread, so they are in flight together; only the counting
-// is predicated. Wave 0 then scans the bins, 32 per lane.
+// is predicated. Every thread then takes kBinsPerThread bins of the digit search.
 template <bool kPos>
 __device__ __forceinline__ void radix_pass(MergeShared& sh, int n, const uint32_t* K, const int32_t* P, uint32_t kstar,
                                            uint32_t prefix, uint32_t mask, int shift, int d, uint32_t need, int tid) {
@@ -135,14 +139,14 @@ __device__ __forceinline__ void radix_pass(MergeShared& sh, int n, const uint32_
     }
   }
   __syncthreads();
-  // digit search with every thread: thread t owns selection-order bins 2t and 2t + 1
+  // digit search with every thread: thread t owns selection-order bins kBinsPerThread * t .. + kBinsPerThread - 1
   const bool descending = !kPos;
   const int nb = 1 << d;
-  uint32_t c[2], local = 0;
-  int binof[2];
+  uint32_t c[kBinsPerThread], local = 0;
+  int binof[kBinsPerThread];
 #pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int o = 2 * tid + e;
+  for (int e = 0; e < kBinsPerThread; ++e) {
+    const int o = kBinsPerThread * tid + e;
     binof[e] = descending ? nb - 1 - o : o;
     c[e] = 0;
     if (o < nb)
@@ -158,12 +162,69 @@ __device__ __forceinline__ void radix_pass(MergeShared& sh, int n, const uint32_
   for (int w = 0; w < kMergeWaves; ++w) before_w += w < wave ? (uint32_t)sh.wsum[w] : 0u;
   const uint32_t incl = before_w + winc, excl = incl - local;
   if (excl < need && incl >= need) {
-    const bool first = excl + c[0] >= need;
-    sh.digit = (uint32_t)binof[first ? 0 : 1];
-    sh.before = first ? excl : excl + c[0];
-    sh.in_bin = c[first ? 0 : 1];
+    uint32_t run = excl;
+    bool found = false;
+#pragma unroll
+    for (int e = 0; e < kBinsPerThread; ++e) {
+      if (!found && run + c[e] >= need) {
+        found = true;
+        sh.digit = (uint32_t)binof[e];
+        sh.before = run;
+        sh.in_bin = c[e];
+      }
+      run += c[e];
+    }
   }
   __syncthreads();
+}
+
+// The k-th entry when at most 64 entries are left in its bin: the `ties` entries whose key matches (prefix, mask)
+// are listed in LDS (in the histogram area, free after a pass) and one wave ranks them exactly in (key desc,
+// position asc) order; positions are distinct, so exactly one entry has rank need - 1. Its key and position are
+// kstar and pstar: every entry above it in that order, and no other, is kept. All threads must call.
+__device__ __forceinline__ void small_bin_finish(MergeShared& sh, int n, const uint32_t* K, const int32_t* P,
+                                                 uint32_t prefix, uint32_t mask, uint32_t need, int tid,
+                                                 uint32_t* kstar, int32_t* pstar) {
+  uint32_t* lk = &sh.u.hist[0][0];
+  int32_t* lp = reinterpret_cast<int32_t*>(&sh.u.hist[0][kWave]);
+  if (tid == 0) sh.small_n = 0;
+  __syncthreads();
+  for (int base = 0; base < n; base += 4 * kMergeThreads) {
+    uint32_t kv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = base + j * kMergeThreads + tid;
+      kv[j] = K[i < n ? i : n - 1];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = base + j * kMergeThreads + tid;
+      if (i < n && (kv[j] & mask) == prefix) {
+        const uint32_t o = atomicAdd(&sh.small_n, 1u);
+        lk[o] = kv[j];
+        lp[o] = P[i];
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < kWave) {
+    const int m = (int)sh.small_n;
+    const uint32_t mk = tid < m ? lk[tid] : 0u;
+    const int32_t mp = tid < m ? lp[tid] : 0x7FFFFFFF;
+    int rank = 0;
+    for (int j = 0; j < m; ++j) {
+      const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)mk, j);
+      const int32_t pj = __builtin_amdgcn_readlane(mp, j);
+      rank += (kj > mk || (kj == mk && pj < mp)) ? 1 : 0;
+    }
+    if (tid < m && rank == (int)need - 1) {
+      sh.small_key = mk;
+      sh.small_pos = mp;
+    }
+  }
+  __syncthreads();
+  *kstar = sh.small_key;
+  *pstar = sh.small_pos;
 }
 
 // Ascending bitonic sort of a[0, n2) in LDS (n2 a power of two, >= 2), all threads of the block.
@@ -243,33 +304,49 @@ __device__ __forceinline__ void merge_body(MergeShared& sh, int b, int k, const 
     }
   }
   if (cb) {
+    // segments are taken 1024 at a time. The segment of each entry of a chunk's concatenation is first written
+    // into that entry's position slot (one wave per segment); then every thread requests its entries eight at once,
+    // from unconditional addresses (entries past the end read entry 0 of the chunk's first segment), so that the
+    // whole chunk arrives in one round trip instead of one per segment. Each entry's slot is read and then
+    // overwritten by the one thread that owns the entry.
     for (int w0 = 0; w0 < in.n_seg; w0 += kMergeThreads) {
       const int w = w0 + tid;
       const int c = w < in.n_seg ? (int)in.seg_cnt[(int64_t)b * in.n_seg + w] : 0;
       int total;
       const int ex = block_scan(sh, c, tid, &total);
-      sh.u.seg.off[tid] = n + ex;
-      sh.u.seg.cnt[tid] = c;
+      sh.u.seg.off[tid] = ex;
       __syncthreads();
       const int nw = in.n_seg - w0 < kMergeThreads ? in.n_seg - w0 : kMergeThreads;
       for (int j = wave; j < nw; j += kMergeWaves) {
-        const Cand* src = cb + (int64_t)(w0 + j) * in.seg_cap;
-        const int cnt = sh.u.seg.cnt[j], off = sh.u.seg.off[j];
-        for (int e0 = 0; e0 < cnt; e0 += 4 * kWave) {
-          Cand c4[4];
+        const int o = sh.u.seg.off[j];
+        const int cnt = (j + 1 < nw ? sh.u.seg.off[j + 1] : total) - o;
+        for (int e = lane; e < cnt; e += kWave) P[n + o + e] = j;
+      }
+      __syncthreads();
+      const Cand* chunk = cb + (int64_t)w0 * in.seg_cap;
+      constexpr int kPer = 8;  // entries per thread in flight together
+      for (int e0 = 0; e0 < total; e0 += kPer * kMergeThreads) {
+        Cand c8[kPer];
+        int js[kPer];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int e = e0 + u * kWave + lane;
-            c4[u] = e < cnt ? src[e] : Cand{0u, 0};
-          }
+        for (int u = 0; u < kPer; ++u) {
+          const int e = e0 + u * kMergeThreads + tid;
+          const int v = P[n + (e < total ? e : total - 1)];
+          js[u] = e < total ? v : 0;
+        }
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int e = e0 + u * kWave + lane;
-            if (e < cnt) {
-              K[off + e] = c4[u].key;
-              P[off + e] = c4[u].pos;
-              note_minmax(lmin, lmax, c4[u].key);
-            }
+        for (int u = 0; u < kPer; ++u) {
+          const int e = e0 + u * kMergeThreads + tid;
+          const int within = e < total ? e - sh.u.seg.off[js[u]] : 0;
+          c8[u] = chunk[(int64_t)js[u] * in.seg_cap + within];
+        }
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+          const int e = e0 + u * kMergeThreads + tid;
+          if (e < total) {
+            K[n + e] = c8[u].key;
+            P[n + e] = c8[u].pos;
+            note_minmax(lmin, lmax, c8[u].key);
           }
         }
       }
@@ -298,6 +375,7 @@ __device__ __forceinline__ void merge_body(MergeShared& sh, int b, int k, const 
     int bits = kmin == kmax ? 0 : 32 - __clz(kmin ^ kmax);  // low bits that still differ
     uint32_t mask = bits == 32 ? 0u : ~((1u << bits) - 1u);
     uint32_t prefix = kmin & mask;
+    bool small = false;
     while (bits > 0) {
       const int d = bits < kDigitBits ? bits : kDigitBits;
       const int shift = bits - d;
@@ -307,12 +385,18 @@ __device__ __forceinline__ void merge_body(MergeShared& sh, int b, int k, const 
       prefix |= sh.digit << shift;
       mask |= ((1u << d) - 1u) << shift;
       bits -= d;
+      // few entries left in the k-th key's bin: rank them in one wave instead of more passes over all entries
+      if (ties <= (uint32_t)kWave && (bits > 0 || need < ties)) {
+        small_bin_finish(sh, n, K, P, prefix, mask, need, tid, &kstar, &pstar);
+        small = true;
+        break;
+      }
     }
-    kstar = prefix;
-    if (need < ties) {
+    if (!small) kstar = prefix;
+    if (!small && need < ties) {
       // several candidates share the k-th key: keep the `need` lowest positions among them
       uint32_t pprefix = 0, pmask = 0, pneed = need;
-      // positions are below 2^31: digits of bits 30..20, 19..9 and 8..0
+      // positions are below 2^31: digits of bits 30..19, 18..7 and 6..0
       for (int pbits = 31; pbits > 0;) {
         const int d = pbits < kDigitBits ? pbits : kDigitBits;
         const int shift = pbits - d;
@@ -335,14 +419,11 @@ __device__ __forceinline__ void merge_body(MergeShared& sh, int b, int k, const 
     uint32_t kv[kRounds];
     int32_t pv[kRounds];
 #pragma unroll
-    for (int r = 0; r < kRounds; ++r) {
+    for (int r = 0; r < kRounds; ++r) {  // unconditional (clamped) reads, all in flight together
       const int i = base + r * kMergeThreads + tid;
-      kv[r] = 0u;
-      pv[r] = 0;
-      if (i < n) {
-        kv[r] = K[i];
-        pv[r] = P[i];
-      }
+      const int ic = i < n ? i : n - 1;
+      kv[r] = K[ic];
+      pv[r] = P[ic];
       f[r] = i < n && (n < k || kv[r] > kstar || (kv[r] == kstar && pv[r] <= pstar));
     }
     const int got = batch_slots(sh, f, slot, tid);

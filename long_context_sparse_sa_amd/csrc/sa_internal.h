@@ -141,12 +141,12 @@ struct StreamPlan {
   int nq;            // queries per workgroup
   int run_keys;      // positions per workgroup (a multiple of 64) = segment capacity
   int64_t slots;     // workgroups (= statistics slots = segments) per query over all launches
-  int64_t pub_ld;    // words per query row of the statistics area: the slots and a group counter
+  int64_t pub_ld;    // words per query row of the statistics area: one slot per workgroup of the call
   int top_words;     // words per query of the kept-statistics sketch
 };
 bool stream_supported(const IndexerArgs& a);
 StreamPlan stream_plan(const IndexerArgs& a, int64_t end);
-// pub [B, p.pub_ld] 32-bit slots and counters (zeroed by the call's first launch); thr [B]; top [B, p.top_words];
+// pub [B, p.pub_ld] 32-bit slots (zeroed before the call's first launch); thr [B]; top [B, p.top_words];
 // seg_cnt [B, p.slots]; cand [B, p.slots * p.run_keys]. spin_limit: polls of the other workgroups' publication
 // before going on without them.
 hipError_t launch_stream_decode(const IndexerArgs& a, int k, int n_sink, int n_window, const StreamPlan& p,
