@@ -325,6 +325,10 @@ SA_API int sa_msa_select(const void* q, int q_dtype, const float* w, const void*
  *        lse = -inf.
  *   ws / ws_bytes: at least sa_sparse_attn_workspace(B, H, d_qk, d_v, max_rows, dtype) bytes, where
  *        max_rows >= n_sink + n_window + idx_ld bounds every read set.
+ *   Precision: softmax and accumulation in fp32. When a query's rows are split over several workgroups (few
+ *   queries), each split's partial row is kept in the workspace in fp16 after an exact power-of-two scaling per
+ *   (head, half of the value columns) that brings it into [-1, 1]; this adds at most 2^-12 of that partial's
+ *   largest |value| to each element before the exact merge.
  * ------------------------------------------------------------------------------------------------------------- */
 SA_API size_t sa_sparse_attn_workspace(int32_t B, int32_t H, int32_t d_qk, int32_t d_v, int64_t max_rows,
                                        int dtype);

@@ -13,8 +13,9 @@
 //    by asynchronous DMA (72 x 16-byte chunks per 1152-byte row), S^T = K Q^T runs on the 32x32x16 bf16 MFMA with
 //    each wave's 32 query heads register-resident over its 288 dims (the two halves add their partial scores
 //    through LDS), the online softmax runs in the log2 domain, and O^T = V^T P^T takes V through LDS transpose
-//    reads so that P never leaves registers. Rows are split over workgroups; k_attn_combine merges the splits by
-//    their (max, sum).
+//    reads so that P never leaves registers. Rows are split over workgroups when queries are few; each split's
+//    partial rows go to the workspace in fp16, scaled per (head, column half) by a power of two into [-1, 1], and
+//    k_attn_combine merges the splits by their (max, sum).
 #include <math.h>
 
 #include "sa_device.h"
@@ -25,6 +26,16 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// Split partials: floats per (query, head, split) after the fp16 row: max, sum, and the power-of-two factor of each
+// half of the value columns.
+constexpr int kMlWords = 4;
+
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float x) {  // round to nearest even
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+}
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t u) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)u);
+}
 
 struct RowList {
   int ns, nw, nsel, w0;
@@ -229,7 +240,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
                                                    const int32_t* __restrict__ idx, int idx_ld,
                                                    const int32_t* __restrict__ n_sel, int n_sink, int n_window,
                                                    float scale_log2, int n_splits, int n_units,
-                                                   float* __restrict__ part_o, float* __restrict__ part_ml,
+                                                   uint16_t* __restrict__ part_o, float* __restrict__ part_ml,
                                                    uint16_t* __restrict__ out, float* __restrict__ lse) {
   constexpr int DVH = DV / 2;   // value columns per wave
   constexpr int NT = DVH / 32;  // 32-wide output tiles per wave
@@ -275,8 +286,8 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
       if (lse && tid < 64) lse[(int64_t)b * H + 64 * hg + tid] = -INFINITY;
     } else if (tid < 64) {
       const int64_t bh0 = (int64_t)b * H + 64 * hg + tid;
-      part_ml[(bh0 * n_splits + split) * 2 + 0] = -INFINITY;
-      part_ml[(bh0 * n_splits + split) * 2 + 1] = 0.f;
+      part_ml[(bh0 * n_splits + split) * kMlWords + 0] = -INFINITY;
+      part_ml[(bh0 * n_splits + split) * kMlWords + 1] = 0.f;
     }
     return;
   }
@@ -507,18 +518,39 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
         *reinterpret_cast<uint2*>(ostage + (32 * hb + j) * kOutLd + dv0 + 32 * nt + 8 * g4 + 4 * hsel) = uint2{lo, hi};
       }
     __syncthreads();
-    for (int e = tid; e < 64 * (DV / 8); e += 256) {
-      const int h = e / (DV / 8), c = 8 * (e % (DV / 8));
-      *reinterpret_cast<uint4*>(out + ((int64_t)b * H + 64 * hg + h) * DV + c) =
-          *reinterpret_cast<const uint4*>(ostage + h * kOutLd + c);
+    // 64 rows of DV / 8 16-byte chunks: a whole number per thread, all read before any is stored
+    constexpr int kPerT = 64 * (DV / 8) / 256;
+    static_assert(kPerT * 256 == 64 * (DV / 8), "the output chunks divide evenly over the threads");
+    uint16_t* obase = out + ((int64_t)b * H + 64 * hg) * DV;
+    uint4 oc[kPerT];
+#pragma unroll
+    for (int i = 0; i < kPerT; ++i) {
+      const int e = tid + 256 * i, h = e / (DV / 8), c = 8 * (e % (DV / 8));
+      oc[i] = *reinterpret_cast<const uint4*>(ostage + h * kOutLd + c);
+    }
+#pragma unroll
+    for (int i = 0; i < kPerT; ++i) {
+      const int e = tid + 256 * i;
+      *reinterpret_cast<uint4*>(obase + e * 8) = oc[i];  // rows of one workgroup are contiguous in out
     }
     if (lse && dh == 0 && hsel == 0) lse[bh] = (m_use + log2f(l_run)) * kLn2;
   } else {
-    // the partial rows leave through LDS (the tile buffers are free now), one head block at a time, so that every
-    // row of DV floats is written by consecutive threads as whole lines instead of 16 bytes per head per store
-    constexpr int kStageLd = DV + 4;  // padded row: the lanes of a column write land in different banks
-    static_assert(32 * kStageLd * 4 <= kNBuf * kTileBytes, "a head block's partial rows fit in the tile buffers");
-    float* stage = reinterpret_cast<float*>(&tiles[0][0]);
+    // Split partials in fp16: each (head, half of the value columns) is scaled by a power of two 2^-e with
+    // 2^e > its largest |o| (exact in fp32), so that its values lie in [-1, 1] where fp16 keeps 11 significant bits;
+    // 2^e goes with (m, l). The rows leave through LDS (the tile buffers are free now), one head block at a time,
+    // so that every row is written by consecutive threads as whole lines.
+    float amax = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(o[nt][r]));
+    amax = halves_max(amax);  // lanes j and j + 32 hold the same head
+    int ex = 0;
+    (void)frexpf(amax, &ex);  // amax < 2^ex (ex = 0 for amax = 0)
+    const float down = ldexpf(1.f, -ex);
+    constexpr int kStageLd = DV + 8;  // padded row of fp16: the lanes of a column write land in different banks
+    static_assert(32 * kStageLd * 2 <= kNBuf * kTileBytes, "a head block's partial rows fit in the tile buffers");
+    uint16_t* stage = reinterpret_cast<uint16_t*>(&tiles[0][0]);
     __syncthreads();  // every wave is done with the tile buffers
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
@@ -526,60 +558,85 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4)
-            *reinterpret_cast<f32x4*>(stage + j * kStageLd + dv0 + 32 * nt + 8 * g4 + 4 * hsel) =
-                f32x4{o[nt][4 * g4], o[nt][4 * g4 + 1], o[nt][4 * g4 + 2], o[nt][4 * g4 + 3]};
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const uint32_t lo = f32_to_f16_bits(o[nt][4 * g4 + 0] * down) | (f32_to_f16_bits(o[nt][4 * g4 + 1] * down) << 16);
+            const uint32_t hi = f32_to_f16_bits(o[nt][4 * g4 + 2] * down) | (f32_to_f16_bits(o[nt][4 * g4 + 3] * down) << 16);
+            *reinterpret_cast<uint2*>(stage + j * kStageLd + dv0 + 32 * nt + 8 * g4 + 4 * hsel) = uint2{lo, hi};
+          }
       }
       __syncthreads();
-      for (int e = tid; e < 32 * (DV / 4); e += 256) {
-        const int h = e / (DV / 4), c = 4 * (e % (DV / 4));
-        const int64_t bh_h = (int64_t)b * H + 64 * hg + 32 * blk + h;
-        *reinterpret_cast<f32x4*>(part_o + (bh_h * n_splits + split) * DV + c) =
-            *reinterpret_cast<const f32x4*>(stage + h * kStageLd + c);
+      // 32 rows of DV / 8 16-byte chunks, a whole number per thread, all read before any is stored; row h of the
+      // block sits h * n_splits rows after the block's first row
+      constexpr int kPerT = 32 * (DV / 8) / 256;
+      static_assert(kPerT * 256 == 32 * (DV / 8), "the partial chunks divide evenly over the threads");
+      uint16_t* pbase = part_o + (((int64_t)b * H + 64 * hg + 32 * blk) * n_splits + split) * DV;
+      const int row_step = n_splits * DV;
+      uint4 pc[kPerT];
+#pragma unroll
+      for (int i = 0; i < kPerT; ++i) {
+        const int e = tid + 256 * i, h = e / (DV / 8), c = 8 * (e % (DV / 8));
+        pc[i] = *reinterpret_cast<const uint4*>(stage + h * kStageLd + c);
+      }
+#pragma unroll
+      for (int i = 0; i < kPerT; ++i) {
+        const int e = tid + 256 * i, h = e / (DV / 8), c = 8 * (e % (DV / 8));
+        *reinterpret_cast<uint4*>(pbase + h * row_step + c) = pc[i];
       }
       __syncthreads();
     }
-    if (dh == 0 && hsel == 0) {
-      part_ml[(bh * n_splits + split) * 2 + 0] = m_use;
-      part_ml[(bh * n_splits + split) * 2 + 1] = l_run;
+    if (hsel == 0) {
+      float* ml = part_ml + (bh * n_splits + split) * kMlWords;
+      if (dh == 0) {
+        ml[0] = m_use;
+        ml[1] = l_run;
+      }
+      ml[2 + dh] = ldexpf(1.f, ex);
     }
   }
 }
 
-// Exact merge of the row splits of one (query, head): o = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i.
-// One block per (query, head); thread i owns four value columns. Its first eight split rows are requested before
-// anything else, and every thread derives the split weights itself from the (max, sum) pairs, which are the same
-// for the whole block (uniform loads), so the block needs no barrier. A split with no rows has max -inf and no
-// value row (its workspace row is never written): its weight is 0 and its row is skipped, not multiplied.
+// Exact merge of the row splits of one (query, head): o = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i, where split
+// i's row O_i is its fp16 row times the power of two stored for its half of the columns. One block per (query,
+// head); thread i owns four value columns. Its first eight split rows are requested before anything else, and
+// every thread derives the split weights itself from the (max, sum) pairs, which are the same for the whole block
+// (uniform loads), so the block needs no barrier. A split with no rows has max -inf and no value row (its
+// workspace row is never written): its weight is 0 and its row is skipped, not multiplied.
 constexpr int kCombineThreads = 192;  // four columns each: d_v <= 768
 constexpr int kCombineBatch = 8;
 
+__device__ __forceinline__ f32x4 f16x4_to_f32(uint2 v) {
+  return f32x4{f16_bits_to_f32(v.x & 0xFFFFu), f16_bits_to_f32(v.x >> 16), f16_bits_to_f32(v.y & 0xFFFFu),
+               f16_bits_to_f32(v.y >> 16)};
+}
+
 template <int DT>
-__global__ __launch_bounds__(kCombineThreads) void k_attn_combine(const float* __restrict__ part_o,
+__global__ __launch_bounds__(kCombineThreads) void k_attn_combine(const uint16_t* __restrict__ part_o,
                                                                   const float* __restrict__ part_ml, int n_splits,
                                                                   int d_v, void* __restrict__ out,
                                                                   float* __restrict__ lse) {
   const int64_t bh = blockIdx.x;
   const int dv = 4 * (int)threadIdx.x;
   const bool act = dv < d_v;
-  const float* ml = part_ml + bh * n_splits * 2;
-  const float* po = part_o + bh * n_splits * d_v + (act ? dv : 0);
-  // the first kCombineBatch splits' partials and (max, sum) pairs, all requested before any is used: indices past
-  // the last split are clamped to it (loads are never predicated, so that they stay in flight together) and the
-  // duplicates are skipped below
-  f32x4 v[kCombineBatch];
-  float mv[kCombineBatch], lv[kCombineBatch];
+  const int half = dv < d_v / 2 ? 0 : 1;  // d_v / 2 is a multiple of 4: the four columns share a half
+  const float* ml = part_ml + bh * n_splits * kMlWords;
+  const uint16_t* po = part_o + bh * n_splits * d_v + (act ? dv : 0);
+  // the first kCombineBatch splits' partials and (max, sum, factor) triples, all requested before any is used:
+  // indices past the last split are clamped to it (loads are never predicated, so that they stay in flight
+  // together) and the duplicates are skipped below
+  uint2 v[kCombineBatch];
+  float mv[kCombineBatch], lv[kCombineBatch], fv[kCombineBatch];
 #pragma unroll
   for (int u = 0; u < kCombineBatch; ++u) {
     const int i = u < n_splits ? u : n_splits - 1;
-    v[u] = *reinterpret_cast<const f32x4*>(po + (int64_t)i * d_v);
-    mv[u] = ml[2 * i];
-    lv[u] = ml[2 * i + 1];
+    v[u] = *reinterpret_cast<const uint2*>(po + (int64_t)i * d_v);
+    mv[u] = ml[kMlWords * i];
+    lv[u] = ml[kMlWords * i + 1];
+    fv[u] = ml[kMlWords * i + 2 + half];
   }
   float M = -INFINITY;
 #pragma unroll
   for (int u = 0; u < kCombineBatch; ++u) M = u < n_splits ? fmaxf(M, mv[u]) : M;
-  for (int i = kCombineBatch; i < n_splits; ++i) M = fmaxf(M, ml[2 * i]);
+  for (int i = kCombineBatch; i < n_splits; ++i) M = fmaxf(M, ml[kMlWords * i]);
   float Ls = 0.f;
   f32x4 acc = f32x4{};
   if (M != -INFINITY) {
@@ -587,21 +644,22 @@ __global__ __launch_bounds__(kCombineThreads) void k_attn_combine(const float* _
     for (int u = 0; u < kCombineBatch; ++u) {
       const float w = u < n_splits ? exp2f(mv[u] - M) : 0.f;
       Ls += w * lv[u];
-      if (w > 0.f) acc += w * v[u];  // a split without rows has max -inf, weight 0, and unwritten partials
+      if (w > 0.f) acc += (w * fv[u]) * f16x4_to_f32(v[u]);  // a split without rows has weight 0
     }
     for (int i0 = kCombineBatch; i0 < n_splits; i0 += kCombineBatch) {
 #pragma unroll
       for (int u = 0; u < kCombineBatch; ++u) {
         const int i = i0 + u < n_splits ? i0 + u : n_splits - 1;
-        v[u] = *reinterpret_cast<const f32x4*>(po + (int64_t)i * d_v);
-        mv[u] = ml[2 * i];
-        lv[u] = ml[2 * i + 1];
+        v[u] = *reinterpret_cast<const uint2*>(po + (int64_t)i * d_v);
+        mv[u] = ml[kMlWords * i];
+        lv[u] = ml[kMlWords * i + 1];
+        fv[u] = ml[kMlWords * i + 2 + half];
       }
 #pragma unroll
       for (int u = 0; u < kCombineBatch; ++u) {
         const float w = i0 + u < n_splits ? exp2f(mv[u] - M) : 0.f;
         Ls += w * lv[u];
-        if (w > 0.f) acc += w * v[u];
+        if (w > 0.f) acc += (w * fv[u]) * f16x4_to_f32(v[u]);
       }
     }
   }
@@ -648,9 +706,10 @@ AttnPlan attn_plan(int B, int H, int d_qk, int d_v, int64_t max_rows, int dtype,
   return p;
 }
 
+// Per (query, head, split): d_v fp16 partial values, then kMlWords floats (max, sum, one factor per column half).
 size_t attn_workspace_bytes(const AttnPlan& p, int B, int H, int d_v) {
   if (!p.mfma || p.n_splits <= 1) return 0;
-  return (size_t)B * H * p.n_splits * ((size_t)d_v + 2) * sizeof(float);
+  return (size_t)B * H * p.n_splits * ((size_t)d_v * sizeof(uint16_t) + kMlWords * sizeof(float));
 }
 
 // attn_plan never uses more than max(ceil(256 / units), ceil(tiles / (kMaxRowsPerSplit / kTileRows))) splits,
@@ -663,7 +722,7 @@ size_t attn_workspace_bound(int B, int H, int d_qk, int d_v, int64_t max_rows, i
   const int64_t s1 = (256 + units - 1) / units;
   const int64_t s2 = (tiles + kMaxRowsPerSplit / kTileRows - 1) / (kMaxRowsPerSplit / kTileRows);
   const int64_t s = s1 > s2 ? s1 : s2;
-  return (size_t)B * H * s * ((size_t)d_v + 2) * sizeof(float);
+  return (size_t)B * H * s * ((size_t)d_v * sizeof(uint16_t) + kMlWords * sizeof(float));
 }
 
 hipError_t launch_attn(const AttnArgs& a, const AttnPlan& p, void* ws, hipStream_t st) {
@@ -682,8 +741,8 @@ hipError_t launch_attn(const AttnArgs& a, const AttnPlan& p, void* ws, hipStream
     return hipGetLastError();
   }
   if ((uint64_t)a.kv_ld * 2 > 0xffffffffull) return hipErrorInvalidValue;  // row byte stride is a 32-bit multiplier
-  float* part_o = reinterpret_cast<float*>(ws);
-  float* part_ml = part_o ? part_o + (size_t)a.B * a.H * p.n_splits * a.d_v : nullptr;
+  uint16_t* part_o = reinterpret_cast<uint16_t*>(ws);
+  float* part_ml = part_o ? reinterpret_cast<float*>(part_o + (size_t)a.B * a.H * p.n_splits * a.d_v) : nullptr;
   const int HG = a.H / 64;
   const int n_units = a.B * p.n_splits;
   dim3 grid((unsigned)((n_units + 7) / 8 * 8 * HG));
