@@ -4,14 +4,14 @@
 // are read in addition).
 //
 // Build (once per cache):
-//   counts (atomics) -> offsets (exclusive scan) -> per-chunk bucket counts -> per-(chunk, bucket) start indices
-//   -> stable scatter (one wave per chunk, positions in ascending order) -> representatives (fp64 sums, one wave
-//   per bucket, rounded once to fp32).
+//   per-chunk bucket histograms -> column scan (each bucket's count in earlier chunks, and its total) -> offsets
+//   (exclusive scan of the totals) -> stable scatter (positions in ascending order within each bucket) ->
+//   representatives (fp64 sums, rounded once to fp32).
 // Select (per step):
 //   four lanes per bucket score q . rep for every query and write one key per (query, bucket) -> one workgroup per
-//   query chooses the exact top-b (ties to the lower bucket id) and expands the chosen buckets' member ranges
-//   inside [sink end, window start), sorted ascending by binning the positions (a bitonic sort when the bins
-//   crowd).
+//   query chooses the exact top-b (ties to the lower bucket id) and expands the chosen buckets' members inside
+//   [sink end, window start): all members are fetched in one round trip, compacted, and sorted ascending by
+//   binning the positions (a bitonic sort when the bins crowd).
 #include <mutex>
 
 #include "sa_device.h"
@@ -527,6 +527,10 @@ __global__ __launch_bounds__(1024) void k_choose_expand(const uint32_t* __restri
     *total = all;
     return before + incl - v;
   };
+  uint64_t* sorted = reinterpret_cast<uint64_t*>(buf);  // buf is free until the expansion
+  int nc = 0;
+  bool have_rng = false;  // rng_lo / rng_n of the chosen buckets are already set (block-uniform)
+  {
   uint32_t* hist = reinterpret_cast<uint32_t*>(tmp);  // tmp is free until the expansion sorts
   uint32_t need = (uint32_t)top_b, prefix = 0u, pmask = 0u;
   int n_valid = 0;
@@ -570,8 +574,7 @@ __global__ __launch_bounds__(1024) void k_choose_expand(const uint32_t* __restri
     need -= sel_before;
     __syncthreads();
   }
-  const int nc = full ? top_b : n_valid;
-  uint64_t* sorted = reinterpret_cast<uint64_t*>(buf);  // buf is free until the expansion
+  nc = full ? top_b : n_valid;
   if (fast) {
     // the n <= kFastCand candidates as ascending (~key, id) = score desc, id asc; the rank of each is the number
     // of candidates before it, and ranks below top_b are the chosen buckets in rank order
@@ -583,15 +586,22 @@ __global__ __launch_bounds__(1024) void k_choose_expand(const uint32_t* __restri
     __syncthreads();
     const int n = (int)sel_n;
     if (tid < n) {
+      // each candidate also requests its bucket's member-list bounds before ranking, so that the expansion finds
+      // them ready
       const uint64_t me = sorted[tid];
+      const int id = (int)(uint32_t)me;
+      const int o0 = offsets[id], o1 = offsets[id + 1];
       int r = 0;
 #pragma unroll 8
       for (int j = 0; j < n; ++j) r += sorted[j] < me ? 1 : 0;
       if (r < top_b) {
-        chosen[r] = (int32_t)(uint32_t)me;
-        if (buckets_out) buckets_out[(int64_t)b * top_b + r] = (int32_t)(uint32_t)me;
+        chosen[r] = id;
+        rng_lo[r] = o0;
+        rng_n[r] = o1 - o0;
+        if (buckets_out) buckets_out[(int64_t)b * top_b + r] = id;
       }
     }
+    have_rng = true;
   } else {
     const uint32_t kstar = prefix;  // with full: chosen = slots above kstar + `need` of the slots equal to it
     uint32_t id_lim = 0xFFFFFFFFu;  // slots equal to kstar are chosen when their id is below this
@@ -664,6 +674,7 @@ __global__ __launch_bounds__(1024) void k_choose_expand(const uint32_t* __restri
         buckets_out[(int64_t)b * top_b + tid] = tid < nc ? (int32_t)(uint32_t)sorted[tid] : -1;
     }
   }
+  }
   __syncthreads();
 
   // ---- expansion
@@ -671,6 +682,62 @@ __global__ __launch_bounds__(1024) void k_choose_expand(const uint32_t* __restri
   const int ns = n_sink < tb + 1 ? n_sink : tb + 1;
   int w0 = tb - n_window + 1;
   w0 = w0 > ns ? w0 : ns;
+  int32_t* out = idx + (int64_t)b * cap;
+  // member-list bounds of every chosen bucket, one thread per bucket (a single round trip), unless the choice
+  // already fetched them
+  if (!have_rng) {
+    if (tid < nc) {
+      const int c = chosen[tid];
+      const int o0 = offsets[c];
+      rng_lo[tid] = o0;
+      rng_n[tid] = offsets[c + 1] - o0;
+    }
+    __syncthreads();
+  }
+  int total_all;
+  const int all_base = block_scan(tid < nc ? rng_n[tid] : 0, &total_all);
+  int total = 0;
+  if (total_all <= kMaxExpand) {  // block-uniform
+    // every member of the chosen buckets at once: the bucket of each entry of their concatenation is written into
+    // tmp (one wave per bucket), then every thread requests eight entries together (clamped, unconditional
+    // loads); the members inside [ns, w0) are compacted into buf in any order (the sort below orders them)
+    if (tid < nc) rng_base[tid] = all_base;
+    if (tid == 0) sel_n = 0u;
+    __syncthreads();
+    for (int i = wave; i < nc; i += kWaves) {
+      const int base = rng_base[i], n = rng_n[i];
+      for (int j = lane; j < n; j += kWave) tmp[base + j] = i;
+    }
+    __syncthreads();
+    constexpr int kPer = 8;
+    for (int e0 = 0; e0 < total_all; e0 += kPer * 1024) {
+      int32_t mv[kPer];
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int e = e0 + u * 1024 + tid;
+        const int ec = e < total_all ? e : total_all - 1;
+        const int seg = tmp[ec];
+        mv[u] = members[rng_lo[seg] + (ec - rng_base[seg])];
+      }
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int e = e0 + u * 1024 + tid;
+        const bool keep = e < total_all && mv[u] >= ns && mv[u] < w0;
+        const uint64_t mk = ballot(keep);
+        uint32_t base = 0u;
+        if (lane == 0 && mk) base = atomicAdd(&sel_n, (uint32_t)__popcll(mk));
+        base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+        if (keep) buf[base + lanes_below(mk)] = mv[u];
+      }
+    }
+    __syncthreads();
+    total = (int)sel_n;
+    if (total > cap) {
+      for (int i = tid; i < cap; i += 1024) out[i] = -1;
+      if (tid == 0) n_sel[b] = -total;
+      return;
+    }
+  } else {
   // each chosen bucket's members in [ns, w0): one wave per bucket counts, 64 members per load, how many lie below
   // ns and below w0 (members are ascending, so the counts are the range's bounds)
   for (int i = wave; i < nc; i += kWaves) {
@@ -700,14 +767,13 @@ __global__ __launch_bounds__(1024) void k_choose_expand(const uint32_t* __restri
   }
   if (lane == kWave - 1) wsum[wave] = incl;
   __syncthreads();
-  int before = 0, total = 0;
+  int before = 0;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
     before += w < wave ? wsum[w] : 0;
     total += wsum[w];
   }
   if (tid < nc) rng_base[tid] = before + incl - v;
-  int32_t* out = idx + (int64_t)b * cap;
   if (total > cap) {
     for (int i = tid; i < cap; i += 1024) out[i] = -1;
     if (tid == 0) n_sel[b] = -total;
@@ -720,11 +786,18 @@ __global__ __launch_bounds__(1024) void k_choose_expand(const uint32_t* __restri
     for (int j = lane; j < n; j += kWave) buf[base + j] = members[lo + j];
   }
   __syncthreads();
+  }
   // sort the positions (distinct: a position belongs to one bucket only) by binning them over [ns, w0) into 1024
   // bins of equal width, one per thread, then sorting each bin's few entries in registers; a bin that gets more
   // than kBinMax entries (clustered positions) sends the whole query to a bitonic sort instead
+  // bin = floor((v - ns) * 1024 / span) in double: monotone in v, below 1024 for v < w0 (the product stays far
+  // more than one double ulp under 1024), and the same rounding for the count and the scatter
   const int64_t span = (int64_t)w0 - ns > 0 ? (int64_t)w0 - ns : 1;
-  auto bin_of = [&](int32_t v) { return (int)(((int64_t)(v - ns) * 1024) / span); };
+  const double bin_scale = 1024.0 / (double)span;
+  auto bin_of = [&](int32_t v) {
+    const int bn = (int)((double)(v - ns) * bin_scale);
+    return bn < 1023 ? bn : 1023;
+  };
   bin_cnt[tid] = 0;
   if (tid == 0) overflow = 0;
   __syncthreads();
