@@ -101,7 +101,9 @@ __global__ __launch_bounds__(256) void k_score_valu(const void* __restrict__ q, 
 // register ring, converted and committed to two LDS buffers. Emitted candidates are staged per wave in LDS and
 // flushed, in position order, to the workgroup's own segment whenever the stage could overflow and at the end;
 // the segment's count is stored last.
-template <int NMT, bool E4M3, int NQ>
+// G2: block maxima of the two 32-head groups of each 64-head query in one wave (row 2 b + g of the keys; t holds
+// one entry per (query, group) and the query's is read at 2 b).
+template <int NMT, bool E4M3, int NQ, bool G2 = false>
 __global__ __launch_bounds__(64 * NQ) void k_score_mfma(const void* __restrict__ q, const float* __restrict__ w,
                                                         const void* __restrict__ k, int64_t k_ld, int64_t L, int B,
                                                         const int32_t* __restrict__ t, int64_t lo, int64_t hi,
@@ -137,7 +139,7 @@ __global__ __launch_bounds__(64 * NQ) void k_score_mfma(const void* __restrict__
   uint32_t thr = 0;
   int64_t tb = L - 1;
   if (active) {
-    tb = t ? (int64_t)t[b] : L - 1;
+    tb = t ? (int64_t)t[G2 ? 2 * b : b] : L - 1;
     if (mode == kScoreEmit && thr_key) thr = thr_key[b];
     load_query<NMT, E4M3>(q, w, b, lane, qa, wv);
   }
@@ -154,6 +156,25 @@ __global__ __launch_bounds__(64 * NQ) void k_score_mfma(const void* __restrict__
   };
   auto process_tile = [&](const char* tile, int64_t s0) {
     if (!active || s0 >= hi) return;
+    if constexpr (G2) {
+      static_assert(NMT == 2, "two 32-head groups per 64-head query");
+      if (s0 / page_len >= tb / page_len) return;  // only the blocks before the local one are ranked
+      const float2 sc = score_tile_groups(tile, lane, qa, wv);
+      const bool in_range = s0 + lane < hi;
+      uint32_t k0 = in_range ? score_key(sc.x) : 0u, k1 = in_range ? score_key(sc.y) : 0u;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const uint32_t x0 = __shfl_xor(k0, o, kWave), x1 = __shfl_xor(k1, o, kWave);
+        k0 = x0 > k0 ? x0 : k0;
+        k1 = x1 > k1 ? x1 : k1;
+      }
+      if (lane == 0) {
+        uint32_t* row = reinterpret_cast<uint32_t*>(scores) + (int64_t)(2 * b) * scores_ld + s0 / page_len;
+        atomicMax(row, k0);
+        atomicMax(row + scores_ld, k1);
+      }
+      return;
+    }
     // block maxima rank only the blocks before the one holding t (page_len is the block length, a multiple of 64,
     // so a tile lies in one block)
     if (mode == kScoreBlockMax && s0 / page_len >= tb / page_len) return;
@@ -318,6 +339,7 @@ __global__ __launch_bounds__(64 * NQ) void k_stream_select(const void* __restric
 constexpr int stream_wg_keys(bool e4m3, int nq) { return (!e4m3 && nq == 4) ? 4096 : 8192; }
 constexpr int kStreamMaxWgs = 512;    // workgroups per query group and launch (eight slots per lane)
 constexpr int kStreamTopCap = 1024;   // kept statistics of earlier launches per query (r <= 512 of them are needed)
+constexpr int kStreamTargetWgs = 256;  // workgroups a launch aims for, over all its query groups
 
 struct StreamArgs {
   int64_t lo, hi;        // positions of this launch
@@ -547,7 +569,7 @@ void mfma_grid(int B, int NQ, int64_t n_tiles, int64_t* n_wg, int64_t* run) {
   *run = (n_tiles + *n_wg - 1) / *n_wg;
 }
 
-template <int NMT, bool FP8, int NQ>
+template <int NMT, bool FP8, int NQ, bool G2 = false>
 hipError_t launch_mfma(const IndexerArgs& a, int64_t lo, int64_t hi, int mode, float* scores, int64_t scores_ld,
                        int n_sink, int n_window, const uint32_t* thr, Cand* cand, int64_t cand_ld,
                        uint32_t* seg_cnt, hipStream_t st, int page_subs = 1, int page_len = 1, int64_t tok_L = 0) {
@@ -556,7 +578,7 @@ hipError_t launch_mfma(const IndexerArgs& a, int64_t lo, int64_t hi, int mode, f
   mfma_grid(a.B, NQ, n_tiles, &n_wg, &run);
   if (n_tiles < 1 || a.B < 1) return hipSuccess;
   dim3 grid((unsigned)n_wg, (unsigned)((a.B + NQ - 1) / NQ));
-  SA_LAUNCH((k_score_mfma<NMT, FP8, NQ>), grid, dim3(64 * NQ), 0, st, a.q, a.w, a.k, a.k_ld, a.L, a.B, a.t,
+  SA_LAUNCH((k_score_mfma<NMT, FP8, NQ, G2>), grid, dim3(64 * NQ), 0, st, a.q, a.w, a.k, a.k_ld, a.L, a.B, a.t,
                      lo, hi, mode, scores, scores_ld, n_sink, n_window, thr, cand, cand_ld, seg_cnt, a.clear, a.clear_n,
                      page_subs, page_len, tok_L);
   return hipGetLastError();
@@ -634,6 +656,17 @@ hipError_t launch_block_max(const IndexerArgs& a, int block, uint32_t* keys, int
   float* out = reinterpret_cast<float*>(keys);  // the block-max mode writes uint32 keys through the scores pointer
   const bool wide = a.B >= 8;
   const bool fp8 = a.q_dtype == 2;
+  if (a.groups2) {
+    // rows are (query, group) pairs of 32 heads; one wave takes both groups of a query (a 64-head query)
+    IndexerArgs aq = a;
+    aq.B = a.B / 2;
+    aq.H = 64;
+    const bool wq = aq.B >= 8;
+    if (fp8) return wq ? launch_mfma<2, true, 8, true>(aq, 0, a.L, kScoreBlockMax, out, keys_ld, 0, 0, nullptr, nullptr, 0, nullptr, st, 1, block, a.L)
+                       : launch_mfma<2, true, 4, true>(aq, 0, a.L, kScoreBlockMax, out, keys_ld, 0, 0, nullptr, nullptr, 0, nullptr, st, 1, block, a.L);
+    return wq ? launch_mfma<2, false, 8, true>(aq, 0, a.L, kScoreBlockMax, out, keys_ld, 0, 0, nullptr, nullptr, 0, nullptr, st, 1, block, a.L)
+              : launch_mfma<2, false, 4, true>(aq, 0, a.L, kScoreBlockMax, out, keys_ld, 0, 0, nullptr, nullptr, 0, nullptr, st, 1, block, a.L);
+  }
   if (a.H == 64) {
     if (fp8) return wide ? launch_mfma<2, true, 8>(a, 0, a.L, kScoreBlockMax, out, keys_ld, 0, 0, nullptr, nullptr, 0, nullptr, st, 1, block, a.L)
                          : launch_mfma<2, true, 4>(a, 0, a.L, kScoreBlockMax, out, keys_ld, 0, 0, nullptr, nullptr, 0, nullptr, st, 1, block, a.L);
@@ -651,10 +684,18 @@ bool stream_supported(const IndexerArgs& a) { return score_uses_mfma(a); }
 StreamPlan stream_plan(const IndexerArgs& a, int64_t end) {
   StreamPlan p{};
   p.nq = a.B >= 8 ? 8 : 4;
-  p.run_keys = stream_wg_keys(a.q_dtype == 2, p.nq) / p.nq;
+  // positions per workgroup: enough workgroups for the whole chip (about kStreamTargetWgs over all query groups),
+  // at most the workgroup's LDS capacity, a whole number of tiles
+  const int64_t cap_keys = stream_wg_keys(a.q_dtype == 2, p.nq) / p.nq;
+  const int64_t groups = (a.B + p.nq - 1) / p.nq;
+  const int64_t target = kStreamTargetWgs / groups > 1 ? kStreamTargetWgs / groups : 1;
+  int64_t run = (end + target - 1) / target;
+  run = (run + kTileKeys - 1) / kTileKeys * kTileKeys;
+  run = run < kTileKeys ? kTileKeys : (run > cap_keys ? cap_keys : run);
+  p.run_keys = (int)run;
   p.end = end;
   // launch ranges hold whole runs, so the workgroup count of all launches together does not depend on how many
-  // workgroups one launch has; the first query row of each group also holds one flag per workgroup
+  // workgroups one launch has
   p.slots = (end + p.run_keys - 1) / p.run_keys;
   p.pub_ld = p.slots;
   p.top_words = kStreamTopCap + 1;

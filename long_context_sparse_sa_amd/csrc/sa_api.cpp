@@ -706,10 +706,9 @@ SA_API int sa_hi_select(const void* q, int q_dtype, const float* w, const void* 
 // ---------------------------------------------------------------------------------------------------------------
 namespace {
 
-// The flat selection over pooled keys: few queries over a short pooled cache (up to 2^16 micro-blocks) take the
-// split-L algorithm, whose first key range already prunes the rest (measured faster there than the streaming
-// bound, which needs many workgroups per query to become tight); otherwise the library's own choice.
-int qsa_algo(int64_t Lp, int32_t B) { return (B < 64 && Lp <= (1 << 16)) ? SA_TOPK_SPLIT_L : SA_TOPK_AUTO; }
+// The flat selection over pooled keys takes the library's own choice for the shape (the streaming bound for few
+// queries, whose runs per workgroup shrink with the pooled cache so that a short one still fills the chip).
+int qsa_algo(int64_t, int32_t) { return SA_TOPK_AUTO; }
 
 struct QsaWs {
   int64_t Lp;        // pooled rows
@@ -835,7 +834,8 @@ SA_API int sa_msa_select(const void* q, int q_dtype, const float* w, const void*
   // merge over the row's block keys: the keys are few, one per block)
   e = sa::launch_fill_u32(w2.keys, (int64_t)Bp * w2.keys_ld, 0u, s);
   if (e != hipSuccess) return hip_fail(e, "sa_msa_select (clear)");
-  const sa::IndexerArgs a = make_indexer(q, q_dtype, w, k, k_dtype, k_ld, L, Bp, H / G, d, w2.tq);
+  sa::IndexerArgs a = make_indexer(q, q_dtype, w, k, k_dtype, k_ld, L, Bp, H / G, d, w2.tq);
+  a.groups2 = G == 2 && H == 64;  // both groups of a query in one wave: one key-tile read per query, not per group
   e = sa::launch_block_max(a, block, w2.keys, w2.keys_ld, s);
   if (e != hipSuccess) return hip_fail(e, "sa_msa_select (block maxima)");
   if (k_blocks > 1) {

@@ -33,6 +33,9 @@ struct IndexerArgs {
   // saves a separate fill launch).
   uint32_t* clear = nullptr;
   int64_t clear_n = 0;
+  // Block maxima only: the B rows are (query, group) pairs, two 32-head groups per 64-head query, which one wave
+  // scores together (the query's t is row 2 b's).
+  bool groups2 = false;
 };
 
 // One emitted candidate: (order-preserving key of the fp32 score, position).

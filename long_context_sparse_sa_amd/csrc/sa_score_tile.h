@@ -195,6 +195,66 @@ __device__ __forceinline__ float score_frags(FR&& frag, const bf16x8 (&qa)[NMT][
   return fold_halves(part0, part1);
 }
 
+// Two head groups of 32 heads (the two M-tiles of a 64-head query), each summed on its own: the same MFMAs and
+// schedule as score_frags<2>, with the ReLU-weighted head sum kept per tile. Lane l returns the two group scores of
+// position l of the tile.
+template <typename FR>
+__device__ __forceinline__ float2 score_frags_groups(FR&& frag, const bf16x8 (&qa)[2][kSteps],
+                                                    const float (&wv)[2][16]) {
+  constexpr int NMT = 2;
+  constexpr int kChunk = NMT * 16 / kSteps;
+  bf16x8 fr[kSteps];
+#pragma unroll
+  for (int ks = 0; ks < kSteps; ++ks) fr[ks] = frag(0, ks);
+  f32x16 acc0[NMT], acc1[NMT];
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt) {
+    acc0[mt] = f32x16{};
+    acc1[mt] = f32x16{};
+  }
+#pragma unroll
+  for (int ks = 0; ks < kSteps; ++ks) {
+    const bf16x8 bk = fr[ks];
+    fr[ks] = frag(1, ks);
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) acc0[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt][ks], bk, acc0[mt], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  float part0[NMT] = {0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < kSteps; ++ks) {
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) acc1[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt][ks], fr[ks], acc1[mt], 0, 0, 0);
+#pragma unroll
+    for (int e = 0; e < kChunk; ++e) {
+      const int idx = ks * kChunk + e;
+      part0[idx / 16] = fmaf(wv[idx / 16][idx % 16], relu(acc0[idx / 16][idx % 16]), part0[idx / 16]);
+    }
+  }
+#pragma unroll
+  for (int ks = 0; ks < kSteps; ++ks) {
+    __builtin_amdgcn_sched_group_barrier(0x008, NMT, 0);       // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 2 * kChunk, 0);  // VALU
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  float part1[NMT] = {0.f, 0.f};
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) part1[mt] = fmaf(wv[mt][r], relu(acc1[mt][r]), part1[mt]);
+  return float2{fold_halves(part0[0], part1[0]), fold_halves(part0[1], part1[1])};
+}
+
+__device__ __forceinline__ float2 score_tile_groups(const char* tile, int lane, const bf16x8 (&qa)[2][kSteps],
+                                                   const float (&wv)[2][16]) {
+  const int hs = lane >> 5;
+  return score_frags_groups(
+      [&](int nt, int ks) {
+        return *reinterpret_cast<const bf16x8*>(tile + tile_off(32 * nt + (lane & 31), 2 * ks + hs));
+      },
+      qa, wv);
+}
+
 template <int NMT>
 __device__ __forceinline__ float score_tile(const char* tile, int lane, const bf16x8 (&qa)[NMT][kSteps],
                                            const float (&wv)[NMT][16]) {
