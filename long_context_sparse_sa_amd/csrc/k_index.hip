@@ -687,7 +687,7 @@ StreamPlan stream_plan(const IndexerArgs& a, int64_t end) {
   // positions per workgroup: enough workgroups for the whole chip (about kStreamTargetWgs over all query groups),
   // at most the workgroup's LDS capacity, a whole number of tiles
   const int64_t cap_keys = stream_wg_keys(a.q_dtype == 2, p.nq) / p.nq;
-  const int64_t groups = (a.B + p.nq - 1) / p.nq;
+  const int64_t groups = a.B > p.nq ? (a.B + p.nq - 1) / p.nq : 1;
   const int64_t target = kStreamTargetWgs / groups > 1 ? kStreamTargetWgs / groups : 1;
   int64_t run = (end + target - 1) / target;
   run = (run + kTileKeys - 1) / kTileKeys * kTileKeys;
