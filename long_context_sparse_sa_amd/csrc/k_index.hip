@@ -641,7 +641,9 @@ hipError_t launch_page_scores(const IndexerArgs& m, int page_subs, int page_len,
   if (!score_uses_mfma(m) || m.q_dtype != 1 || page_subs < 1 || page_subs > 64 || (page_subs & (page_subs - 1)))
     return hipErrorInvalidValue;
   if (m.B < 1 || m.L < 1) return hipSuccess;
-  const bool wide = m.B >= 8;
+  // eight queries per workgroup share each key tile for mid-sized batches; many queries (a prefill chunk) take
+  // four, so that two workgroups share a CU (measured faster there, as for the per-query streaming select)
+  const bool wide = m.B >= 8 && m.B < 64;
   if (m.H == 64) {
     if (wide) return launch_mfma<2, false, 8>(m, 0, m.L, kScorePage, scores, scores_ld, 0, 0, nullptr, nullptr, 0, nullptr, st, page_subs, page_len, tok_L);
     return launch_mfma<2, false, 4>(m, 0, m.L, kScorePage, scores, scores_ld, 0, 0, nullptr, nullptr, 0, nullptr, st, page_subs, page_len, tok_L);
