@@ -537,8 +537,8 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
   } else {
     // Split partials in fp16: each (head, half of the value columns) is scaled by a power of two 2^-e with
     // 2^e > its largest |o| (exact in fp32), so that its values lie in [-1, 1] where fp16 keeps 11 significant bits;
-    // 2^e goes with (m, l). The rows leave through LDS (the tile buffers are free now), one head block at a time,
-    // so that every row is written by consecutive threads as whole lines.
+    // 2^e goes with (m, l). The rows of both head blocks leave through LDS together (the tile buffers are free
+    // now), so that every row is written by consecutive threads as whole lines.
     float amax = 0.f;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
@@ -549,40 +549,34 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
     (void)frexpf(amax, &ex);  // amax < 2^ex (ex = 0 for amax = 0)
     const float down = ldexpf(1.f, -ex);
     constexpr int kStageLd = DV + 8;  // padded row of fp16: the lanes of a column write land in different banks
-    static_assert(32 * kStageLd * 2 <= kNBuf * kTileBytes, "a head block's partial rows fit in the tile buffers");
+    static_assert(64 * kStageLd * 2 <= kNBuf * kTileBytes, "the workgroup's partial rows fit in the tile buffers");
     uint16_t* stage = reinterpret_cast<uint16_t*>(&tiles[0][0]);
     __syncthreads();  // every wave is done with the tile buffers
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      if (hb == blk) {
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const uint32_t lo = f32_to_f16_bits(o[nt][4 * g4 + 0] * down) | (f32_to_f16_bits(o[nt][4 * g4 + 1] * down) << 16);
-            const uint32_t hi = f32_to_f16_bits(o[nt][4 * g4 + 2] * down) | (f32_to_f16_bits(o[nt][4 * g4 + 3] * down) << 16);
-            *reinterpret_cast<uint2*>(stage + j * kStageLd + dv0 + 32 * nt + 8 * g4 + 4 * hsel) = uint2{lo, hi};
-          }
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const uint32_t lo = f32_to_f16_bits(o[nt][4 * g4 + 0] * down) | (f32_to_f16_bits(o[nt][4 * g4 + 1] * down) << 16);
+        const uint32_t hi = f32_to_f16_bits(o[nt][4 * g4 + 2] * down) | (f32_to_f16_bits(o[nt][4 * g4 + 3] * down) << 16);
+        *reinterpret_cast<uint2*>(stage + (32 * hb + j) * kStageLd + dv0 + 32 * nt + 8 * g4 + 4 * hsel) = uint2{lo, hi};
       }
-      __syncthreads();
-      // 32 rows of DV / 8 16-byte chunks, a whole number per thread, all read before any is stored; row h of the
-      // block sits h * n_splits rows after the block's first row
-      constexpr int kPerT = 32 * (DV / 8) / 256;
-      static_assert(kPerT * 256 == 32 * (DV / 8), "the partial chunks divide evenly over the threads");
-      uint16_t* pbase = part_o + (((int64_t)b * H + 64 * hg + 32 * blk) * n_splits + split) * DV;
-      const int row_step = n_splits * DV;
-      uint4 pc[kPerT];
+    __syncthreads();
+    // 64 rows of DV / 8 16-byte chunks, a whole number per thread, all read before any is stored; row h of the
+    // workgroup sits h * n_splits rows after its first row
+    constexpr int kPerT = 64 * (DV / 8) / 256;
+    static_assert(kPerT * 256 == 64 * (DV / 8), "the partial chunks divide evenly over the threads");
+    uint16_t* pbase = part_o + (((int64_t)b * H + 64 * hg) * n_splits + split) * DV;
+    const int row_step = n_splits * DV;
+    uint4 pc[kPerT];
 #pragma unroll
-      for (int i = 0; i < kPerT; ++i) {
-        const int e = tid + 256 * i, h = e / (DV / 8), c = 8 * (e % (DV / 8));
-        pc[i] = *reinterpret_cast<const uint4*>(stage + h * kStageLd + c);
-      }
+    for (int i = 0; i < kPerT; ++i) {
+      const int e = tid + 256 * i, h = e / (DV / 8), c = 8 * (e % (DV / 8));
+      pc[i] = *reinterpret_cast<const uint4*>(stage + h * kStageLd + c);
+    }
 #pragma unroll
-      for (int i = 0; i < kPerT; ++i) {
-        const int e = tid + 256 * i, h = e / (DV / 8), c = 8 * (e % (DV / 8));
-        *reinterpret_cast<uint4*>(pbase + h * row_step + c) = pc[i];
-      }
-      __syncthreads();
+    for (int i = 0; i < kPerT; ++i) {
+      const int e = tid + 256 * i, h = e / (DV / 8), c = 8 * (e % (DV / 8));
+      *reinterpret_cast<uint4*>(pbase + h * row_step + c) = pc[i];
     }
     if (hsel == 0) {
       float* ml = part_ml + (bh * n_splits + split) * kMlWords;
