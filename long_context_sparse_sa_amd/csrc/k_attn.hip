@@ -219,13 +219,15 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Grid: 1-D. A unit is (query b, row split); every unit has H / 64 head groups. Block id
-// (u / 8) * 8 * HG + hg * 8 + u % 8 puts all head groups of unit u on the same XCD (block id mod 8), so the
-// second gather of a tile's rows is served by that XCD's L2.
+// Grid: 1-D, a multiple of 8 blocks. A unit is (query b, row split); every unit has H / 64 head groups. Blocks are
+// dealt to the 8 XCDs by block id mod 8, so XCD x takes the x-th eighth of the (unit, head group) list in order:
+// all head groups of a unit, and normally every split of a query, share one XCD's L2. The second gather of a
+// tile's rows and the query rows of every split after the first are then served by that L2.
 __device__ __forceinline__ void attn_block(int HG, int* u, int* hg) {
   const int blk = (int)blockIdx.x;
-  *u = (blk / (8 * HG)) * 8 + blk % 8;
-  *hg = (blk / 8) % HG;
+  const int g = (blk % 8) * (int)(gridDim.x / 8) + blk / 8;
+  *u = g / HG;
+  *hg = g % HG;
 }
 
 // Workgroup = 4 waves = 2 head blocks of 32 heads x 2 halves. The two waves of a head block each compute S^T = K Q^T
