@@ -248,7 +248,9 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
   constexpr int NT = DVH / 32;  // 32-wide output tiles per wave
   __shared__ __attribute__((aligned(1024))) char tiles[kNBuf][kTileBytes];
   __shared__ int32_t pos_s[kMaxRowsPerSplit];
-  __shared__ f32x4 exch[4][4][kWave];  // partial S^T of each wave, by register group and lane
+  // partial S^T of each wave, by tile parity, register group and lane: with one barrier per tile a wave may write
+  // the next tile's scores before its partner has read this tile's, so consecutive tiles use different halves
+  __shared__ f32x4 exch[2][4][4][kWave];
   const int HG = H / 64;
   int u, hg;
   attn_block(HG, &u, &hg);
@@ -379,13 +381,6 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
   // One tile: S^T, the online softmax, O^T. kPartial: the split's last tile is not full (rows past its end are
   // masked to -inf); only that tile pays for the mask.
   auto process = [&](int tile, auto partial) __attribute__((always_inline)) {
-    // wait for this tile's copies; the next tile may stay in flight
-    if (tile + 1 < n_tiles) wait_vmem_below<kDmaPerWave>();
-    else wait_vmem_below<0>();
-    lds_barrier();
-    // the copies of tile + kNBuf - 1, into the buffer every wave finished with before the barrier (issued in one
-    // burst: spreading them over the MFMAs measured slower)
-    if (tile + kNBuf - 1 < n_tiles) issue(tile + kNBuf - 1, (tile + kNBuf - 1) % kNBuf);
     // this tile's fragment bases, made opaque so that the compiler keeps one register per base and folds every
     // constant into the instruction offset (instead of hoisting base + constant sums out of the loop)
     const uint32_t tbase = tiles_lds + (uint32_t)((tile % kNBuf) * kTileBytes);
@@ -413,11 +408,17 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) exch[wave][g4][lane] = f32x4{s[4 * g4], s[4 * g4 + 1], s[4 * g4 + 2], s[4 * g4 + 3]};
+    for (int g4 = 0; g4 < 4; ++g4)
+      exch[tile & 1][wave][g4][lane] = f32x4{s[4 * g4], s[4 * g4 + 1], s[4 * g4 + 2], s[4 * g4 + 3]};
+    // one barrier per tile: it hands over the partial scores, shows the next tile's copies landed (every wave
+    // waits for its own first), and shows every wave done with the previous tile's buffer, which the copies of
+    // tile + kNBuf - 1 then refill
+    wait_vmem_below<0>();
     lds_barrier();
+    if (tile + kNBuf - 1 < n_tiles) issue(tile + kNBuf - 1, (tile + kNBuf - 1) % kNBuf);
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
-      const f32x4 other = exch[wave ^ 1][g4][lane];
+      const f32x4 other = exch[tile & 1][wave ^ 1][g4][lane];
 #pragma unroll
       for (int e = 0; e < 4; ++e) s[4 * g4 + e] += other[e];
     }
@@ -497,6 +498,11 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const uint16_t* __restrict__ 
 
   const int n_pre = n_tiles < kNBuf - 1 ? n_tiles : kNBuf - 1;
   for (int p = 0; p < n_pre; ++p) issue(p, p);
+  // the first tile's copies landed and are visible to every wave; later tiles are waited for at the barrier of the
+  // tile before them
+  if (n_pre > 1) wait_vmem_below<kDmaPerWave>();
+  else wait_vmem_below<0>();
+  lds_barrier();
   const int n_full = n_my / kTileRows;
   for (int tile = 0; tile < n_full; ++tile) process(tile, BoolTag<false>{});
   if (n_full < n_tiles) process(n_full, BoolTag<true>{});
