@@ -373,10 +373,11 @@ def main():
         i_flops = perf.indexer_flops(pairs, wl.H_I, wl.d_I)
         i_bytes = perf.indexer_bytes(wl.L, wl.B, wl.H_I, wl.d_I, wl.idx_dtype)
         peak = perf.PEAK_TFLOPS["bf16" if idx_mfma else "f32_vector"]
-        # the scoring kernel is the select call's longest; it runs every indexer flop except where the cache is
-        # scored in several ranges (few queries beyond 2^20 positions), where the whole entry point is reported
+        # the scoring kernel is the select call's longest; it runs every indexer flop where the call is one scoring
+        # launch (the per-query kernel, or the stream's fill, scoring launch and merge). Where the positions are
+        # scored in several launches (few queries over many positions) the whole entry point is reported.
         per_query = idx_mfma and wl.B >= 64
-        one_scorer = per_query or not idx_mfma or wl.L <= (1 << 20)
+        one_scorer = per_query or not idx_mfma or len(sel_kernels) == 3
         if one_scorer:
             t_sel_k = max(sel_kernels) * 1e-3
             sname = ("k_stream_select" if per_query else "k_score_stream") if idx_mfma else "k_score_valu"
