@@ -383,7 +383,7 @@ def main():
             sname = ("k_stream_select" if per_query else "k_score_stream") if idx_mfma else "k_score_valu"
         else:
             t_sel_k = t_sel
-            sname = "sa_select_topk (on-chip stream over 2^20 positions, then emission ranges and merges)"
+            sname = "sa_select_topk (the whole call: several scoring launches and merges)"
         tf = i_flops / t_sel_k / 1e12
         gbps = i_bytes / t_sel_k / 1e9
         # the bound is whichever peak the algorithmic work needs longer at: the matrix unit for many queries, the
