@@ -397,8 +397,7 @@ __global__ __launch_bounds__(256) void k_bucket_scores(const void* __restrict__ 
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      acc[u] += __shfl_xor(acc[u], 1, kWave);
-      acc[u] += __shfl_xor(acc[u], 2, kWave);
+      acc[u] = quad_sum(acc[u]);
     }
     if (qtr == 0 && in) {
 #pragma unroll
@@ -449,8 +448,7 @@ __global__ __launch_bounds__(256) void k_tree_children(const void* __restrict__ 
     } else {
       for (int x = qtr; x < d; x += 4) acc = fmaf(qrow[x], r[x], acc);
     }
-    acc += __shfl_xor(acc, 1, kWave);
-    acc += __shfl_xor(acc, 2, kWave);
+    acc = quad_sum(acc);
     if (qtr == 0 && in)
       keys[(int64_t)b * n_next + child] = offsets[child + 1] > offsets[child] ? score_key(acc) : 0u;
   }

@@ -161,13 +161,8 @@ __global__ __launch_bounds__(64 * NQ) void k_score_mfma(const void* __restrict__
       if (s0 / page_len >= tb / page_len) return;  // only the blocks before the local one are ranked
       const float2 sc = score_tile_groups(tile, lane, qa, wv);
       const bool in_range = s0 + lane < hi;
-      uint32_t k0 = in_range ? score_key(sc.x) : 0u, k1 = in_range ? score_key(sc.y) : 0u;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const uint32_t x0 = __shfl_xor(k0, o, kWave), x1 = __shfl_xor(k1, o, kWave);
-        k0 = x0 > k0 ? x0 : k0;
-        k1 = x1 > k1 ? x1 : k1;
-      }
+      const uint32_t k0 = wave_max_u32(in_range ? score_key(sc.x) : 0u);
+      const uint32_t k1 = wave_max_u32(in_range ? score_key(sc.y) : 0u);
       if (lane == 0) {
         uint32_t* row = reinterpret_cast<uint32_t*>(scores) + (int64_t)(2 * b) * scores_ld + s0 / page_len;
         atomicMax(row, k0);
@@ -185,21 +180,15 @@ __global__ __launch_bounds__(64 * NQ) void k_score_mfma(const void* __restrict__
     if (mode == kScoreBlockMax) {
       // every position of a block before the local one is visible; the block's key is the max of its scores'
       // keys (score_key is order-preserving), combined over its tiles with an atomic max
-      uint32_t kv = in_range ? score_key(score) : 0u;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const uint32_t x = __shfl_xor(kv, o, kWave);
-        kv = x > kv ? x : kv;
-      }
+      const uint32_t kv = wave_max_u32(in_range ? score_key(score) : 0u);
       if (lane == 0) atomicMax(reinterpret_cast<uint32_t*>(scores) + (int64_t)b * scores_ld + s0 / page_len, kv);
     } else if (mode == kScorePage) {
       // the rows are the sub-block mean keys of the hierarchical index; page p = rows [p G, (p + 1) G) (G divides
       // the 64 rows of a tile, tiles start at multiples of 64): its score sums theirs, rows past the last add 0
-      float v = in_range ? score : 0.f;
-      for (int o = 1; o < page_subs; o <<= 1) v += __shfl_xor(v, o, kWave);
+      const float v = group_sum(in_range ? score : 0.f, page_subs);
       if ((lane & (page_subs - 1)) == 0 && in_range) {
         const int64_t page = s / page_subs;
-        const int64_t tq = t ? (int64_t)t[b] : tok_L - 1;
+        const int64_t tq = t ? tb : tok_L - 1;
         scores[(int64_t)b * scores_ld + page - lo / page_subs] = page * page_len <= tq ? v : -INFINITY;
       }
     } else if (mode == kScoreDense) {

@@ -72,6 +72,37 @@ __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 __device__ __forceinline__ float wave_shfl_xor(float v, int m) { return __shfl_xor(v, m, kWave); }
 
+// Lane swaps inside each row of 16 lanes as DPP operand modifiers (no LDS round trip). Each is an xor of the lane
+// index: 0xB1 = quad_perm [1, 0, 3, 2] (lane ^ 1), 0x4E = quad_perm [2, 3, 0, 1] (lane ^ 2), 0x141 =
+// row_half_mirror (lane ^ 7), 0x140 = row_mirror (lane ^ 15).
+template <int Ctrl>
+__device__ __forceinline__ uint32_t dpp_swap(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, Ctrl, 0xF, 0xF, false);
+}
+template <int Ctrl>
+__device__ __forceinline__ float dpp_swap(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), Ctrl, 0xF, 0xF, false));
+}
+// Sum over each aligned quad of lanes, in every lane of it; the pairing of an xor-shuffle tree (lane ^ 1, then
+// lane ^ 2), so the rounding is the same.
+__device__ __forceinline__ float quad_sum(float x) {
+  x += dpp_swap<0xB1>(x);
+  x += dpp_swap<0x4E>(x);
+  return x;
+}
+// Sum over each aligned group of n lanes (n a power of two, at most 64), in every lane of it. Up to 16 lanes the
+// partner sums come through DPP: after the quad sum, lane ^ 7 and then lane ^ 15 lie in the other quad and the other
+// half-row, which by then hold their own sums, so the pairing is again that of an xor-shuffle tree.
+__device__ __forceinline__ float group_sum(float x, int n) {
+  if (n >= 2) x += dpp_swap<0xB1>(x);
+  if (n >= 4) x += dpp_swap<0x4E>(x);
+  if (n >= 8) x += dpp_swap<0x141>(x);
+  if (n >= 16) x += dpp_swap<0x140>(x);
+  if (n >= 32) x += __shfl_xor(x, 16, kWave);
+  if (n >= 64) x += __shfl_xor(x, 32, kWave);
+  return x;
+}
+
 // One VALU lane exchange (v_permlane32_swap: lanes 32..63 of the first operand trade places with lanes 0..31 of
 // the second). The sum of the two results is, in lane l < 32, a_l + a_{l+32} and, in lane l >= 32, b_{l-32} + b_l:
 // two half-wave pair sums in one register.

@@ -82,21 +82,25 @@ __device__ __forceinline__ void wave_batched(const Cand* buf, int n, int lane, F
   }
 }
 
+// Minimum / maximum over the wave, the same in every lane: DPP swaps reduce each row of 16 lanes, then the four
+// row results are read as scalars.
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint32_t x = __shfl_xor(v, o, kWave);
-    v = x < v ? x : v;
-  }
-  return v;
+  v = min(v, dpp_swap<0xB1>(v));
+  v = min(v, dpp_swap<0x4E>(v));
+  v = min(v, dpp_swap<0x141>(v));
+  v = min(v, dpp_swap<0x140>(v));
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0), r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32), r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return min(min(r0, r1), min(r2, r3));
 }
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint32_t x = __shfl_xor(v, o, kWave);
-    v = x > v ? x : v;
-  }
-  return v;
+  v = max(v, dpp_swap<0xB1>(v));
+  v = max(v, dpp_swap<0x4E>(v));
+  v = max(v, dpp_swap<0x141>(v));
+  v = max(v, dpp_swap<0x140>(v));
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0), r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32), r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return max(max(r0, r1), max(r2, r3));
 }
 
 __device__ __noinline__ uint32_t wave_select_compact(Cand* buf, int n, int k, uint32_t* hist, int lane) {
