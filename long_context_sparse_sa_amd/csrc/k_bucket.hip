@@ -16,6 +16,7 @@
 
 #include "sa_device.h"
 #include "sa_internal.h"
+#include "sa_wave_select.h"
 
 namespace sa {
 namespace {
@@ -507,12 +508,7 @@ __global__ __launch_bounds__(1024) void k_choose_expand(const uint32_t* __restri
   };
   // block sum of one value per thread, with this thread's exclusive prefix
   auto block_scan = [&](int v, int* total) {
-    int incl = v;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int x = __shfl_up(incl, o, kWave);
-      if (lane >= o) incl += x;
-    }
+    const int incl = (int)wave_inclusive_scan((uint32_t)v, lane);
     if (lane == kWave - 1) wsum[wave] = incl;
     __syncthreads();
     int before = 0, all = 0;
@@ -637,9 +633,7 @@ __global__ __launch_bounds__(1024) void k_choose_expand(const uint32_t* __restri
         for (int size = 2; size <= kWave; size <<= 1)
 #pragma unroll
           for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            const uint32_t olo = (uint32_t)__shfl_xor((int)(uint32_t)v, stride, kWave);
-            const uint32_t ohi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), stride, kWave);
-            const uint64_t o = ((uint64_t)ohi << 32) | olo;
+            const uint64_t o = lane_xor64(v, stride);
             const bool keep_min = ((lane & stride) == 0) == ((lane & size) == 0);  // lower lane of an ascending pair
             v = keep_min ? (o < v ? o : v) : (o > v ? o : v);
           }
@@ -757,12 +751,7 @@ __global__ __launch_bounds__(1024) void k_choose_expand(const uint32_t* __restri
   __syncthreads();
   // output offsets of the ranges (exclusive scan over the chosen buckets, one per thread)
   const int v = tid < nc ? rng_n[tid] : 0;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int x = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += x;
-  }
+  const int incl = (int)wave_inclusive_scan((uint32_t)v, lane);
   if (lane == kWave - 1) wsum[wave] = incl;
   __syncthreads();
   int before = 0;
@@ -803,12 +792,7 @@ __global__ __launch_bounds__(1024) void k_choose_expand(const uint32_t* __restri
   __syncthreads();
   const int my_cnt = bin_cnt[tid];
   if (my_cnt > kBinMax) overflow = 1;
-  int incl2 = my_cnt;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int x = __shfl_up(incl2, o, kWave);
-    if (lane >= o) incl2 += x;
-  }
+  const int incl2 = (int)wave_inclusive_scan((uint32_t)my_cnt, lane);
   if (lane == kWave - 1) wsum[wave] = incl2;
   __syncthreads();
   int before2 = 0;

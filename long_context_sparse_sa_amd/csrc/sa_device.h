@@ -83,6 +83,22 @@ template <int Ctrl>
 __device__ __forceinline__ float dpp_swap(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), Ctrl, 0xF, 0xF, false));
 }
+// The value of lane ^ s (s a power of two below 64). Strides up to 8 stay inside a row of 16 lanes and come through
+// DPP swaps, composed where one swap is not enough: lane ^ 4 = (lane ^ 7) ^ 3 and lane ^ 8 = (lane ^ 15) ^ 7
+// (0x1B = quad_perm [3, 2, 1, 0], lane ^ 3). Every lane takes the same swaps, so no lane-dependent choice can turn
+// into a branch under which a swap would read a lane switched off. Strides 16 and 32 use a lane permute.
+__device__ __forceinline__ uint32_t lane_xor(uint32_t x, int s) {
+  switch (s) {
+    case 1: return dpp_swap<0xB1>(x);
+    case 2: return dpp_swap<0x4E>(x);
+    case 4: return dpp_swap<0x1B>(dpp_swap<0x141>(x));
+    case 8: return dpp_swap<0x141>(dpp_swap<0x140>(x));
+    default: return (uint32_t)__shfl_xor((int)x, s, kWave);
+  }
+}
+__device__ __forceinline__ uint64_t lane_xor64(uint64_t x, int s) {
+  return ((uint64_t)lane_xor((uint32_t)(x >> 32), s) << 32) | lane_xor((uint32_t)x, s);
+}
 // Sum over each aligned quad of lanes, in every lane of it; the pairing of an xor-shuffle tree (lane ^ 1, then
 // lane ^ 2), so the rounding is the same.
 __device__ __forceinline__ float quad_sum(float x) {
