@@ -354,12 +354,8 @@ __device__ __forceinline__ void merge_body(MergeShared& sh, int b, int k, const 
       __syncthreads();
     }
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint32_t x = __shfl_xor(lmin, o, kWave), y = __shfl_xor(lmax, o, kWave);
-    lmin = x < lmin ? x : lmin;
-    lmax = y > lmax ? y : lmax;
-  }
+  lmin = wave_min_u32(lmin);
+  lmax = wave_max_u32(lmax);
   if (lane == 0) {
     atomicMin(&sh.kmin, lmin);
     atomicMax(&sh.kmax, lmax);
