@@ -53,10 +53,10 @@ __device__ __forceinline__ uint32_t find_digit(const uint32_t* hist, uint32_t ne
     run += c[i];
   }
   const uint64_t m = ballot(found >= 0);
-  const int src = m ? (int)__builtin_ctzll(m) : 0;
-  const int o = __shfl(found, src, kWave);
-  *before = __shfl(fb, src, kWave);
-  *in_bin = __shfl(fc, src, kWave);
+  const int src = m ? (int)__builtin_ctzll(m) : 0;  // uniform: the values are read as scalars
+  const int o = __builtin_amdgcn_readlane(found, src);
+  *before = (uint32_t)__builtin_amdgcn_readlane((int)fb, src);
+  *in_bin = (uint32_t)__builtin_amdgcn_readlane((int)fc, src);
   return (uint32_t)(descending ? 255 - o : o);
 }
 
