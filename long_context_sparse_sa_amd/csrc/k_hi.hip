@@ -126,9 +126,8 @@ __global__ __launch_bounds__(64) void k_hi_fine(const void* __restrict__ q, cons
     if (lane == 0) *cnt_out = 0u;
     return;
   }
-  bf16x8 qa[NMT][kSteps];
-  float wv[NMT][16];
-  load_query<NMT, false>(q, w, b, lane, qa, wv);
+  QueryFrags<NMT> qf;
+  qf.template load<false>(q, w, b, lane);
   const int tiles_per_page = page_len / kTileKeys;
   const int n_tiles = (i1 - i0) * tiles_per_page;
   const char* kbytes = reinterpret_cast<const char*>(k);
@@ -176,7 +175,7 @@ __global__ __launch_bounds__(64) void k_hi_fine(const void* __restrict__ q, cons
     // complete in order, and the wait makes the copy visible to the fragment reads in any case
     store_tile_lds(tile, lane, ring[sl]);
     wait_lds();
-    const float score = score_tile<NMT>(tile, lane, qa, wv);
+    const float score = qf.score(tile, lane);
     const int64_t s = s0 + lane;
     const bool cand = s < L && s >= n_sink && s <= cand_end;
     const uint32_t key = score_key(score);

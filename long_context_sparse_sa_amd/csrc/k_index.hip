@@ -134,14 +134,17 @@ __global__ __launch_bounds__(64 * NQ) void k_score_mfma(const void* __restrict__
   const char* kbytes = reinterpret_cast<const char*>(k);
   const int64_t ld_bytes = k_ld * (E4M3 ? 1 : 2);
 
+  // two separately summed 32-head groups keep the 32x32x16 fragments; every other mode scores through QueryFrags
   bf16x8 qa[NMT][kSteps];
   float wv[NMT][16];
+  QueryFrags<NMT> qf;
   uint32_t thr = 0;
   int64_t tb = L - 1;
   if (active) {
     tb = t ? (int64_t)t[G2 ? 2 * b : b] : L - 1;
     if (mode == kScoreEmit && thr_key) thr = thr_key[b];
-    load_query<NMT, E4M3>(q, w, b, lane, qa, wv);
+    if constexpr (G2) load_query<NMT, E4M3>(q, w, b, lane, qa, wv);
+    else qf.template load<E4M3>(q, w, b, lane);
   }
   // no wait here: the query loads are older than every tile copy and loads complete in issue order, so the first
   // tile's wait (at most two tiles of copies outstanding) also covers them
@@ -174,7 +177,7 @@ __global__ __launch_bounds__(64 * NQ) void k_score_mfma(const void* __restrict__
     // so a tile lies in one block)
     if (mode == kScoreBlockMax && s0 / page_len >= tb / page_len) return;
     if (mode == kScoreEmit && n_emit > kStage - kTileKeys) flush();
-    const float score = score_tile<NMT>(tile, lane, qa, wv);
+    const float score = qf.score(tile, lane);
     const int64_t s = s0 + lane;  // lane order is position order
     const bool in_range = s < hi;
     if (mode == kScoreBlockMax) {
@@ -241,9 +244,8 @@ __global__ __launch_bounds__(64 * NQ) void k_stream_select(const void* __restric
   const int64_t tb = active ? (t ? (int64_t)t[b] : L - 1) : -1;
   const int64_t cand_end = active ? tb - n_window : -1;  // last candidate position (inclusive)
   if (lane == 0) wave_end[wave] = cand_end;
-  bf16x8 qa[NMT][kSteps];
-  float wv[NMT][16];
-  if (active) load_query<NMT, E4M3>(q, w, b, lane, qa, wv);
+  QueryFrags<NMT> qf;
+  if (active) qf.template load<E4M3>(q, w, b, lane);
   __syncthreads();
   int64_t end = wave_end[0];
   for (int i = 1; i < NQ; ++i) end = wave_end[i] > end ? wave_end[i] : end;
@@ -256,7 +258,7 @@ __global__ __launch_bounds__(64 * NQ) void k_stream_select(const void* __restric
   const int cend = (int)cand_end;  // positions fit in 32 bits
   auto score_and_emit = [&](const char* tile, int64_t s0) {
     if (!active || s0 > cand_end) return;
-    const float score = score_tile<NMT>(tile, lane, qa, wv);
+    const float score = qf.score(tile, lane);
     const int s = (int)s0 + lane;  // lane order is position order
     const uint32_t key = score_key(score);
     const bool cand = s >= n_sink && s <= cend;
@@ -387,12 +389,11 @@ __global__ __launch_bounds__(64 * NQ) void k_score_stream(const void* __restrict
   const char* kbytes = reinterpret_cast<const char*>(k);
   const int64_t ld_bytes = k_ld * (E4M3 ? 1 : 2);
 
-  bf16x8 qa[NMT][kSteps];
-  float wv[NMT][16];
+  QueryFrags<NMT> qf;
   int64_t tb = L - 1;
   if (active) {
     tb = t ? (int64_t)t[b] : L - 1;
-    load_query<NMT, E4M3>(q, w, b, lane, qa, wv);
+    qf.template load<E4M3>(q, w, b, lane);
   }
   // the query and weight loads complete before the first tile copy is issued: the compiler then knows them done,
   // instead of waiting for them inside the tile loop, where its vmcnt waits would also drain the copies in flight
@@ -400,7 +401,7 @@ __global__ __launch_bounds__(64 * NQ) void k_score_stream(const void* __restrict
   walk_tiles<E4M3, NQ, kNBuf>(kbytes, ld_bytes, L, n_tiles, tile_start, tiles, wave, lane,
                               [&](const char* tile, int64_t i) {
                                 if (!active) return;
-                                const float score = score_tile<NMT>(tile, lane, qa, wv);
+                                const float score = qf.score(tile, lane);
                                 const int64_t s = tile_start(i) + lane;
                                 const bool cand = s < a.hi && is_candidate(s, tb, a.n_sink, a.n_window);
                                 keys_s[wave][i * kTileKeys + lane] = cand ? score_key(score) : 0u;

@@ -126,6 +126,13 @@ __device__ __forceinline__ float fold_halves(float a, float b) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+// The same over rows of 16 lanes (v_permlane16_swap: the odd rows of the first operand trade places with the even
+// rows of the second). The sum of the two results is, in the even rows, a_l + a_{l+16} and, in the odd rows,
+// b_{l-16} + b_l.
+__device__ __forceinline__ float fold_rows(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 

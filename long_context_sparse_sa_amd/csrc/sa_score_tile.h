@@ -12,11 +12,12 @@ namespace tile {
 
 constexpr int kTileKeys = 64;
 
-// NMT = H / 32 head tiles per query, d = 128. The dot products always run on the bf16 32x32x16 MFMA: products of
-// bf16 operands are exact in fp32 and are summed in fp32. E4M3-stored keys and queries are converted exactly to
-// bf16 on the way into LDS and registers. The fp8 MFMA is not used: on 128-long dot products its internal
-// accumulation was measured to lose up to 1.8e-4 (mean 1.7e-5) of the sum of |products|, against 2.6e-7 for the
-// bf16 MFMA on the converted values, and that would move scores by more than the selection tolerance.
+// NMT = H / 32 head tiles per query, d = 128. The dot products always run on a bf16 MFMA (32x32x16 for 32 heads,
+// 16x16x32 for 64 heads, below): products of bf16 operands are exact in fp32 and are summed in fp32. E4M3-stored
+// keys and queries are converted exactly to bf16 on the way into LDS and registers. The fp8 MFMA is not used: on
+// 128-long dot products its internal accumulation was measured to lose up to 1.8e-4 (mean 1.7e-5) of the sum of
+// |products|, against 2.6e-7 for the bf16 MFMA on the converted values, and that would move scores by more than
+// the selection tolerance.
 //
 // LDS key tile: 64 positions x 256 bytes of bf16; the 16-byte chunk c of position n is stored at chunk
 // c ^ (n % 16) so that the 32 lanes reading one chunk column spread over the banks.
@@ -265,6 +266,131 @@ __device__ __forceinline__ float score_tile(const char* tile, int lane, const bf
       },
       qa, wv);
 }
+
+// ---- 64 heads on the 16x16x32 MFMA ----------------------------------------------------------------------------
+// The same scores for 64 heads with four M-tiles of 16 heads, four N-tiles of 16 positions and four k-steps of 32
+// dims: as many MFMA flops and LDS fragment bytes per tile, a quarter of the accumulator registers per instruction,
+// and half the head-weight registers. On random bf16 operands this shape sustains a higher issue rate than the
+// 32x32x16 one (a loop of each, two waves per SIMD: about 0.8 against 0.65 of the peak), and the scorer loop with
+// its ReLU-weighted head sum and LDS fragment reads goes from about 0.60 to 0.69.
+//
+// Operands: A (queries) lane l holds head 16 mt + l % 16, dims 32 ks + 8 (l / 16) .. + 7; B (keys) lane l holds
+// position 16 nt + l % 16, the same dims; the accumulator of (mt, nt) holds, in lane l, position 16 nt + l % 16
+// for heads 16 mt + 4 (l / 16) + r, r < 4. The key tile in LDS is the one above (chunk c of position n at chunk
+// slot c ^ (n % 16)): the 16 lanes of a row read 16 positions at one chunk, spread over every bank.
+constexpr int kSteps16 = 4;
+
+template <bool E4M3>
+__device__ __forceinline__ void load_query16(const void* q, const float* w, int64_t b, int lane,
+                                             bf16x8 (&qa)[4][kSteps16], float (&wv)[4][4]) {
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int64_t e0 = (b * 64 + 16 * mt + (lane & 15)) * 128 + (lane >> 4) * 8;
+#pragma unroll
+    for (int ks = 0; ks < kSteps16; ++ks) {
+      if constexpr (E4M3) {
+        const int2 raw = *reinterpret_cast<const int2*>(reinterpret_cast<const char*>(q) + e0 + ks * 32);
+        qa[mt][ks] = e4m3x8_to_bf16(raw.x, raw.y);
+      } else {
+        qa[mt][ks] = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const uint16_t*>(q) + e0 + ks * 32);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) wv[mt][r] = w[b * 64 + 16 * mt + 4 * (lane >> 4) + r];
+  }
+}
+
+// Scores of the 64 positions of a tile (lane l: position l). Half 0 (N-tiles 0, 1) runs first with its eight key
+// fragments read up front; each ring slot is refilled with the matching half-1 fragment once its MFMAs are issued.
+// The half-1 MFMAs are interleaved with the half-0 ReLU-weighted head sum (four MFMAs, then eight VALU
+// instructions, per fragment). Each lane sums its 16 heads of each N-tile; two lane exchanges then add the four
+// lane rows that hold the other heads of the same position.
+template <typename FR>
+__device__ __forceinline__ float score_frags16(FR&& frag, const bf16x8 (&qa)[4][kSteps16], const float (&wv)[4][4]) {
+  bf16x8 fr[8];  // slot i = 4 n + ks: N-tile n of the half being multiplied, k-step ks
+#pragma unroll
+  for (int i = 0; i < 8; ++i) fr[i] = frag(i >> 2, i & 3);
+  f32x4 acc0[2][4], acc1[2][4];  // [N-tile within the half][mt]
+#pragma unroll
+  for (int n = 0; n < 2; ++n)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      acc0[n][mt] = f32x4{};
+      acc1[n][mt] = f32x4{};
+    }
+  // half 0
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const bf16x8 bk = fr[i];
+    fr[i] = frag(2 + (i >> 2), i & 3);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+      acc0[i >> 2][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][i & 3], bk, acc0[i >> 2][mt], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // half 1, with the half-0 head sum in the MFMA shadow (32 products over the eight fragments)
+  float p[4] = {0.f, 0.f, 0.f, 0.f};  // this lane's head sums of N-tiles 0..3
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+      acc1[i >> 2][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mt][i & 3], fr[i], acc1[i >> 2][mt], 0, 0, 0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int idx = 4 * i + e, n = idx >> 4, mt = (idx >> 2) & 3, r = idx & 3;
+      p[n] = fmaf(wv[mt][r], relu(acc0[n][mt][r]), p[n]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // VALU
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int n = 0; n < 2; ++n)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[2 + n] = fmaf(wv[mt][r], relu(acc1[n][mt][r]), p[2 + n]);
+  // lanes l and l ^ 32 hold heads of rows {0, 2} and {1, 3} of the same positions: the first exchange leaves
+  // N-tiles 0 and 1 in lanes 0..31 and N-tiles 2 and 3 in lanes 32..63 (rows 0 + 2 or 1 + 3 added); the second
+  // adds rows l and l ^ 16, so that lane l holds all 64 heads of position l
+  return fold_rows(fold_halves(p[0], p[2]), fold_halves(p[1], p[3]));
+}
+
+__device__ __forceinline__ float score_tile16(const char* tile, int lane, const bf16x8 (&qa)[4][kSteps16],
+                                              const float (&wv)[4][4]) {
+  const int row = lane >> 4;
+  return score_frags16(
+      [&](int nt, int ks) {
+        return *reinterpret_cast<const bf16x8*>(tile + tile_off(16 * nt + (lane & 15), 4 * ks + row));
+      },
+      qa, wv);
+}
+
+// A query's register-resident fragments and head weights, and the score of an LDS key tile: 32 heads on the
+// 32x32x16 MFMA, 64 heads on the 16x16x32 one.
+template <int NMT>
+struct QueryFrags {
+  bf16x8 qa[NMT][kSteps];
+  float wv[NMT][16];
+  template <bool E4M3>
+  __device__ __forceinline__ void load(const void* q, const float* w, int64_t b, int lane) {
+    load_query<NMT, E4M3>(q, w, b, lane, qa, wv);
+  }
+  __device__ __forceinline__ float score(const char* tile, int lane) const { return score_tile<NMT>(tile, lane, qa, wv); }
+};
+template <>
+struct QueryFrags<2> {
+  bf16x8 qa[4][kSteps16];
+  float wv[4][4];
+  template <bool E4M3>
+  __device__ __forceinline__ void load(const void* q, const float* w, int64_t b, int lane) {
+    load_query16<E4M3>(q, w, b, lane, qa, wv);
+  }
+  __device__ __forceinline__ float score(const char* tile, int lane) const { return score_tile16(tile, lane, qa, wv); }
+};
 
 // The B fragments of the 64-position tile at s0 straight from global memory into registers (rows past L - 1 are
 // clamped to it; they are never scored). Plain loads: the compiler places the waits before their first use.
