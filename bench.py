@@ -80,6 +80,26 @@ def copy_bandwidth_gbps(torch, nbytes=1 << 30, reps=5):
     return round(2 * nbytes / sorted(ts)[len(ts) // 2] / 1e9, 1)
 
 
+def bf16_gemm_tflops(torch, n=8192, reps=5):
+    """The library's dense bf16 GEMM (n x n x n, N(0,1) operands, hipBLASLt through torch.mm), timed with events:
+    the box's reachable matrix-core rate on random data, beside the spec peak the rooflines divide by."""
+    g = torch.Generator(device="cuda").manual_seed(1)
+    a = torch.randn((n, n), generator=g, device="cuda").to(torch.bfloat16)
+    b = torch.randn((n, n), generator=g, device="cuda").to(torch.bfloat16)
+    c = torch.mm(a, b)
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.mm(a, b, out=c)
+        e1.record()
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    del a, b, c
+    torch.cuda.empty_cache()
+    return round(2.0 * n ** 3 / sorted(ts)[len(ts) // 2] / 1e12, 1)
+
+
 class StageTimer:
     """Per-kernel durations of library calls from events the library records after each of its launches."""
 
@@ -140,6 +160,7 @@ def main():
     wl = get_workload(args.workload, **over)
     torch.manual_seed(0)
     copy_gbps = copy_bandwidth_gbps(torch)
+    gemm_tflops = bf16_gemm_tflops(torch)
 
     # ---------------- inputs, rotated copies of the caches --------------------------------------------------------
     base = gen.make_inputs(wl, device=dev)
@@ -271,6 +292,24 @@ def main():
     ms_per_step = 1e3 * total_s / args.steps
     step_ms = sorted(a.elapsed_time(b) for a, b in step_ev)
     pct = lambda v, p: v[min(len(v) - 1, int(round(p * (len(v) - 1))))]
+
+    # hot cache: every step on the same copy, whose caches then stay in the 256 MB Infinity Cache when they fit
+    # (the timed steps above rotate copies so that each step reads them from HBM)
+    hot = None
+    if n_copies > 1 and per_copy < (256 << 20):
+        hot_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.steps)]
+        select(0)
+        attend(0)
+        for i in range(args.steps):
+            hot_ev[i][0].record(stream)
+            select(0)
+            attend(0)
+            hot_ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        hot_ms = sorted(a.elapsed_time(b) for a, b in hot_ev)[len(hot_ev) // 2]
+        hot = {"ms_per_step": round(hot_ms, 4), "value": round(wl.B / (hot_ms * 1e-3), 1), "unit": "queries/s",
+               "cache_bytes": per_copy}
 
     # ---------------- per-call and per-kernel HIP events on the launch stream -------------------------------------
     # entry points: one event before and one after each call; kernels: the library's stage events (which add a
@@ -426,7 +465,10 @@ def main():
         "stage_ms": {"select": round(t_sel * 1e3, 4), "attn": round(t_att * 1e3, 4)},
         "roofline": dominant, "roofline_other": other,
         "measured_copy_gbps": copy_gbps,
+        "measured_bf16_gemm_tflops": gemm_tflops,
     }
+    if hot:
+        res["hot_cache"] = hot
     if is_bucket:
         res["bucket_build_ms_per_cache"] = round(build_ms, 3)
         if is_tree:

@@ -65,7 +65,7 @@ __device__ __forceinline__ uint32_t find_digit(const uint32_t* hist, uint32_t ne
 // `hist` is 256 words of LDS private to this wave. Every lane must call it with the same n.
 // Every pass reads the buffer kBatchW entries per lane at a time, so the loads of a batch are in flight together;
 // the key passes cover only the bits below the prefix that every key shares.
-constexpr int kBatchW = 8;
+constexpr int kBatchW = 16;
 
 template <typename F>
 __device__ __forceinline__ void wave_batched(const Cand* buf, int n, int lane, F f) {
