@@ -134,17 +134,13 @@ __global__ __launch_bounds__(64 * NQ) void k_score_mfma(const void* __restrict__
   const char* kbytes = reinterpret_cast<const char*>(k);
   const int64_t ld_bytes = k_ld * (E4M3 ? 1 : 2);
 
-  // two separately summed 32-head groups keep the 32x32x16 fragments; every other mode scores through QueryFrags
-  bf16x8 qa[NMT][kSteps];
-  float wv[NMT][16];
   QueryFrags<NMT> qf;
   uint32_t thr = 0;
   int64_t tb = L - 1;
   if (active) {
     tb = t ? (int64_t)t[G2 ? 2 * b : b] : L - 1;
     if (mode == kScoreEmit && thr_key) thr = thr_key[b];
-    if constexpr (G2) load_query<NMT, E4M3>(q, w, b, lane, qa, wv);
-    else qf.template load<E4M3>(q, w, b, lane);
+    qf.template load<E4M3>(q, w, b, lane);
   }
   // no wait here: the query loads are older than every tile copy and loads complete in issue order, so the first
   // tile's wait (at most two tiles of copies outstanding) also covers them
@@ -162,7 +158,7 @@ __global__ __launch_bounds__(64 * NQ) void k_score_mfma(const void* __restrict__
     if constexpr (G2) {
       static_assert(NMT == 2, "two 32-head groups per 64-head query");
       if (s0 / page_len >= tb / page_len) return;  // only the blocks before the local one are ranked
-      const float2 sc = score_tile_groups(tile, lane, qa, wv);
+      const float2 sc = qf.score_groups(tile, lane);
       const bool in_range = s0 + lane < hi;
       const uint32_t k0 = wave_max_u32(in_range ? score_key(sc.x) : 0u);
       const uint32_t k1 = wave_max_u32(in_range ? score_key(sc.y) : 0u);

@@ -196,66 +196,6 @@ __device__ __forceinline__ float score_frags(FR&& frag, const bf16x8 (&qa)[NMT][
   return fold_halves(part0, part1);
 }
 
-// Two head groups of 32 heads (the two M-tiles of a 64-head query), each summed on its own: the same MFMAs and
-// schedule as score_frags<2>, with the ReLU-weighted head sum kept per tile. Lane l returns the two group scores of
-// position l of the tile.
-template <typename FR>
-__device__ __forceinline__ float2 score_frags_groups(FR&& frag, const bf16x8 (&qa)[2][kSteps],
-                                                    const float (&wv)[2][16]) {
-  constexpr int NMT = 2;
-  constexpr int kChunk = NMT * 16 / kSteps;
-  bf16x8 fr[kSteps];
-#pragma unroll
-  for (int ks = 0; ks < kSteps; ++ks) fr[ks] = frag(0, ks);
-  f32x16 acc0[NMT], acc1[NMT];
-#pragma unroll
-  for (int mt = 0; mt < NMT; ++mt) {
-    acc0[mt] = f32x16{};
-    acc1[mt] = f32x16{};
-  }
-#pragma unroll
-  for (int ks = 0; ks < kSteps; ++ks) {
-    const bf16x8 bk = fr[ks];
-    fr[ks] = frag(1, ks);
-#pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) acc0[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt][ks], bk, acc0[mt], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  float part0[NMT] = {0.f, 0.f};
-#pragma unroll
-  for (int ks = 0; ks < kSteps; ++ks) {
-#pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) acc1[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mt][ks], fr[ks], acc1[mt], 0, 0, 0);
-#pragma unroll
-    for (int e = 0; e < kChunk; ++e) {
-      const int idx = ks * kChunk + e;
-      part0[idx / 16] = fmaf(wv[idx / 16][idx % 16], relu(acc0[idx / 16][idx % 16]), part0[idx / 16]);
-    }
-  }
-#pragma unroll
-  for (int ks = 0; ks < kSteps; ++ks) {
-    __builtin_amdgcn_sched_group_barrier(0x008, NMT, 0);       // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x002, 2 * kChunk, 0);  // VALU
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  float part1[NMT] = {0.f, 0.f};
-#pragma unroll
-  for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) part1[mt] = fmaf(wv[mt][r], relu(acc1[mt][r]), part1[mt]);
-  return float2{fold_halves(part0[0], part1[0]), fold_halves(part0[1], part1[1])};
-}
-
-__device__ __forceinline__ float2 score_tile_groups(const char* tile, int lane, const bf16x8 (&qa)[2][kSteps],
-                                                   const float (&wv)[2][16]) {
-  const int hs = lane >> 5;
-  return score_frags_groups(
-      [&](int nt, int ks) {
-        return *reinterpret_cast<const bf16x8*>(tile + tile_off(32 * nt + (lane & 31), 2 * ks + hs));
-      },
-      qa, wv);
-}
-
 template <int NMT>
 __device__ __forceinline__ float score_tile(const char* tile, int lane, const bf16x8 (&qa)[NMT][kSteps],
                                            const float (&wv)[NMT][16]) {
@@ -305,8 +245,11 @@ __device__ __forceinline__ void load_query16(const void* q, const float* w, int6
 // The half-1 MFMAs are interleaved with the half-0 ReLU-weighted head sum (four MFMAs, then eight VALU
 // instructions, per fragment). Each lane sums its 16 heads of each N-tile; two lane exchanges then add the four
 // lane rows that hold the other heads of the same position.
-template <typename FR>
-__device__ __forceinline__ float score_frags16(FR&& frag, const bf16x8 (&qa)[4][kSteps16], const float (&wv)[4][4]) {
+// NG = 1: one sum over the 64 heads; NG = 2: the two 32-head groups (head tiles 0-1 and 2-3) summed on their own,
+// returned as (group 0, group 1).
+template <int NG, typename FR>
+__device__ __forceinline__ auto score_frags16(FR&& frag, const bf16x8 (&qa)[4][kSteps16], const float (&wv)[4][4]) {
+  static_assert(NG == 1 || NG == 2, "one or two head groups");
   bf16x8 fr[8];  // slot i = 4 n + ks: N-tile n of the half being multiplied, k-step ks
 #pragma unroll
   for (int i = 0; i < 8; ++i) fr[i] = frag(i >> 2, i & 3);
@@ -329,7 +272,11 @@ __device__ __forceinline__ float score_frags16(FR&& frag, const bf16x8 (&qa)[4][
     __builtin_amdgcn_sched_barrier(0);
   }
   // half 1, with the half-0 head sum in the MFMA shadow (32 products over the eight fragments)
-  float p[4] = {0.f, 0.f, 0.f, 0.f};  // this lane's head sums of N-tiles 0..3
+  float p[NG][4];  // this lane's head sums of N-tiles 0..3, per group
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int n = 0; n < 4; ++n) p[g][n] = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
 #pragma unroll
@@ -338,7 +285,8 @@ __device__ __forceinline__ float score_frags16(FR&& frag, const bf16x8 (&qa)[4][
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int idx = 4 * i + e, n = idx >> 4, mt = (idx >> 2) & 3, r = idx & 3;
-      p[n] = fmaf(wv[mt][r], relu(acc0[n][mt][r]), p[n]);
+      float& acc = p[mt * NG / 4][n];
+      acc = fmaf(wv[mt][r], relu(acc0[n][mt][r]), acc);
     }
   }
 #pragma unroll
@@ -352,17 +300,33 @@ __device__ __forceinline__ float score_frags16(FR&& frag, const bf16x8 (&qa)[4][
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) p[2 + n] = fmaf(wv[mt][r], relu(acc1[n][mt][r]), p[2 + n]);
+      for (int r = 0; r < 4; ++r) {
+        float& acc = p[mt * NG / 4][2 + n];
+        acc = fmaf(wv[mt][r], relu(acc1[n][mt][r]), acc);
+      }
   // lanes l and l ^ 32 hold heads of rows {0, 2} and {1, 3} of the same positions: the first exchange leaves
   // N-tiles 0 and 1 in lanes 0..31 and N-tiles 2 and 3 in lanes 32..63 (rows 0 + 2 or 1 + 3 added); the second
-  // adds rows l and l ^ 16, so that lane l holds all 64 heads of position l
-  return fold_rows(fold_halves(p[0], p[2]), fold_halves(p[1], p[3]));
+  // adds rows l and l ^ 16, so that lane l holds all the group's heads of position l
+  auto fold = [&](const float (&q)[4]) { return fold_rows(fold_halves(q[0], q[2]), fold_halves(q[1], q[3])); };
+  if constexpr (NG == 1) return fold(p[0]);
+  else return float2{fold(p[0]), fold(p[1])};
 }
 
 __device__ __forceinline__ float score_tile16(const char* tile, int lane, const bf16x8 (&qa)[4][kSteps16],
                                               const float (&wv)[4][4]) {
   const int row = lane >> 4;
-  return score_frags16(
+  return score_frags16<1>(
+      [&](int nt, int ks) {
+        return *reinterpret_cast<const bf16x8*>(tile + tile_off(16 * nt + (lane & 15), 4 * ks + row));
+      },
+      qa, wv);
+}
+
+// The two 32-head groups of a 64-head query, summed on their own: lane l returns (group 0, group 1) of position l.
+__device__ __forceinline__ float2 score_tile16_groups(const char* tile, int lane, const bf16x8 (&qa)[4][kSteps16],
+                                                      const float (&wv)[4][4]) {
+  const int row = lane >> 4;
+  return score_frags16<2>(
       [&](int nt, int ks) {
         return *reinterpret_cast<const bf16x8*>(tile + tile_off(16 * nt + (lane & 15), 4 * ks + row));
       },
@@ -390,6 +354,9 @@ struct QueryFrags<2> {
     load_query16<E4M3>(q, w, b, lane, qa, wv);
   }
   __device__ __forceinline__ float score(const char* tile, int lane) const { return score_tile16(tile, lane, qa, wv); }
+  __device__ __forceinline__ float2 score_groups(const char* tile, int lane) const {
+    return score_tile16_groups(tile, lane, qa, wv);
+  }
 };
 
 // The B fragments of the 64-position tile at s0 straight from global memory into registers (rows past L - 1 are
