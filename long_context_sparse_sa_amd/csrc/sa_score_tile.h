@@ -211,8 +211,8 @@ __device__ __forceinline__ float score_tile(const char* tile, int lane, const bf
 // The same scores for 64 heads with four M-tiles of 16 heads, four N-tiles of 16 positions and four k-steps of 32
 // dims: as many MFMA flops and LDS fragment bytes per tile, a quarter of the accumulator registers per instruction,
 // and half the head-weight registers. On random bf16 operands this shape sustains a higher issue rate than the
-// 32x32x16 one (a loop of each, two waves per SIMD: about 0.8 against 0.65 of the peak), and the scorer loop with
-// its ReLU-weighted head sum and LDS fragment reads goes from about 0.60 to 0.69.
+// 32x32x16 one (a loop of each on random operands, two waves per SIMD: 0.76-0.79 against 0.62-0.70 of the peak),
+// and the scorer loop with its ReLU-weighted head sum and LDS fragment reads goes from about 0.56 to 0.60.
 //
 // Operands: A (queries) lane l holds head 16 mt + l % 16, dims 32 ks + 8 (l / 16) .. + 7; B (keys) lane l holds
 // position 16 nt + l % 16, the same dims; the accumulator of (mt, nt) holds, in lane l, position 16 nt + l % 16
