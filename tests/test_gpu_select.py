@@ -60,7 +60,8 @@ ALGOS = [sa.SA_TOPK_SPLIT_L, sa.SA_TOPK_PER_QUERY, sa.SA_TOPK_RADIX, sa.SA_TOPK_
 @pytest.mark.parametrize("B", [6, 9])
 def test_topk_integer_exact_with_ties(algo, dtype, B):
     """Integer-valued q, k in {-2..2} and w in {0,1,2}: scores are exact, selection must match bit for bit.
-    B = 6 runs 4-query workgroups, B = 9 runs 8-query workgroups with a partly empty second group."""
+    B = 6 runs 4-query workgroups; B = 9 runs 8-query workgroups with a partly empty second group in the dense and
+    emitting scorer, and three 4-query workgroups (the last partly empty) in the streaming select."""
     H, d, L, kk = 64, 128, 40000, 700
     q, w, k = _inputs(5, B, H, d, L, dtype, integer=True)
     ts = ([L - 1, 39000, 20000, 17000, 5000, 900, 33333, 123, 39999])[:B]
@@ -74,6 +75,22 @@ def test_topk_integer_exact_with_ties(algo, dtype, B):
             assert np.unique(sc).size < sc.size / 4        # heavy ties are really exercised
         got = selected(idx[b], nsel[b].item())
         np.testing.assert_array_equal(got, ref)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "e4m3"])
+def test_topk_stream_eight_query_groups(dtype):
+    """The streaming select takes 8-query workgroups from 32 queries up: B = 33 leaves one query in the last group.
+    Integer inputs, exact scores, bit-exact selection."""
+    B, H, d, L, kk = 33, 64, 128, 6000, 300
+    q, w, k = _inputs(21, B, H, d, L, dtype, integer=True)
+    ts = [L - 1 - 97 * b for b in range(B)]
+    t = torch.tensor(ts, dtype=torch.int32, device=DEV)
+    idx, nsel = sa.sa_select_topk(q, w, k, kk, n_sink=2, n_window=30, t=t, algo=sa.SA_TOPK_STREAM)
+    torch.cuda.synchronize()
+    qf, wf, kf = to_f64(q), w.double().cpu().numpy(), to_f64(k)
+    for b in range(B):
+        ref, sc, cand = O.select_topk(qf[b], wf[b], kf, ts[b], kk, 2, 30)
+        np.testing.assert_array_equal(selected(idx[b], nsel[b].item()), ref)
 
 
 @pytest.mark.parametrize("algo", ALGOS)
